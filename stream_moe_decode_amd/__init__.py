@@ -1,0 +1,164 @@
+"""Python binding of the MI355X decode library (``libflint.so``, C ABI in ``include/flint.h``).
+
+Argument marshalling only: every step of the decode path runs in the library's
+HIP kernels.  PyTorch is used by callers for device memory and streams; this
+module passes raw device pointers (``tensor.data_ptr()``) and the HIP stream
+handle through.  Importing the module does not load the library; the first
+call does, and raises if ``libflint.so`` has not been built (there is no
+fallback path).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libflint.so")
+
+OK, EINVAL, ENOMEM, EHIP, ECAPACITY, ETIMEOUT, ENORESIDENT, EDEVICE = range(8)
+W_F32, W_BF16, W_INT4G64 = 0, 1, 2
+STATUS_NAMES = {0: "FLINT_OK", 1: "FLINT_EINVAL", 2: "FLINT_ENOMEM", 3: "FLINT_EHIP", 4: "FLINT_ECAPACITY",
+                5: "FLINT_ETIMEOUT", 6: "FLINT_ENORESIDENT", 7: "FLINT_EDEVICE"}
+
+# every symbol include/flint.h declares
+EXPORTS = ("flint_decode_init", "flint_decode_free", "flint_kv_alloc", "flint_kv_free", "flint_kv_set_lengths",
+           "flint_kv_get_lengths", "flint_kv_layer_ptrs", "flint_decode_step", "flint_decode_step_debug",
+           "flint_prefill_chunk", "flint_sync", "flint_device_info", "flint_last_error")
+
+
+class FlintError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(f"{STATUS_NAMES.get(status, status)}: {msg}")
+        self.status = status
+
+
+class Config(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in (
+        "n_layers", "n_dense_layers", "hidden", "n_q_heads", "n_kv_heads", "head_dim", "vocab", "dense_inter",
+        "n_experts", "top_k", "expert_inter", "weight_type", "router_renorm", "grid")] + [
+        ("rope_theta", ctypes.c_float), ("rms_eps", ctypes.c_float)]
+
+
+class Mat(ctypes.Structure):
+    _fields_ = [("w", ctypes.c_void_p), ("scales", ctypes.c_void_p)]
+
+
+class Weights(ctypes.Structure):
+    _fields_ = [("embed", ctypes.c_void_p), ("lm_head", ctypes.c_void_p), ("final_norm", ctypes.c_void_p),
+                ("attn_norm", ctypes.c_void_p), ("post_norm", ctypes.c_void_p)] + [
+        (n, Mat) for n in ("qkv", "o", "dense_gate", "dense_up", "dense_down", "router", "exp_gate", "exp_up",
+                           "exp_down")]
+
+
+class Debug(ctypes.Structure):
+    _fields_ = [("logits", ctypes.c_void_p), ("routes", ctypes.c_void_p), ("route_w", ctypes.c_void_p),
+                ("resid", ctypes.c_void_p), ("resid_layer", ctypes.c_int32), ("pad", ctypes.c_int32),
+                ("phase_ts", ctypes.c_void_p)]
+
+
+_lib = None
+
+
+def lib():
+    """Load libflint.so (raises if it is missing: there is no fallback)."""
+    global _lib
+    if _lib is None:
+        try:  # bind to the HIP runtime torch ships, so the process has exactly one
+            import torch  # noqa: F401
+        except ImportError:
+            pass
+        if not os.path.exists(LIB_PATH):
+            raise FileNotFoundError(f"{LIB_PATH} is not built; run __graft_entry__.build()")
+        L = ctypes.CDLL(LIB_PATH)
+        vp, i32, P = ctypes.c_void_p, ctypes.c_int32, ctypes.POINTER
+        sig = {
+            "flint_decode_init": [P(Config), P(Weights), vp, P(vp)],
+            "flint_decode_free": [vp],
+            "flint_kv_alloc": [vp, i32, i32, P(vp)],
+            "flint_kv_free": [vp],
+            "flint_kv_set_lengths": [vp, vp],
+            "flint_kv_get_lengths": [vp, vp],
+            "flint_kv_layer_ptrs": [vp, i32, P(vp), P(vp)],
+            "flint_decode_step": [vp, vp, vp, vp],
+            "flint_decode_step_debug": [vp, vp, vp, vp, P(Debug)],
+            "flint_prefill_chunk": [vp, vp, i32, vp, i32, vp],
+            "flint_sync": [vp],
+            "flint_device_info": [vp, P(i32), P(i32), P(i32)],
+        }
+        for name, args in sig.items():
+            f = getattr(L, name)
+            f.argtypes = args
+            f.restype = ctypes.c_int
+        L.flint_last_error.argtypes = []
+        L.flint_last_error.restype = ctypes.c_char_p
+        _lib = L
+    return _lib
+
+
+def _check(rc: int):
+    if rc != OK:
+        raise FlintError(rc, lib().flint_last_error().decode())
+
+
+def last_error() -> str:
+    return lib().flint_last_error().decode()
+
+
+def decode_init(cfg: Config, weights: Weights, stream: int = 0) -> int:
+    ctx = ctypes.c_void_p()
+    _check(lib().flint_decode_init(ctypes.byref(cfg), ctypes.byref(weights), ctypes.c_void_p(stream),
+                                   ctypes.byref(ctx)))
+    return ctx.value
+
+
+def decode_free(ctx: int):
+    _check(lib().flint_decode_free(ctx))
+
+
+def kv_alloc(ctx: int, batch: int, max_tokens: int) -> int:
+    kv = ctypes.c_void_p()
+    _check(lib().flint_kv_alloc(ctx, batch, max_tokens, ctypes.byref(kv)))
+    return kv.value
+
+
+def kv_free(kv: int):
+    _check(lib().flint_kv_free(kv))
+
+
+def kv_set_lengths(kv: int, lengths):
+    arr = (ctypes.c_int32 * len(lengths))(*lengths)
+    _check(lib().flint_kv_set_lengths(kv, ctypes.cast(arr, ctypes.c_void_p)))
+
+
+def kv_get_lengths(kv: int, batch: int):
+    arr = (ctypes.c_int32 * batch)()
+    _check(lib().flint_kv_get_lengths(kv, ctypes.cast(arr, ctypes.c_void_p)))
+    return list(arr)
+
+
+def kv_layer_ptrs(kv: int, layer: int):
+    k, v = ctypes.c_void_p(), ctypes.c_void_p()
+    _check(lib().flint_kv_layer_ptrs(kv, layer, ctypes.byref(k), ctypes.byref(v)))
+    return k.value, v.value
+
+
+def decode_step(ctx: int, tokens_ptr: int, kv: int, out_ptr: int):
+    _check(lib().flint_decode_step(ctx, tokens_ptr, kv, out_ptr))
+
+
+def decode_step_debug(ctx: int, tokens_ptr: int, kv: int, out_ptr: int, dbg: Debug | None):
+    _check(lib().flint_decode_step_debug(ctx, tokens_ptr, kv, out_ptr, ctypes.byref(dbg) if dbg is not None else None))
+
+
+def prefill_chunk(ctx: int, kv: int, seq: int, tokens_ptr: int, n: int, out_ptr: int):
+    _check(lib().flint_prefill_chunk(ctx, kv, seq, tokens_ptr, n, out_ptr))
+
+
+def sync(ctx: int):
+    _check(lib().flint_sync(ctx))
+
+
+def device_info(ctx: int):
+    g, b, l = ctypes.c_int32(), ctypes.c_int32(), ctypes.c_int32()
+    _check(lib().flint_device_info(ctx, ctypes.byref(g), ctypes.byref(b), ctypes.byref(l)))
+    return g.value, b.value, l.value

@@ -1,0 +1,86 @@
+// Internal interface between the host runtime and the persistent decode kernel.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace flint {
+
+constexpr int NT = 256;                 // threads per workgroup (4 waves of 64)
+constexpr int NW = NT / 64;             // waves per workgroup
+constexpr int MAX_H = 2048;             // residual width
+constexpr int MAX_QD = 2048;            // n_q_heads * head_dim
+constexpr int MAX_HBUF = 6144;          // dense_inter, or top_k * expert_inter
+constexpr int MAX_E = 64;               // experts (top-k runs inside one wave)
+constexpr int MAX_K = 8;                // top_k
+constexpr int MAX_GQ = 8;               // query heads per kv head
+constexpr int MAX_HD = 128;             // head_dim
+constexpr int MAX_P = 512;              // attention positions scored per chunk
+constexpr int MAX_YROWS = 1024;         // GEMV results a workgroup keeps per phase
+constexpr int MAX_GATHER = 4096;        // 32-bit words of the merge gather buffer
+constexpr int NCOPY = 8;                // replicas of broadcast exchanges (one per XCD)
+constexpr int TAGS_PER_LAUNCH = 1024;   // exchange tags one launch may use
+constexpr uint64_t SPIN_TIMEOUT = 100000000ull;  // 1 s of the 100 MHz wall clock
+
+enum { W_F32 = 0, W_BF16 = 1, W_I4 = 2 };
+enum { ERR_TIMEOUT = 1u, ERR_TOKEN = 2u, ERR_POS = 4u };
+
+struct Mat {
+  const uint8_t* w;      // row-major [rows][in] (fp32 / bf16) or int4 codes [rows][in/2]
+  const uint16_t* s;     // int4 only: bf16 scales [rows][in/64]
+};
+
+struct KArgs {
+  // model dimensions
+  int H, nq, nkv, hd, V, L, n_dense, DI, E, K, EI, renorm;
+  float eps;
+  int S;                 // attention splits per kv head (grid / n_kv_heads)
+  // weights (library-owned, canonical layout)
+  const uint8_t* embed;
+  const uint8_t* lmhead;
+  const float* fnorm;
+  const float* anorm;
+  const float* pnorm;
+  Mat qkv, o, dg, du, dd, router, eg, eu, ed;
+  // KV cache [L][B][nkv][cap][hd] in the activation type
+  uint8_t* kc;
+  uint8_t* vc;
+  int B, cap;
+  const float2* rope;    // [cap][hd/2] (cos, sin)
+  int32_t* len;          // [B] device lengths
+  // this launch
+  const int32_t* tokens;
+  int tok_idx, seq;
+  int32_t* out_ids;
+  int out_idx;
+  uint32_t epoch;
+  // scratch
+  uint64_t* x_qkv;       // [NCOPY][2][qkv_rows]            q/k/v after RoPE (fp32)
+  uint64_t* x_part;      // [2][nq][hd + 2][S]              attention partials (fp32)
+  uint64_t* x_o;         // [NCOPY][2][o_slots]             merged attention output
+  uint64_t* x_res1;      // [NCOPY][2][H]                   residual after o_proj (fp32)
+  uint64_t* x_h;         // [NCOPY][2][h_slots]             SwiGLU output
+  uint64_t* x_res2;      // [NCOPY][2][H]                   residual after the MLP (fp32)
+  int qkv_rows, o_slots, h_slots;
+  uint32_t* err;         // device error word
+  uint32_t* herr;        // host-mapped error word
+  unsigned long long* amax;  // packed argmax key
+  uint32_t* done;        // workgroups finished with lm_head
+  // optional outputs
+  float* dbg_logits;
+  int32_t* dbg_routes;
+  float* dbg_rw;
+  float* dbg_resid;
+  int dbg_resid_layer;
+  uint64_t* dbg_ts;
+};
+
+// Launch the persistent kernel for weight type wt on `stream`.
+hipError_t launch_decode(int wt, const KArgs& a, int grid, hipStream_t stream);
+// Zero `n` 64-bit words with a fill kernel.
+hipError_t launch_fill(uint64_t* p, size_t n, hipStream_t stream);
+// Static LDS bytes of the persistent kernel.
+int kernel_lds_bytes(int wt);
+// Co-resident workgroups per CU of the persistent kernel.
+hipError_t kernel_occupancy(int wt, int* per_cu);
+
+}  // namespace flint

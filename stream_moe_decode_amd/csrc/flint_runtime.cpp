@@ -1,0 +1,488 @@
+// Host runtime behind the C ABI of include/flint.h: argument checks, the
+// library-owned copies of the weights, the KV cache, the RoPE table (computed
+// in double), the kernel's scratch, and one persistent-kernel launch per
+// sequence and step.
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <new>
+#include <string>
+#include <vector>
+
+#include "../../include/flint.h"
+#include "flint_internal.h"
+
+using namespace flint;
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return code;
+}
+
+#define HIPCHECK(x)                                                                              \
+  do {                                                                                           \
+    hipError_t e_ = (x);                                                                         \
+    if (e_ != hipSuccess) return fail(FLINT_EHIP, "%s failed: %s", #x, hipGetErrorString(e_)); \
+  } while (0)
+
+size_t elem_bytes_act(int wt) { return wt == FLINT_W_F32 ? 4 : 2; }
+
+// Bytes of a [rows][in] matrix in the layer weight format (codes only for int4).
+size_t mat_bytes(int wt, size_t rows, size_t in) {
+  return wt == FLINT_W_F32 ? rows * in * 4 : (wt == FLINT_W_BF16 ? rows * in * 2 : rows * in / 2);
+}
+size_t scale_bytes(int wt, size_t rows, size_t in) { return wt == FLINT_W_INT4G64 ? rows * (in / 64) * 2 : 0; }
+
+}  // namespace
+
+struct flint_ctx {
+  flint_config cfg;
+  hipStream_t stream;
+  int device;
+  int grid;
+  int S;
+  std::vector<void*> allocs;  // library-owned device memory
+  KArgs base;                 // weights and scratch filled in; per-launch fields set at launch
+  uint32_t* herr_host;        // host-mapped error word
+  uint64_t* xbuf;
+  size_t xbuf_words;
+  uint64_t launches;
+  int live_kv;
+};
+
+struct flint_kv {
+  flint_ctx* ctx;
+  int batch, max_tokens;
+  void* k;
+  void* v;
+  int32_t* len;
+  float* rope;
+  std::vector<int32_t> hlen;
+};
+
+namespace {
+
+int dalloc(flint_ctx* c, void** p, size_t bytes) {
+  *p = nullptr;
+  if (bytes == 0) return FLINT_OK;
+  hipError_t e = hipMalloc(p, bytes);
+  if (e != hipSuccess) return fail(FLINT_ENOMEM, "hipMalloc(%zu bytes): %s", bytes, hipGetErrorString(e));
+  c->allocs.push_back(*p);
+  return FLINT_OK;
+}
+
+void release(flint_ctx* c) {
+  for (void* p : c->allocs) (void)hipFree(p);
+  c->allocs.clear();
+  if (c->herr_host) (void)hipHostFree(c->herr_host);
+  c->herr_host = nullptr;
+}
+
+int check_config(const flint_config* c) {
+  if (!c) return fail(FLINT_EINVAL, "cfg is NULL");
+  if (c->weight_type < FLINT_W_F32 || c->weight_type > FLINT_W_INT4G64)
+    return fail(FLINT_EINVAL, "weight_type %d unknown", c->weight_type);
+  if (c->n_layers < 1 || c->n_layers > 120) return fail(FLINT_EINVAL, "n_layers %d not in [1, 120]", c->n_layers);
+  if (c->n_dense_layers < 0 || c->n_dense_layers > c->n_layers)
+    return fail(FLINT_EINVAL, "n_dense_layers %d not in [0, n_layers]", c->n_dense_layers);
+  if (c->hidden < 64 || c->hidden > MAX_H || c->hidden % 64)
+    return fail(FLINT_EINVAL, "hidden %d must be a multiple of 64 in [64, %d]", c->hidden, MAX_H);
+  if (c->head_dim != 64 && c->head_dim != 128) return fail(FLINT_EINVAL, "head_dim %d must be 64 or 128", c->head_dim);
+  if (c->n_kv_heads < 1 || c->n_q_heads < c->n_kv_heads || c->n_q_heads % c->n_kv_heads ||
+      c->n_q_heads / c->n_kv_heads > MAX_GQ)
+    return fail(FLINT_EINVAL, "n_q_heads %d / n_kv_heads %d: need a divisor ratio <= %d", c->n_q_heads, c->n_kv_heads,
+                MAX_GQ);
+  if (c->n_q_heads * c->head_dim > MAX_QD)
+    return fail(FLINT_EINVAL, "n_q_heads * head_dim = %d exceeds %d", c->n_q_heads * c->head_dim, MAX_QD);
+  if (c->vocab < 1) return fail(FLINT_EINVAL, "vocab %d", c->vocab);
+  if (c->n_dense_layers > 0 && (c->dense_inter < 64 || c->dense_inter % 64 || c->dense_inter > MAX_HBUF))
+    return fail(FLINT_EINVAL, "dense_inter %d must be a multiple of 64 in [64, %d]", c->dense_inter, MAX_HBUF);
+  if (c->n_dense_layers < c->n_layers) {
+    if (c->n_experts < 1 || c->n_experts > MAX_E) return fail(FLINT_EINVAL, "n_experts %d not in [1, %d]", c->n_experts, MAX_E);
+    if (c->top_k < 1 || c->top_k > MAX_K || c->top_k > c->n_experts)
+      return fail(FLINT_EINVAL, "top_k %d not in [1, min(%d, n_experts)]", c->top_k, MAX_K);
+    if (c->expert_inter < 64 || c->expert_inter % 64 || c->top_k * c->expert_inter > MAX_HBUF)
+      return fail(FLINT_EINVAL, "expert_inter %d must be a multiple of 64 with top_k * expert_inter <= %d",
+                  c->expert_inter, MAX_HBUF);
+  }
+  if (!(c->rms_eps >= 0.f) || !(c->rope_theta > 0.f)) return fail(FLINT_EINVAL, "rms_eps / rope_theta invalid");
+  if (c->router_renorm != 0 && c->router_renorm != 1) return fail(FLINT_EINVAL, "router_renorm must be 0 or 1");
+  if (c->grid < 0) return fail(FLINT_EINVAL, "grid %d < 0", c->grid);
+  return FLINT_OK;
+}
+
+// Per-phase sizes a workgroup keeps in LDS for grid G.
+int check_grid(const flint_config* c, int G) {
+  auto ceil_div = [](long a, long b) { return (a + b - 1) / b; };
+  const int hd = c->head_dim, QD = c->n_q_heads * hd;
+  if (G < c->n_kv_heads) return fail(FLINT_EINVAL, "grid %d smaller than n_kv_heads", G);
+  const int S = G / c->n_kv_heads;
+  long need = 2 * ceil_div((c->n_q_heads + 2 * c->n_kv_heads) * hd / 2, G);
+  if (c->n_dense_layers > 0) need = std::max(need, 4 * ceil_div(c->dense_inter / 2, G));
+  if (c->n_dense_layers < c->n_layers) {
+    need = std::max(need, 4 * ceil_div(c->top_k * c->expert_inter / 2, G));
+    need = std::max(need, (long)c->top_k * ceil_div(c->hidden, G));
+  }
+  need = std::max(need, ceil_div(c->hidden, G));
+  if (need > MAX_YROWS) return fail(FLINT_EINVAL, "grid %d too small: %ld rows per workgroup > %d", G, need, MAX_YROWS);
+  long ne = std::min<long>(hd, 2 * ceil_div(QD / 2, G));
+  if ((2 + ne) * S > MAX_GATHER)
+    return fail(FLINT_EINVAL, "grid %d: attention merge needs %ld words > %d", G, (2 + ne) * S, MAX_GATHER);
+  return FLINT_OK;
+}
+
+int copy_in(flint_ctx* c, const void* src, size_t bytes, const uint8_t** dst, const char* what) {
+  if (bytes == 0) {
+    *dst = nullptr;
+    return FLINT_OK;
+  }
+  if (!src) return fail(FLINT_EINVAL, "weights.%s is NULL", what);
+  void* p;
+  int rc = dalloc(c, &p, bytes);
+  if (rc) return rc;
+  HIPCHECK(hipMemcpyAsync(p, src, bytes, hipMemcpyDeviceToDevice, c->stream));
+  *dst = (const uint8_t*)p;
+  return FLINT_OK;
+}
+
+int copy_mat(flint_ctx* c, const flint_mat& m, size_t count, size_t rows, size_t in, Mat* out, const char* what) {
+  const int wt = c->cfg.weight_type;
+  int rc = copy_in(c, m.w, count * mat_bytes(wt, rows, in), &out->w, what);
+  if (rc) return rc;
+  out->s = nullptr;
+  if (wt == FLINT_W_INT4G64 && count) {
+    const uint8_t* s;
+    if (!m.scales) return fail(FLINT_EINVAL, "weights.%s.scales is NULL", what);
+    rc = copy_in(c, m.scales, count * scale_bytes(wt, rows, in), &s, what);
+    if (rc) return rc;
+    out->s = (const uint16_t*)s;
+  }
+  return FLINT_OK;
+}
+
+int latched_error(flint_ctx* c) {
+  uint32_t e = __atomic_load_n(c->herr_host, __ATOMIC_ACQUIRE);
+  if (!e) return FLINT_OK;
+  // clear the device and host words so the error is reported once; the kernel
+  // always completes its argmax hand-off, so no other state needs repair
+  __atomic_store_n(c->herr_host, 0u, __ATOMIC_RELEASE);
+  (void)hipMemsetAsync(c->base.err, 0, sizeof(uint32_t), c->stream);
+  if (e & ERR_TIMEOUT) return fail(FLINT_ETIMEOUT, "a cross-workgroup wait timed out in an earlier step");
+  if (e & ERR_TOKEN) return fail(FLINT_EDEVICE, "an earlier step read a token id outside [0, vocab)");
+  return fail(FLINT_EDEVICE, "an earlier step found a device length outside [0, max_tokens)");
+}
+
+int launch(flint_ctx* c, flint_kv* kv, const int32_t* tokens, int tok_idx, int seq, int32_t* out, int out_idx,
+           const flint_debug* dbg) {
+  if (c->launches > 0 && c->launches % (1ull << 22) == 0) {
+    // tags restart: clear every exchange slot so no stale tag can match
+    HIPCHECK(launch_fill(c->xbuf, c->xbuf_words, c->stream));
+  }
+  KArgs a = c->base;
+  a.kc = (uint8_t*)kv->k;
+  a.vc = (uint8_t*)kv->v;
+  a.B = kv->batch;
+  a.cap = kv->max_tokens;
+  a.rope = (const float2*)kv->rope;
+  a.len = kv->len;
+  a.tokens = tokens;
+  a.tok_idx = tok_idx;
+  a.seq = seq;
+  a.out_ids = out;
+  a.out_idx = out_idx;
+  a.epoch = 1u + (uint32_t)(c->launches % (1ull << 22)) * (uint32_t)TAGS_PER_LAUNCH;
+  if (dbg) {
+    const int H = c->cfg.hidden, V = c->cfg.vocab, L = c->cfg.n_layers, K = c->cfg.top_k;
+    a.dbg_logits = dbg->logits ? dbg->logits + (size_t)seq * V : nullptr;
+    a.dbg_routes = dbg->routes ? dbg->routes + (size_t)seq * L * K : nullptr;
+    a.dbg_rw = dbg->route_w ? dbg->route_w + (size_t)seq * L * K : nullptr;
+    a.dbg_resid = dbg->resid ? dbg->resid + (size_t)seq * H : nullptr;
+    a.dbg_resid_layer = dbg->resid_layer;
+    a.dbg_ts = seq == 0 ? dbg->phase_ts : nullptr;
+  }
+  HIPCHECK(launch_decode(c->cfg.weight_type, a, c->grid, c->stream));
+  c->launches++;
+  return FLINT_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* flint_last_error(void) { return g_last_error.c_str(); }
+
+int flint_decode_init(const flint_config* cfg, const flint_weights* w, void* hip_stream, flint_ctx** out) {
+  if (!out) return fail(FLINT_EINVAL, "out is NULL");
+  *out = nullptr;
+  int rc = check_config(cfg);
+  if (rc) return rc;
+  if (!w) return fail(FLINT_EINVAL, "weights is NULL");
+  flint_ctx* c = new (std::nothrow) flint_ctx();
+  if (!c) return fail(FLINT_ENOMEM, "host allocation failed");
+  c->cfg = *cfg;
+  c->stream = (hipStream_t)hip_stream;
+  c->herr_host = nullptr;
+  auto bail = [&](int code) {
+    release(c);
+    delete c;
+    return code;
+  };
+  if (hipGetDevice(&c->device) != hipSuccess) return bail(fail(FLINT_EHIP, "hipGetDevice failed"));
+  hipDeviceProp_t prop;
+  if (hipGetDeviceProperties(&prop, c->device) != hipSuccess) return bail(fail(FLINT_EHIP, "hipGetDeviceProperties failed"));
+  int per_cu = 0;
+  if (kernel_occupancy(cfg->weight_type, &per_cu) != hipSuccess) return bail(fail(FLINT_EHIP, "occupancy query failed"));
+  const int resident = per_cu * prop.multiProcessorCount;
+  c->grid = cfg->grid ? cfg->grid : prop.multiProcessorCount;
+  if (c->grid > resident)
+    return bail(fail(FLINT_ENORESIDENT, "grid %d exceeds the %d workgroups that can be co-resident", c->grid, resident));
+  if ((rc = check_grid(cfg, c->grid))) return bail(rc);
+  c->S = c->grid / cfg->n_kv_heads;
+
+  const int wt = cfg->weight_type;
+  const size_t L = cfg->n_layers, ND = cfg->n_dense_layers, NM = L - ND, H = cfg->hidden, V = cfg->vocab;
+  const size_t hd = cfg->head_dim, QR = (cfg->n_q_heads + 2 * cfg->n_kv_heads) * hd, QD = cfg->n_q_heads * hd;
+  const size_t DI = cfg->dense_inter, E = cfg->n_experts, EI = cfg->expert_inter;
+  KArgs& a = c->base;
+  memset(&a, 0, sizeof a);
+  a.H = (int)H;
+  a.nq = cfg->n_q_heads;
+  a.nkv = cfg->n_kv_heads;
+  a.hd = (int)hd;
+  a.V = (int)V;
+  a.L = (int)L;
+  a.n_dense = (int)ND;
+  a.DI = (int)DI;
+  a.E = NM ? (int)E : 0;
+  a.K = cfg->top_k;
+  a.EI = (int)EI;
+  a.renorm = cfg->router_renorm;
+  a.eps = cfg->rms_eps;
+  a.S = c->S;
+
+  const size_t eb = elem_bytes_act(wt);
+  if ((rc = copy_in(c, w->embed, V * H * eb, &a.embed, "embed"))) return bail(rc);
+  if ((rc = copy_in(c, w->lm_head, V * H * eb, &a.lmhead, "lm_head"))) return bail(rc);
+  const uint8_t* p;
+  if ((rc = copy_in(c, w->final_norm, H * 4, &p, "final_norm"))) return bail(rc);
+  a.fnorm = (const float*)p;
+  if ((rc = copy_in(c, w->attn_norm, L * H * 4, &p, "attn_norm"))) return bail(rc);
+  a.anorm = (const float*)p;
+  if ((rc = copy_in(c, w->post_norm, L * H * 4, &p, "post_norm"))) return bail(rc);
+  a.pnorm = (const float*)p;
+  if ((rc = copy_mat(c, w->qkv, L, QR, H, &a.qkv, "qkv"))) return bail(rc);
+  if ((rc = copy_mat(c, w->o, L, H, QD, &a.o, "o"))) return bail(rc);
+  if ((rc = copy_mat(c, w->dense_gate, ND, DI, H, &a.dg, "dense_gate"))) return bail(rc);
+  if ((rc = copy_mat(c, w->dense_up, ND, DI, H, &a.du, "dense_up"))) return bail(rc);
+  if ((rc = copy_mat(c, w->dense_down, ND, H, DI, &a.dd, "dense_down"))) return bail(rc);
+  if ((rc = copy_mat(c, w->router, NM, E, H, &a.router, "router"))) return bail(rc);
+  if ((rc = copy_mat(c, w->exp_gate, NM * E, EI, H, &a.eg, "exp_gate"))) return bail(rc);
+  if ((rc = copy_mat(c, w->exp_up, NM * E, EI, H, &a.eu, "exp_up"))) return bail(rc);
+  if ((rc = copy_mat(c, w->exp_down, NM * E, H, EI, &a.ed, "exp_down"))) return bail(rc);
+
+  // scratch: tagged exchange slots
+  const bool act32 = wt == FLINT_W_F32;
+  a.qkv_rows = (int)QR;
+  a.o_slots = (int)(act32 ? QD : QD / 2);
+  size_t hmax = std::max(ND ? DI : 0, NM ? (size_t)cfg->top_k * EI : 0);
+  a.h_slots = (int)std::max<size_t>(1, act32 ? hmax : hmax / 2);
+  const size_t n_qkv = NCOPY * 2 * QR, n_part = 2 * (size_t)cfg->n_q_heads * (hd + 2) * c->S;
+  const size_t n_o = NCOPY * 2 * (size_t)a.o_slots, n_res = NCOPY * 2 * H, n_h = NCOPY * 2 * (size_t)a.h_slots;
+  c->xbuf_words = n_qkv + n_part + n_o + 2 * n_res + n_h;
+  void* xb;
+  if ((rc = dalloc(c, &xb, c->xbuf_words * 8 + 256))) return bail(rc);
+  c->xbuf = (uint64_t*)xb;
+  a.x_qkv = c->xbuf;
+  a.x_part = a.x_qkv + n_qkv;
+  a.x_o = a.x_part + n_part;
+  a.x_res1 = a.x_o + n_o;
+  a.x_h = a.x_res1 + n_res;
+  a.x_res2 = a.x_h + n_h;
+  void* misc;
+  if ((rc = dalloc(c, &misc, 256))) return bail(rc);
+  a.err = (uint32_t*)misc;
+  a.done = (uint32_t*)((char*)misc + 64);
+  a.amax = (unsigned long long*)((char*)misc + 128);
+  if (hipHostMalloc((void**)&c->herr_host, 64, hipHostMallocMapped) != hipSuccess)
+    return bail(fail(FLINT_ENOMEM, "hipHostMalloc of the error word failed"));
+  *c->herr_host = 0;
+  void* herr_dev = nullptr;
+  if (hipHostGetDevicePointer(&herr_dev, c->herr_host, 0) != hipSuccess)
+    return bail(fail(FLINT_EHIP, "hipHostGetDevicePointer failed"));
+  a.herr = (uint32_t*)herr_dev;
+  if (launch_fill(c->xbuf, c->xbuf_words, c->stream) != hipSuccess) return bail(fail(FLINT_EHIP, "fill kernel failed"));
+  if (hipMemsetAsync(misc, 0, 256, c->stream) != hipSuccess) return bail(fail(FLINT_EHIP, "hipMemsetAsync failed"));
+  if (hipStreamSynchronize(c->stream) != hipSuccess) return bail(fail(FLINT_EHIP, "hipStreamSynchronize failed"));
+  c->launches = 0;
+  c->live_kv = 0;
+  *out = c;
+  return FLINT_OK;
+}
+
+int flint_decode_free(flint_ctx* c) {
+  if (!c) return FLINT_OK;
+  if (c->live_kv) return fail(FLINT_EINVAL, "free the %d flint_kv of this ctx first", c->live_kv);
+  (void)hipStreamSynchronize(c->stream);
+  release(c);
+  delete c;
+  return FLINT_OK;
+}
+
+int flint_kv_alloc(flint_ctx* c, int32_t batch, int32_t max_tokens, flint_kv** out) {
+  if (!out) return fail(FLINT_EINVAL, "out is NULL");
+  *out = nullptr;
+  if (!c) return fail(FLINT_EINVAL, "ctx is NULL");
+  if (batch < 1 || batch > 4096) return fail(FLINT_EINVAL, "batch %d not in [1, 4096]", batch);
+  if (max_tokens < 1 || max_tokens > (1 << 22)) return fail(FLINT_EINVAL, "max_tokens %d not in [1, 2^22]", max_tokens);
+  const flint_config& cfg = c->cfg;
+  const size_t per = (size_t)cfg.n_layers * batch * cfg.n_kv_heads * max_tokens * cfg.head_dim *
+                     elem_bytes_act(cfg.weight_type);
+  flint_kv* kv = new (std::nothrow) flint_kv();
+  if (!kv) return fail(FLINT_ENOMEM, "host allocation failed");
+  kv->ctx = c;
+  kv->batch = batch;
+  kv->max_tokens = max_tokens;
+  kv->k = kv->v = nullptr;
+  kv->len = nullptr;
+  kv->rope = nullptr;
+  auto bail = [&](int code) {
+    if (kv->k) (void)hipFree(kv->k);
+    if (kv->v) (void)hipFree(kv->v);
+    if (kv->len) (void)hipFree(kv->len);
+    if (kv->rope) (void)hipFree(kv->rope);
+    delete kv;
+    return code;
+  };
+  if (hipMalloc(&kv->k, per) != hipSuccess || hipMalloc(&kv->v, per) != hipSuccess)
+    return bail(fail(FLINT_ENOMEM, "KV cache of 2 x %zu bytes", per));
+  if (hipMalloc((void**)&kv->len, sizeof(int32_t) * batch) != hipSuccess) return bail(fail(FLINT_ENOMEM, "lengths"));
+  // RoPE table: cos, sin of p * theta^(-2i/d) in double, stored fp32 [max_tokens][d/2][2]
+  const int half = cfg.head_dim / 2;
+  std::vector<float> tab((size_t)max_tokens * half * 2);
+  for (int pos = 0; pos < max_tokens; ++pos)
+    for (int i = 0; i < half; ++i) {
+      const double ang = (double)pos * pow((double)cfg.rope_theta, -2.0 * i / (double)cfg.head_dim);
+      tab[((size_t)pos * half + i) * 2] = (float)cos(ang);
+      tab[((size_t)pos * half + i) * 2 + 1] = (float)sin(ang);
+    }
+  if (hipMalloc((void**)&kv->rope, tab.size() * 4) != hipSuccess) return bail(fail(FLINT_ENOMEM, "RoPE table"));
+  if (hipMemsetAsync(kv->k, 0, per, c->stream) != hipSuccess || hipMemsetAsync(kv->v, 0, per, c->stream) != hipSuccess ||
+      hipMemsetAsync(kv->len, 0, sizeof(int32_t) * batch, c->stream) != hipSuccess ||
+      hipMemcpyAsync(kv->rope, tab.data(), tab.size() * 4, hipMemcpyHostToDevice, c->stream) != hipSuccess ||
+      hipStreamSynchronize(c->stream) != hipSuccess)
+    return bail(fail(FLINT_EHIP, "KV cache initialisation failed"));
+  kv->hlen.assign(batch, 0);
+  c->live_kv++;
+  *out = kv;
+  return FLINT_OK;
+}
+
+int flint_kv_free(flint_kv* kv) {
+  if (!kv) return FLINT_OK;
+  (void)hipStreamSynchronize(kv->ctx->stream);
+  (void)hipFree(kv->k);
+  (void)hipFree(kv->v);
+  (void)hipFree(kv->len);
+  (void)hipFree(kv->rope);
+  kv->ctx->live_kv--;
+  delete kv;
+  return FLINT_OK;
+}
+
+int flint_kv_set_lengths(flint_kv* kv, const int32_t* lengths) {
+  if (!kv || !lengths) return fail(FLINT_EINVAL, "kv or lengths is NULL");
+  for (int b = 0; b < kv->batch; ++b)
+    if (lengths[b] < 0 || lengths[b] > kv->max_tokens)
+      return fail(FLINT_EINVAL, "length[%d] = %d not in [0, %d]", b, lengths[b], kv->max_tokens);
+  HIPCHECK(hipMemcpyAsync(kv->len, lengths, sizeof(int32_t) * kv->batch, hipMemcpyHostToDevice, kv->ctx->stream));
+  HIPCHECK(hipStreamSynchronize(kv->ctx->stream));
+  kv->hlen.assign(lengths, lengths + kv->batch);
+  return FLINT_OK;
+}
+
+int flint_kv_get_lengths(flint_kv* kv, int32_t* lengths) {
+  if (!kv || !lengths) return fail(FLINT_EINVAL, "kv or lengths is NULL");
+  HIPCHECK(hipMemcpyAsync(lengths, kv->len, sizeof(int32_t) * kv->batch, hipMemcpyDeviceToHost, kv->ctx->stream));
+  HIPCHECK(hipStreamSynchronize(kv->ctx->stream));
+  return FLINT_OK;
+}
+
+int flint_kv_layer_ptrs(flint_kv* kv, int32_t layer, void** k, void** v) {
+  if (!kv || !k || !v) return fail(FLINT_EINVAL, "NULL argument");
+  const flint_config& cfg = kv->ctx->cfg;
+  if (layer < 0 || layer >= cfg.n_layers) return fail(FLINT_EINVAL, "layer %d not in [0, %d)", layer, cfg.n_layers);
+  const size_t per_layer = (size_t)kv->batch * cfg.n_kv_heads * kv->max_tokens * cfg.head_dim *
+                           elem_bytes_act(cfg.weight_type);
+  *k = (char*)kv->k + per_layer * layer;
+  *v = (char*)kv->v + per_layer * layer;
+  return FLINT_OK;
+}
+
+int flint_decode_step_debug(flint_ctx* c, const int32_t* tokens, flint_kv* kv, int32_t* out_ids,
+                            const flint_debug* dbg) {
+  if (!c || !kv || !tokens || !out_ids) return fail(FLINT_EINVAL, "NULL argument");
+  if (kv->ctx != c) return fail(FLINT_EINVAL, "kv belongs to another ctx");
+  int rc = latched_error(c);
+  if (rc) return rc;
+  for (int b = 0; b < kv->batch; ++b)
+    if (kv->hlen[b] + 1 > kv->max_tokens)
+      return fail(FLINT_ECAPACITY, "sequence %d: length %d + 1 exceeds max_tokens %d", b, kv->hlen[b], kv->max_tokens);
+  for (int b = 0; b < kv->batch; ++b) {
+    rc = launch(c, kv, tokens, b, b, out_ids, b, dbg);
+    if (rc) return rc;
+    kv->hlen[b]++;
+  }
+  return FLINT_OK;
+}
+
+int flint_decode_step(flint_ctx* c, const int32_t* tokens, flint_kv* kv, int32_t* out_ids) {
+  return flint_decode_step_debug(c, tokens, kv, out_ids, nullptr);
+}
+
+int flint_prefill_chunk(flint_ctx* c, flint_kv* kv, int32_t seq, const int32_t* tokens, int32_t n, int32_t* out_id) {
+  if (!c || !kv || !tokens || !out_id) return fail(FLINT_EINVAL, "NULL argument");
+  if (kv->ctx != c) return fail(FLINT_EINVAL, "kv belongs to another ctx");
+  if (seq < 0 || seq >= kv->batch) return fail(FLINT_EINVAL, "seq %d not in [0, %d)", seq, kv->batch);
+  if (n < 1 || n > 4096) return fail(FLINT_EINVAL, "n %d not in [1, 4096]", n);
+  int rc = latched_error(c);
+  if (rc) return rc;
+  if (kv->hlen[seq] + n > kv->max_tokens)
+    return fail(FLINT_ECAPACITY, "sequence %d: length %d + %d exceeds max_tokens %d", seq, kv->hlen[seq], n,
+                kv->max_tokens);
+  // positions in order; each launch writes its greedy id to out_id[0], the
+  // last one is the id after the chunk
+  for (int i = 0; i < n; ++i) {
+    rc = launch(c, kv, tokens, i, seq, out_id, 0, nullptr);
+    if (rc) return rc;
+    kv->hlen[seq]++;
+  }
+  return FLINT_OK;
+}
+
+int flint_sync(flint_ctx* c) {
+  if (!c) return fail(FLINT_EINVAL, "ctx is NULL");
+  HIPCHECK(hipStreamSynchronize(c->stream));
+  return latched_error(c);
+}
+
+int flint_device_info(flint_ctx* c, int32_t* grid, int32_t* block, int32_t* lds_bytes) {
+  if (!c) return fail(FLINT_EINVAL, "ctx is NULL");
+  if (grid) *grid = c->grid;
+  if (block) *block = NT;
+  if (lds_bytes) *lds_bytes = kernel_lds_bytes(c->cfg.weight_type);
+  return FLINT_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,79 @@
+"""Shared helpers of the GPU parity tests (device model from the seeded
+generator, and the comparison rules).
+
+Comparison rules (the tolerances stated for this library):
+  * logits: max |gpu - oracle| / max |oracle| <= 1e-4 (fp32 model) or 2e-2 (bf16 / int4);
+  * routes: the GPU's top-k set equals the oracle's, or, where the oracle's
+    k-th / (k+1)-th router logits are within 1e-3 * max|z|, is a valid top-k
+    within that margin (the oracle then follows the GPU's set);
+  * token ids: identical unless the oracle's top-2 logit gap is below 1e-3 of
+    max |logit| (then the oracle follows the GPU's token).
+"""
+import numpy as np
+import torch
+
+import oracle
+import synth
+from stream_moe_decode_amd import decode_step_debug, prefill_chunk, sync
+from stream_moe_decode_amd.loader import DeviceModel, make_debug
+
+TIE_EPS = 1e-3
+
+
+def logits_tol(cfg):
+    return 1e-4 if cfg.weight_type == synth.F32 else 2e-2
+
+
+def rel_err(g, o):
+    g = np.asarray(g, np.float64)
+    o = np.asarray(o, np.float64)
+    return float(np.max(np.abs(g - o)) / max(np.max(np.abs(o)), 1e-30))
+
+
+def build(cfg, grid=0, layers=None):
+    if layers is None:
+        def layer_fn(l):
+            return synth.layer(cfg, l)
+    else:
+        def layer_fn(l):
+            return layers[l]
+    return DeviceModel(cfg, layer_fn, synth.head(cfg), grid=grid)
+
+
+def make_oracle(cfg, cap, layers=None, batch=1):
+    fn = (lambda l: synth.layer(cfg, l)) if layers is None else (lambda l: layers[l])
+    return oracle.Oracle(cfg, fn, synth.head(cfg), cap=cap, batch=batch)
+
+
+class Stepper:
+    """Runs GPU decode steps with debug outputs and checks each against the oracle."""
+
+    def __init__(self, cfg, model, kv, orc, seq=0):
+        self.cfg, self.model, self.kv, self.orc, self.seq = cfg, model, kv, orc, seq
+        self.dev = model.device
+        self.tok = torch.zeros(kv.batch, dtype=torch.int32, device=self.dev)
+        self.out = torch.zeros(kv.batch, dtype=torch.int32, device=self.dev)
+        self.dbg, self.t = make_debug(cfg, kv.batch, self.dev, resid_layer=0)
+        self.report = []
+
+    def step(self, token: int):
+        """One GPU step on `token` and the oracle's step on the same token; returns the checked GPU id."""
+        cfg = self.cfg
+        self.tok[self.seq] = token
+        decode_step_debug(self.model.ctx, self.tok.data_ptr(), self.kv.handle, self.out.data_ptr(), self.dbg)
+        sync(self.model.ctx)
+        g_logits = self.t["logits"][self.seq].cpu().numpy()
+        g_routes = self.t["routes"][self.seq].cpu().numpy()
+        g_id = int(self.out[self.seq].item())
+        r = self.orc.forward(self.seq, np.array([token], np.int32), ref_routes=g_routes[None], tie_eps=TIE_EPS)
+        err = rel_err(g_logits, r["logits"][0])
+        moe = [l for l in range(cfg.n_layers) if l >= cfg.n_dense_layers]
+        flags = r["route_flags"][0, moe] if moe else np.zeros(0)
+        assert not (flags == 2).any(), f"routes differ beyond a near tie at layers {np.nonzero(flags == 2)[0]}"
+        assert err <= logits_tol(cfg), f"logits max rel err {err:.3g} > {logits_tol(cfg)}"
+        o_id = int(r["ids"][0])
+        near = r["gap"][0] < TIE_EPS
+        assert g_id == o_id or near, f"token {g_id} != oracle {o_id} (gap {r['gap'][0]:.3g})"
+        assert g_id == int(np.argmax(g_logits)) or np.max(g_logits) == g_logits[g_id]
+        self.report.append({"err": err, "near_route": int((flags == 1).sum()), "near_token": bool(near and g_id != o_id)})
+        return g_id
