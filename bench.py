@@ -1,0 +1,233 @@
+#!/usr/bin/env python3
+"""Single-stream greedy decode benchmark of the persistent HIP decode kernel.
+
+Workload (default ``int4_49``): 49 layers (0-1 dense SwiGLU, 2-48 MoE with 64
+experts, top-6), hidden 2048, GQA 16/4 x 128, vocab 65536, int4 group-64
+weights with bf16 scales (embedding and lm_head bf16), random-init weights
+~N(0, 0.02), a synthetic resident KV cache of 8,022 positions ~N(0, 1), then
+K greedy decode steps with the token fed back on the device.  One step is one
+kernel launch (the whole decode step).
+
+Prints one JSON line: tokens/s, ms/step, the HBM roofline of the decode
+kernel (algorithmic bytes per launch / mean launch time from HIP events on
+the launch stream), per-phase time per layer from in-kernel timestamps, and
+the CPU oracle timed on a bounded sample of the same workload.
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+METRIC = "single-stream decode tok/s + achieved HBM GB/s (% of peak), 49-layer int4"
+
+
+def weight_bytes_per_step(cfg) -> int:
+    """Weight bytes one decode step must read: every layer's attention weights and
+    norms, the dense MLPs, the router and the top_k selected experts of each MoE
+    layer, one embedding row, the final norm and the whole lm_head."""
+    import synth
+    H, V = cfg.hidden, cfg.vocab
+
+    def mat(rows, cols):
+        if cfg.weight_type == synth.INT4G64:
+            return rows * cols // 2 + rows * (cols // 64) * 2
+        return rows * cols * (4 if cfg.weight_type == synth.F32 else 2)
+
+    eb = 4 if cfg.weight_type == synth.F32 else 2
+    b = H * eb + V * H * eb + H * 4
+    for l in range(cfg.n_layers):
+        b += 2 * H * 4 + mat(cfg.qkv_rows, H) + mat(H, cfg.q_dim)
+        if l < cfg.n_dense_layers:
+            b += 2 * mat(cfg.dense_inter, H) + mat(H, cfg.dense_inter)
+        else:
+            b += mat(cfg.n_experts, H) + cfg.top_k * (2 * mat(cfg.expert_inter, H) + mat(H, cfg.expert_inter))
+    return b
+
+
+def kv_bytes_per_position(cfg) -> int:
+    import synth
+    return cfg.n_layers * 2 * cfg.n_kv_heads * cfg.head_dim * (4 if cfg.weight_type == synth.F32 else 2)
+
+
+def step_bytes(cfg, pos: int) -> int:
+    """Algorithmic HBM bytes of the step at position pos: weights, the K/V of the
+    pos resident positions read once, and the new position's K/V written."""
+    return weight_bytes_per_step(cfg) + kv_bytes_per_position(cfg) * (pos + 1)
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=256)
+    ap.add_argument("--warmup", type=int, default=8)
+    ap.add_argument("--config", default="int4_49")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-steps", type=int, default=4, help="decode steps the oracle is timed on")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run one 1 GiB device copy (counter calibration under rocprofv3 --pmc)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (--gpus {args.gpus} requested): the decode step is a "
+              "single-GPU kernel; see the design notes for how it would shard.", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import synth
+    from stream_moe_decode_amd import decode_step, decode_step_debug, device_info, lib, sync
+    from stream_moe_decode_amd.loader import DeviceModel, make_debug
+
+    lib()
+    cfg = synth.CONFIGS[args.config]
+    assert cfg.batch == 1, "single-stream workloads only"
+    cpu = not args.no_cpu_baseline
+    t_gen = time.perf_counter()
+    cache = {} if cpu else None
+
+    def layer_fn(l):
+        if l % 8 == 0:
+            log(f"generating layer {l}/{cfg.n_layers} ({time.perf_counter() - t_gen:.0f} s)")
+        d = synth.layer(cfg, l)
+        if cache is not None:
+            cache[l] = d
+        return d
+
+    head = synth.head(cfg)
+    model = DeviceModel(cfg, layer_fn, head)
+    resident = cfg.resident
+    cap = resident + max(args.warmup, 1) + args.steps + 8
+    kv = model.kv(1, cap)
+    for l in range(cfg.n_layers):
+        if resident:
+            k, v = synth.resident_kv(cfg, l, 0, resident)
+            kv.load_resident(l, 0, k, v)
+    kv.set_lengths([resident])
+    log(f"model + KV ready in {time.perf_counter() - t_gen:.1f} s; grid/block/lds = {device_info(model.ctx)}")
+    dev = model.device
+    first = int(synth.tokens(cfg, 1, stream=11)[0])
+    tok = torch.tensor([first], dtype=torch.int32, device=dev)
+
+    if args.copy_calibration:
+        a = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        b = torch.empty_like(a)
+        b.copy_(a)
+        torch.cuda.synchronize()
+        del a, b
+
+    # warm-up, then roll the cache back so the timed steps start at `resident`
+    for _ in range(args.warmup):
+        decode_step(model.ctx, tok.data_ptr(), kv.handle, tok.data_ptr())
+    sync(model.ctx)
+    kv.set_lengths([resident])
+    tok.fill_(first)
+    torch.cuda.synchronize()
+
+    K = args.steps
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(K)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(K)]
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for i in range(K):
+        starts[i].record()
+        decode_step(model.ctx, tok.data_ptr(), kv.handle, tok.data_ptr())
+        ends[i].record()
+    e1.record()
+    torch.cuda.synchronize()
+    sync(model.ctx)
+    total_ms = e0.elapsed_time(e1)
+    kern_ms = [s.elapsed_time(e) for s, e in zip(starts, ends)]
+    bytes_total = sum(step_bytes(cfg, resident + i) for i in range(K))
+    mean_kern_s = sum(kern_ms) / K / 1e3
+    achieved = bytes_total / K / mean_kern_s / 1e9
+    log(f"{K} steps: {total_ms:.2f} ms total, kernel mean {1e3 * mean_kern_s:.1f} us, "
+        f"min {1e3 * min(kern_ms):.1f} us, max {1e3 * max(kern_ms):.1f} us")
+
+    # per-phase time per layer (workgroup 0's wall-clock stamps), one extra step at `resident`
+    kv.set_lengths([resident])
+    tok.fill_(first)
+    dbg, t = make_debug(cfg, 1, dev, logits=True, routes=False, phase_ts=True)
+    decode_step_debug(model.ctx, tok.data_ptr(), kv.handle, tok.data_ptr(), dbg)
+    sync(model.ctx)
+    ts = t["phase_ts"].cpu().numpy().astype(np.int64)
+    gpu_logits0 = t["logits"][0].cpu().numpy()
+    gpu_id0 = int(tok.item())
+    tick_us = 0.01  # 100 MHz
+    att, moe = [], []
+    prev = ts[0, 0]
+    for l in range(cfg.n_layers):
+        row = ts[l + 1]
+        if l >= cfg.n_dense_layers:
+            att.append((row[3] - prev) * tick_us)
+            moe.append((row[6] - row[3]) * tick_us)
+        prev = row[6]
+    head_us = (ts[0, 1] - prev) * tick_us
+    phases = {"attention_us_per_layer": round(float(np.mean(att)), 2) if att else None,
+              "moe_us_per_layer": round(float(np.mean(moe)), 2) if moe else None,
+              "head_us": round(float(head_us), 2), "source": "workgroup-0 s_memrealtime stamps, one step at "
+                                                             f"position {resident}"}
+    model.free()
+
+    cpu_baseline = None
+    if cpu:
+        import oracle
+        orc = oracle.Oracle(cfg, lambda l: cache[l], head, cap=resident + args.cpu_steps + 2)
+        for l in range(cfg.n_layers):
+            if resident:
+                k, v = synth.resident_kv(cfg, l, 0, resident)
+                orc.set_resident(0, l, k, v)
+        orc.len[0] = resident
+        cores = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+        t0 = time.perf_counter()
+        toks = [first]
+        r0 = None
+        for i in range(args.cpu_steps):
+            r = orc.forward(0, np.array([toks[-1]], np.int32))
+            if r0 is None:
+                r0 = r
+            toks.append(int(r["ids"][0]))
+        dt = time.perf_counter() - t0
+        err = float(np.max(np.abs(gpu_logits0 - r0["logits"][0])) / np.max(np.abs(r0["logits"][0])))
+        cpu_baseline = {"value": round(args.cpu_steps / dt, 4), "unit": "tok/s", "cores": cores, "kind": "oracle",
+                        "sample": f"{args.cpu_steps} greedy decode steps at positions {resident}.."
+                                  f"{resident + args.cpu_steps - 1} of the same model and cache (scalar C++, "
+                                  f"double accumulation, OpenMP over output rows), {dt:.1f} s",
+                        "parity_first_step": {"logits_max_rel_err": err, "gpu_token": gpu_id0,
+                                              "oracle_token": int(r0["ids"][0]),
+                                              "oracle_top2_gap": float(r0["gap"][0])}}
+        log(f"oracle: {dt:.1f} s for {args.cpu_steps} steps; first-step logits rel err {err:.3g}")
+
+    value = K / (total_ms / 1e3)
+    wb = weight_bytes_per_step(cfg)
+    out = {
+        "metric": METRIC, "value": round(value, 2), "unit": "tok/s", "n_gpus": 1, "steps": K,
+        "warmup": args.warmup, "ms_per_step": round(total_ms / K, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": f"{cfg.name}: {cfg.n_layers} layers ({cfg.n_dense_layers} dense), hidden {cfg.hidden}, "
+                               f"{cfg.n_experts} experts top-{cfg.top_k}, weights "
+                               f"{ {0: 'fp32', 1: 'bf16', 2: 'int4-g64 (bf16 embed/lm_head)'}[cfg.weight_type] }, "
+                               f"{resident} resident KV positions, {K} greedy tokens",
+                   "global_batch": 1, "seq_len": resident + K, "parallelism": "none (one GPU)"},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "bytes_per_launch": int(bytes_total / K), "weight_bytes_per_step": wb,
+                     "kernel_mean_us": round(1e6 * mean_kern_s, 2),
+                     "roofline_tok_s": round(HBM_PEAK_GBS * 1e9 / (bytes_total / K), 1)},
+        "phases": phases,
+        "cpu_baseline": cpu_baseline,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()
