@@ -166,7 +166,7 @@ def main():
     att, moe = [], []
     prev = ts[0, 0]
     for l in range(cfg.n_layers):
-        row = ts[l + 1]
+        row = ts[l + 1]   # stamps of layer l: [3] residual after o_proj gathered, [6] after the MLP
         if l >= cfg.n_dense_layers:
             att.append((row[3] - prev) * tick_us)
             moe.append((row[6] - row[3]) * tick_us)

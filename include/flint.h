@@ -113,8 +113,9 @@ typedef struct flint_debug {
   float* resid;         /* [batch][hidden] fp32 residual after layer resid_layer */
   int32_t resid_layer;
   int32_t pad;
-  uint64_t* phase_ts;   /* [n_layers + 1][8] wall-clock stamps (100 MHz) of workgroup 0 at
-                           phase boundaries, for sequence 0 */
+  uint64_t* phase_ts;   /* [n_layers + 1][16] wall-clock stamps (100 MHz) of workgroup 0 at
+                           phase boundaries, for sequence 0 (row 0: start, end, argmax published;
+                           row l + 1: layer l) */
 } flint_debug;
 
 /* ------------------------------------------------------------- entry points */

@@ -9,15 +9,19 @@ constexpr int NT = 256;                 // threads per workgroup (4 waves of 64)
 constexpr int NW = NT / 64;             // waves per workgroup
 constexpr int MAX_H = 2048;             // residual width
 constexpr int MAX_QD = 2048;            // n_q_heads * head_dim
-constexpr int MAX_HBUF = 6144;          // dense_inter, or top_k * expert_inter
+constexpr int MAX_HBUF = 6144;          // dense_inter, or top_k * expert_inter (bf16 elements; fp32: half)
 constexpr int MAX_E = 64;               // experts (top-k runs inside one wave)
 constexpr int MAX_K = 8;                // top_k
 constexpr int MAX_GQ = 8;               // query heads per kv head
 constexpr int MAX_HD = 128;             // head_dim
-constexpr int MAX_P = 512;              // attention positions scored per chunk
 constexpr int MAX_YROWS = 1024;         // GEMV results a workgroup keeps per phase
 constexpr int MAX_GATHER = 4096;        // 32-bit words of the merge gather buffer
+constexpr int KV_PASSES = 3;            // attention: K rows held in registers, 64 B per thread per pass
+constexpr int KV_CHUNK_BYTES = KV_PASSES * NT * 64;  // K (registers) and V (LDS) bytes per attention chunk
+constexpr int MAX_CHUNK_POS = KV_CHUNK_BYTES / 128;  // positions per chunk for the smallest row (64 bf16)
 constexpr int NCOPY = 8;                // replicas of broadcast exchanges (one per XCD)
+// LDS weight staging, in items (one 16-byte chunk per lane of a wave) per wave
+constexpr int QKV_CAP = 4, O_CAP = 2, R_CAP = 16, GU_CAP = 12, DN_CAP = 6;
 constexpr int TAGS_PER_LAUNCH = 1024;   // exchange tags one launch may use
 constexpr uint64_t SPIN_TIMEOUT = 100000000ull;  // 1 s of the 100 MHz wall clock
 
@@ -29,43 +33,44 @@ struct Mat {
   const uint16_t* s;     // int4 only: bf16 scales [rows][in/64]
 };
 
-struct KArgs {
-  // model dimensions
+// Per-context constants, kept in device memory for the kernel's lifetime.
+struct KStatic {
   int H, nq, nkv, hd, V, L, n_dense, DI, E, K, EI, renorm;
   float eps;
   int S;                 // attention splits per kv head (grid / n_kv_heads)
-  // weights (library-owned, canonical layout)
+  int qkv_rows, o_slots, h_slots;
+  int poll_sleep;        // s_sleep(8) repetitions between polls of a stale slot
+  int sentinels;         // slots polled by wave 0 before the bulk read (1..64)
   const uint8_t* embed;
   const uint8_t* lmhead;
   const float* fnorm;
   const float* anorm;
   const float* pnorm;
   Mat qkv, o, dg, du, dd, router, eg, eu, ed;
-  // KV cache [L][B][nkv][cap][hd] in the activation type
-  uint8_t* kc;
-  uint8_t* vc;
-  int B, cap;
-  const float2* rope;    // [cap][hd/2] (cos, sin)
-  int32_t* len;          // [B] device lengths
-  // this launch
-  const int32_t* tokens;
-  int tok_idx, seq;
-  int32_t* out_ids;
-  int out_idx;
-  uint32_t epoch;
-  // scratch
   uint64_t* x_qkv;       // [NCOPY][2][qkv_rows]            q/k/v after RoPE (fp32)
   uint64_t* x_part;      // [2][nq][hd + 2][S]              attention partials (fp32)
   uint64_t* x_o;         // [NCOPY][2][o_slots]             merged attention output
   uint64_t* x_res1;      // [NCOPY][2][H]                   residual after o_proj (fp32)
   uint64_t* x_h;         // [NCOPY][2][h_slots]             SwiGLU output
   uint64_t* x_res2;      // [NCOPY][2][H]                   residual after the MLP (fp32)
-  int qkv_rows, o_slots, h_slots;
   uint32_t* err;         // device error word
   uint32_t* herr;        // host-mapped error word
   unsigned long long* amax;  // packed argmax key
   uint32_t* done;        // workgroups finished with lm_head
-  // optional outputs
+};
+
+// Per-launch arguments (passed by value).
+struct KDyn {
+  uint8_t* kc;           // KV cache [L][B][nkv][cap][hd] in the activation type
+  uint8_t* vc;
+  int B, cap;
+  const float2* rope;    // [cap][hd/2] (cos, sin)
+  int32_t* len;          // [B] device lengths
+  const int32_t* tokens;
+  int tok_idx, seq;
+  int32_t* out_ids;
+  int out_idx;
+  uint32_t epoch;
   float* dbg_logits;
   int32_t* dbg_routes;
   float* dbg_rw;
@@ -74,8 +79,10 @@ struct KArgs {
   uint64_t* dbg_ts;
 };
 
-// Launch the persistent kernel for weight type wt on `stream`.
-hipError_t launch_decode(int wt, const KArgs& a, int grid, hipStream_t stream);
+// True if the compile-time 2048-wide shape (and a 256-workgroup grid) matches.
+bool shape_is_static(const KStatic& k, int grid);
+// Launch the persistent kernel for weight type wt on `stream` (stat: the compile-time shape).
+hipError_t launch_decode(int wt, bool stat, const KStatic* ks, const KDyn& d, int grid, hipStream_t stream);
 // Zero `n` 64-bit words with a fill kernel.
 hipError_t launch_fill(uint64_t* p, size_t n, hipStream_t stream);
 // Static LDS bytes of the persistent kernel.

@@ -6,6 +6,7 @@
 #include <math.h>
 #include <stdarg.h>
 #include <stdio.h>
+#include <stdlib.h>
 #include <string.h>
 
 #include <new>
@@ -54,7 +55,9 @@ struct flint_ctx {
   int grid;
   int S;
   std::vector<void*> allocs;  // library-owned device memory
-  KArgs base;                 // weights and scratch filled in; per-launch fields set at launch
+  KStatic base;               // weights, dimensions and scratch (host copy)
+  KStatic* kdev;              // the same, in device memory, read by the kernel
+  bool stat;                  // the compile-time 2048-wide kernel applies
   uint32_t* herr_host;        // host-mapped error word
   uint64_t* xbuf;
   size_t xbuf_words;
@@ -107,16 +110,20 @@ int check_config(const flint_config* c) {
   if (c->n_q_heads * c->head_dim > MAX_QD)
     return fail(FLINT_EINVAL, "n_q_heads * head_dim = %d exceeds %d", c->n_q_heads * c->head_dim, MAX_QD);
   if (c->vocab < 1) return fail(FLINT_EINVAL, "vocab %d", c->vocab);
-  if (c->n_dense_layers > 0 && (c->dense_inter < 64 || c->dense_inter % 64 || c->dense_inter > MAX_HBUF))
+  if (c->n_dense_layers > 0 && (c->dense_inter < 64 || c->dense_inter % 64 || c->dense_inter > (c->weight_type == FLINT_W_F32 ? MAX_HBUF / 2 : MAX_HBUF)))
     return fail(FLINT_EINVAL, "dense_inter %d must be a multiple of 64 in [64, %d]", c->dense_inter, MAX_HBUF);
   if (c->n_dense_layers < c->n_layers) {
     if (c->n_experts < 1 || c->n_experts > MAX_E) return fail(FLINT_EINVAL, "n_experts %d not in [1, %d]", c->n_experts, MAX_E);
     if (c->top_k < 1 || c->top_k > MAX_K || c->top_k > c->n_experts)
       return fail(FLINT_EINVAL, "top_k %d not in [1, min(%d, n_experts)]", c->top_k, MAX_K);
-    if (c->expert_inter < 64 || c->expert_inter % 64 || c->top_k * c->expert_inter > MAX_HBUF)
+    if (c->expert_inter < 64 || c->expert_inter % 64 || c->top_k * c->expert_inter > (c->weight_type == FLINT_W_F32 ? MAX_HBUF / 2 : MAX_HBUF))
       return fail(FLINT_EINVAL, "expert_inter %d must be a multiple of 64 with top_k * expert_inter <= %d",
                   c->expert_inter, MAX_HBUF);
   }
+  if (c->weight_type == FLINT_W_INT4G64 &&
+      (c->hidden % 128 || (c->n_q_heads * c->head_dim) % 128 ||
+       (c->n_dense_layers > 0 && c->dense_inter % 128) || (c->n_dense_layers < c->n_layers && c->expert_inter % 128)))
+    return fail(FLINT_EINVAL, "int4 weights need every input width to be a multiple of 128");
   if (!(c->rms_eps >= 0.f) || !(c->rope_theta > 0.f)) return fail(FLINT_EINVAL, "rms_eps / rope_theta invalid");
   if (c->router_renorm != 0 && c->router_renorm != 1) return fail(FLINT_EINVAL, "router_renorm must be 0 or 1");
   if (c->grid < 0) return fail(FLINT_EINVAL, "grid %d < 0", c->grid);
@@ -190,7 +197,8 @@ int launch(flint_ctx* c, flint_kv* kv, const int32_t* tokens, int tok_idx, int s
     // tags restart: clear every exchange slot so no stale tag can match
     HIPCHECK(launch_fill(c->xbuf, c->xbuf_words, c->stream));
   }
-  KArgs a = c->base;
+  KDyn a;
+  memset(&a, 0, sizeof a);
   a.kc = (uint8_t*)kv->k;
   a.vc = (uint8_t*)kv->v;
   a.B = kv->batch;
@@ -212,7 +220,7 @@ int launch(flint_ctx* c, flint_kv* kv, const int32_t* tokens, int tok_idx, int s
     a.dbg_resid_layer = dbg->resid_layer;
     a.dbg_ts = seq == 0 ? dbg->phase_ts : nullptr;
   }
-  HIPCHECK(launch_decode(c->cfg.weight_type, a, c->grid, c->stream));
+  HIPCHECK(launch_decode(c->cfg.weight_type, c->stat, c->kdev, a, c->grid, c->stream));
   c->launches++;
   return FLINT_OK;
 }
@@ -255,7 +263,7 @@ int flint_decode_init(const flint_config* cfg, const flint_weights* w, void* hip
   const size_t L = cfg->n_layers, ND = cfg->n_dense_layers, NM = L - ND, H = cfg->hidden, V = cfg->vocab;
   const size_t hd = cfg->head_dim, QR = (cfg->n_q_heads + 2 * cfg->n_kv_heads) * hd, QD = cfg->n_q_heads * hd;
   const size_t DI = cfg->dense_inter, E = cfg->n_experts, EI = cfg->expert_inter;
-  KArgs& a = c->base;
+  KStatic& a = c->base;
   memset(&a, 0, sizeof a);
   a.H = (int)H;
   a.nq = cfg->n_q_heads;
@@ -271,6 +279,12 @@ int flint_decode_init(const flint_config* cfg, const flint_weights* w, void* hip
   a.renorm = cfg->router_renorm;
   a.eps = cfg->rms_eps;
   a.S = c->S;
+  // exchange polling: tuning knobs for experiments (defaults are the measured best)
+  a.poll_sleep = getenv("FLINT_POLL_SLEEP") ? atoi(getenv("FLINT_POLL_SLEEP")) : 0;
+  a.sentinels = getenv("FLINT_SENTINELS") ? atoi(getenv("FLINT_SENTINELS")) : 64;
+  if (a.sentinels < 1) a.sentinels = 1;
+  if (a.sentinels > 64) a.sentinels = 64;
+  if (a.poll_sleep < 0) a.poll_sleep = 0;
 
   const size_t eb = elem_bytes_act(wt);
   if ((rc = copy_in(c, w->embed, V * H * eb, &a.embed, "embed"))) return bail(rc);
@@ -322,6 +336,12 @@ int flint_decode_init(const flint_config* cfg, const flint_weights* w, void* hip
   if (hipHostGetDevicePointer(&herr_dev, c->herr_host, 0) != hipSuccess)
     return bail(fail(FLINT_EHIP, "hipHostGetDevicePointer failed"));
   a.herr = (uint32_t*)herr_dev;
+  c->stat = cfg->weight_type != FLINT_W_F32 && shape_is_static(a, c->grid) && !getenv("FLINT_GENERIC_KERNEL");
+  void* kd;
+  if ((rc = dalloc(c, &kd, sizeof(KStatic)))) return bail(rc);
+  c->kdev = (KStatic*)kd;
+  if (hipMemcpyAsync(kd, &a, sizeof(KStatic), hipMemcpyHostToDevice, c->stream) != hipSuccess)
+    return bail(fail(FLINT_EHIP, "copy of the kernel constants failed"));
   if (launch_fill(c->xbuf, c->xbuf_words, c->stream) != hipSuccess) return bail(fail(FLINT_EHIP, "fill kernel failed"));
   if (hipMemsetAsync(misc, 0, 256, c->stream) != hipSuccess) return bail(fail(FLINT_EHIP, "hipMemsetAsync failed"));
   if (hipStreamSynchronize(c->stream) != hipSuccess) return bail(fail(FLINT_EHIP, "hipStreamSynchronize failed"));

@@ -190,6 +190,6 @@ def make_debug(cfg, batch: int, device, logits=True, routes=True, resid_layer=No
         dbg.resid = t["resid"].data_ptr()
         dbg.resid_layer = resid_layer
     if phase_ts:
-        t["phase_ts"] = torch.zeros((cfg.n_layers + 1, 8), dtype=torch.int64, device=device)
+        t["phase_ts"] = torch.zeros((cfg.n_layers + 1, 16), dtype=torch.int64, device=device)
         dbg.phase_ts = t["phase_ts"].data_ptr()
     return dbg, t
