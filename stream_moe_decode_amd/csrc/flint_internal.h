@@ -15,13 +15,13 @@ constexpr int MAX_K = 8;                // top_k
 constexpr int MAX_GQ = 8;               // query heads per kv head
 constexpr int MAX_HD = 128;             // head_dim
 constexpr int MAX_YROWS = 1024;         // GEMV results a workgroup keeps per phase
+constexpr int MAX_QPAIRS = 64;          // RoPE pairs of the QKV rows one workgroup owns
 constexpr int MAX_GATHER = 4096;        // 32-bit words of the merge gather buffer
-constexpr int KV_PASSES = 3;            // attention: K rows held in registers, 64 B per thread per pass
-constexpr int KV_CHUNK_BYTES = KV_PASSES * NT * 64;  // K (registers) and V (LDS) bytes per attention chunk
-constexpr int MAX_CHUNK_POS = KV_CHUNK_BYTES / 128;  // positions per chunk for the smallest row (64 bf16)
+constexpr int KV_LDS = 32768;           // bytes of K (and of V) rows per attention chunk
+constexpr int MAX_CHUNK_POS = KV_LDS / 128;  // positions per chunk for the smallest row (64 bf16)
 constexpr int NCOPY = 8;                // replicas of broadcast exchanges (one per XCD)
 // LDS weight staging, in items (one 16-byte chunk per lane of a wave) per wave
-constexpr int QKV_CAP = 4, O_CAP = 2, R_CAP = 16, GU_CAP = 12, DN_CAP = 6;
+constexpr int QKV_CAP = 4, O_CAP = 2, R_CAP = 16, GU_CAP = 12, DN_CAP = 6, LM_CAP = 16;
 constexpr int TAGS_PER_LAUNCH = 1024;   // exchange tags one launch may use
 constexpr uint64_t SPIN_TIMEOUT = 100000000ull;  // 1 s of the 100 MHz wall clock
 

@@ -18,14 +18,17 @@
 // are still stale, so the waiting workgroups do not flood the memory system
 // with loads.  Slots read by every workgroup are replicated once per XCD so
 // that each replica is read by the 32 workgroups of one XCD only.  Tags are
-// unique per launch, layer and phase, so no flag ever needs resetting;
-// buffers alternate by layer parity so a slot is rewritten only after every
-// reader has consumed it.
+// unique per launch, layer and phase, so no flag ever needs resetting and no
+// slot needs ordering against another; buffers alternate by layer parity so a
+// slot is rewritten only after every reader has consumed it.
 //
-// Weights of a phase are loaded into registers before the exchange that
-// precedes the phase is waited for, so the HBM latency of activation-
-// independent bytes hides behind the exchange; only the selected experts'
-// weights are fetched after the routing decision.
+// Every byte a phase reads from HBM that does not depend on the phase's input
+// (weight panels, the K/V rows of the attention split, norm weights) is
+// brought into LDS by direct-to-LDS DMA (global_load_lds) before the exchange
+// that precedes the phase is waited for, so its latency hides behind the
+// exchange; only the selected experts' weights are fetched after the routing
+// decision.  GEMVs keep the lane's activation chunk in registers when every
+// row of the phase shares it.
 //
 // Per layer the exchanges are: q/k/v -> attention partials -> merged
 // attention output -> residual after o_proj -> SwiGLU output -> residual
@@ -38,6 +41,13 @@ namespace flint {
 
 typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2_t;
 typedef __attribute__((address_space(3))) void lds_void;
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+
+// Every device pointer the kernel dereferences is cast to the global address
+// space: generic (flat) accesses would also count against the LDS wait counter.
+#define GLOBAL __attribute__((address_space(1)))
+template <class T> __device__ __forceinline__ GLOBAL T* gp(T* p) { return (GLOBAL T*)p; }
 
 // ---------------------------------------------------------------- scalars
 
@@ -55,10 +65,10 @@ __device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
 __device__ __forceinline__ uint64_t now() { return __builtin_amdgcn_s_memrealtime(); }
 __device__ __forceinline__ uint32_t xcc_id() { return __builtin_amdgcn_s_getreg((31 << 11) | 20); }
 __device__ __forceinline__ uint64_t xload(const uint64_t* p) {
-  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+  return __hip_atomic_load(gp(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
 }
 __device__ __forceinline__ void xstore(uint64_t* p, uint64_t v) {
-  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+  __hip_atomic_store(gp(p), v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
 }
 __device__ __forceinline__ uint64_t slot(uint32_t tag, uint32_t payload) { return ((uint64_t)tag << 32) | payload; }
 // Start of workgroup w's share of `total` items split over G (total * G < 2^32).
@@ -70,8 +80,18 @@ __device__ __forceinline__ int div_small(int n, int d, float inv) {
   q -= q * d > n;
   return q;
 }
-// wait until every vector memory operation of this wave has completed (vmcnt(0))
-__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+// s_waitcnt vmcnt(N): all but this wave's N most recent vector memory operations have completed
+template <int N> __device__ __forceinline__ void wait_vmem_n() {
+  static_assert(N >= 0 && N < 64, "vmcnt has 6 bits");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
+}
+__device__ __forceinline__ void wait_vmem() { wait_vmem_n<0>(); }
+// wait until this wave's LDS operations have completed (lgkmcnt(0))
+__device__ __forceinline__ void wait_lds() { __builtin_amdgcn_s_waitcnt(0xC07F); }
+__device__ __forceinline__ void dma16(const void* g, void* l) {
+  __builtin_amdgcn_global_load_lds(g, (lds_void*)l, 16, 0, 0);
+}
+__device__ __forceinline__ void dma4(const void* g, void* l) { __builtin_amdgcn_global_load_lds(g, (lds_void*)l, 4, 0, 0); }
 
 template <int WT> constexpr bool kAct32 = (WT == W_F32);
 template <int WT> constexpr int kChunkElems = WT == W_F32 ? 4 : (WT == W_BF16 ? 8 : 32);
@@ -83,47 +103,61 @@ template <int WT> __device__ __forceinline__ float act_round(float v) { return k
 
 // ---------------------------------------------------------------- shared memory
 
-struct AttnLds {
-  float qs[MAX_GQ * MAX_HD];             // scaled queries of one kv-head group
-  float kn[MAX_HD], vn[MAX_HD];          // the new token's k, v
-  float sc[MAX_GQ * MAX_CHUNK_POS];      // scores / probabilities of a chunk
-  float red[MAX_GQ * 512];               // P.V partial sums of thread subsets
-  float ocur[MAX_GQ * MAX_HD];           // running attention output
-  uint4 vbuf[KV_CHUNK_BYTES / 16];       // V rows of a chunk (LDS DMA target)
-};
 // Weight staging in LDS: item i of wave w is 64 lanes x 16 B at w16[(i * NW + w) * 64 + lane]
 // and, for int4, the dword holding the item's scale at s32[(i * NW + w) * 64 + lane].
 template <int CAP> struct StageLds {
   uint4 w16[CAP * NW * 64];
   uint32_t s32[CAP * NW * 64];
 };
-struct MlpLds {
-  uint32_t hbuf[MAX_HBUF / 2];           // SwiGLU output as GEMV input (also the lm_head input)
+// The phases of a layer reuse one region: each layout is live from the DMA that
+// fills it (issued after a barrier that ends the previous layout's reads) to
+// the last read of its phase.
+struct AttnLds {                         // QKV and attention
+  StageLds<QKV_CAP> sq;                  // QKV weights (staged during the previous layer)
+  uint4 kbuf[KV_LDS / 16];               // K rows of a chunk
+  uint4 vbuf[KV_LDS / 16];               // V rows of a chunk
+  float qs[MAX_GQ * MAX_HD];             // queries of the kv-head group, pre-scaled
+  float kn[MAX_HD], vn[MAX_HD];          // the new token's k, v (activation-rounded)
+  float sc[MAX_GQ * MAX_CHUNK_POS];      // scores of a chunk, [head][position]
+  float pt[MAX_GQ * MAX_CHUNK_POS];      // probabilities of a chunk, [position][head (padded to 4 or 8)]
+  float fac[MAX_GQ], mst[MAX_GQ], lst[MAX_GQ];  // per head: rescale of the running output, running max and sum
+};
+struct MergeLds {                        // split merge and o_proj
+  StageLds<O_CAP> so;                    // o_proj weights (staged during the merge)
+  uint32_t gbuf[MAX_GATHER];             // gathered attention partials
+};
+struct MlpLds {                          // gate/up and down
+  StageLds<GU_CAP> gu;
+  StageLds<DN_CAP> dn;
+  uint32_t hbuf[MAX_HBUF / 2];           // SwiGLU output as the down GEMV input
   float asumH[MAX_HBUF / 32];
-  StageLds<GU_CAP> gu;                   // gate/up weights
-  StageLds<DN_CAP> dn;                   // down weights
+};
+struct HeadLds {                         // lm_head: two staging buffers (bf16 / fp32 rows: no scales)
+  uint4 a[LM_CAP * NW * 64], b[LM_CAP * NW * 64];
 };
 
 struct Smem {
+  KStatic ks;                            // the context, copied once per launch: its fields are read with
+                                         // LDS loads, never with vector loads that would wait for the DMAs
   float xres[MAX_H];                     // residual (every workgroup keeps all of it)
-  uint32_t actA[MAX_QD];                 // GEMV input: fp32 words or bf16 pairs
+  uint32_t actA[MAX_QD];                 // GEMV input: fp32 words or bf16 pairs (also the lm_head input)
   float asumA[MAX_QD / 32];              // int4: sum of each 32-element chunk of actA
+  float gn[MAX_H];                       // weights of the next RMSNorm (DMA target)
   float ytmp[MAX_YROWS];                 // this workgroup's GEMV results of a phase
-  StageLds<QKV_CAP> sq;                  // QKV weights (staged during the previous layer)
-  StageLds<O_CAP> so;                    // o_proj weights (staged during the merge)
+  f32x2_t rcs[MAX_QPAIRS];               // RoPE (cos, sin) of this workgroup's QKV pairs at this position
   union {
     AttnLds att;
+    MergeLds mg;
     StageLds<R_CAP> rt;                  // router weights (staged during the o_proj exchange)
     MlpLds mlp;
-    uint32_t gbuf[MAX_GATHER];           // gathered attention partials
+    HeadLds head;
   } u;
-  float mrun[MAX_GQ], lrun[MAX_GQ], alpha[MAX_GQ], lsum[MAX_GQ];
   float z[MAX_E];                        // router logits
   int sel[MAX_K];
   float wsel[MAX_K];
   float wred[NW * 2];
   unsigned long long best[NW];
-  int flag;
+  int flag;                              // sticky: a wait of this workgroup failed
 };
 
 // ---------------------------------------------------------------- reductions
@@ -238,6 +272,32 @@ template <int WT> __device__ __forceinline__ void act_sums(const uint32_t* act, 
     }
   }
 }
+// RMSNorm of the residual with the weights sm.gn (brought in by this
+// workgroup's DMA), as the next GEMV input actA in the layout of OW.
+template <int WT, int OW = WT>
+__device__ __forceinline__ void rmsnorm_act(Smem& sm, int H, float eps, bool sums) {
+  const int tid = threadIdx.x;
+  wait_vmem();  // this wave's part of sm.gn has landed; block_sum's barrier publishes it
+  float ss = 0.f;
+  for (int e = tid; e < H; e += NT) ss += sm.xres[e] * sm.xres[e];
+  ss = block_sum(sm, ss);
+  const float inv = 1.0f / sqrtf(ss / (float)H + eps);
+  for (int e = tid; e < H; e += NT) act_put<OW>(sm.actA, e, act_round<WT>(sm.xres[e] * inv * sm.gn[e]));
+  __syncthreads();
+  if (sums) {
+    act_sums<OW>(sm.actA, sm.asumA, H);
+    __syncthreads();
+  }
+}
+// Bring n floats (n a multiple of 64) into sm.gn by DMA; wave w moves 1 KB units w, w + NW, ...
+__device__ __forceinline__ void gn_issue(Smem& sm, const float* src, int n) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int units = n / 4;  // 16-byte units
+  for (int gi = wave; gi * 64 < units; gi += NW) {
+    const int unit = min(gi * 64 + lane, units - 1);
+    dma16(src + 4 * unit, &sm.gn[gi * 256]);
+  }
+}
 
 // ---------------------------------------------------------------- GEMV
 
@@ -258,45 +318,76 @@ __device__ __forceinline__ RowSrc mrow(const Mat& m, long long row, int in, cons
   return r;
 }
 
+// One lane's activation chunk: 4 fp32, 8 bf16 or (int4 weights) 32 bf16 and their sum.
+template <int WT> struct ActC {
+  uint4 a[WT == W_I4 ? 4 : 1];
+  float s;
+};
+template <int WT> __device__ __forceinline__ ActC<WT> act_chunk(const uint32_t* act, const float* asum, int c) {
+  ActC<WT> r;
+  if constexpr (WT == W_I4) {
+    const uint4* p = reinterpret_cast<const uint4*>(act + 16 * c);
+    r.a[0] = p[0];
+    r.a[1] = p[1];
+    r.a[2] = p[2];
+    r.a[3] = p[3];
+    r.s = asum[c];
+  } else {
+    r.a[0] = *reinterpret_cast<const uint4*>(act + 4 * c);
+    r.s = 0.f;
+  }
+  return r;
+}
+
+// int4 unpack constants held in VGPRs: with them in registers one v_and_or_b32
+// turns a shifted word into two bf16 values (a VOP3 operand cannot be a literal).
+struct I4K {
+  uint32_t m, mag;
+};
+__device__ __forceinline__ I4K i4k() {
+  I4K k;
+  asm volatile("v_mov_b32 %0, 0xf000f" : "=v"(k.m));
+  asm volatile("v_mov_b32 %0, 0x43004300" : "=v"(k.mag));
+  return k;
+}
+
 // Dot product of one 16-byte weight chunk with the matching activation chunk.
 template <int WT>
-__device__ __forceinline__ float chunk_dot(uint4 w, const RowSrc& r, int c, float scale) {
+__device__ __forceinline__ float chunk_dot(uint4 w, const ActC<WT>& x, float scale, const I4K& k4) {
   if constexpr (WT == W_F32) {
-    float4 x = *reinterpret_cast<const float4*>(r.act + 4 * c);
-    float acc = __uint_as_float(w.x) * x.x;
-    acc = fmaf(__uint_as_float(w.y), x.y, acc);
-    acc = fmaf(__uint_as_float(w.z), x.z, acc);
-    return fmaf(__uint_as_float(w.w), x.w, acc);
+    const uint4 a = x.a[0];
+    float acc = __uint_as_float(w.x) * __uint_as_float(a.x);
+    acc = fmaf(__uint_as_float(w.y), __uint_as_float(a.y), acc);
+    acc = fmaf(__uint_as_float(w.z), __uint_as_float(a.z), acc);
+    return fmaf(__uint_as_float(w.w), __uint_as_float(a.w), acc);
   } else if constexpr (WT == W_BF16) {
-    uint4 x = *reinterpret_cast<const uint4*>(r.act + 4 * c);
-    float acc = dot2(w.x, x.x, 0.f);
-    acc = dot2(w.y, x.y, acc);
-    acc = dot2(w.z, x.z, acc);
-    return dot2(w.w, x.w, acc);
+    const uint4 a = x.a[0];
+    float acc = dot2(w.x, a.x, 0.f);
+    acc = dot2(w.y, a.y, acc);
+    acc = dot2(w.z, a.z, acc);
+    return dot2(w.w, a.w, acc);
   } else {
     // nibble n of a word becomes bf16 (128 + n) via 0x4300 | n; the chunk sum
     // of the activation removes the 128 + 8 offset: sum (u - 8) a = sum (128 + u) a - 136 sum a
-    const uint4* xp = reinterpret_cast<const uint4*>(r.act + 16 * c);
     const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
     float a0 = 0.f, a1 = 0.f;
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
-      uint4 x = xp[k];
-      uint32_t q = ww[k];
-      a0 = dot2((q & 0x000F000Fu) | 0x43004300u, x.x, a0);
-      a1 = dot2(((q >> 4) & 0x000F000Fu) | 0x43004300u, x.y, a1);
-      a0 = dot2(((q >> 8) & 0x000F000Fu) | 0x43004300u, x.z, a0);
-      a1 = dot2(((q >> 12) & 0x000F000Fu) | 0x43004300u, x.w, a1);
+      const uint4 a = x.a[k];
+      const uint32_t q = ww[k];
+      a0 = dot2((q & k4.m) | k4.mag, a.x, a0);
+      a1 = dot2(((q >> 4) & k4.m) | k4.mag, a.y, a1);
+      a0 = dot2(((q >> 8) & k4.m) | k4.mag, a.z, a0);
+      a1 = dot2(((q >> 12) & k4.m) | k4.mag, a.w, a1);
     }
-    return scale * ((a0 + a1) - 136.0f * r.asum[c]);
+    return scale * ((a0 + a1) - 136.0f * x.s);
   }
 }
 
 // Lane geometry of a GEMV over `nrows` rows of width `in`: each row is read in
-// 16-byte chunks by a group of LPR lanes (64, or fewer for short rows, several
-// rows per wave).  A lane's work is a list of NI items (row pass p, chunk j),
-// processed in register-staged blocks of R items whose loads are all in flight
-// together.
+// 16-byte chunks by a group of LPR lanes (64, or fewer for short rows, RPW
+// rows side by side in a wave).  A wave's work is a list of NI items (row
+// pass p, chunk j), staged in LDS and computed in rounds.
 struct Geo {
   int nrows, C, LPR, RPW, CPL, NI, sub, li, wave;
 };
@@ -310,7 +401,7 @@ template <int WT> __device__ __forceinline__ Geo geo(int nrows, int in) {
   g.RPW = 64 / LPR;
   g.CPL = (g.C + LPR - 1) / LPR;
   const int lane = threadIdx.x & 63;
-  g.wave = threadIdx.x >> 6;
+  g.wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   g.sub = lane / LPR;
   g.li = lane % LPR;
   const int npass = (nrows + NW * g.RPW - 1) / (NW * g.RPW);
@@ -318,91 +409,15 @@ template <int WT> __device__ __forceinline__ Geo geo(int nrows, int in) {
   return g;
 }
 
-template <int R> struct Stage {
-  uint4 w[R];
-  float s[R];
-};
-
-template <int WT, int R, class RowFn>
-__device__ __forceinline__ void stage_load(Stage<R>& st, const Geo& g, int blk, RowFn rowfn) {
-  int p = (blk * R) / g.CPL, j = blk * R - p * g.CPL;
-#pragma unroll
-  for (int i = 0; i < R; ++i, (++j == g.CPL ? (j = 0, ++p) : 0)) {
-    const int k = blk * R + i;
-    if (k < g.NI) {
-      const int r = g.wave * g.RPW + p * NW * g.RPW + g.sub, c = g.li + j * g.LPR;
-      if (r < g.nrows && c < g.C) {
-        const RowSrc src = rowfn(r);
-        st.w[i] = *reinterpret_cast<const uint4*>(src.w + 16ll * c);
-        if constexpr (WT == W_I4) st.s[i] = bf2f(src.s[c >> 1]);
-      }
-    }
-  }
-}
-
-template <int WT, int R, class RowFn, class OutFn>
-__device__ __forceinline__ void stage_compute(const Stage<R>& st, const Geo& g, int blk, float& acc, RowFn rowfn,
-                                              OutFn outfn) {
-  int p = (blk * R) / g.CPL, j = blk * R - p * g.CPL;
-#pragma unroll
-  for (int i = 0; i < R; ++i, (++j == g.CPL ? (j = 0, ++p) : 0)) {
-    const int k = blk * R + i;
-    if (k < g.NI) {  // uniform across the wave
-      const int r = g.wave * g.RPW + p * NW * g.RPW + g.sub, c = g.li + j * g.LPR;
-      if (r < g.nrows && c < g.C) acc += chunk_dot<WT>(st.w[i], rowfn(r), c, WT == W_I4 ? st.s[i] : 1.f);
-      if (j == g.CPL - 1) {
-        const float v = group_sum(acc, g.LPR);
-        if (g.li == 0 && r < g.nrows) outfn(r, v);
-        acc = 0.f;
-      }
-    }
-  }
-}
-
-// Run a GEMV whose first block may already be staged (`pre`).  With DB the
-// blocks are double-buffered (the next block's loads are in flight during
-// compute); without it a phase that fits one block holds a single stage.
-template <int WT, int R, bool DB, class RowFn, class OutFn>
-__device__ __forceinline__ void gemv_run(const Geo& g, Stage<R>& A, bool pre, RowFn rowfn, OutFn outfn) {
-  const int nb = (g.NI + R - 1) / R;
-  float acc = 0.f;
-  if constexpr (DB) {
-    if (!pre) stage_load<WT, R>(A, g, 0, rowfn);
-    Stage<R> B;
-    for (int b = 0; b < nb; b += 2) {
-      if (b + 1 < nb) stage_load<WT, R>(B, g, b + 1, rowfn);
-      stage_compute<WT, R>(A, g, b, acc, rowfn, outfn);
-      if (b + 1 < nb) {
-        if (b + 2 < nb) stage_load<WT, R>(A, g, b + 2, rowfn);
-        stage_compute<WT, R>(B, g, b + 1, acc, rowfn, outfn);
-      }
-    }
-  } else {
-    for (int b = 0; b < nb; ++b) {
-      if (b > 0 || !pre) stage_load<WT, R>(A, g, b, rowfn);
-      stage_compute<WT, R>(A, g, b, acc, rowfn, outfn);
-    }
-  }
-}
-
-// LDS-staged GEMV: the items of a phase are brought into LDS by DMA (no
-// registers held, so every load of the phase is in flight at once and the
-// loads can be issued long before the activation is ready), then each wave
-// computes its own items from LDS.  Phases with more items than the staging
-// area holds run in rounds.
+// LDS staging: the items of a round are brought into LDS by DMA (no registers
+// held, so every load of the round is in flight at once and can be issued
+// long before the activation is ready), then each wave computes its own items.
 struct LStage {
   uint4* w16;
   uint32_t* s32;
   int cap;
 };
 template <int CAP> __device__ __forceinline__ LStage lstage(StageLds<CAP>& s) { return LStage{s.w16, s.s32, CAP}; }
-
-__device__ __forceinline__ void dma16(const void* g, void* l) {
-  __builtin_amdgcn_global_load_lds(g, (lds_void*)l, 16, 0, 0);
-}
-__device__ __forceinline__ void dma4(const void* g, void* l) { __builtin_amdgcn_global_load_lds(g, (lds_void*)l, 4, 0, 0); }
-// wait until this wave's LDS reads have completed (lgkmcnt(0))
-__device__ __forceinline__ void wait_lds() { __builtin_amdgcn_s_waitcnt(0xC07F); }
 
 template <int WT, class RowFn>
 __device__ __forceinline__ void lstage_issue(const LStage& st, const Geo& g, int round, RowFn rowfn) {
@@ -423,48 +438,313 @@ __device__ __forceinline__ void lstage_issue(const LStage& st, const Geo& g, int
   }
 }
 
-template <int WT, class RowFn, class OutFn>
-__device__ __forceinline__ void lstage_compute(const LStage& st, const Geo& g, int round, float& acc, RowFn rowfn,
+// Issue NIS items (known at compile time) starting at item k0: every chunk
+// address first (any LDS reads the row function needs are batched), then the
+// DMA instructions back to back.
+template <int WT, int NIS, class RowFn>
+__device__ __forceinline__ void lstage_issue_static(const LStage& st, const Geo& g, int k0, RowFn rowfn) {
+  const uint8_t* wp[NIS];
+  const uint16_t* sp[NIS];
+  bool ok[NIS];
+#pragma unroll
+  for (int i = 0; i < NIS; ++i) {
+    const int k = k0 + i, p = k / g.CPL, j = k - p * g.CPL;
+    const int r = g.wave * g.RPW + p * NW * g.RPW + g.sub, c = g.li + j * g.LPR;
+    ok[i] = r < g.nrows && c < g.C;
+    const RowSrc src = rowfn(ok[i] ? r : 0);
+    wp[i] = src.w + 16ll * c;
+    sp[i] = WT == W_I4 ? src.s + ((c >> 1) & ~1) : nullptr;
+  }
+#pragma unroll
+  for (int i = 0; i < NIS; ++i)
+    if (ok[i]) {
+      dma16(wp[i], &st.w16[(i * NW + g.wave) * 64]);
+      if constexpr (WT == W_I4) dma4(sp[i], &st.s32[(i * NW + g.wave) * 64]);
+    }
+}
+// Round 0 of a GEMV: the static issue when its NIS items fit the capacity, else the general loop.
+template <int WT, int NIS, int CAP, class RowFn>
+__device__ __forceinline__ void issue_auto(const LStage& st, const Geo& g, RowFn rowfn) {
+  if constexpr (NIS > 0 && NIS <= CAP) lstage_issue_static<WT, NIS>(st, g, 0, rowfn);
+  else lstage_issue<WT>(st, g, 0, rowfn);
+}
+
+// A lane's activation chunks for a phase whose rows all share one input (CPLR chunks per lane).
+template <int WT, int CPLR> struct ActRegs {
+  ActC<WT> c[CPLR > 0 ? CPLR : 1];
+};
+template <int WT, int CPLR>
+__device__ __forceinline__ ActRegs<WT, CPLR> act_regs(const Geo& g, const uint32_t* act, const float* asum) {
+  ActRegs<WT, CPLR> r;
+  if constexpr (CPLR > 0) {
+#pragma unroll
+    for (int j = 0; j < CPLR; ++j) {
+      const int c = g.li + j * g.LPR;
+      r.c[j] = act_chunk<WT>(act, asum, c < g.C ? c : 0);
+    }
+  }
+  return r;
+}
+
+// bf16 scale of chunk c from the staged dword holding the scales of groups (c / 2) & ~1 and + 1
+__device__ __forceinline__ float chunk_scale(uint32_t sw, int c) {
+  return bf2f(((c >> 1) & 1) ? (sw >> 16) : (sw & 0xFFFFu));
+}
+template <int WT>
+__device__ __forceinline__ float item_dot(const LStage& st, int slot, int c, const ActC<WT>& a, const I4K& k4) {
+  const uint4 w = st.w16[slot];
+  float scale = 1.f;
+  if constexpr (WT == W_I4) scale = chunk_scale(st.s32[slot], c);
+  return chunk_dot<WT>(w, a, scale, k4);
+}
+
+// Sum over the wave of R rows at once (R a power of two, at most 16).  Lane
+// bit 5, then bits 4, 3, 2 split the rows between lanes: each step pairs two
+// partial rows, every lane keeps one of them and adds its partner lane's copy
+// (permlane swaps across 32 and 16 lanes, then DPP mirrors within 16 and 8),
+// so a step halves the values a lane carries; the lane bits left over are
+// summed.  On return every lane holds the total of row row_of<R>(lane).
+template <int R> __device__ __forceinline__ int row_of(int lane) {
+  constexpr int LG = R >= 16 ? 4 : R >= 8 ? 3 : R >= 4 ? 2 : R >= 2 ? 1 : 0;
+  int r = LG > 0 ? (lane >> 5) & 1 : 0;
+#pragma unroll
+  for (int j = 1; j < LG; ++j) r |= ((lane >> (5 - j)) & 1) << (LG - j);
+  return r;
+}
+template <int CTRL>
+__device__ __forceinline__ float keep_add(float x, float y, bool hi) {  // hi ? y + partner's y : x + partner's x
+  const float keep = hi ? y : x, send = hi ? x : y;
+  return keep + dpp<CTRL>(send);
+}
+template <int R> __device__ __forceinline__ float reduce_rows(const float (&a)[R]) {
+  static_assert(R == 1 || R == 2 || R == 4 || R == 8 || R == 16, "rows per reduction");
+  const int lane = threadIdx.x & 63;
+  if constexpr (R == 1) {
+    return wave_sum(a[0]);
+  } else {
+    float b[R / 2];  // lane ^ 32: lanes 0-31 keep row 2k, lanes 32-63 row 2k + 1
+#pragma unroll
+    for (int k = 0; k < R / 2; ++k) {
+      const auto s = __builtin_amdgcn_permlane32_swap(__float_as_int(a[2 * k]), __float_as_int(a[2 * k + 1]), false, false);
+      b[k] = __int_as_float(s[0]) + __int_as_float(s[1]);
+    }
+    if constexpr (R == 2) {
+      float v = b[0];
+      v += dpp<DPP_XOR1>(v);
+      v += dpp<DPP_XOR2>(v);
+      v += dpp<DPP_HALF_MIRROR>(v);
+      v += dpp<DPP_MIRROR>(v);
+      return v + swap16(v);
+    } else {
+      float c[R / 4];  // lane ^ 16: lanes with bit 4 clear keep b[k], set keep b[k + R / 4]
+#pragma unroll
+      for (int k = 0; k < R / 4; ++k) {
+        const auto s = __builtin_amdgcn_permlane16_swap(__float_as_int(b[k]), __float_as_int(b[k + R / 4]), false, false);
+        c[k] = __int_as_float(s[0]) + __int_as_float(s[1]);
+      }
+      if constexpr (R == 4) {
+        float v = c[0];
+        v += dpp<DPP_XOR1>(v);
+        v += dpp<DPP_XOR2>(v);
+        v += dpp<DPP_HALF_MIRROR>(v);
+        return v + dpp<DPP_MIRROR>(v);
+      } else {
+        const bool h3 = lane & 8;
+        float d[R / 8];  // mirror within 16 lanes (partner 15 - l): bit 3 picks the row
+#pragma unroll
+        for (int k = 0; k < R / 8; ++k) d[k] = keep_add<DPP_MIRROR>(c[k], c[k + R / 8], h3);
+        if constexpr (R == 8) {
+          float v = d[0];
+          v += dpp<DPP_XOR1>(v);
+          v += dpp<DPP_XOR2>(v);
+          return v + dpp<DPP_HALF_MIRROR>(v);
+        } else {
+          const bool h2 = lane & 4;  // mirror within 8 lanes (partner 7 - l): bit 2 picks the row
+          float v = keep_add<DPP_HALF_MIRROR>(d[0], d[1], h2);
+          v += dpp<DPP_XOR1>(v);
+          return v + dpp<DPP_XOR2>(v);
+        }
+      }
+    }
+  }
+}
+
+// Compute NIS staged items of this wave in one pass (static shapes: 64 lanes
+// per row, every item valid, CPLR chunks per row, activation in registers):
+// all LDS reads first, then the dot products, then one reduction for the
+// wave's rows.  p0: row pass of the first item.
+template <int WT, int CPLR, int NIS, class OutFn>
+__device__ __forceinline__ void compute_static(const LStage& st, const Geo& g, int p0, const ActRegs<WT, CPLR>& ar,
                                                OutFn outfn) {
+  static_assert(CPLR > 0 && NIS % CPLR == 0 && NIS / CPLR <= 16, "whole rows, at most 16 per wave");
+  constexpr int NR = NIS / CPLR;
+  constexpr int R = NR <= 1 ? 1 : NR <= 2 ? 2 : NR <= 4 ? 4 : NR <= 8 ? 8 : 16;
+  const int lane = threadIdx.x & 63;
+  const I4K k4 = i4k();
+  uint4 w[NIS];
+  uint32_t s[NIS];
+#pragma unroll
+  for (int i = 0; i < NIS; ++i) {
+    w[i] = st.w16[(i * NW + g.wave) * 64 + lane];
+    if constexpr (WT == W_I4) s[i] = st.s32[(i * NW + g.wave) * 64 + lane];
+  }
+  float acc[R];
+#pragma unroll
+  for (int p = 0; p < R; ++p) {
+    acc[p] = 0.f;
+    if (p < NR) {
+#pragma unroll
+      for (int j = 0; j < CPLR; ++j)
+        acc[p] += chunk_dot<WT>(w[p * CPLR + j], ar.c[j], WT == W_I4 ? chunk_scale(s[p * CPLR + j], lane + 64 * j) : 1.f,
+                                k4);
+    }
+  }
+  const float v = reduce_rows<R>(acc);
+  const int rho = row_of<R>(lane);
+  if ((lane & (64 / R - 1)) == 0 && rho < NR) {
+    const int r = g.wave + (p0 + rho) * NW;
+    if (r < g.nrows) outfn(r, v);
+  }
+}
+
+// Compute NIS staged items of this wave whose activation chunk depends on the
+// row (read from LDS through rowfn), any lanes per row, one chunk per lane per
+// row (static shapes): loads of a batch of NB items first, then their dot
+// products, a sum over each row's lanes per item.
+template <int WT, int NIS, int NB, class RowFn, class OutFn>
+__device__ __forceinline__ void compute_static_rows(const LStage& st, const Geo& g, RowFn rowfn, OutFn outfn) {
+  static_assert(NIS % NB == 0, "whole batches");
+  const int lane = threadIdx.x & 63;
+  const I4K k4 = i4k();
+  const int c = g.li;
+#pragma unroll
+  for (int b0 = 0; b0 < NIS; b0 += NB) {
+    uint4 w[NB];
+    uint32_t s[NB];
+    ActC<WT> a[NB];
+    int r[NB];
+#pragma unroll
+    for (int i = 0; i < NB; ++i) {
+      r[i] = g.wave * g.RPW + (b0 + i) * NW * g.RPW + g.sub;
+      const int slot = ((b0 + i) * NW + g.wave) * 64 + lane;
+      w[i] = st.w16[slot];
+      if constexpr (WT == W_I4) s[i] = st.s32[slot];
+      const RowSrc src = rowfn(r[i] < g.nrows ? r[i] : 0);
+      a[i] = act_chunk<WT>(src.act, src.asum, c < g.C ? c : 0);
+    }
+#pragma unroll
+    for (int i = 0; i < NB; ++i) {
+      float acc = 0.f;
+      if (c < g.C) acc = chunk_dot<WT>(w[i], a[i], WT == W_I4 ? chunk_scale(s[i], c) : 1.f, k4);
+      const float v = group_sum(acc, g.LPR);
+      if (g.li == 0 && r[i] < g.nrows) outfn(r[i], v);
+    }
+  }
+}
+
+// A staged GEMV of the static shape whose items fit one round of NIS items per wave.
+template <int WT, int CPLR, int NIS, class RowFn, class OutFn>
+__device__ __forceinline__ void gemv_static(const LStage& st, const Geo& g, bool issued, const ActRegs<WT, CPLR>& ar,
+                                            RowFn rowfn, OutFn outfn) {
+  if (!issued) lstage_issue_static<WT, NIS>(st, g, 0, rowfn);
+  wait_vmem();
+  compute_static<WT, CPLR, NIS>(st, g, 0, ar, outfn);
+}
+
+// The single-round static path when the wave's NIS items (known at compile
+// time, 0 = not) fit the capacity CAP, else the general rounds.
+template <int WT, int CPLR, int NIS, int CAP, class RowFn, class OutFn>
+__device__ __forceinline__ void gemv_auto(const LStage& st, const Geo& g, bool issued, const ActRegs<WT, CPLR>& ar,
+                                          RowFn rowfn, OutFn outfn) {
+  if constexpr (CPLR > 0 && NIS > 0 && NIS <= CAP && NIS / CPLR <= 16)
+    gemv_static<WT, CPLR, NIS>(st, g, issued, ar, rowfn, outfn);
+  else
+    gemv_lds<WT, CPLR>(st, g, issued, ar, rowfn, outfn);
+}
+
+// Compute round `round` of this wave's items.  CPLR > 0: every row has CPLR
+// chunks per lane, the capacity is a multiple of CPLR and the activation is in
+// registers; CPLR == 0: any geometry, the activation read from LDS per item.
+template <int WT, int CPLR, class RowFn, class OutFn>
+__device__ __forceinline__ void lstage_compute(const LStage& st, const Geo& g, int round, float& acc,
+                                               const ActRegs<WT, CPLR>& ar, RowFn rowfn, OutFn outfn) {
   const int k0 = round * st.cap;
   const int n = min(st.cap, g.NI - k0);
   const int lane = threadIdx.x & 63;
-  int p = k0 / g.CPL, j = k0 - p * g.CPL;
+  const I4K k4 = i4k();
+  if constexpr (CPLR > 0) {
+    int p = k0 / CPLR;
 #pragma unroll 2
-  for (int i = 0; i < n; ++i) {
-    const int r = g.wave * g.RPW + p * NW * g.RPW + g.sub, c = g.li + j * g.LPR;
-    if (r < g.nrows && c < g.C) {
-      const uint4 w = st.w16[(i * NW + g.wave) * 64 + lane];
-      float scale = 1.f;
-      if constexpr (WT == W_I4) {
-        const uint32_t sw = st.s32[(i * NW + g.wave) * 64 + lane];
-        scale = bf2f(((c >> 1) & 1) ? (sw >> 16) : (sw & 0xFFFFu));
+    for (int i0 = 0; i0 < n; i0 += CPLR, ++p) {
+      const int r = g.wave * g.RPW + p * NW * g.RPW + g.sub;
+#pragma unroll
+      for (int j = 0; j < CPLR; ++j) {
+        const int c = g.li + j * g.LPR;
+        if (r < g.nrows && c < g.C) acc += item_dot<WT>(st, ((i0 + j) * NW + g.wave) * 64 + lane, c, ar.c[j], k4);
       }
-      acc += chunk_dot<WT>(w, rowfn(r), c, scale);
-    }
-    if (j == g.CPL - 1) {  // uniform across the wave
       const float v = group_sum(acc, g.LPR);
       if (g.li == 0 && r < g.nrows) outfn(r, v);
       acc = 0.f;
     }
-    if (++j == g.CPL) {
-      j = 0;
-      ++p;
+  } else {
+    int p = k0 / g.CPL, j = k0 - p * g.CPL;
+#pragma unroll 2
+    for (int i = 0; i < n; ++i) {
+      const int r = g.wave * g.RPW + p * NW * g.RPW + g.sub, c = g.li + j * g.LPR;
+      if (r < g.nrows && c < g.C) {
+        const RowSrc src = rowfn(r);
+        acc += item_dot<WT>(st, (i * NW + g.wave) * 64 + lane, c, act_chunk<WT>(src.act, src.asum, c), k4);
+      }
+      if (j == g.CPL - 1) {  // uniform across the wave
+        const float v = group_sum(acc, g.LPR);
+        if (g.li == 0 && r < g.nrows) outfn(r, v);
+        acc = 0.f;
+      }
+      if (++j == g.CPL) {
+        j = 0;
+        ++p;
+      }
     }
   }
 }
 
 // Run a staged GEMV; `issued`: round 0 was already issued.  The activation
-// (read through rowfn) must be in LDS and visible to this wave.
-template <int WT, class RowFn, class OutFn>
-__device__ __forceinline__ void gemv_lds(const LStage& st, const Geo& g, bool issued, RowFn rowfn, OutFn outfn) {
+// must be in LDS (and, for CPLR > 0, in `ar`) before the call.
+template <int WT, int CPLR, class RowFn, class OutFn>
+__device__ __forceinline__ void gemv_lds(const LStage& st, const Geo& g, bool issued, const ActRegs<WT, CPLR>& ar,
+                                         RowFn rowfn, OutFn outfn) {
   const int nr = (g.NI + st.cap - 1) / st.cap;
   float acc = 0.f;
   for (int b = 0; b < nr; ++b) {
-    if (b > 0) wait_lds();
+    if (b > 0) wait_lds();  // this wave's reads of the previous round are done before the DMA reuses the slots
     if (b > 0 || !issued) lstage_issue<WT>(st, g, b, rowfn);
     wait_vmem();
-    lstage_compute<WT>(st, g, b, acc, rowfn, outfn);
+    lstage_compute<WT, CPLR>(st, g, b, acc, ar, rowfn, outfn);
+  }
+}
+
+// Streaming GEMV with two staging buffers: round b + 1 is in flight while
+// round b is computed.  Static shapes only: every lane of every item valid
+// (whole rows of 64 lanes, rows a multiple of the waves, items a multiple of
+// CAP), so a round issues exactly CAP DMA instructions per wave (no scales)
+// and the older round can be waited for with vmcnt(CAP).
+template <int WT, int CPLR, int CAP, class RowFn, class OutFn>
+__device__ __forceinline__ void gemv_stream(const LStage& A, const LStage& B, const Geo& g,
+                                            const ActRegs<WT, CPLR>& ar, RowFn rowfn, OutFn outfn) {
+  static_assert(WT != W_I4 && CPLR > 0 && CAP % CPLR == 0, "streamed GEMV: bf16 / fp32 rows, activation in registers");
+  const int nr = g.NI / CAP;
+  if (nr > 0) lstage_issue_static<WT, CAP>(A, g, 0, rowfn);
+  for (int b = 0; b < nr; ++b) {
+    const LStage& cur = (b & 1) ? B : A;
+    const LStage& nxt = (b & 1) ? A : B;
+    if (b + 1 < nr) {
+      wait_lds();  // this wave's reads of round b - 1 (in nxt) are done
+      lstage_issue_static<WT, CAP>(nxt, g, (b + 1) * CAP, rowfn);
+      wait_vmem_n<CAP>();  // round b + 1 issued CAP loads: round b has landed
+    } else {
+      wait_vmem();
+    }
+    compute_static<WT, CPLR, CAP>(cur, g, b * (CAP / CPLR), ar, outfn);
   }
 }
 
@@ -485,15 +765,15 @@ __device__ __forceinline__ void backoff(const Waiter& wt) {
 // Latch an error: atomically in device memory, by a plain system-scope store
 // in the host-mapped word (the host only tests it for non-zero).
 __device__ __forceinline__ void raise_error(const Waiter& wt, uint32_t bits) {
-  __hip_atomic_fetch_or(wt.err, bits, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
-  __hip_atomic_store(wt.herr, bits, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+  __hip_atomic_fetch_or(gp(wt.err), bits, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+  __hip_atomic_store(gp(wt.herr), bits, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
 }
 
 // True once this wait should give up: another wait has timed out, or this one
 // has run for longer than the timeout (which it then reports).
 __device__ __forceinline__ bool poll_timed_out(const Waiter& wt, uint64_t t0, uint32_t it) {
   if ((it & 15) == 0 &&
-      (__hip_atomic_load(wt.err, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM) & ERR_TIMEOUT))
+      (__hip_atomic_load(gp(wt.err), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM) & ERR_TIMEOUT))
     return true;
   if (now() - t0 > SPIN_TIMEOUT) {
     raise_error(wt, ERR_TIMEOUT);
@@ -502,11 +782,9 @@ __device__ __forceinline__ bool poll_timed_out(const Waiter& wt, uint64_t t0, ui
   return false;
 }
 
-// Make a thread's abort decision the workgroup's (uniform) decision.
+// Barrier that also makes any thread's abort the workgroup's (uniform) decision.
+// The LDS flag is sticky: after a failed wait the launch only winds down.
 __device__ __forceinline__ bool sync_ok(Smem& sm, Waiter& wt) {
-  __syncthreads();
-  if (threadIdx.x == 0) sm.flag = 0;
-  __syncthreads();
   if (wt.abort) sm.flag = 1;
   __syncthreads();
   wt.abort = sm.flag != 0;
@@ -519,8 +797,8 @@ __device__ __forceinline__ bool sync_ok(Smem& sm, Waiter& wt) {
 // re-polls only those still stale.  Called by the whole workgroup; returns
 // false (uniformly) if a wait failed.
 template <class IndexFn, class SentFn, class PutFn>
-__device__ __forceinline__ bool gather(Smem& sm, const uint64_t* src, int n, uint32_t tag, IndexFn index, SentFn sent, int nsent,
-                       PutFn put, Waiter& wt) {
+__device__ __forceinline__ bool gather(Smem& sm, const uint64_t* src, int n, uint32_t tag, IndexFn index, SentFn sent,
+                                       int nsent, PutFn put, Waiter& wt) {
   const int tid = threadIdx.x;
   if (nsent > wt.sentinels) nsent = wt.sentinels;
   if (tid < 64 && tid < nsent && !wt.abort) {
@@ -585,10 +863,18 @@ __device__ __forceinline__ bool gather_flat(Smem& sm, const uint64_t* src, int n
       ns, put, wt);
 }
 
-// Replicated exchange buffer: [NCOPY][2 parities][n] slots.
-__device__ __forceinline__ void put_all(uint64_t* base, int n, int par, int idx, uint64_t v) {
-#pragma unroll
-  for (int c = 0; c < NCOPY; ++c) xstore(base + (size_t)(c * 2 + par) * n + idx, v);
+// Publish `count` values into a replicated exchange buffer [NCOPY][2 parities][n]:
+// thread t stores value t % count of replica t / count, so neighbouring lanes
+// write neighbouring slots and a wave's stores cover whole cache lines;
+// val(i, idx) returns the payload of value i and sets its slot index.
+template <class ValFn>
+__device__ __forceinline__ void publish(uint64_t* base, int n, int par, int count, uint32_t tag, ValFn val) {
+  for (int t = threadIdx.x; t < count * NCOPY; t += NT) {
+    const int c = t / count, i = t - c * count;
+    int idx;
+    const uint32_t v = val(i, idx);
+    xstore(base + (size_t)(c * 2 + par) * n + idx, slot(tag, v));
+  }
 }
 __device__ __forceinline__ const uint64_t* copy_of(const uint64_t* base, int n, int par) {
   return base + (size_t)((xcc_id() & (NCOPY - 1)) * 2 + par) * n;
@@ -596,33 +882,15 @@ __device__ __forceinline__ const uint64_t* copy_of(const uint64_t* base, int n, 
 
 // ---------------------------------------------------------------- attention data
 
-// K rows of positions [c0, c0 + np) to registers: TPP threads per row, 64 B each,
-// KV_PASSES passes of NT / TPP positions; rows past np re-read the last one.
-template <int WT>
-__device__ __forceinline__ void load_k(uint4 (&kreg)[KV_PASSES][4], const uint8_t* kbase, int c0, int np, int rowb) {
-  const int TPP = rowb / 64, PPP = NT / TPP;
-  const int pp = threadIdx.x / TPP, pt = threadIdx.x % TPP;
-#pragma unroll
-  for (int p = 0; p < KV_PASSES; ++p) {
-    const int i = p * PPP + pp;
-    const int tau = c0 + (i < np ? i : np - 1);
-    const uint4* src = reinterpret_cast<const uint4*>(kbase + (size_t)tau * rowb + pt * 64);
-#pragma unroll
-    for (int k = 0; k < 4; ++k) kreg[p][k] = src[k];
-  }
-}
-// V rows of positions [c0, c0 + np) into LDS by DMA, 1 KB per wave instruction.
-__device__ __forceinline__ void load_v(uint4* vbuf, const uint8_t* vbase, int c0, int np, int rowb) {
+// Rows [c0, c0 + np) of one (layer, sequence, kv head) cache slice into LDS,
+// 1 KB per wave instruction; lanes past the end re-read the last 16 bytes.
+__device__ __forceinline__ void kv_issue(uint4* buf, const uint8_t* base, int c0, int np, int rowb) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const uint8_t* vsrc = vbase + (size_t)c0 * rowb;
+  const uint8_t* src = base + (size_t)c0 * rowb;
   const int units = np * rowb / 16;
-#pragma unroll
-  for (int q = 0; q < KV_CHUNK_BYTES / (NT * 16); ++q) {
-    const int gi = q * NW + wave;
-    if (gi * 64 < units) {
-      const int unit = min(gi * 64 + lane, units - 1);
-      __builtin_amdgcn_global_load_lds(vsrc + (size_t)unit * 16, (lds_void*)&vbuf[gi * 64], 16, 0, 0);
-    }
+  for (int gi = wave; gi * 64 < units; gi += NW) {
+    const int unit = min(gi * 64 + lane, units - 1);
+    dma16(src + (size_t)unit * 16, &buf[gi * 64]);
   }
 }
 
@@ -641,12 +909,31 @@ struct Shape2048 {
   static constexpr int G = 256, H = 2048, HD = 128, NQ = 16, NKV = 4, V = 65536, DI = 6144, E = 64, K = 6, EI = 768;
 };
 
+// Chunks per lane of a GEMV over rows of `in` elements staged CAP items at a
+// time, when the shape is static and CAP holds whole rows (0: the dynamic path).
+template <int WT, class SH> constexpr int cpl_fit(int in, int cap) {
+  if (!SH::kStatic) return 0;
+  const int C = in / kChunkElems<WT>;
+  const int cpl = C >= 64 ? (C + 63) / 64 : 1;
+  return cap % cpl == 0 ? cpl : 0;
+}
+
+// Items per wave of a GEMV whose workgroups own `per_wg` rows each (0 unless
+// the rows split evenly over the waves), at cpl chunks per row.
+constexpr int nis_of(int per_wg, int cpl) { return cpl > 0 && per_wg > 0 && per_wg % NW == 0 ? per_wg / NW * cpl : 0; }
+constexpr int even_share(int total, int G) { return G > 0 && total % G == 0 ? total / G : 0; }
+
 template <int WT, class SH>
 __global__ void __launch_bounds__(NT, 1) decode_kernel(const KStatic* __restrict__ ksp, const KDyn d) {
   __shared__ Smem sm;
-  const KStatic& ks = *ksp;
   constexpr bool SS = SH::kStatic;
-  const int G = SS ? SH::G : (int)gridDim.x, W = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int G = SS ? SH::G : (int)gridDim.x, W = blockIdx.x, tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  static_assert(sizeof(KStatic) % 4 == 0, "context copied as words");
+  for (int i = tid; i < (int)(sizeof(KStatic) / 4); i += NT)
+    reinterpret_cast<uint32_t*>(&sm.ks)[i] = gp(reinterpret_cast<const uint32_t*>(ksp))[i];
+  __syncthreads();
+  const KStatic& ks = sm.ks;
   const int H = SS ? SH::H : ks.H, hd = SS ? SH::HD : ks.hd, nq = SS ? SH::NQ : ks.nq, nkv = SS ? SH::NKV : ks.nkv;
   const int QD = nq * hd, Gq = nq / nkv, L = ks.L;
   const int V_ = SS ? SH::V : ks.V, DI_ = SS ? SH::DI : ks.DI, E_ = SS ? SH::E : ks.E, K_ = SS ? SH::K : ks.K;
@@ -655,15 +942,37 @@ __global__ void __launch_bounds__(NT, 1) decode_kernel(const KStatic* __restrict
   const int OSL = kAct32<WT> ? QD : QD / 2;                      // slots of the merged attention output
   const int HSLOTS = ks.h_slots;                                 // slots of the SwiGLU output exchange
   Waiter wt{ks.err, ks.herr, ks.poll_sleep, ks.sentinels, false};
+  // context values used inside DMA issue loops and publishes, held in registers
+  const Mat m_qkv = ks.qkv, m_o = ks.o, m_r = ks.router, m_dg = ks.dg, m_du = ks.du, m_dd = ks.dd;
+  const Mat m_eg = ks.eg, m_eu = ks.eu, m_ed = ks.ed;
+  const float *const p_anorm = ks.anorm, *const p_pnorm = ks.pnorm, *const p_fnorm = ks.fnorm;
+  uint64_t *const x_qkv = ks.x_qkv, *const x_part = ks.x_part, *const x_o = ks.x_o;
+  uint64_t *const x_res1 = ks.x_res1, *const x_h = ks.x_h, *const x_res2 = ks.x_res2;
   uint8_t* const kc = d.kc;
   uint8_t* const vc = d.vc;
   const int seq = d.seq, B = d.B, cap = d.cap;
-  const float2* const rope = d.rope;
-  uint64_t* const stamps = (d.dbg_ts != nullptr && W == 0 && tid == 0) ? d.dbg_ts : nullptr;
+  GLOBAL uint64_t* const stamps = (d.dbg_ts != nullptr && W == 0 && tid == 0) ? gp(d.dbg_ts) : nullptr;
+  // chunks per lane of each GEMV of the static shape (0: dynamic geometry, activation read from LDS)
+  constexpr int HW = WT == W_I4 ? W_BF16 : WT;  // the head is bf16 (or fp32) even when the layers are int4
+  constexpr int CP_QKV = cpl_fit<WT, SH>(SH::H, QKV_CAP), CP_O = cpl_fit<WT, SH>(SH::NQ * SH::HD, O_CAP);
+  constexpr int CP_R = cpl_fit<WT, SH>(SH::H, R_CAP), CP_GU = cpl_fit<WT, SH>(SH::H, GU_CAP);
+  constexpr int CP_DN = cpl_fit<WT, SH>(SH::DI, DN_CAP), CP_LM = cpl_fit<HW, SH>(SH::H, LM_CAP);
+  // items per wave of each GEMV of the static shape (0: general rounds)
+  constexpr int NI_QKV = nis_of(2 * even_share((SH::NQ + 2 * SH::NKV) * SH::HD / 2, SH::G), CP_QKV);
+  constexpr int NI_O = nis_of(even_share(SH::H, SH::G), CP_O), NI_R = nis_of(SH::E, CP_R);
+  constexpr int NI_GUM = nis_of(4 * even_share(SH::K * SH::EI / 2, SH::G), CP_GU);
+  constexpr int NI_GUD = nis_of(4 * even_share(SH::DI / 2, SH::G), CP_GU);
+  constexpr int NI_DND = nis_of(even_share(SH::H, SH::G), CP_DN);
+  // MoE down: K rows per output row, one chunk per lane (rows of expert_inter fit one lane group)
+  constexpr int C_DN = SS ? SH::EI / kChunkElems<WT> : 0;
+  constexpr int RPW_DN = C_DN > 0 && C_DN <= 32 ? (C_DN <= 16 ? (C_DN <= 8 ? 8 : 4) : 2) : 1;
+  constexpr int NI_DNM = SS && C_DN > 0 && C_DN <= 64 && (even_share(SH::H, SH::G) * SH::K) % (NW * RPW_DN) == 0
+                             ? even_share(SH::H, SH::G) * SH::K / (NW * RPW_DN)
+                             : 0;
 
   // token and position of this step (every workgroup makes the same choice)
-  int tok = d.tokens[d.tok_idx];
-  const int pos = d.len[seq];
+  int tok = gp(d.tokens)[d.tok_idx];
+  const int pos = gp(d.len)[seq];
   if (pos < 0 || pos >= cap) {
     if (W == 0 && tid == 0) raise_error(wt, ERR_POS);
     return;
@@ -673,14 +982,7 @@ __global__ void __launch_bounds__(NT, 1) decode_kernel(const KStatic* __restrict
     tok = 0;
   }
   if (stamps) stamps[0] = now();
-
-  // embedding row -> residual
-  for (int e = tid; e < H; e += NT) {
-    if constexpr (kAct32<WT>)
-      sm.xres[e] = reinterpret_cast<const float*>(ks.embed)[(long long)tok * H + e];
-    else
-      sm.xres[e] = bf2f(reinterpret_cast<const uint16_t*>(ks.embed)[(long long)tok * H + e]);
-  }
+  if (tid == 0) sm.flag = 0;
 
   const int T = pos + 1;
   const int S = nkv > 0 ? G / nkv : 0;  // attention splits per kv head
@@ -690,9 +992,7 @@ __global__ void __launch_bounds__(NT, 1) decode_kernel(const KStatic* __restrict
   const float qscale = 1.0f / sqrtf((float)hd);
   const int ebytes = kAct32<WT> ? 4 : 2;
   const int rowb = hd * ebytes;                 // bytes of one cached K or V row
-  const int TPP = rowb / 64;                    // threads per K row (64 B each)
-  const int PPP = NT / TPP;                     // positions per register pass
-  const int CHP = KV_PASSES * PPP;              // positions per attention chunk
+  const int CHP = KV_LDS / rowb;                // positions per attention chunk
   const size_t kvstride = (size_t)cap * hd;     // elements per (layer, seq, kv head)
   bool ok = true;  // false once a wait failed: skip to the argmax hand-off so the launch still ends cleanly
 
@@ -703,86 +1003,96 @@ __global__ void __launch_bounds__(NT, 1) decode_kernel(const KStatic* __restrict
   auto qkv_rowfn = [&](int l) {
     return [&, l](int q) {
       const int u = qpb + q / 2, head = u / half, i = u % half;
-      return mrow<WT>(ks.qkv, (long long)l * QR + head * hd + i + (q & 1) * half, H, sm.actA, sm.asumA);
+      return mrow<WT>(m_qkv, (long long)l * QR + head * hd + i + (q & 1) * half, H, sm.actA, sm.asumA);
     };
   };
-  lstage_issue<WT>(lstage(sm.sq), gq, 0, qkv_rowfn(0));
   // this workgroup's shares of every other phase (the same in every layer)
   const int orb = part(H, G, W), ore = part(H, G, W + 1);               // o_proj and down rows
   const int mpb = part(QD / 2, G, W), mpe = part(QD / 2, G, W + 1);     // merged output dim pairs
   const int dpb = part(DI_ / 2, G, W), dpe = part(DI_ / 2, G, W + 1);  // dense SwiGLU pairs
   const int xpb = part(K_ * EI_ / 2, G, W), xpe = part(K_ * EI_ / 2, G, W + 1);  // expert pairs
   const float inv_ei = 1.0f / (float)EI_, inv_k = 1.0f / (float)K_;
+  // QKV weights and the first attention chunk of layer l (into the shared region)
+  auto issue_attn_front = [&](int l) {
+    issue_auto<WT, NI_QKV, QKV_CAP>(lstage(sm.u.att.sq), gq, qkv_rowfn(l));
+    if (attn && t1 > t0) {
+      const size_t cb = (((size_t)l * B + seq) * nkv + aj) * kvstride * ebytes;
+      const int np0 = min(CHP, t1 - t0);
+      kv_issue(sm.u.att.kbuf, kc + cb, t0, np0, rowb);
+      kv_issue(sm.u.att.vbuf, vc + cb, t0, np0, rowb);
+    }
+  };
+
+  issue_attn_front(0);
+  gn_issue(sm, p_anorm, H);
+  for (int e = tid; e < H; e += NT) {  // embedding row -> residual
+    if constexpr (kAct32<WT>)
+      sm.xres[e] = gp(reinterpret_cast<const float*>(ks.embed))[(long long)tok * H + e];
+    else
+      sm.xres[e] = bf2f(gp(reinterpret_cast<const uint16_t*>(ks.embed))[(long long)tok * H + e]);
+  }
+  for (int q2 = tid; q2 < qpe - qpb; q2 += NT)  // RoPE of this workgroup's pairs at this position
+    sm.rcs[q2] = *(GLOBAL const f32x2_t*)(d.rope + (size_t)pos * half + (qpb + q2) % half);
+  wait_vmem();
   __syncthreads();
 
   for (int l = 0; l < L; ++l) {
     const uint32_t tag = d.epoch + (uint32_t)l * 8u;
     const int par = l & 1;
-    uint64_t* stamp = stamps ? stamps + (size_t)(l + 1) * 16 : nullptr;
+    GLOBAL uint64_t* stamp = stamps ? stamps + (size_t)(l + 1) * 16 : nullptr;
     const size_t cbase = (((size_t)l * B + seq) * nkv + (attn ? aj : 0)) * kvstride;
     const uint8_t* const kbase = kc + cbase * ebytes;
     const uint8_t* const vbase = vc + cbase * ebytes;
-
-    // ---------------- attention data of the first chunk: K rows to registers, V rows to LDS
-    uint4 kreg[KV_PASSES][4];
-    if (attn && t1 > t0) {
-      const int np0 = min(CHP, t1 - t0);
-      load_k<WT>(kreg, kbase, t0, np0, rowb);
-      load_v(sm.u.att.vbuf, vbase, t0, np0, rowb);
-    }
+    const bool dense = l < ks.n_dense;
+    const int lmoe = l - ks.n_dense;
 
     // ---------------- input RMSNorm (recomputed by every workgroup)
-    {
-      float ss = 0.f;
-      for (int e = tid; e < H; e += NT) ss += sm.xres[e] * sm.xres[e];
-      ss = block_sum(sm, ss);
-      const float inv = 1.0f / sqrtf(ss / (float)H + ks.eps);
-      const float* g = ks.anorm + (size_t)l * H;
-      for (int e = tid; e < H; e += NT) act_put<WT>(sm.actA, e, act_round<WT>(sm.xres[e] * inv * g[e]));
-      __syncthreads();
-      act_sums<WT>(sm.actA, sm.asumA, H);
-      __syncthreads();
-    }
+    rmsnorm_act<WT>(sm, H, ks.eps, true);
+    if (stamp) stamp[0] = now();
 
-    if (stamp) stamp[7] = now();
-    // ---------------- QKV rows (staged earlier), RoPE, KV append, publish
-    gemv_lds<WT>(lstage(sm.sq), gq, true, qkv_rowfn(l), [&](int q, float v) { sm.ytmp[q] = v; });
-    if (stamp) stamp[8] = now();
+    // ---------------- QKV rows (staged during the previous layer), RoPE, publish, KV append
+    {
+      const auto ar = act_regs<WT, CP_QKV>(gq, sm.actA, sm.asumA);
+      gemv_auto<WT, CP_QKV, NI_QKV, QKV_CAP>(lstage(sm.u.att.sq), gq, true, ar, qkv_rowfn(l),
+                                             [&](int q, float v) { sm.ytmp[q] = v; });
+    }
     __syncthreads();
-    for (int q2 = tid; q2 < qpe - qpb; q2 += NT) {
-      const int u = qpb + q2, head = u / half, i = u % half;
-      float y0 = sm.ytmp[2 * q2], y1 = sm.ytmp[2 * q2 + 1];
-      if (head < nq + nkv) {  // q and k heads are rotated
-        const float2 cs = rope[(size_t)pos * half + i];
-        const float r0 = y0 * cs.x - y1 * cs.y, r1 = y1 * cs.x + y0 * cs.y;
-        y0 = r0;
-        y1 = r1;
+    if (stamp) stamp[1] = now();
+    for (int q2 = tid; q2 < qpe - qpb; q2 += NT) {  // RoPE on q and k heads: pairs (i, i + hd/2)
+      const int head = (qpb + q2) / half;
+      if (head < nq + nkv) {
+        const f32x2_t cs = sm.rcs[q2];
+        const float y0 = sm.ytmp[2 * q2], y1 = sm.ytmp[2 * q2 + 1];
+        sm.ytmp[2 * q2] = y0 * cs.x - y1 * cs.y;
+        sm.ytmp[2 * q2 + 1] = y1 * cs.x + y0 * cs.y;
       }
-      const int row0 = head * hd + i, row1 = row0 + half;
-      put_all(ks.x_qkv, QR, par, row0, slot(tag + 0, __float_as_uint(y0)));
-      put_all(ks.x_qkv, QR, par, row1, slot(tag + 0, __float_as_uint(y1)));
-      if (head >= nq) {  // append K or V of kv head j at position pos
+    }
+    __syncthreads();
+    publish(x_qkv, QR, par, 2 * (qpe - qpb), tag + 0, [&](int q, int& idx) {
+      const int u = qpb + q / 2, head = u / half;
+      idx = head * hd + u % half + (q & 1) * half;
+      return __float_as_uint(sm.ytmp[q]);
+    });
+    for (int q = tid; q < 2 * (qpe - qpb); q += NT) {  // append K (after RoPE) and V at this position
+      const int u = qpb + q / 2, head = u / half, i = u % half + (q & 1) * half;
+      if (head >= nq) {
         const bool isk = head < nq + nkv;
         const int j = isk ? head - nq : head - nq - nkv;
-        const size_t off = (((size_t)l * B + seq) * nkv + j) * kvstride + (size_t)pos * hd;
+        const size_t off = (((size_t)l * B + seq) * nkv + j) * kvstride + (size_t)pos * hd + i;
         uint8_t* base = isk ? kc : vc;
-        if constexpr (kAct32<WT>) {
-          reinterpret_cast<float*>(base)[off + i] = y0;
-          reinterpret_cast<float*>(base)[off + i + half] = y1;
-        } else {
-          reinterpret_cast<uint16_t*>(base)[off + i] = (uint16_t)f2bf(y0);
-          reinterpret_cast<uint16_t*>(base)[off + i + half] = (uint16_t)f2bf(y1);
-        }
+        if constexpr (kAct32<WT>) gp(reinterpret_cast<float*>(base))[off] = sm.ytmp[q];
+        else gp(reinterpret_cast<uint16_t*>(base))[off] = (uint16_t)f2bf(sm.ytmp[q]);
       }
     }
-    if (stamp) stamp[0] = now();
+    gn_issue(sm, p_pnorm + (size_t)l * H, H);  // post-attention norm weights, read after the o_proj exchange
+    if (stamp) stamp[2] = now();
 
     // ---------------- attention partial over positions [t0, t1) of kv head aj
     if (attn) {
       const int h0 = aj * Gq;
       AttnLds& at = sm.u.att;
       if (t0 < t1) {
-        const uint64_t* src = copy_of(ks.x_qkv, QR, par);
+        const uint64_t* src = copy_of(x_qkv, QR, par);
         const int nqs = Gq * hd;
         const bool last = t1 == T;  // this split holds the new token: its k, v come from the exchange
         const int n = nqs + (last ? 2 * hd : 0);
@@ -805,224 +1115,259 @@ __global__ void __launch_bounds__(NT, 1) decode_kernel(const KStatic* __restrict
         ok = sync_ok(sm, wt);
       }
       if (!ok) break;
-      if (stamp) stamp[9] = now();
+      if (stamp) stamp[3] = now();
+      // running output: every wave accumulates all heads over its positions (lane: DPV dims)
+      constexpr int DPVM = MAX_HD / 64;
+      const int DPV = hd / 64, PST = Gq <= 4 ? 4 : 8;
+      float o[MAX_GQ][DPVM];
+#pragma unroll
+      for (int h = 0; h < MAX_GQ; ++h)
+#pragma unroll
+        for (int e = 0; e < DPVM; ++e) o[h][e] = 0.f;
       if (tid < Gq) {
-        sm.mrun[tid] = -INFINITY;
-        sm.lrun[tid] = 0.f;
+        at.mst[tid] = -INFINITY;
+        at.lst[tid] = 0.f;
       }
-      for (int i = tid; i < Gq * hd; i += NT) at.ocur[i] = 0.f;
       for (int c0 = t0; c0 < t1; c0 += CHP) {
         const int np = min(CHP, t1 - c0);
         if (c0 != t0) {  // later chunks (long contexts): load now
-          load_k<WT>(kreg, kbase, c0, np, rowb);
-          load_v(at.vbuf, vbase, c0, np, rowb);
+          __syncthreads();  // every wave is done with the previous chunk
+          kv_issue(at.kbuf, kbase, c0, np, rowb);
+          kv_issue(at.vbuf, vbase, c0, np, rowb);
         }
         wait_vmem();
         __syncthreads();
-        if (stamp && c0 == t0) stamp[10] = now();
-        // the new token's V row replaces whatever the DMA read for it
-        if (pos >= c0 && pos < c0 + np)
+        // the new token's row: k, v from the exchange replace what the DMA read
+        if (pos >= c0 && pos < c0 + np) {
+          uint8_t* kr = reinterpret_cast<uint8_t*>(at.kbuf) + (size_t)(pos - c0) * rowb;
+          uint8_t* vr = reinterpret_cast<uint8_t*>(at.vbuf) + (size_t)(pos - c0) * rowb;
           for (int e = tid; e < hd; e += NT) {
-            uint8_t* row = reinterpret_cast<uint8_t*>(at.vbuf) + (size_t)(pos - c0) * rowb;
-            if constexpr (kAct32<WT>) reinterpret_cast<float*>(row)[e] = at.vn[e];
-            else reinterpret_cast<uint16_t*>(row)[e] = (uint16_t)f2bf(at.vn[e]);
-          }
-        // scores: TPP threads per position, 64 B of the K row each, from registers
-        {
-          const int pp = tid / TPP, pt = tid % TPP;
-          constexpr int DPT = kAct32<WT> ? 16 : 32;  // dims per thread
-#pragma unroll
-          for (int p = 0; p < KV_PASSES; ++p) {
-            const int i = p * PPP + pp;
-            const int tau = c0 + i;
-            float kf[DPT];
-            if (tau == pos) {
-#pragma unroll
-              for (int e = 0; e < DPT; ++e) kf[e] = at.kn[pt * DPT + e];
-            } else if constexpr (kAct32<WT>) {
-#pragma unroll
-              for (int k = 0; k < 4; ++k) {
-                kf[4 * k] = __uint_as_float(kreg[p][k].x);
-                kf[4 * k + 1] = __uint_as_float(kreg[p][k].y);
-                kf[4 * k + 2] = __uint_as_float(kreg[p][k].z);
-                kf[4 * k + 3] = __uint_as_float(kreg[p][k].w);
-              }
-            } else {
-#pragma unroll
-              for (int k = 0; k < 4; ++k) {
-                const uint4 x = kreg[p][k];
-                kf[8 * k] = bf2f(x.x & 0xFFFF);
-                kf[8 * k + 1] = bf2f(x.x >> 16);
-                kf[8 * k + 2] = bf2f(x.y & 0xFFFF);
-                kf[8 * k + 3] = bf2f(x.y >> 16);
-                kf[8 * k + 4] = bf2f(x.z & 0xFFFF);
-                kf[8 * k + 5] = bf2f(x.z >> 16);
-                kf[8 * k + 6] = bf2f(x.w & 0xFFFF);
-                kf[8 * k + 7] = bf2f(x.w >> 16);
-              }
-            }
-#pragma unroll 1
-            for (int h = 0; h < Gq; ++h) {
-              const float4* q4 = reinterpret_cast<const float4*>(at.qs + h * hd + pt * DPT);
-              float t = 0.f;
-#pragma unroll
-              for (int e = 0; e < DPT / 4; ++e) {
-                const float4 q = q4[e];
-                t = fmaf(q.x, kf[4 * e], t);
-                t = fmaf(q.y, kf[4 * e + 1], t);
-                t = fmaf(q.z, kf[4 * e + 2], t);
-                t = fmaf(q.w, kf[4 * e + 3], t);
-              }
-              t = group_sum(t, TPP);
-              if (pt == 0 && i < np) at.sc[h * CHP + i] = t;
-            }
-          }
-        }
-        __syncthreads();
-        // chunk max per head (wave w handles heads w, w + NW, ...)
-        for (int h = wave; h < Gq; h += NW) {
-          float m = -INFINITY;
-          for (int i = lane; i < np; i += 64) m = fmaxf(m, at.sc[h * CHP + i]);
-          m = wave_max(m);
-          if (lane == 0) {
-            const float mn = fmaxf(sm.mrun[h], m);
-            sm.alpha[h] = sm.mrun[h] == -INFINITY ? 0.f : __expf(sm.mrun[h] - mn);
-            sm.mrun[h] = mn;
-          }
-        }
-        __syncthreads();
-        for (int i = tid; i < Gq * np; i += NT) {
-          const int h = i / np, k = i % np;
-          at.sc[h * CHP + k] = __expf(at.sc[h * CHP + k] - sm.mrun[h]);
-        }
-        __syncthreads();
-        for (int h = wave; h < Gq; h += NW) {
-          float t = 0.f;
-          for (int i = lane; i < np; i += 64) t += at.sc[h * CHP + i];
-          t = wave_sum(t);
-          if (lane == 0) sm.lsum[h] = t;
-        }
-        // P.V from the LDS V rows: thread = (dim pair dp, subset sb)
-        {
-          const int DP = hd / 2, NS = NT / DP;
-          const int dp = tid % DP, sb = tid / DP;
-          float acc0[MAX_GQ], acc1[MAX_GQ];
-#pragma unroll
-          for (int h = 0; h < MAX_GQ; ++h) acc0[h] = acc1[h] = 0.f;
-          const uint8_t* vb = reinterpret_cast<const uint8_t*>(at.vbuf);
-#pragma unroll 4
-          for (int i = sb; i < np; i += NS) {
-            float v0, v1;
             if constexpr (kAct32<WT>) {
-              const float2 v2 = reinterpret_cast<const float2*>(vb + (size_t)i * rowb)[dp];
-              v0 = v2.x;
-              v1 = v2.y;
+              reinterpret_cast<float*>(kr)[e] = at.kn[e];
+              reinterpret_cast<float*>(vr)[e] = at.vn[e];
             } else {
-              const uint32_t v2 = reinterpret_cast<const uint32_t*>(vb + (size_t)i * rowb)[dp];
-              v0 = bf2f(v2 & 0xFFFF);
-              v1 = bf2f(v2 >> 16);
+              reinterpret_cast<uint16_t*>(kr)[e] = (uint16_t)f2bf(at.kn[e]);
+              reinterpret_cast<uint16_t*>(vr)[e] = (uint16_t)f2bf(at.vn[e]);
             }
+          }
+          __syncthreads();
+        }
+        // scores: LPK lanes read one K row (16 B each), RPI rows per wave instruction
+        {
+          constexpr int DPL = kAct32<WT> ? 4 : 8;  // dims per lane
+          const int LPK = rowb / 16, RPI = 64 / LPK;
+          const int seg = lane % LPK, rsub = lane / LPK;
+          const int ninstr = (np + RPI - 1) / RPI;
+          for (int hg = 0; hg < Gq; hg += 4) {
+            float qv[4][DPL];
 #pragma unroll
-            for (int h = 0; h < MAX_GQ; ++h)
-              if (h < Gq) {
-                const float p = at.sc[h * CHP + i];
-                acc0[h] = fmaf(p, v0, acc0[h]);
-                acc1[h] = fmaf(p, v1, acc1[h]);
+            for (int a = 0; a < 4; ++a)
+#pragma unroll
+              for (int e = 0; e < DPL; ++e) qv[a][e] = hg + a < Gq ? at.qs[(hg + a) * hd + seg * DPL + e] : 0.f;
+            for (int it = wave; it < ninstr; it += NW) {
+              const uint4 kr = at.kbuf[it * 64 + lane];
+              float kf[DPL];
+              if constexpr (kAct32<WT>) {
+                kf[0] = __uint_as_float(kr.x);
+                kf[1] = __uint_as_float(kr.y);
+                kf[2] = __uint_as_float(kr.z);
+                kf[3] = __uint_as_float(kr.w);
+              } else {
+                const uint32_t kw[4] = {kr.x, kr.y, kr.z, kr.w};
+#pragma unroll
+                for (int k = 0; k < 4; ++k) {
+                  kf[2 * k] = bf2f(kw[k] & 0xFFFFu);
+                  kf[2 * k + 1] = bf2f(kw[k] >> 16);
+                }
               }
+              const int row = it * RPI + rsub;
+#pragma unroll
+              for (int a = 0; a < 4; ++a) {
+                float t = 0.f;
+#pragma unroll
+                for (int e = 0; e < DPL; ++e) t = fmaf(qv[a][e], kf[e], t);
+                t = group_sum(t, LPK);
+                if (seg == a && hg + a < Gq && row < np) at.sc[(hg + a) * CHP + row] = t;
+              }
+            }
+          }
+        }
+        __syncthreads();
+        // softmax, one wave per head: probabilities to pt, the running max / sum and rescale factor to LDS
+        for (int h = wave; h < Gq; h += NW) {
+          const float* sh = at.sc + h * CHP;
+          float mc = -INFINITY;
+          for (int i = lane; i < np; i += 64) mc = fmaxf(mc, sh[i]);
+          mc = wave_max(mc);
+          const float mo = at.mst[h];
+          const float mn = fmaxf(mo, mc);
+          const float alpha = mo == -INFINITY ? 0.f : __expf(mo - mn);
+          float ls = 0.f;
+          for (int i = lane; i < np; i += 64) {
+            const float pr = __expf(sh[i] - mn);
+            at.pt[i * PST + h] = pr;
+            ls += pr;
+          }
+          ls = wave_sum(ls);
+          if (lane == 0) {
+            at.fac[h] = alpha;
+            at.mst[h] = mn;
+            at.lst[h] = at.lst[h] * alpha + ls;
+          }
+        }
+        if (Gq < PST)  // padding heads of pt stay zero
+          for (int i = tid; i < np * (PST - Gq); i += NT) at.pt[(i / (PST - Gq)) * PST + Gq + i % (PST - Gq)] = 0.f;
+        __syncthreads();
+        // P.V: wave w takes positions w, w + NW, ...; all heads at once
+#pragma unroll
+        for (int h = 0; h < MAX_GQ; ++h) {
+          const float f = h < Gq ? at.fac[h] : 0.f;
+#pragma unroll
+          for (int e = 0; e < DPVM; ++e) o[h][e] *= f;
+        }
+        const uint8_t* vb = reinterpret_cast<const uint8_t*>(at.vbuf);
+#pragma unroll 4
+        for (int i = wave; i < np; i += NW) {
+          float pr[MAX_GQ];
+          const float4 p0 = *reinterpret_cast<const float4*>(at.pt + i * PST);
+          pr[0] = p0.x;
+          pr[1] = p0.y;
+          pr[2] = p0.z;
+          pr[3] = p0.w;
+          if (PST == 8) {
+            const float4 p1 = *reinterpret_cast<const float4*>(at.pt + i * PST + 4);
+            pr[4] = p1.x;
+            pr[5] = p1.y;
+            pr[6] = p1.z;
+            pr[7] = p1.w;
+          } else {
+            pr[4] = pr[5] = pr[6] = pr[7] = 0.f;
+          }
+          float v[DPVM];
+          const uint8_t* row = vb + (size_t)i * rowb;
+          if constexpr (kAct32<WT>) {
+            if (DPV == 2) {
+              const float2 v2 = reinterpret_cast<const float2*>(row)[lane];
+              v[0] = v2.x;
+              v[DPVM - 1] = v2.y;
+            } else {
+              v[0] = reinterpret_cast<const float*>(row)[lane];
+            }
+          } else {
+            if (DPV == 2) {
+              const uint32_t v2 = reinterpret_cast<const uint32_t*>(row)[lane];
+              v[0] = bf2f(v2 & 0xFFFFu);
+              v[DPVM - 1] = bf2f(v2 >> 16);
+            } else {
+              v[0] = bf2f(reinterpret_cast<const uint16_t*>(row)[lane]);
+            }
           }
 #pragma unroll
           for (int h = 0; h < MAX_GQ; ++h)
-            if (h < Gq) {
-              at.red[(sb * MAX_GQ + h) * hd + 2 * dp] = acc0[h];
-              at.red[(sb * MAX_GQ + h) * hd + 2 * dp + 1] = acc1[h];
-            }
-          __syncthreads();
-          for (int i = tid; i < Gq * hd; i += NT) {
-            const int h = i / hd, e = i % hd;
-            float t = 0.f;
-            for (int k = 0; k < NS; ++k) t += at.red[(k * MAX_GQ + h) * hd + e];
-            at.ocur[i] = at.ocur[i] * sm.alpha[h] + t;
-          }
-          __syncthreads();
-          if (tid < Gq) sm.lrun[tid] = sm.lrun[tid] * sm.alpha[tid] + sm.lsum[tid];
-          __syncthreads();
+            if (h < PST)
+#pragma unroll
+              for (int e = 0; e < DPVM; ++e)
+                if (e < DPV) o[h][e] = fmaf(pr[h], v[e], o[h][e]);
         }
       }
-      // publish (m, l, o) of each head: slot ((h * (hd + 2) + field) * S + split);
-      // l and o first, m (the field the merge polls) once they have completed
-      uint64_t* dst = ks.x_part + (size_t)par * nq * (hd + 2) * S;
-      for (int i = tid; i < Gq * (hd + 1); i += NT) {
-        const int h = i / (hd + 1), f = 1 + i % (hd + 1);
-        const float v = f == 1 ? sm.lrun[h] : at.ocur[h * hd + f - 2];
-        xstore(dst + ((size_t)(h0 + h) * (hd + 2) + f) * S + as, slot(tag + 1, __float_as_uint(v)));
-      }
-      wait_vmem();
+      // sum the waves' outputs (the K rows are dead: their buffer holds the partial sums)
+      float* red = reinterpret_cast<float*>(at.kbuf);
       __syncthreads();
-      if (tid < Gq)
-        xstore(dst + ((size_t)(h0 + tid) * (hd + 2)) * S + as, slot(tag + 1, __float_as_uint(sm.mrun[tid])));
+#pragma unroll
+      for (int h = 0; h < MAX_GQ; ++h)
+        if (h < Gq)
+#pragma unroll
+          for (int e = 0; e < DPVM; ++e)
+            if (e < DPV) red[(wave * MAX_GQ + h) * hd + lane * DPV + e] = o[h][e];
+      __syncthreads();
+      // publish (m, l, o) of each head of this split, contiguous: slot ((split * Gq + h) * (hd + 2) + field)
+      // of the kv head's block; every slot is tagged
+      uint64_t* dst = x_part + (size_t)par * nq * (hd + 2) * S + ((size_t)aj * S + as) * Gq * (hd + 2);
+      for (int idx = tid; idx < Gq * hd; idx += NT) {
+        const int h = idx / hd, e = idx % hd;
+        float t = 0.f;
+#pragma unroll
+        for (int w = 0; w < NW; ++w) t += red[(w * MAX_GQ + h) * hd + e];
+        xstore(dst + (size_t)h * (hd + 2) + 2 + e, slot(tag + 1, __float_as_uint(t)));
+      }
+      if (tid < 2 * Gq) {
+        const int h = tid >> 1;
+        const float v = (tid & 1) ? at.lst[h] : at.mst[h];
+        xstore(dst + (size_t)h * (hd + 2) + (tid & 1), slot(tag + 1, __float_as_uint(v)));
+      }
     }
-    if (stamp) stamp[1] = now();
+    if (stamp) stamp[4] = now();
 
     // o_proj rows of this workgroup: stage their weights before the merge waits
+    __syncthreads();  // the attention layout of the shared region is dead
     const Geo go = geo<WT>(ore - orb, QD);
-    auto o_rowfn = [&](int q) { return mrow<WT>(ks.o, (long long)l * H + orb + q, QD, sm.actA, sm.asumA); };
-    lstage_issue<WT>(lstage(sm.so), go, 0, o_rowfn);
+    auto o_rowfn = [&](int q) { return mrow<WT>(m_o, (long long)l * H + orb + q, QD, sm.actA, sm.asumA); };
+    issue_auto<WT, NI_O, O_CAP>(lstage(sm.u.mg.so), go, o_rowfn);
 
     // ---------------- merge the splits: this workgroup's pairs of output dims
     {
       const int pb = mpb, pe = mpe;
-      const uint64_t* srcp = ks.x_part + (size_t)par * nq * (hd + 2) * S;
+      const uint64_t* srcp = x_part + (size_t)par * nq * (hd + 2) * S;
       int e0 = 2 * pb;
       while (e0 < 2 * pe) {  // one head at a time (uniform loop)
         const int h = e0 / hd, eh0 = e0 % hd;
         const int ne = min(2 * pe, (h + 1) * hd) - e0;  // elements of head h in range (even)
-        const int n = (2 + ne) * S;
+        const int nf = 2 + ne, n = nf * S;  // gathered as [split][m, l, this range of o]
+        const float inv_nf = 1.0f / (float)nf;
+        const size_t hblk = (size_t)(h / Gq) * S * Gq * (hd + 2) + (size_t)(h % Gq) * (hd + 2);
         ok = gather(
             sm, srcp, n, tag + 1,
             [&](int i) {
-              const int f = i / S, s = i % S;
-              const int field = f < 2 ? f : 2 + eh0 + (f - 2);
-              return ((size_t)h * (hd + 2) + field) * S + s;
+              const int sp = div_small(i, nf, inv_nf), f = i - sp * nf;
+              return hblk + (size_t)sp * Gq * (hd + 2) + (f < 2 ? f : 2 + eh0 + (f - 2));
             },
-            [=](int k, int m) { return (int)(((long long)(k + 1) * S) / m) - 1; }, S < 64 ? S : 64,  // m fields
-            [&](int i, uint32_t p) { sm.u.gbuf[i] = p; }, wt);
+            [=](int k, int m) { return (((k + 1) * S) / m - 1) * nf; }, S < 64 ? S : 64,  // m fields
+            [&](int i, uint32_t p) { sm.u.mg.gbuf[i] = p; }, wt);
         if (!ok) break;
         // one wave per output pair, lanes over splits: log-sum-exp merge
         for (int k = wave; k < ne / 2; k += NW) {
           float M = -INFINITY;
-          for (int s = lane; s < S; s += 64) M = fmaxf(M, __uint_as_float(sm.u.gbuf[s]));
+          for (int s = lane; s < S; s += 64) M = fmaxf(M, __uint_as_float(sm.u.mg.gbuf[s * nf]));
           M = wave_max(M);
           float Lsum = 0.f, O0 = 0.f, O1 = 0.f;
           for (int s = lane; s < S; s += 64) {
-            const float m = __uint_as_float(sm.u.gbuf[s]);
+            const uint32_t* gs = sm.u.mg.gbuf + s * nf;
+            const float m = __uint_as_float(gs[0]);
             const float w = m == -INFINITY ? 0.f : __expf(m - M);
-            Lsum = fmaf(w, __uint_as_float(sm.u.gbuf[S + s]), Lsum);
-            O0 = fmaf(w, __uint_as_float(sm.u.gbuf[(2 + 2 * k) * S + s]), O0);
-            O1 = fmaf(w, __uint_as_float(sm.u.gbuf[(3 + 2 * k) * S + s]), O1);
+            Lsum = fmaf(w, __uint_as_float(gs[1]), Lsum);
+            O0 = fmaf(w, __uint_as_float(gs[2 + 2 * k]), O0);
+            O1 = fmaf(w, __uint_as_float(gs[3 + 2 * k]), O1);
           }
           Lsum = wave_sum(Lsum);
           O0 = wave_sum(O0);
           O1 = wave_sum(O1);
           if (lane == 0) {
-            const float o0 = act_round<WT>(O0 / Lsum), o1 = act_round<WT>(O1 / Lsum);
-            const int e = e0 + 2 * k;
-            if constexpr (kAct32<WT>) {
-              put_all(ks.x_o, OSL, par, e, slot(tag + 2, __float_as_uint(o0)));
-              put_all(ks.x_o, OSL, par, e + 1, slot(tag + 2, __float_as_uint(o1)));
-            } else {
-              put_all(ks.x_o, OSL, par, e / 2, slot(tag + 2, f2bf(o0) | (f2bf(o1) << 16)));
-            }
+            sm.ytmp[e0 - 2 * pb + 2 * k] = act_round<WT>(O0 / Lsum);
+            sm.ytmp[e0 - 2 * pb + 2 * k + 1] = act_round<WT>(O1 / Lsum);
           }
         }
         __syncthreads();
         e0 += ne;
       }
+      if (ok) {  // publish the merged dims: fp32 one per slot, else a bf16 pair
+        const int nv = 2 * (pe - pb);
+        if constexpr (kAct32<WT>)
+          publish(x_o, OSL, par, nv, tag + 2, [&](int i, int& idx) {
+            idx = 2 * pb + i;
+            return __float_as_uint(sm.ytmp[i]);
+          });
+        else
+          publish(x_o, OSL, par, nv / 2, tag + 2, [&](int i, int& idx) {
+            idx = pb + i;
+            return f2bf(sm.ytmp[2 * i]) | (f2bf(sm.ytmp[2 * i + 1]) << 16);
+          });
+      }
     }
     if (!ok) break;
-    if (stamp) stamp[2] = now();
+    if (stamp) stamp[5] = now();
 
     // ---------------- o_proj rows + residual
-    ok = gather_flat(sm, copy_of(ks.x_o, OSL, par), OSL, tag + 2,
+    ok = gather_flat(sm, copy_of(x_o, OSL, par), OSL, tag + 2,
                      [&](int i, uint32_t p) {
                        if constexpr (kAct32<WT>) {
                          act_put<WT>(sm.actA, i, __uint_as_float(p));
@@ -1033,126 +1378,171 @@ __global__ void __launch_bounds__(NT, 1) decode_kernel(const KStatic* __restrict
                      },
                      wt);
     if (!ok) break;
-    if (stamp) stamp[11] = now();
+    if (stamp) stamp[6] = now();
     act_sums<WT>(sm.actA, sm.asumA, QD);
     __syncthreads();
-    gemv_lds<WT>(lstage(sm.so), go, true, o_rowfn, [&](int q, float v) {
-      const int r = orb + q;
-      put_all(ks.x_res1, H, par, r, slot(tag + 3, __float_as_uint(sm.xres[r] + v)));
-    });
-    if (stamp) stamp[12] = now();
-    // router rows (all of them, every workgroup): stage before waiting for the residual
-    const bool dense = l < ks.n_dense;
-    const int lmoe = l - ks.n_dense;
-    const Geo gr = geo<WT>(dense ? 0 : E_, H);
-    auto r_rowfn = [&](int q) { return mrow<WT>(ks.router, (long long)lmoe * E_ + q, H, sm.actA, sm.asumA); };
-    if (!dense) lstage_issue<WT>(lstage(sm.u.rt), gr, 0, r_rowfn);
+    {
+      const auto ar = act_regs<WT, CP_O>(go, sm.actA, sm.asumA);
+      gemv_auto<WT, CP_O, NI_O, O_CAP>(lstage(sm.u.mg.so), go, true, ar, o_rowfn, [&](int q, float v) { sm.ytmp[q] = v; });
+    }
     __syncthreads();
-    ok = gather_flat(sm, copy_of(ks.x_res1, H, par), H, tag + 3,
+    publish(x_res1, H, par, ore - orb, tag + 3, [&](int q, int& idx) {
+      idx = orb + q;
+      return __float_as_uint(sm.xres[orb + q] + sm.ytmp[q]);
+    });
+    if (stamp) stamp[7] = now();
+    // router rows (all of them, every workgroup): stage before waiting for the residual
+    const Geo gr = geo<WT>(dense ? 0 : E_, H);
+    auto r_rowfn = [&](int q) { return mrow<WT>(m_r, (long long)lmoe * E_ + q, H, sm.actA, sm.asumA); };
+    if (!dense) issue_auto<WT, NI_R, R_CAP>(lstage(sm.u.rt), gr, r_rowfn);
+    ok = gather_flat(sm, copy_of(x_res1, H, par), H, tag + 3,
                      [&](int i, uint32_t p) { sm.xres[i] = __uint_as_float(p); }, wt);
     if (!ok) break;
-    if (stamp) stamp[3] = now();
+    if (stamp) stamp[8] = now();
 
     // ---------------- post-attention RMSNorm (recomputed by every workgroup)
-    {
-      float ss = 0.f;
-      for (int e = tid; e < H; e += NT) ss += sm.xres[e] * sm.xres[e];
-      ss = block_sum(sm, ss);
-      const float inv = 1.0f / sqrtf(ss / (float)H + ks.eps);
-      const float* g = ks.pnorm + (size_t)l * H;
-      for (int e = tid; e < H; e += NT) act_put<WT>(sm.actA, e, act_round<WT>(sm.xres[e] * inv * g[e]));
-      __syncthreads();
-      act_sums<WT>(sm.actA, sm.asumA, H);
-      __syncthreads();
-    }
+    rmsnorm_act<WT>(sm, H, ks.eps, true);
+    if (stamp) stamp[9] = now();
 
     int nunit, inner;  // SwiGLU elements this layer produces, and the down projection's input width
     if (dense) {
       nunit = DI_;
       inner = DI_;
+      if (W == 0 && tid < K_) {
+        if (d.dbg_routes) gp(d.dbg_routes)[(size_t)l * K_ + tid] = -1;
+        if (d.dbg_rw) gp(d.dbg_rw)[(size_t)l * K_ + tid] = 0.f;
+      }
     } else {
       // ------------ router (every workgroup computes all logits) and top-k
-      gemv_lds<WT>(lstage(sm.u.rt), gr, true, r_rowfn, [&](int q, float v) { sm.z[q] = v; });
-      __syncthreads();
-      if (stamp) stamp[13] = now();
-      if (tid < 64) {
-        const float zl = lane < E_ ? sm.z[lane] : -INFINITY;
-        float zsel = zl;
-        const float zmax = wave_max(zl);
-        const float den = wave_sum(lane < E_ ? __expf(zl - zmax) : 0.f);
-        float wsum = 0.f;
-        for (int r = 0; r < K_; ++r) {
-          float bv = zsel;
-          int bi = lane;
-          wave_argmax(bv, bi);
-          if (lane == bi) zsel = -INFINITY;
-          const float w = __expf(bv - zmax) / den;
-          wsum += w;
-          if (lane == 0) {
-            sm.sel[r] = bi;
-            sm.wsel[r] = w;
-          }
-        }
-        if (ks.renorm && lane < K_) sm.wsel[lane] = sm.wsel[lane] / wsum;
+      {
+        const auto ar = act_regs<WT, CP_R>(gr, sm.actA, sm.asumA);
+        gemv_auto<WT, CP_R, NI_R, R_CAP>(lstage(sm.u.rt), gr, true, ar, r_rowfn, [&](int q, float v) { sm.z[q] = v; });
       }
       __syncthreads();
+      if (stamp) stamp[10] = now();
+      // top-k by rank, in every wave (identical results; a wave reads only its own writes):
+      // lane e counts the experts that beat it (larger logit, or equal logit and lower index)
+      {
+        const float zl = lane < E_ ? sm.z[lane] : -INFINITY;
+        const uint32_t u = __float_as_uint(zl);
+        const uint32_t ord = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+        const uint64_t key = lane < E_ ? (((uint64_t)ord << 32) | (uint32_t)(63 - lane)) : 0ull;
+        const uint32_t khi = (uint32_t)(key >> 32), klo = (uint32_t)key;
+        // wave w compares against experts 16 w .. 16 w + 15; the partial counts meet in LDS (the SwiGLU
+        // buffer is unused until the SwiGLU exchange)
+        int* rk = reinterpret_cast<int*>(sm.u.mlp.hbuf);
+        int part = 0;
+#pragma unroll
+        for (int jj = 0; jj < MAX_E / NW; ++jj) {
+          const int j = wave * (MAX_E / NW) + jj;
+          const uint64_t kj = ((uint64_t)__builtin_amdgcn_readlane(khi, j) << 32) | __builtin_amdgcn_readlane(klo, j);
+          part += j < E_ && kj > key;
+        }
+        rk[wave * 64 + lane] = part;
+        __syncthreads();
+        int rank = 0;
+#pragma unroll
+        for (int w = 0; w < NW; ++w) rank += rk[w * 64 + lane];
+        const float zmax = wave_max(zl);
+        const float pe = lane < E_ ? __expf(zl - zmax) : 0.f;
+        const float den = wave_sum(pe);
+        const float w = pe / den;
+        const float wsum = wave_sum(lane < E_ && rank < K_ ? w : 0.f);
+        if (lane < E_ && rank < K_) {
+          sm.sel[rank] = lane;
+          sm.wsel[rank] = ks.renorm ? w / wsum : w;
+        }
+        wait_lds();
+        __builtin_amdgcn_wave_barrier();
+      }
       if (W == 0 && tid < K_) {
-        if (d.dbg_routes) d.dbg_routes[(size_t)l * K_ + tid] = sm.sel[tid];
-        if (d.dbg_rw) d.dbg_rw[(size_t)l * K_ + tid] = sm.wsel[tid];
+        if (d.dbg_routes) gp(d.dbg_routes)[(size_t)l * K_ + tid] = sm.sel[tid];
+        if (d.dbg_rw) gp(d.dbg_rw)[(size_t)l * K_ + tid] = sm.wsel[tid];
       }
       nunit = K_ * EI_;
       inner = EI_;
+      if (stamp) stamp[11] = now();
     }
-    if (dense && W == 0 && tid < K_) {
-      if (d.dbg_routes) d.dbg_routes[(size_t)l * K_ + tid] = -1;
-      if (d.dbg_rw) d.dbg_rw[(size_t)l * K_ + tid] = 0.f;
-    }
-    if (stamp) stamp[4] = now();
 
-    // ---------------- gate/up rows of this workgroup's SwiGLU elements; down rows staged too
+    // ---------------- gate/up rows of this workgroup's SwiGLU elements
     const int upb = dense ? dpb : xpb, upe = dense ? dpe : xpe;
     const int ue0 = 2 * upb, une = 2 * (upe - upb);
     const int drb = orb, dre = ore;
     const int K = K_;
     const int wstride = kAct32<WT> ? inner : inner / 2;  // words of one rank's h
+    // this workgroup's units are contiguous: unless they span more than two experts, the selected
+    // experts of the first and the next rank are all a row needs
+    const Mat mg = dense ? m_dg : m_eg, mu = dense ? m_du : m_eu;
+    const int gk0 = dense ? 0 : div_small(ue0, EI_, inv_ei);
+    const bool two = !dense && une <= EI_;
+    const int gsel0 = dense ? 0 : sm.sel[gk0], gsel1 = (!dense && gk0 + 1 < K_) ? sm.sel[gk0 + 1] : gsel0;
+    const int gub = (gk0 + 1) * EI_;  // first unit of the next rank
     auto gu_rowfn = [&](int q) {
       const int u = ue0 + q / 2;
-      const Mat& m = (q & 1) ? (dense ? ks.du : ks.eu) : (dense ? ks.dg : ks.eg);
-      const long long row =
-          dense ? (long long)l * DI_ + u : ((long long)lmoe * E_ + sm.sel[div_small(u, EI_, inv_ei)]) * EI_ + u - div_small(u, EI_, inv_ei) * EI_;
-      return mrow<WT>(m, row, H, sm.actA, sm.asumA);
+      long long row;
+      if (dense) {
+        row = (long long)l * DI_ + u;
+      } else if (two) {
+        const bool nx = u >= gub;
+        row = ((long long)lmoe * E_ + (nx ? gsel1 : gsel0)) * EI_ + u - (nx ? gub : gub - EI_);
+      } else {
+        const int k = div_small(u, EI_, inv_ei);
+        row = ((long long)lmoe * E_ + sm.sel[k]) * EI_ + u - k * EI_;
+      }
+      return mrow<WT>((q & 1) ? mu : mg, row, H, sm.actA, sm.asumA);
     };
     auto dn_rowfn = [&](int q) {
-      if (dense) return mrow<WT>(ks.dd, (long long)l * H + drb + q, inner, sm.u.mlp.hbuf, sm.u.mlp.asumH);
+      if (dense) return mrow<WT>(m_dd, (long long)l * H + drb + q, inner, sm.u.mlp.hbuf, sm.u.mlp.asumH);
       const int qk = div_small(q, K, inv_k);
       const int r = drb + qk, k = q - qk * K;
-      return mrow<WT>(ks.ed, ((long long)lmoe * E_ + sm.sel[k]) * H + r, inner, sm.u.mlp.hbuf + k * wstride,
+      return mrow<WT>(m_ed, ((long long)lmoe * E_ + sm.sel[k]) * H + r, inner, sm.u.mlp.hbuf + k * wstride,
+                      sm.u.mlp.asumH + k * (inner / 32));
+    };
+    // the static MoE down visits its rows expert by expert: geometry row rp is output row rp % R8 of
+    // rank rp / R8 (R8 = rows per workgroup), so every item of a wave reads one expert
+    const int R8 = dre - drb;
+    auto dn_rowfn_x = [&](int rp) {
+      const int k = rp / R8, r = drb + rp - k * R8;
+      return mrow<WT>(m_ed, ((long long)lmoe * E_ + sm.sel[k]) * H + r, inner, sm.u.mlp.hbuf + k * wstride,
                       sm.u.mlp.asumH + k * (inner / 32));
     };
     const Geo ggu = geo<WT>(2 * une, H);
     const Geo gdn = geo<WT>(dense ? dre - drb : (dre - drb) * K, inner);
-    lstage_issue<WT>(lstage(sm.u.mlp.gu), ggu, 0, gu_rowfn);
-    lstage_issue<WT>(lstage(sm.u.mlp.dn), gdn, 0, dn_rowfn);
-    gemv_lds<WT>(lstage(sm.u.mlp.gu), ggu, true, gu_rowfn, [&](int q, float v) { sm.ytmp[q] = v; });
-    __syncthreads();
-    if (stamp) stamp[14] = now();
-    for (int k = tid; k < une / 2; k += NT) {
-      float hv[2];
-#pragma unroll
-      for (int t = 0; t < 2; ++t) {
-        const float g = sm.ytmp[4 * k + 2 * t], u = sm.ytmp[4 * k + 2 * t + 1];
-        hv[t] = act_round<WT>(g / (1.0f + __expf(-g)) * u);
-      }
-      const int e = ue0 + 2 * k;
-      if constexpr (kAct32<WT>) {
-        put_all(ks.x_h, HSLOTS, par, e, slot(tag + 4, __float_as_uint(hv[0])));
-        put_all(ks.x_h, HSLOTS, par, e + 1, slot(tag + 4, __float_as_uint(hv[1])));
-      } else {
-        put_all(ks.x_h, HSLOTS, par, e / 2, slot(tag + 4, f2bf(hv[0]) | (f2bf(hv[1]) << 16)));
-      }
+    if (dense) issue_auto<WT, NI_GUD, GU_CAP>(lstage(sm.u.mlp.gu), ggu, gu_rowfn);
+    else issue_auto<WT, NI_GUM, GU_CAP>(lstage(sm.u.mlp.gu), ggu, gu_rowfn);
+    {
+      const auto ar = act_regs<WT, CP_GU>(ggu, sm.actA, sm.asumA);
+      auto out = [&](int q, float v) { sm.ytmp[q] = v; };
+      if (dense) gemv_auto<WT, CP_GU, NI_GUD, GU_CAP>(lstage(sm.u.mlp.gu), ggu, true, ar, gu_rowfn, out);
+      else gemv_auto<WT, CP_GU, NI_GUM, GU_CAP>(lstage(sm.u.mlp.gu), ggu, true, ar, gu_rowfn, out);
     }
+    __syncthreads();
+    // SwiGLU of this workgroup's units: fp32 one value per slot, else a bf16 pair of adjacent units
+    if constexpr (kAct32<WT>)
+      publish(x_h, HSLOTS, par, une, tag + 4, [&](int k, int& idx) {
+        const float g = sm.ytmp[2 * k], u = sm.ytmp[2 * k + 1];
+        idx = ue0 + k;
+        return __float_as_uint(g / (1.0f + __expf(-g)) * u);
+      });
+    else
+      publish(x_h, HSLOTS, par, une / 2, tag + 4, [&](int k, int& idx) {
+        uint32_t hv[2];
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+          const float g = sm.ytmp[4 * k + 2 * t], u = sm.ytmp[4 * k + 2 * t + 1];
+          hv[t] = f2bf(g / (1.0f + __expf(-g)) * u);
+        }
+        idx = ue0 / 2 + k;
+        return hv[0] | (hv[1] << 16);
+      });
+    // the down weights and the next norm's weights load during the SwiGLU exchange
+    if (dense) issue_auto<WT, NI_DND, DN_CAP>(lstage(sm.u.mlp.dn), gdn, dn_rowfn);
+    else if constexpr (NI_DNM > 0 && NI_DNM <= DN_CAP) lstage_issue_static<WT, NI_DNM>(lstage(sm.u.mlp.dn), gdn, 0, dn_rowfn_x);
+    else lstage_issue<WT>(lstage(sm.u.mlp.dn), gdn, 0, dn_rowfn);
+    gn_issue(sm, l + 1 < L ? p_anorm + (size_t)(l + 1) * H : p_fnorm, H);
+    if (stamp) stamp[12] = now();
     // ---------------- gather the SwiGLU output, down projection + residual
-    ok = gather_flat(sm, copy_of(ks.x_h, HSLOTS, par), kAct32<WT> ? nunit : nunit / 2, tag + 4,
+    ok = gather_flat(sm, copy_of(x_h, HSLOTS, par), kAct32<WT> ? nunit : nunit / 2, tag + 4,
                      [&](int i, uint32_t p) {
                        // element e of rank r lives at hbuf element r * inner + e: the same flat index
                        if constexpr (kAct32<WT>) {
@@ -1166,61 +1556,84 @@ __global__ void __launch_bounds__(NT, 1) decode_kernel(const KStatic* __restrict
     if (!ok) break;
     act_sums<WT>(sm.u.mlp.hbuf, sm.u.mlp.asumH, nunit);
     __syncthreads();
-    if (stamp) stamp[5] = now();
+    if (stamp) stamp[13] = now();
     if (dense) {
-      gemv_lds<WT>(lstage(sm.u.mlp.dn), gdn, true, dn_rowfn, [&](int q, float v) {
-        const int r = drb + q;
-        put_all(ks.x_res2, H, par, r, slot(tag + 5, __float_as_uint(sm.xres[r] + v)));
-      });
+      const auto ar = act_regs<WT, CP_DN>(gdn, sm.u.mlp.hbuf, sm.u.mlp.asumH);
+      gemv_auto<WT, CP_DN, NI_DND, DN_CAP>(lstage(sm.u.mlp.dn), gdn, true, ar, dn_rowfn,
+                                           [&](int q, float v) { sm.ytmp[q] = v; });
     } else {
-      gemv_lds<WT>(lstage(sm.u.mlp.dn), gdn, true, dn_rowfn, [&](int q, float v) { sm.ytmp[q] = v; });
-      __syncthreads();
-      for (int q = tid; q < dre - drb; q += NT) {
-        float y = 0.f;
-        for (int k = 0; k < K; ++k) y = fmaf(sm.wsel[k], sm.ytmp[q * K + k], y);
-        const int r = drb + q;
-        put_all(ks.x_res2, H, par, r, slot(tag + 5, __float_as_uint(sm.xres[r] + y)));
+      auto out = [&](int q, float v) { sm.ytmp[q] = v; };
+      if constexpr (NI_DNM > 0 && NI_DNM <= DN_CAP) {
+        wait_vmem();
+        compute_static_rows<WT, NI_DNM, NI_DNM % 3 == 0 ? 3 : 1>(lstage(sm.u.mlp.dn), gdn, dn_rowfn_x,
+                                                                 [&](int rp, float v) {
+                                                                   const int k = rp / R8;
+                                                                   sm.ytmp[(rp - k * R8) * K + k] = v;
+                                                                 });
+      } else {
+        const ActRegs<WT, 0> none{};
+        gemv_lds<WT, 0>(lstage(sm.u.mlp.dn), gdn, true, none, dn_rowfn, out);
       }
     }
-    if (stamp) stamp[15] = now();
-    // next layer's QKV rows: stage before waiting for the residual
-    if (l + 1 < L) lstage_issue<WT>(lstage(sm.sq), gq, 0, qkv_rowfn(l + 1));
     __syncthreads();
-    ok = gather_flat(sm, copy_of(ks.x_res2, H, par), H, tag + 5,
+    publish(x_res2, H, par, dre - drb, tag + 5, [&](int q, int& idx) {
+      idx = drb + q;
+      float y;
+      if (dense) {
+        y = sm.ytmp[q];
+      } else {
+        y = 0.f;
+        for (int k = 0; k < K; ++k) y = fmaf(sm.wsel[k], sm.ytmp[q * K + k], y);
+      }
+      return __float_as_uint(sm.xres[drb + q] + y);
+    });
+    // the shared region is free: the next layer's QKV weights and first attention chunk load during the exchange
+    if (l + 1 < L) issue_attn_front(l + 1);
+    if (stamp) stamp[14] = now();
+    ok = gather_flat(sm, copy_of(x_res2, H, par), H, tag + 5,
                      [&](int i, uint32_t p) { sm.xres[i] = __uint_as_float(p); }, wt);
     if (!ok) break;
-    if (stamp) stamp[6] = now();
+    if (stamp) stamp[15] = now();
     if (d.dbg_resid && W == 0 && l == d.dbg_resid_layer)
-      for (int e = tid; e < H; e += NT) d.dbg_resid[e] = sm.xres[e];
+      for (int e = tid; e < H; e += NT) gp(d.dbg_resid)[e] = sm.xres[e];
   }
 
-  // ---------------- final norm, lm_head, argmax
+  // ---------------- final norm (its weights are in sm.gn), lm_head, argmax
   {
-    float ss = 0.f;
-    for (int e = tid; e < H; e += NT) ss += sm.xres[e] * sm.xres[e];
-    ss = block_sum(sm, ss);
-    const float inv = 1.0f / sqrtf(ss / (float)H + ks.eps);
-    // the head is bf16 (or fp32) even when the layers are int4: natural element order
-    constexpr int HW = WT == W_I4 ? W_BF16 : WT;
-    uint32_t* fact = sm.u.mlp.hbuf;
-    for (int e = tid; e < H; e += NT) act_put<HW>(fact, e, act_round<WT>(sm.xres[e] * inv * ks.fnorm[e]));
     __syncthreads();
+    rmsnorm_act<WT, HW>(sm, H, ks.eps, false);
     const int vb = ok ? part(V_, G, W) : 0, ve = ok ? part(V_, G, W + 1) : 0;
     float bv = -INFINITY;
     int bi = 0x7FFFFFFF;
     const Mat lmh{ks.lmhead, nullptr};
     float* const dbg_logits = d.dbg_logits;
     const Geo gl = geo<HW>(ve - vb, H);
-    Stage<4> st_l;
-    gemv_run<HW, 4, true>(gl, st_l, false, [&](int q) { return mrow<HW>(lmh, vb + q, H, fact, nullptr); },
-                    [&](int q, float v) {
-                      const int r = vb + q;
-                      if (dbg_logits) dbg_logits[r] = v;
-                      if (v > bv || (v == bv && r < bi)) {
-                        bv = v;
-                        bi = r;
-                      }
-                    });
+    auto lm_rowfn = [&](int q) { return mrow<HW>(lmh, vb + q, H, sm.actA, nullptr); };
+    // debug logits wait in LDS: a global store inside the streamed loop would upset its load count
+    auto lm_out = [&](int q, float v) {
+      const int r = vb + q;
+      if (dbg_logits) {
+        if (q < MAX_YROWS) sm.ytmp[q] = v;
+        else gp(dbg_logits)[r] = v;
+      }
+      if (v > bv || (v == bv && r < bi)) {
+        bv = v;
+        bi = r;
+      }
+    };
+    const auto ar = act_regs<HW, CP_LM>(gl, sm.actA, nullptr);
+    static_assert(!SS || (SH::V % SH::G == 0 && ((SH::V / SH::G) / NW * CP_LM) % LM_CAP == 0 &&
+                          (SH::H / kChunkElems<HW>) % 64 == 0),
+                  "the streamed lm_head needs whole rows in every lane and whole rounds");
+    if constexpr (CP_LM > 0)
+      gemv_stream<HW, CP_LM, LM_CAP>(LStage{sm.u.head.a, nullptr, LM_CAP}, LStage{sm.u.head.b, nullptr, LM_CAP}, gl, ar,
+                                     lm_rowfn, lm_out);
+    else
+      gemv_lds<HW, 0>(LStage{sm.u.head.a, nullptr, LM_CAP}, gl, false, ar, lm_rowfn, lm_out);
+    if (dbg_logits) {
+      __syncthreads();
+      for (int q = tid; q < min(ve - vb, MAX_YROWS); q += NT) gp(dbg_logits)[vb + q] = sm.ytmp[q];
+    }
     // best of the workgroup: max logit, then lowest id
     wave_argmax(bv, bi);
     const uint32_t u = __float_as_uint(bv);
@@ -1232,15 +1645,15 @@ __global__ void __launch_bounds__(NT, 1) decode_kernel(const KStatic* __restrict
     if (tid == 0) {
       unsigned long long k = 0;
       for (int w = 0; w < NW; ++w) k = sm.best[w] > k ? sm.best[w] : k;
-      __hip_atomic_fetch_max(ks.amax, k, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      const uint32_t prev = __hip_atomic_fetch_add(ks.done, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_fetch_max(gp(ks.amax), k, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      const uint32_t prev = __hip_atomic_fetch_add(gp(ks.done), 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
       if (prev == (uint32_t)G - 1) {  // last workgroup: publish the token, reset for the next launch
         const unsigned long long fin =
-            __hip_atomic_exchange(ks.amax, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        __hip_atomic_store(ks.done, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        d.out_ids[d.out_idx] = (int32_t)(0xFFFFFFFFu - (uint32_t)(fin & 0xFFFFFFFFull));
-        d.len[seq] = pos + 1;
-        if (d.dbg_ts) d.dbg_ts[2] = now();
+            __hip_atomic_exchange(gp(ks.amax), 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(gp(ks.done), 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        gp(d.out_ids)[d.out_idx] = (int32_t)(0xFFFFFFFFu - (uint32_t)(fin & 0xFFFFFFFFull));
+        gp(d.len)[seq] = pos + 1;
+        if (d.dbg_ts) gp(d.dbg_ts)[2] = now();
       }
     }
   }

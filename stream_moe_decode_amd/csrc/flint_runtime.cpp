@@ -143,7 +143,10 @@ int check_grid(const flint_config* c, int G) {
     need = std::max(need, (long)c->top_k * ceil_div(c->hidden, G));
   }
   need = std::max(need, ceil_div(c->hidden, G));
+  need = std::max(need, 2 * ceil_div(QD / 2, G));  // merged attention dims
   if (need > MAX_YROWS) return fail(FLINT_EINVAL, "grid %d too small: %ld rows per workgroup > %d", G, need, MAX_YROWS);
+  const long pairs = ceil_div((c->n_q_heads + 2 * c->n_kv_heads) * hd / 2, G);
+  if (pairs > MAX_QPAIRS) return fail(FLINT_EINVAL, "grid %d too small: %ld RoPE pairs per workgroup > %d", G, pairs, MAX_QPAIRS);
   long ne = std::min<long>(hd, 2 * ceil_div(QD / 2, G));
   if ((2 + ne) * S > MAX_GATHER)
     return fail(FLINT_EINVAL, "grid %d: attention merge needs %ld words > %d", G, (2 + ne) * S, MAX_GATHER);
