@@ -60,6 +60,21 @@ def step_bytes(cfg, pos: int) -> int:
     return weight_bytes_per_step(cfg) + kv_bytes_per_position(cfg) * (pos + 1)
 
 
+def measured_traffic():
+    """HBM bytes per launch from the committed counter summary, if it was taken on this kernel source."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", "decode_kernel_int4_49_traffic.txt")
+    src = os.path.join(ROOT, "stream_moe_decode_amd", "csrc", "flint_kernel.hip")
+    try:
+        kv = dict(l.strip().split("=", 1) for l in open(path) if "=" in l and not l.startswith("#"))
+        digest = hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
+    except OSError:
+        return None
+    if kv.get("kernel_sha256_16") != digest:
+        return None
+    return int(1024 * (float(kv["fetch_kib"]) * float(kv["fetch_scale"]) + float(kv["write_kib"]) * float(kv["write_scale"])))
+
+
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
@@ -150,7 +165,7 @@ def main():
     bytes_total = sum(step_bytes(cfg, resident + i) for i in range(K))
     mean_kern_s = sum(kern_ms) / K / 1e3
     achieved = bytes_total / K / mean_kern_s / 1e9
-    log(f"{K} steps: {total_ms:.2f} ms total, kernel mean {1e3 * mean_kern_s:.1f} us, "
+    log(f"{K} steps: {total_ms:.2f} ms total, kernel mean {1e6 * mean_kern_s:.1f} us, "
         f"min {1e3 * min(kern_ms):.1f} us, max {1e3 * max(kern_ms):.1f} us")
 
     # per-phase time per layer (workgroup 0's wall-clock stamps), one extra step at `resident`
@@ -166,11 +181,12 @@ def main():
     att, moe = [], []
     prev = ts[0, 0]
     for l in range(cfg.n_layers):
-        row = ts[l + 1]   # stamps of layer l: [3] residual after o_proj gathered, [6] after the MLP
+        # stamps of layer l (kernel order): [8] residual after o_proj gathered, [15] residual after the MLP
+        row = ts[l + 1]
         if l >= cfg.n_dense_layers:
-            att.append((row[3] - prev) * tick_us)
-            moe.append((row[6] - row[3]) * tick_us)
-        prev = row[6]
+            att.append((row[8] - prev) * tick_us)
+            moe.append((row[15] - row[8]) * tick_us)
+        prev = row[15]
     head_us = (ts[0, 1] - prev) * tick_us
     phases = {"attention_us_per_layer": round(float(np.mean(att)), 2) if att else None,
               "moe_us_per_layer": round(float(np.mean(moe)), 2) if moe else None,
@@ -219,7 +235,8 @@ def main():
                                f"{resident} resident KV positions, {K} greedy tokens",
                    "global_batch": 1, "seq_len": resident + K, "parallelism": "none (one GPU)"},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": measured_traffic() if args.config == "int4_49" else None,
                      "bytes_per_launch": int(bytes_total / K), "weight_bytes_per_step": wb,
                      "kernel_mean_us": round(1e6 * mean_kern_s, 2),
                      "roofline_tok_s": round(HBM_PEAK_GBS * 1e9 / (bytes_total / K), 1)},

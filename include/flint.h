@@ -114,8 +114,12 @@ typedef struct flint_debug {
   int32_t resid_layer;
   int32_t pad;
   uint64_t* phase_ts;   /* [n_layers + 1][16] wall-clock stamps (100 MHz) of workgroup 0 at
-                           phase boundaries, for sequence 0 (row 0: start, end, argmax published;
-                           row l + 1: layer l) */
+                           phase boundaries, for sequence 0.  Row 0: start, end, argmax published.
+                           Row l + 1 (layer l), in order: 0 input norm, 1 QKV, 2 q/k/v published,
+                           3 q gathered, 4 attention partial published, 5 splits merged, 6 merged
+                           output gathered, 7 o_proj published, 8 residual gathered, 9 post norm,
+                           10 router, 11 top-k (10 and 11 are 0 on dense layers), 12 SwiGLU
+                           published, 13 SwiGLU gathered, 14 MLP residual published, 15 gathered */
 } flint_debug;
 
 /* ------------------------------------------------------------- entry points */
