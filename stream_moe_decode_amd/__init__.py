@@ -17,6 +17,8 @@ LIB_PATH = os.path.join(_HERE, "libflint.so")
 
 OK, EINVAL, ENOMEM, EHIP, ECAPACITY, ETIMEOUT, ENORESIDENT, EDEVICE = range(8)
 W_F32, W_BF16, W_INT4G64 = 0, 1, 2
+(FLINT_OK, FLINT_EINVAL, FLINT_ENOMEM, FLINT_EHIP, FLINT_ECAPACITY, FLINT_ETIMEOUT, FLINT_ENORESIDENT,
+ FLINT_EDEVICE) = range(8)
 STATUS_NAMES = {0: "FLINT_OK", 1: "FLINT_EINVAL", 2: "FLINT_ENOMEM", 3: "FLINT_EHIP", 4: "FLINT_ECAPACITY",
                 5: "FLINT_ETIMEOUT", 6: "FLINT_ENORESIDENT", 7: "FLINT_EDEVICE"}
 
