@@ -5,7 +5,7 @@
 
 namespace flint {
 
-constexpr int NT = 256;                 // threads per workgroup (4 waves of 64)
+constexpr int NT = 512;                 // threads per workgroup (8 waves of 64: two per SIMD)
 constexpr int NW = NT / 64;             // waves per workgroup
 constexpr int MAX_H = 2048;             // residual width
 constexpr int MAX_QD = 2048;            // n_q_heads * head_dim
@@ -21,7 +21,7 @@ constexpr int KV_LDS = 32768;           // bytes of K (and of V) rows per attent
 constexpr int MAX_CHUNK_POS = KV_LDS / 128;  // positions per chunk for the smallest row (64 bf16)
 constexpr int NCOPY = 8;                // replicas of broadcast exchanges (one per XCD)
 // LDS weight staging, in items (one 16-byte chunk per lane of a wave) per wave
-constexpr int QKV_CAP = 4, O_CAP = 2, R_CAP = 16, GU_CAP = 12, DN_CAP = 6, LM_CAP = 16;
+constexpr int QKV_CAP = 2, O_CAP = 1, R_CAP = 8, GU_CAP = 6, DN_CAP = 3, LM_CAP = 8;
 constexpr int TAGS_PER_LAUNCH = 1024;   // exchange tags one launch may use
 constexpr uint64_t SPIN_TIMEOUT = 100000000ull;  // 1 s of the 100 MHz wall clock
 

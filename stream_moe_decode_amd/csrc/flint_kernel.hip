@@ -918,9 +918,10 @@ template <int WT, class SH> constexpr int cpl_fit(int in, int cap) {
   return cap % cpl == 0 ? cpl : 0;
 }
 
-// Items per wave of a GEMV whose workgroups own `per_wg` rows each (0 unless
-// the rows split evenly over the waves), at cpl chunks per row.
-constexpr int nis_of(int per_wg, int cpl) { return cpl > 0 && per_wg > 0 && per_wg % NW == 0 ? per_wg / NW * cpl : 0; }
+// Items per wave of a GEMV whose workgroups own `per_wg` rows each, at cpl
+// chunks per row (the last row pass of some waves may be empty: those rows
+// are neither loaded nor stored).
+constexpr int nis_of(int per_wg, int cpl) { return cpl > 0 && per_wg > 0 ? (per_wg + NW - 1) / NW * cpl : 0; }
 constexpr int even_share(int total, int G) { return G > 0 && total % G == 0 ? total / G : 0; }
 
 template <int WT, class SH>
