@@ -40,7 +40,7 @@ struct KStatic {
   int S;                 // attention splits per kv head (grid / n_kv_heads)
   int qkv_rows, o_slots, h_slots;
   int poll_sleep;        // s_sleep(8) repetitions between polls of a stale slot
-  int sentinels;         // slots polled by wave 0 before the bulk read (1..64)
+  int sentinels;         // slots polled by wave 0 before the bulk read (0: none, up to 64)
   const uint8_t* embed;
   const uint8_t* lmhead;
   const float* fnorm;

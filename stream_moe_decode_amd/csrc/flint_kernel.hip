@@ -98,6 +98,11 @@ template <int WT> constexpr int kChunkElems = WT == W_F32 ? 4 : (WT == W_BF16 ? 
 template <int WT> __device__ __forceinline__ long long row_bytes(int in) {
   return WT == W_F32 ? 4ll * in : (WT == W_BF16 ? 2ll * in : in / 2);
 }
+// LDS words between consecutive activation chunks.  An int4 chunk (32 bf16,
+// 64 B, read by one lane as four 16-byte loads) is padded to 80 B so that the
+// 16 lanes served together touch all 64 banks once; fp32 / bf16 chunks are
+// one 16-byte load per lane and need no padding.
+template <int WT> constexpr int kChunkWords = WT == W_I4 ? 20 : 4;
 // Activation value as the GEMV input: bf16-rounded unless the model is fp32.
 template <int WT> __device__ __forceinline__ float act_round(float v) { return kAct32<WT> ? v : round_bf16(v); }
 
@@ -129,7 +134,7 @@ struct MergeLds {                        // split merge and o_proj
 struct MlpLds {                          // gate/up and down
   StageLds<GU_CAP> gu;
   StageLds<DN_CAP> dn;
-  uint32_t hbuf[MAX_HBUF / 2];           // SwiGLU output as the down GEMV input
+  uint32_t hbuf[MAX_HBUF / 32 * 20];     // SwiGLU output as the down GEMV input (room for int4 padding)
   float asumH[MAX_HBUF / 32];
 };
 struct HeadLds {                         // lm_head: two staging buffers (bf16 / fp32 rows: no scales)
@@ -250,7 +255,7 @@ template <int WT> __device__ __forceinline__ void act_put(uint32_t* act, int e, 
   if constexpr (kAct32<WT>) {
     act[e] = __float_as_uint(v);
   } else {
-    int p = WT == W_I4 ? ((e & ~7) | ((e & 3) << 1) | ((e >> 2) & 1)) : e;
+    const int p = WT == W_I4 ? (e >> 5) * (2 * kChunkWords<WT>) + ((e & 24) | ((e & 3) << 1) | ((e >> 2) & 1)) : e;
     reinterpret_cast<uint16_t*>(act)[p] = (uint16_t)f2bf(v);
   }
 }
@@ -258,7 +263,7 @@ template <int WT> __device__ __forceinline__ void act_put(uint32_t* act, int e, 
 template <int WT> __device__ __forceinline__ void act_sums(const uint32_t* act, float* asum, int n) {
   if constexpr (WT == W_I4) {
     for (int c = threadIdx.x; c < n / 32; c += NT) {
-      const uint4* p = reinterpret_cast<const uint4*>(act + c * 16);
+      const uint4* p = reinterpret_cast<const uint4*>(act + c * kChunkWords<WT>);
       const uint4 x0 = p[0], x1 = p[1], x2 = p[2], x3 = p[3];
       float s0 = 0.f, s1 = 0.f;
       const uint32_t w[16] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w,
@@ -326,7 +331,7 @@ template <int WT> struct ActC {
 template <int WT> __device__ __forceinline__ ActC<WT> act_chunk(const uint32_t* act, const float* asum, int c) {
   ActC<WT> r;
   if constexpr (WT == W_I4) {
-    const uint4* p = reinterpret_cast<const uint4*>(act + 16 * c);
+    const uint4* p = reinterpret_cast<const uint4*>(act + kChunkWords<WT> * c);
     r.a[0] = p[0];
     r.a[1] = p[1];
     r.a[2] = p[2];
@@ -442,14 +447,14 @@ __device__ __forceinline__ void lstage_issue(const LStage& st, const Geo& g, int
 // address first (any LDS reads the row function needs are batched), then the
 // DMA instructions back to back.
 template <int WT, int NIS, class RowFn>
-__device__ __forceinline__ void lstage_issue_static(const LStage& st, const Geo& g, int k0, RowFn rowfn) {
+__device__ __forceinline__ void lstage_issue_static(const LStage& st, const Geo& g, int k0, RowFn rowfn, int cw) {
   const uint8_t* wp[NIS];
   const uint16_t* sp[NIS];
   bool ok[NIS];
 #pragma unroll
   for (int i = 0; i < NIS; ++i) {
     const int k = k0 + i, p = k / g.CPL, j = k - p * g.CPL;
-    const int r = g.wave * g.RPW + p * NW * g.RPW + g.sub, c = g.li + j * g.LPR;
+    const int r = cw * g.RPW + p * NW * g.RPW + g.sub, c = g.li + j * g.LPR;
     ok[i] = r < g.nrows && c < g.C;
     const RowSrc src = rowfn(ok[i] ? r : 0);
     wp[i] = src.w + 16ll * c;
@@ -458,14 +463,15 @@ __device__ __forceinline__ void lstage_issue_static(const LStage& st, const Geo&
 #pragma unroll
   for (int i = 0; i < NIS; ++i)
     if (ok[i]) {
-      dma16(wp[i], &st.w16[(i * NW + g.wave) * 64]);
-      if constexpr (WT == W_I4) dma4(sp[i], &st.s32[(i * NW + g.wave) * 64]);
+      dma16(wp[i], &st.w16[(i * NW + cw) * 64]);
+      if constexpr (WT == W_I4) dma4(sp[i], &st.s32[(i * NW + cw) * 64]);
     }
 }
+
 // Round 0 of a GEMV: the static issue when its NIS items fit the capacity, else the general loop.
 template <int WT, int NIS, int CAP, class RowFn>
 __device__ __forceinline__ void issue_auto(const LStage& st, const Geo& g, RowFn rowfn) {
-  if constexpr (NIS > 0 && NIS <= CAP) lstage_issue_static<WT, NIS>(st, g, 0, rowfn);
+  if constexpr (NIS > 0 && NIS <= CAP) lstage_issue_static<WT, NIS>(st, g, 0, rowfn, g.wave);
   else lstage_issue<WT>(st, g, 0, rowfn);
 }
 
@@ -646,7 +652,7 @@ __device__ __forceinline__ void compute_static_rows(const LStage& st, const Geo&
 template <int WT, int CPLR, int NIS, class RowFn, class OutFn>
 __device__ __forceinline__ void gemv_static(const LStage& st, const Geo& g, bool issued, const ActRegs<WT, CPLR>& ar,
                                             RowFn rowfn, OutFn outfn) {
-  if (!issued) lstage_issue_static<WT, NIS>(st, g, 0, rowfn);
+  if (!issued) lstage_issue_static<WT, NIS>(st, g, 0, rowfn, g.wave);
   wait_vmem();
   compute_static<WT, CPLR, NIS>(st, g, 0, ar, outfn);
 }
@@ -733,13 +739,13 @@ __device__ __forceinline__ void gemv_stream(const LStage& A, const LStage& B, co
                                             const ActRegs<WT, CPLR>& ar, RowFn rowfn, OutFn outfn) {
   static_assert(WT != W_I4 && CPLR > 0 && CAP % CPLR == 0, "streamed GEMV: bf16 / fp32 rows, activation in registers");
   const int nr = g.NI / CAP;
-  if (nr > 0) lstage_issue_static<WT, CAP>(A, g, 0, rowfn);
+  if (nr > 0) lstage_issue_static<WT, CAP>(A, g, 0, rowfn, g.wave);
   for (int b = 0; b < nr; ++b) {
     const LStage& cur = (b & 1) ? B : A;
     const LStage& nxt = (b & 1) ? A : B;
     if (b + 1 < nr) {
       wait_lds();  // this wave's reads of round b - 1 (in nxt) are done
-      lstage_issue_static<WT, CAP>(nxt, g, (b + 1) * CAP, rowfn);
+      lstage_issue_static<WT, CAP>(nxt, g, (b + 1) * CAP, rowfn, g.wave);
       wait_vmem_n<CAP>();  // round b + 1 issued CAP loads: round b has landed
     } else {
       wait_vmem();
@@ -801,7 +807,7 @@ __device__ __forceinline__ bool gather(Smem& sm, const uint64_t* src, int n, uin
                                        int nsent, PutFn put, Waiter& wt) {
   const int tid = threadIdx.x;
   if (nsent > wt.sentinels) nsent = wt.sentinels;
-  if (tid < 64 && tid < nsent && !wt.abort) {
+  if (tid < 64 && tid < nsent && !wt.abort) {  // sentinels == 0: every thread polls its own slots at once
     const uint64_t* p = src + index(sent(tid, nsent));
     if ((uint32_t)(xload(p) >> 32) != tag) {
       const uint64_t t0 = now();
@@ -816,11 +822,12 @@ __device__ __forceinline__ bool gather(Smem& sm, const uint64_t* src, int n, uin
     }
   }
   if (!sync_ok(sm, wt)) return false;
-  for (int b0 = 0; b0 < n; b0 += 8 * NT) {
+  constexpr int GT = NT;
+  for (int b0 = 0; b0 < n; b0 += 8 * GT) {
     uint64_t v[8];
 #pragma unroll
     for (int k = 0; k < 8; ++k) {
-      const int i = b0 + tid + k * NT;
+      const int i = b0 + tid + k * GT;
       v[k] = i < n ? xload(src + index(i)) : slot(tag, 0);
     }
     uint32_t pending = 0;
@@ -834,7 +841,7 @@ __device__ __forceinline__ bool gather(Smem& sm, const uint64_t* src, int n, uin
         backoff(wt);
 #pragma unroll
         for (int k = 0; k < 8; ++k)
-          if (pending & (1u << k)) v[k] = xload(src + index(b0 + tid + k * NT));
+          if (pending & (1u << k)) v[k] = xload(src + index(b0 + tid + k * GT));
 #pragma unroll
         for (int k = 0; k < 8; ++k)
           if ((pending & (1u << k)) && (uint32_t)(v[k] >> 32) == tag) pending &= ~(1u << k);
@@ -846,7 +853,7 @@ __device__ __forceinline__ bool gather(Smem& sm, const uint64_t* src, int n, uin
     }
 #pragma unroll
     for (int k = 0; k < 8; ++k) {
-      const int i = b0 + tid + k * NT;
+      const int i = b0 + tid + k * GT;
       if (i < n) put(i, (uint32_t)v[k]);
     }
   }
@@ -982,7 +989,10 @@ __global__ void __launch_bounds__(NT, 1) decode_kernel(const KStatic* __restrict
     if (W == 0 && tid == 0) raise_error(wt, ERR_TOKEN);
     tok = 0;
   }
-  if (stamps) stamps[0] = now();
+  if (stamps) {
+    stamps[0] = now();
+    stamps[3] = __builtin_amdgcn_s_memtime();  // shader clock, to relate the stamps to cycles
+  }
   if (tid == 0) sm.flag = 0;
 
   const int T = pos + 1;
@@ -1470,7 +1480,7 @@ __global__ void __launch_bounds__(NT, 1) decode_kernel(const KStatic* __restrict
     const int ue0 = 2 * upb, une = 2 * (upe - upb);
     const int drb = orb, dre = ore;
     const int K = K_;
-    const int wstride = kAct32<WT> ? inner : inner / 2;  // words of one rank's h
+    const int wstride = inner / kChunkElems<WT> * kChunkWords<WT>;  // words of one rank's h
     // this workgroup's units are contiguous: unless they span more than two experts, the selected
     // experts of the first and the next rank are all a row needs
     const Mat mg = dense ? m_dg : m_eg, mu = dense ? m_du : m_eu;
@@ -1538,7 +1548,7 @@ __global__ void __launch_bounds__(NT, 1) decode_kernel(const KStatic* __restrict
       });
     // the down weights and the next norm's weights load during the SwiGLU exchange
     if (dense) issue_auto<WT, NI_DND, DN_CAP>(lstage(sm.u.mlp.dn), gdn, dn_rowfn);
-    else if constexpr (NI_DNM > 0 && NI_DNM <= DN_CAP) lstage_issue_static<WT, NI_DNM>(lstage(sm.u.mlp.dn), gdn, 0, dn_rowfn_x);
+    else if constexpr (NI_DNM > 0 && NI_DNM <= DN_CAP) lstage_issue_static<WT, NI_DNM>(lstage(sm.u.mlp.dn), gdn, 0, dn_rowfn_x, gdn.wave);
     else lstage_issue<WT>(lstage(sm.u.mlp.dn), gdn, 0, dn_rowfn);
     gn_issue(sm, l + 1 < L ? p_anorm + (size_t)(l + 1) * H : p_fnorm, H);
     if (stamp) stamp[12] = now();
@@ -1658,7 +1668,10 @@ __global__ void __launch_bounds__(NT, 1) decode_kernel(const KStatic* __restrict
       }
     }
   }
-  if (stamps) stamps[1] = now();
+  if (stamps) {
+    stamps[1] = now();
+    stamps[4] = __builtin_amdgcn_s_memtime();
+  }
   wait_vmem();
 }
 

@@ -284,8 +284,8 @@ int flint_decode_init(const flint_config* cfg, const flint_weights* w, void* hip
   a.S = c->S;
   // exchange polling: tuning knobs for experiments (defaults are the measured best)
   a.poll_sleep = getenv("FLINT_POLL_SLEEP") ? atoi(getenv("FLINT_POLL_SLEEP")) : 0;
-  a.sentinels = getenv("FLINT_SENTINELS") ? atoi(getenv("FLINT_SENTINELS")) : 64;
-  if (a.sentinels < 1) a.sentinels = 1;
+  a.sentinels = getenv("FLINT_SENTINELS") ? atoi(getenv("FLINT_SENTINELS")) : 0;
+  if (a.sentinels < 0) a.sentinels = 0;
   if (a.sentinels > 64) a.sentinels = 64;
   if (a.poll_sleep < 0) a.poll_sleep = 0;
 
