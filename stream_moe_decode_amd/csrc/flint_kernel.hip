@@ -43,6 +43,8 @@ typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2_t;
 typedef __attribute__((address_space(3))) void lds_void;
 typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
 typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 
 // Every device pointer the kernel dereferences is cast to the global address
 // space: generic (flat) accesses would also count against the LDS wait counter.
@@ -259,21 +261,24 @@ template <int WT> __device__ __forceinline__ void act_put(uint32_t* act, int e, 
     reinterpret_cast<uint16_t*>(act)[p] = (uint16_t)f2bf(v);
   }
 }
+// Sum of the 32 bf16 values of an int4 activation chunk (one fixed order).
+__device__ __forceinline__ float chunk_sum(uint4 x0, uint4 x1, uint4 x2, uint4 x3) {
+  const uint32_t w[16] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w,
+                          x2.x, x2.y, x2.z, x2.w, x3.x, x3.y, x3.z, x3.w};
+  float s0 = 0.f, s1 = 0.f;
+#pragma unroll
+  for (int k = 0; k < 16; k += 2) {
+    s0 += bf2f(w[k] & 0xFFFFu) + bf2f(w[k] >> 16);
+    s1 += bf2f(w[k + 1] & 0xFFFFu) + bf2f(w[k + 1] >> 16);
+  }
+  return s0 + s1;
+}
 // After act_put of n elements (and a barrier): chunk sums for the int4 bias.
 template <int WT> __device__ __forceinline__ void act_sums(const uint32_t* act, float* asum, int n) {
   if constexpr (WT == W_I4) {
     for (int c = threadIdx.x; c < n / 32; c += NT) {
       const uint4* p = reinterpret_cast<const uint4*>(act + c * kChunkWords<WT>);
-      const uint4 x0 = p[0], x1 = p[1], x2 = p[2], x3 = p[3];
-      float s0 = 0.f, s1 = 0.f;
-      const uint32_t w[16] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w,
-                              x2.x, x2.y, x2.z, x2.w, x3.x, x3.y, x3.z, x3.w};
-#pragma unroll
-      for (int k = 0; k < 16; k += 2) {
-        s0 += bf2f(w[k] & 0xFFFFu) + bf2f(w[k] >> 16);
-        s1 += bf2f(w[k + 1] & 0xFFFFu) + bf2f(w[k + 1] >> 16);
-      }
-      asum[c] = s0 + s1;
+      asum[c] = chunk_sum(p[0], p[1], p[2], p[3]);
     }
   }
 }
@@ -901,6 +906,21 @@ __device__ __forceinline__ void kv_issue(uint4* buf, const uint8_t* base, int c0
   }
 }
 
+// K rows [c0, c0 + np) (np <= 128) of one bf16 cache slice with head_dim 128,
+// laid out as the A operand of v_mfma_f32_16x16x32_bf16: 16-byte slot
+// (b * 4 + s) * 64 + L holds dims s * 32 + (L / 16) * 8 .. + 8 of position
+// b * 16 + L % 16 (positions past the end repeat the last one).  The DMA
+// addresses are chosen per lane, so the layout costs nothing.
+__device__ __forceinline__ void k_issue_mfma(uint4* buf, const uint8_t* base, int c0, int np) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int nq = (np + 15) / 16 * 4;
+  for (int q = wave; q < nq; q += NW) {
+    const int b = q >> 2, sk = q & 3;
+    const int pr = min(b * 16 + (lane & 15), np - 1);
+    dma16(base + (size_t)(c0 + pr) * 256 + sk * 64 + (lane >> 4) * 16, &buf[q * 64]);
+  }
+}
+
 // ---------------------------------------------------------------- the kernel
 
 // Model shapes known at compile time let every index, partition and row
@@ -965,6 +985,9 @@ __global__ void __launch_bounds__(NT, 1) decode_kernel(const KStatic* __restrict
   constexpr int CP_QKV = cpl_fit<WT, SH>(SH::H, QKV_CAP), CP_O = cpl_fit<WT, SH>(SH::NQ * SH::HD, O_CAP);
   constexpr int CP_R = cpl_fit<WT, SH>(SH::H, R_CAP), CP_GU = cpl_fit<WT, SH>(SH::H, GU_CAP);
   constexpr int CP_DN = cpl_fit<WT, SH>(SH::DI, DN_CAP), CP_LM = cpl_fit<HW, SH>(SH::H, LM_CAP);
+  // attention scores on MFMA: bf16 cache rows of 128 dims, at most 4 query heads per kv head
+  constexpr bool MFMA_QK = SS && !kAct32<WT> && SH::HD == 128 && SH::NQ / SH::NKV <= 4;
+  constexpr bool ASUM_A = WT == W_I4;  // int4 GEMVs take the chunk sums of actA from LDS
   // items per wave of each GEMV of the static shape (0: general rounds)
   constexpr int NI_QKV = nis_of(2 * even_share((SH::NQ + 2 * SH::NKV) * SH::HD / 2, SH::G), CP_QKV);
   constexpr int NI_O = nis_of(even_share(SH::H, SH::G), CP_O), NI_R = nis_of(SH::E, CP_R);
@@ -1029,7 +1052,8 @@ __global__ void __launch_bounds__(NT, 1) decode_kernel(const KStatic* __restrict
     if (attn && t1 > t0) {
       const size_t cb = (((size_t)l * B + seq) * nkv + aj) * kvstride * ebytes;
       const int np0 = min(CHP, t1 - t0);
-      kv_issue(sm.u.att.kbuf, kc + cb, t0, np0, rowb);
+      if constexpr (MFMA_QK) k_issue_mfma(sm.u.att.kbuf, kc + cb, t0, np0);
+      else kv_issue(sm.u.att.kbuf, kc + cb, t0, np0, rowb);
       kv_issue(sm.u.att.vbuf, vc + cb, t0, np0, rowb);
     }
   };
@@ -1058,7 +1082,7 @@ __global__ void __launch_bounds__(NT, 1) decode_kernel(const KStatic* __restrict
     const int lmoe = l - ks.n_dense;
 
     // ---------------- input RMSNorm (recomputed by every workgroup)
-    rmsnorm_act<WT>(sm, H, ks.eps, true);
+    rmsnorm_act<WT>(sm, H, ks.eps, ASUM_A);
     if (stamp) stamp[0] = now();
 
     // ---------------- QKV rows (staged during the previous layer), RoPE, publish, KV append
@@ -1143,7 +1167,8 @@ __global__ void __launch_bounds__(NT, 1) decode_kernel(const KStatic* __restrict
         const int np = min(CHP, t1 - c0);
         if (c0 != t0) {  // later chunks (long contexts): load now
           __syncthreads();  // every wave is done with the previous chunk
-          kv_issue(at.kbuf, kbase, c0, np, rowb);
+          if constexpr (MFMA_QK) k_issue_mfma(at.kbuf, kbase, c0, np);
+          else kv_issue(at.kbuf, kbase, c0, np, rowb);
           kv_issue(at.vbuf, vbase, c0, np, rowb);
         }
         wait_vmem();
@@ -1157,14 +1182,51 @@ __global__ void __launch_bounds__(NT, 1) decode_kernel(const KStatic* __restrict
               reinterpret_cast<float*>(kr)[e] = at.kn[e];
               reinterpret_cast<float*>(vr)[e] = at.vn[e];
             } else {
-              reinterpret_cast<uint16_t*>(kr)[e] = (uint16_t)f2bf(at.kn[e]);
+              if constexpr (MFMA_QK) {  // the row's dims sit in 16 slots of the operand layout
+                const int pr = pos - c0, b = pr >> 4, i = pr & 15, sk = e >> 5, gq = (e >> 3) & 3;
+                reinterpret_cast<uint16_t*>(at.kbuf)[((b * 4 + sk) * 64 + gq * 16 + i) * 8 + (e & 7)] =
+                    (uint16_t)f2bf(at.kn[e]);
+              } else {
+                reinterpret_cast<uint16_t*>(kr)[e] = (uint16_t)f2bf(at.kn[e]);
+              }
               reinterpret_cast<uint16_t*>(vr)[e] = (uint16_t)f2bf(at.vn[e]);
             }
           }
           __syncthreads();
         }
+        if constexpr (MFMA_QK) {
+          // scores on MFMA: D[position][head] = K[16 positions x 32 dims] . Q^T[32 dims x 16 heads], the
+          // query split into bf16 high and low parts (q = hi + lo to about 16 bits) so the product keeps
+          // fp32-level accuracy; lane L supplies head L % 16 (zero past Gq) and gets positions
+          // (L / 16) * 4 + r of the block
+          const int n = lane & 15, kg = (lane >> 4) * 8;
+          bf16x8_t qh[4], ql[4];
+#pragma unroll
+          for (int sk = 0; sk < 4; ++sk)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+              const float qv = n < Gq ? at.qs[n * hd + sk * 32 + kg + e] : 0.f;
+              const uint32_t hb = f2bf(qv);
+              qh[sk][e] = __builtin_bit_cast(__bf16, (uint16_t)hb);
+              ql[sk][e] = __builtin_bit_cast(__bf16, (uint16_t)f2bf(qv - bf2f(hb)));
+            }
+          const int nb = (np + 15) / 16;
+          for (int b = wave; b < nb; b += NW) {
+            f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int sk = 0; sk < 4; ++sk) {
+              const bf16x8_t a = __builtin_bit_cast(bf16x8_t, at.kbuf[(b * 4 + sk) * 64 + lane]);
+              acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qh[sk], acc, 0, 0, 0);
+              acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, ql[sk], acc, 0, 0, 0);
+            }
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+              const int pr = b * 16 + (lane >> 4) * 4 + r;
+              if (n < Gq && pr < np) at.sc[n * CHP + pr] = acc[r];
+            }
+          }
+        } else {
         // scores: LPK lanes read one K row (16 B each), RPI rows per wave instruction
-        {
           constexpr int DPL = kAct32<WT> ? 4 : 8;  // dims per lane
           const int LPK = rowb / 16, RPI = 64 / LPK;
           const int seg = lane % LPK, rsub = lane / LPK;
@@ -1390,8 +1452,10 @@ __global__ void __launch_bounds__(NT, 1) decode_kernel(const KStatic* __restrict
                      wt);
     if (!ok) break;
     if (stamp) stamp[6] = now();
-    act_sums<WT>(sm.actA, sm.asumA, QD);
-    __syncthreads();
+    if constexpr (ASUM_A) {
+      act_sums<WT>(sm.actA, sm.asumA, QD);
+      __syncthreads();
+    }
     {
       const auto ar = act_regs<WT, CP_O>(go, sm.actA, sm.asumA);
       gemv_auto<WT, CP_O, NI_O, O_CAP>(lstage(sm.u.mg.so), go, true, ar, o_rowfn, [&](int q, float v) { sm.ytmp[q] = v; });
@@ -1412,7 +1476,7 @@ __global__ void __launch_bounds__(NT, 1) decode_kernel(const KStatic* __restrict
     if (stamp) stamp[8] = now();
 
     // ---------------- post-attention RMSNorm (recomputed by every workgroup)
-    rmsnorm_act<WT>(sm, H, ks.eps, true);
+    rmsnorm_act<WT>(sm, H, ks.eps, ASUM_A);
     if (stamp) stamp[9] = now();
 
     int nunit, inner;  // SwiGLU elements this layer produces, and the down projection's input width
