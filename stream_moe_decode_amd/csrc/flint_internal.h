@@ -21,7 +21,7 @@ constexpr int KV_LDS = 32768;           // bytes of K (and of V) rows per attent
 constexpr int MAX_CHUNK_POS = KV_LDS / 128;  // positions per chunk for the smallest row (64 bf16)
 constexpr int NCOPY = 8;                // replicas of broadcast exchanges (one per XCD)
 // LDS weight staging, in items (one 16-byte chunk per lane of a wave) per wave
-constexpr int QKV_CAP = 2, O_CAP = 1, R_CAP = 8, GU_CAP = 6, DN_CAP = 3, LM_CAP = 8;
+constexpr int QKV_CAP = 2, O_CAP = 1, GU_CAP = 6, DN_CAP = 3, LM_CAP = 8;
 constexpr int TAGS_PER_LAUNCH = 1024;   // exchange tags one launch may use
 constexpr uint64_t SPIN_TIMEOUT = 100000000ull;  // 1 s of the 100 MHz wall clock
 
@@ -53,6 +53,7 @@ struct KStatic {
   uint64_t* x_res1;      // [NCOPY][2][H]                   residual after o_proj (fp32)
   uint64_t* x_h;         // [NCOPY][2][h_slots]             SwiGLU output
   uint64_t* x_res2;      // [NCOPY][2][H]                   residual after the MLP (fp32)
+  uint64_t* x_z;         // [NCOPY][2][E]                   router logits (fp32)
   uint32_t* err;         // device error word
   uint32_t* herr;        // host-mapped error word
   unsigned long long* amax;  // packed argmax key

@@ -50,6 +50,11 @@ typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 // space: generic (flat) accesses would also count against the LDS wait counter.
 #define GLOBAL __attribute__((address_space(1)))
 template <class T> __device__ __forceinline__ GLOBAL T* gp(T* p) { return (GLOBAL T*)p; }
+// 16 bytes from global memory into registers.
+__device__ __forceinline__ uint4 ld16(const void* p) {
+  const u32x4_t v = *(GLOBAL const u32x4_t*)p;
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
 
 // ---------------------------------------------------------------- scalars
 
@@ -155,7 +160,7 @@ struct Smem {
   union {
     AttnLds att;
     MergeLds mg;
-    StageLds<R_CAP> rt;                  // router weights (staged during the o_proj exchange)
+    StageLds<(MAX_H / 4 + 63) / 64> rt;  // router rows of this workgroup (staged during the o_proj exchange)
     MlpLds mlp;
     HeadLds head;
   } u;
@@ -975,7 +980,7 @@ __global__ void __launch_bounds__(NT, 1) decode_kernel(const KStatic* __restrict
   const Mat m_eg = ks.eg, m_eu = ks.eu, m_ed = ks.ed;
   const float *const p_anorm = ks.anorm, *const p_pnorm = ks.pnorm, *const p_fnorm = ks.fnorm;
   uint64_t *const x_qkv = ks.x_qkv, *const x_part = ks.x_part, *const x_o = ks.x_o;
-  uint64_t *const x_res1 = ks.x_res1, *const x_h = ks.x_h, *const x_res2 = ks.x_res2;
+  uint64_t *const x_res1 = ks.x_res1, *const x_h = ks.x_h, *const x_res2 = ks.x_res2, *const x_z = ks.x_z;
   uint8_t* const kc = d.kc;
   uint8_t* const vc = d.vc;
   const int seq = d.seq, B = d.B, cap = d.cap;
@@ -983,14 +988,15 @@ __global__ void __launch_bounds__(NT, 1) decode_kernel(const KStatic* __restrict
   // chunks per lane of each GEMV of the static shape (0: dynamic geometry, activation read from LDS)
   constexpr int HW = WT == W_I4 ? W_BF16 : WT;  // the head is bf16 (or fp32) even when the layers are int4
   constexpr int CP_QKV = cpl_fit<WT, SH>(SH::H, QKV_CAP), CP_O = cpl_fit<WT, SH>(SH::NQ * SH::HD, O_CAP);
-  constexpr int CP_R = cpl_fit<WT, SH>(SH::H, R_CAP), CP_GU = cpl_fit<WT, SH>(SH::H, GU_CAP);
+  constexpr int CP_GU = cpl_fit<WT, SH>(SH::H, GU_CAP);
   constexpr int CP_DN = cpl_fit<WT, SH>(SH::DI, DN_CAP), CP_LM = cpl_fit<HW, SH>(SH::H, LM_CAP);
   // attention scores on MFMA: bf16 cache rows of 128 dims, at most 4 query heads per kv head
   constexpr bool MFMA_QK = SS && !kAct32<WT> && SH::HD == 128 && SH::NQ / SH::NKV <= 4;
   constexpr bool ASUM_A = WT == W_I4;  // int4 GEMVs take the chunk sums of actA from LDS
+  constexpr int RCH = (MAX_H / kChunkElems<WT> + 63) / 64;  // router row chunks per lane
   // items per wave of each GEMV of the static shape (0: general rounds)
   constexpr int NI_QKV = nis_of(2 * even_share((SH::NQ + 2 * SH::NKV) * SH::HD / 2, SH::G), CP_QKV);
-  constexpr int NI_O = nis_of(even_share(SH::H, SH::G), CP_O), NI_R = nis_of(SH::E, CP_R);
+  constexpr int NI_O = nis_of(even_share(SH::H, SH::G), CP_O);
   constexpr int NI_GUM = nis_of(4 * even_share(SH::K * SH::EI / 2, SH::G), CP_GU);
   constexpr int NI_GUD = nis_of(4 * even_share(SH::DI / 2, SH::G), CP_GU);
   constexpr int NI_DND = nis_of(even_share(SH::H, SH::G), CP_DN);
@@ -1466,10 +1472,21 @@ __global__ void __launch_bounds__(NT, 1) decode_kernel(const KStatic* __restrict
       return __float_as_uint(sm.xres[orb + q] + sm.ytmp[q]);
     });
     if (stamp) stamp[7] = now();
-    // router rows (all of them, every workgroup): stage before waiting for the residual
-    const Geo gr = geo<WT>(dense ? 0 : E_, H);
-    auto r_rowfn = [&](int q) { return mrow<WT>(m_r, (long long)lmoe * E_ + q, H, sm.actA, sm.asumA); };
-    if (!dense) issue_auto<WT, NI_R, R_CAP>(lstage(sm.u.rt), gr, r_rowfn);
+    // router rows of this workgroup (one wave per row): the first row of each wave is staged before
+    // the wait for the residual (chunk lane + 64 j of the row in item j)
+    const int rbb = dense ? 0 : part(E_, G, W), rbe = dense ? 0 : part(E_, G, W + 1);
+    const int RC = H / kChunkElems<WT>;  // chunks of one router row
+    const LStage rst = lstage(sm.u.rt);
+    auto router_issue = [&](int r) {
+      const RowSrc src = mrow<WT>(m_r, (long long)lmoe * E_ + r, H, nullptr, nullptr);
+#pragma unroll
+      for (int j = 0; j < RCH; ++j) {
+        const int c = lane + 64 * j < RC ? lane + 64 * j : 0;
+        dma16(src.w + 16ll * c, &rst.w16[(j * NW + wave) * 64]);
+        if constexpr (WT == W_I4) dma4(src.s + ((c >> 1) & ~1), &rst.s32[(j * NW + wave) * 64]);
+      }
+    };
+    if (rbb + wave < rbe) router_issue(rbb + wave);
     ok = gather_flat(sm, copy_of(x_res1, H, par), H, tag + 3,
                      [&](int i, uint32_t p) { sm.xres[i] = __uint_as_float(p); }, wt);
     if (!ok) break;
@@ -1488,12 +1505,28 @@ __global__ void __launch_bounds__(NT, 1) decode_kernel(const KStatic* __restrict
         if (d.dbg_rw) gp(d.dbg_rw)[(size_t)l * K_ + tid] = 0.f;
       }
     } else {
-      // ------------ router (every workgroup computes all logits) and top-k
+      // ------------ router: each of its rows computed by one workgroup, the logits exchanged; top-k
       {
-        const auto ar = act_regs<WT, CP_R>(gr, sm.actA, sm.asumA);
-        gemv_auto<WT, CP_R, NI_R, R_CAP>(lstage(sm.u.rt), gr, true, ar, r_rowfn, [&](int q, float v) { sm.z[q] = v; });
+        const I4K k4 = i4k();
+        for (int r = rbb + wave, it = 0; r < rbe; r += NW, ++it) {
+          if (it > 0) {  // more rows than waves (small grids): this wave's reads of the slots are done
+            wait_lds();
+            router_issue(r);
+          }
+          wait_vmem();
+          float acc = 0.f;
+#pragma unroll
+          for (int j = 0; j < RCH; ++j) {
+            const int c = lane + 64 * j;
+            if (c < RC) acc += item_dot<WT>(rst, (j * NW + wave) * 64 + lane, c, act_chunk<WT>(sm.actA, sm.asumA, c), k4);
+          }
+          acc = wave_sum(acc);
+          if (lane < NCOPY) xstore(x_z + (size_t)(lane * 2 + par) * E_ + r, slot(tag + 6, __float_as_uint(acc)));
+        }
       }
-      __syncthreads();
+      ok = gather_flat(sm, copy_of(x_z, E_, par), E_, tag + 6, [&](int i, uint32_t p) { sm.z[i] = __uint_as_float(p); },
+                       wt);
+      if (!ok) break;
       if (stamp) stamp[10] = now();
       // top-k by rank, in every wave (identical results; a wave reads only its own writes):
       // lane e counts the experts that beat it (larger logit, or equal logit and lower index)

@@ -317,7 +317,8 @@ int flint_decode_init(const flint_config* cfg, const flint_weights* w, void* hip
   a.h_slots = (int)std::max<size_t>(1, act32 ? hmax : hmax / 2);
   const size_t n_qkv = NCOPY * 2 * QR, n_part = 2 * (size_t)cfg->n_q_heads * (hd + 2) * c->S;
   const size_t n_o = NCOPY * 2 * (size_t)a.o_slots, n_res = NCOPY * 2 * H, n_h = NCOPY * 2 * (size_t)a.h_slots;
-  c->xbuf_words = n_qkv + n_part + n_o + 2 * n_res + n_h;
+  const size_t n_z = NCOPY * 2 * (size_t)std::max(1, cfg->n_experts);
+  c->xbuf_words = n_qkv + n_part + n_o + 2 * n_res + n_h + n_z;
   void* xb;
   if ((rc = dalloc(c, &xb, c->xbuf_words * 8 + 256))) return bail(rc);
   c->xbuf = (uint64_t*)xb;
@@ -327,6 +328,7 @@ int flint_decode_init(const flint_config* cfg, const flint_weights* w, void* hip
   a.x_res1 = a.x_o + n_o;
   a.x_h = a.x_res1 + n_res;
   a.x_res2 = a.x_h + n_h;
+  a.x_z = a.x_res2 + n_res;
   void* misc;
   if ((rc = dalloc(c, &misc, 256))) return bail(rc);
   a.err = (uint32_t*)misc;
