@@ -1,0 +1,622 @@
+// Batched greedy decode for gfx950 (MI355X): up to 16 sequences per pass.
+//
+// The page "Flint Inference on Apple Silicon: rec Megakernel and Tempo9
+// Compared" (section 4) sets per-token GEMVs, which suit one client, against
+// tiled and grouped contractions once several clients decode together.  Here
+// every weight tile is read once per pass and multiplied against all the
+// sequences' activations on MFMA: v_mfma_f32_16x16x32_bf16 takes 16 weight
+// rows x 32 inputs and 32 inputs x 16 sequences.  int4 weights are unpacked
+// to bf16 in registers and each 64-input group's scale multiplies that
+// group's fp32 products, so the arithmetic matches the dequantised weights.
+//
+// A pass is a sequence of ordinary kernels per layer, on one stream:
+//   input norm -> QKV (RoPE, K/V append) -> attention splits over each
+//   sequence's own length -> split merge -> o_proj -> post norm, router and
+//   top-k -> gate/up of the selected experts (grouped by expert over the
+//   union of the sequences' picks) -> down and combine.
+// Kernels that would need a grid-wide sum (o_proj and down over input chunks
+// or expert chunks) write partial sums that the next norm kernel adds to the
+// residual, so no kernel waits for another workgroup.  The head's argmax uses
+// packed (logit, id) atomic maxima per sequence; the last workgroup to finish
+// publishes the ids and advances the lengths, as the persistent kernel does.
+
+#include "flint_device.h"
+
+namespace flint {
+namespace {
+
+constexpr int BNT = 512, BNW = BNT / 64;
+typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
+
+// Position of element e in a GEMM input row: int4 models store each group of
+// 8 as (0, 4, 1, 5, 2, 6, 3, 7), the order in which a word of 8 codes unpacks.
+template <int WT> __device__ __forceinline__ int act_pos(int e) {
+  return WT == W_I4 ? (e & ~7) | ((e & 3) << 1) | ((e >> 2) & 1) : e;
+}
+__device__ __forceinline__ bf16x8_t as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8_t, v); }
+__device__ __forceinline__ f32x4_t mfma(bf16x8_t a, bf16x8_t b, f32x4_t c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+// 8 int4 codes (element i in bits 4i .. 4i + 3) as the bf16 values 128 + u, in the order (0, 4, 1, 5, 2, 6, 3, 7)
+__device__ __forceinline__ bf16x8_t unpack8(uint32_t q, const I4K& k4) {
+  return as_bf16x8(make_uint4((q & k4.m) | k4.mag, ((q >> 4) & k4.m) | k4.mag, ((q >> 8) & k4.m) | k4.mag,
+                              ((q >> 12) & k4.m) | k4.mag));
+}
+__device__ __forceinline__ void latch(const BArgs& a, uint32_t bits) {
+  __hip_atomic_fetch_or(gp(a.err), bits, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+  __hip_atomic_store(gp(a.herr), bits, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+}
+
+// acc += W[the tile's 16 rows] . x over the 64-input groups [g0, g1), for 16 sequence columns.
+// Lane L supplies row L % 16 of the tile (matrix row rowmap(L % 16)) and column L % 16 (`col`: that
+// sequence's input row, null for a zero column), inputs (L / 16) * 16 + [0, 16) of each group; it
+// accumulates rows (L / 16) * 4 + r of column L % 16.  int4: codes enter as 128 + u, and two MFMAs
+// with the constant -136 as the weight operand remove the offset before the group's scale applies.
+template <int WT, class RowMap>
+__device__ __forceinline__ void mma_groups(f32x4_t& acc, const Mat& m, int in, RowMap rowmap, const uint16_t* col,
+                                           int g0, int g1) {
+  const int lane = threadIdx.x & 63, mr = lane & 15, kg = lane >> 4;
+  const uint8_t* wr = m.w + rowmap(mr) * row_bytes<WT>(in);
+  const uint16_t* sp[4];
+  if constexpr (WT == W_I4) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) sp[r] = m.s + rowmap(4 * kg + r) * (in / 64);
+  }
+  const I4K k4 = i4k();
+  const bf16x8_t bias = as_bf16x8(make_uint4(0xC308C308u, 0xC308C308u, 0xC308C308u, 0xC308C308u));  // bf16 -136
+  constexpr int U = 4;
+  for (int g = g0; g < g1; g += U) {
+    uint32_t wq[U][2];
+    uint4 wb[U][2], b0[U], b1[U];
+    float sc[U][4];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {  // every load of U groups first
+      const int gg = min(g + u, g1 - 1);
+      const int e0 = gg * 64 + kg * 16;
+      if constexpr (WT == W_I4) {
+        const u32x2_t w2 = *(GLOBAL const u32x2_t*)(wr + e0 / 2);
+        wq[u][0] = w2.x;
+        wq[u][1] = w2.y;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) sc[u][r] = bf2f(gp(sp[r])[gg]);
+      } else {
+        wb[u][0] = ld16(wr + 2 * e0);
+        wb[u][1] = ld16(wr + 2 * e0 + 16);
+      }
+      if (col) {
+        b0[u] = ld16(col + e0);
+        b1[u] = ld16(col + e0 + 8);
+      } else {
+        b0[u] = b1[u] = make_uint4(0u, 0u, 0u, 0u);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      if (g + u < g1) {
+        if constexpr (WT == W_I4) {
+          f32x4_t d = {0.f, 0.f, 0.f, 0.f};
+          d = mfma(unpack8(wq[u][0], k4), as_bf16x8(b0[u]), d);
+          d = mfma(unpack8(wq[u][1], k4), as_bf16x8(b1[u]), d);
+          d = mfma(bias, as_bf16x8(b0[u]), d);
+          d = mfma(bias, as_bf16x8(b1[u]), d);
+#pragma unroll
+          for (int r = 0; r < 4; ++r) acc[r] = fmaf(sc[u][r], d[r], acc[r]);
+        } else {
+          acc = mfma(as_bf16x8(wb[u][0]), as_bf16x8(b0[u]), acc);
+          acc = mfma(as_bf16x8(wb[u][1]), as_bf16x8(b1[u]), acc);
+        }
+      }
+    }
+  }
+}
+
+// Sum of the workgroup's 8 wave tiles, returned in wave 0 (other waves get their own tile back).
+__device__ __forceinline__ f32x4_t sum_waves(f32x4_t acc, f32x4_t* red) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  red[wave * 64 + lane] = acc;
+  __syncthreads();
+  if (wave == 0)
+#pragma unroll
+    for (int w = 1; w < BNW; ++w) acc += red[w * 64 + lane];
+  return acc;
+}
+
+__device__ __forceinline__ float bsum(float v, float* wred) {
+  v = wave_sum(v);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  __syncthreads();
+  if (lane == 0) wred[wave] = v;
+  __syncthreads();
+  float t = 0.f;
+#pragma unroll
+  for (int w = 0; w < BNW; ++w) t += wred[w];
+  return t;
+}
+
+enum { NORM_EMBED = 0, NORM_INPUT = 1, NORM_POST = 2, NORM_FINAL = 3 };
+
+// RMSNorm of one sequence's residual (grid: one workgroup per sequence).  The residual first takes the
+// pending partial sums (down of the previous layer, or o_proj); the normalised row becomes the next
+// GEMM input.  NORM_POST of a MoE layer also computes the router logits and the top-k.
+template <int WT>
+__global__ void __launch_bounds__(BNT) bk_norm(const BArgs a, int l, int mode) {
+  __shared__ float xs[MAX_H];
+  __shared__ __attribute__((aligned(16))) uint16_t an[MAX_H];
+  __shared__ float z[MAX_E];
+  __shared__ float wred[BNW];
+  const int n = blockIdx.x, seq = a.seq0 + n, tid = threadIdx.x, H = a.H;
+  float* xg = a.x + (size_t)n * H;
+  if (mode == NORM_EMBED) {
+    int tok = gp(a.tokens)[seq];
+    if (tok < 0 || tok >= a.V) {
+      if (tid == 0) latch(a, ERR_TOKEN);
+      tok = 0;
+    }
+    const uint16_t* er = reinterpret_cast<const uint16_t*>(a.embed) + (size_t)tok * H;
+    for (int e = tid; e < H; e += BNT) xs[e] = bf2f(gp(er)[e]);
+  } else {
+    const float* pp = mode == NORM_POST ? a.opart : a.dpart;
+    const int np = mode == NORM_POST ? OKC : DKC;
+    for (int e = tid; e < H; e += BNT) {
+      float v = gp(xg)[e];
+      for (int p = 0; p < np; ++p) v += gp(pp)[((size_t)p * BT + n) * H + e];
+      xs[e] = v;
+    }
+  }
+  for (int e = tid; e < H; e += BNT) gp(xg)[e] = xs[e];
+  // the residual after layer dbg_resid_layer is complete when the next layer's input norm (or the final norm) adds it up
+  if (a.dbg_resid && ((mode == NORM_INPUT && l - 1 == a.dbg_resid_layer) || (mode == NORM_FINAL && a.L - 1 == a.dbg_resid_layer)))
+    for (int e = tid; e < H; e += BNT) gp(a.dbg_resid)[(size_t)seq * H + e] = xs[e];
+  float ss = 0.f;
+  for (int e = tid; e < H; e += BNT) ss += xs[e] * xs[e];
+  ss = bsum(ss, wred);
+  const float inv = 1.0f / sqrtf(ss / (float)H + a.eps);
+  const float* g = mode == NORM_POST ? a.pnorm + (size_t)l * H : (mode == NORM_FINAL ? a.fnorm : a.anorm + (size_t)l * H);
+  uint16_t* ag = a.act + (size_t)n * a.astride;
+  for (int e = tid; e < H; e += BNT) {
+    const uint16_t v = (uint16_t)f2bf(xs[e] * inv * gp(g)[e]);
+    const int p = mode == NORM_FINAL ? e : act_pos<WT>(e);  // the lm_head is bf16: natural order
+    an[p] = v;
+    gp(ag)[p] = v;
+  }
+  if (mode != NORM_POST) return;
+  if (l < a.n_dense) {  // dense layer: no routing
+    if (tid < a.K) {
+      if (a.dbg_routes) gp(a.dbg_routes)[((size_t)seq * a.L + l) * a.K + tid] = -1;
+      if (a.dbg_rw) gp(a.dbg_rw)[((size_t)seq * a.L + l) * a.K + tid] = 0.f;
+    }
+    return;
+  }
+
+  // router: wave w computes logits w, w + 8, ...; lanes over 16-byte weight chunks
+  __syncthreads();
+  const int lane = tid & 63, wave = tid >> 6, E = a.E;
+  const int lm = l - a.n_dense;
+  const I4K k4 = i4k();
+  constexpr int CE = WT == W_I4 ? 32 : 8;  // inputs per 16-byte chunk
+  const int C = H / CE;
+  for (int e = wave; e < E; e += BNW) {
+    const uint8_t* row = a.router.w + ((long long)lm * E + e) * row_bytes<WT>(H);
+    float acc = 0.f;
+    for (int c = lane; c < C; c += 64) {
+      const uint4 w = ld16(row + 16ll * c);
+      ActC<WT> x;
+      float scale = 1.f;
+      if constexpr (WT == W_I4) {
+        const uint4* p = reinterpret_cast<const uint4*>(an + 32 * c);
+        x.a[0] = p[0];
+        x.a[1] = p[1];
+        x.a[2] = p[2];
+        x.a[3] = p[3];
+        x.s = chunk_sum(x.a[0], x.a[1], x.a[2], x.a[3]);
+        scale = bf2f(gp(a.router.s)[((long long)lm * E + e) * (H / 64) + c / 2]);
+      } else {
+        x.a[0] = *reinterpret_cast<const uint4*>(an + 8 * c);
+        x.s = 0.f;
+      }
+      acc += chunk_dot<WT>(w, x, scale, k4);
+    }
+    acc = wave_sum(acc);
+    if (lane == 0) z[e] = acc;
+  }
+  __syncthreads();
+  if (wave != 0) return;
+  // top-k by rank (larger logit first, equal logits: lower index first), weights softmax over all experts
+  const float zl = lane < E ? z[lane] : -INFINITY;
+  int rank = 0;
+  for (int j = 0; j < E; ++j) {
+    const float zj = z[j];
+    rank += zj > zl || (zj == zl && j < lane);
+  }
+  const float zmax = wave_max(zl);
+  const float pe = lane < E ? __expf(zl - zmax) : 0.f;
+  const float w = pe / wave_sum(pe);
+  const bool pick = lane < E && rank < a.K;
+  const float wsum = wave_sum(pick ? w : 0.f);
+  if (pick) {
+    const float wr = a.renorm ? w / wsum : w;
+    gp(a.sel)[n * a.K + rank] = lane;
+    gp(a.wsel)[n * a.K + rank] = wr;
+    if (a.dbg_routes) gp(a.dbg_routes)[((size_t)seq * a.L + l) * a.K + rank] = lane;
+    if (a.dbg_rw) gp(a.dbg_rw)[((size_t)seq * a.L + l) * a.K + rank] = wr;
+  }
+}
+
+// QKV rows, RoPE, K/V append.  Workgroup t: 8 rotate-half pairs of one head (rows i0 + m and
+// hd/2 + i0 + m, m < 8), so a row and its RoPE partner sit in lanes L and L ^ 32 of the result.
+template <int WT>
+__global__ void __launch_bounds__(BNT) bk_qkv(const BArgs a, int l) {
+  __shared__ f32x4_t red[BNW * 64];
+  const int t = blockIdx.x, lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int hd = a.hd, half = hd / 2, tph = hd / 16;
+  const int hh = t / tph, i0 = (t % tph) * 8;
+  const int QR = (a.nq + 2 * a.nkv) * hd;
+  auto rowmap = [&](int m) -> long long { return (long long)l * QR + hh * hd + (m < 8 ? i0 + m : half + i0 + m - 8); };
+  const int G = a.H / 64, n = lane & 15, kg = lane >> 4;
+  const uint16_t* col = n < a.B ? a.act + (size_t)n * a.astride : nullptr;
+  f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+  mma_groups<WT>(acc, a.qkv, a.H, rowmap, col, part(G, BNW, wave), part(G, BNW, wave + 1));
+  acc = sum_waves(acc, red);
+  if (wave != 0) return;
+  float y[4] = {acc[0], acc[1], acc[2], acc[3]};
+  const int pos = n < a.B ? gp(a.len)[a.seq0 + n] : 0;
+  if (hh < a.nq + a.nkv) {  // RoPE on q and k heads: (y_i, y_{i + hd/2}) rotated by the angle of pair i
+    float p[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) p[r] = swap32(y[r]);
+    if (n < a.B) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const f32x2_t cs = *(GLOBAL const f32x2_t*)(a.rope + (size_t)pos * half + i0 + 4 * (kg & 1) + r);
+        y[r] = kg < 2 ? y[r] * cs.x - p[r] * cs.y : y[r] * cs.x + p[r] * cs.y;
+      }
+    }
+  }
+  if (n >= a.B) return;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int m = 4 * kg + r, d = m < 8 ? i0 + m : half + i0 + m - 8;
+    if (hh < a.nq) {
+      gp(a.q)[(size_t)n * a.nq * hd + hh * hd + d] = y[r];
+    } else {
+      const bool isk = hh < a.nq + a.nkv;
+      const int j = isk ? hh - a.nq : hh - a.nq - a.nkv;
+      const size_t off = ((((size_t)l * a.Bc + a.seq0 + n) * a.nkv + j) * a.cap + pos) * hd + d;
+      gp(reinterpret_cast<uint16_t*>(isk ? a.kc : a.vc))[off] = (uint16_t)f2bf(y[r]);
+    }
+  }
+}
+
+// Attention partial of (split s, kv head j, sequence n) over positions [s P, min(s P + P, len + 1)) of the
+// sequence's own cache (the new token's K/V already appended): scores on MFMA (the query split into bf16 high
+// and low parts), softmax, P.V on the vector units.  Writes (m, l, o) of each query head of the group.
+__global__ void __launch_bounds__(BNT) bk_attn(const BArgs a, int l) {
+  __shared__ uint4 kbuf[ATT_P * 16];   // K rows in the A-operand layout of v_mfma_f32_16x16x32_bf16
+  __shared__ uint4 vbuf[ATT_P * 16];   // V rows
+  __shared__ float qs[4 * 128];
+  __shared__ float sc[4 * ATT_P];      // [head][position]
+  __shared__ float pt[ATT_P * 4];      // [position][head]
+  __shared__ float mst[4], lst[4];
+  const int s = blockIdx.x, j = blockIdx.y, n = blockIdx.z;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int T = gp(a.len)[a.seq0 + n] + 1, t0 = s * ATT_P;
+  if (t0 >= T) return;
+  const int np = min(ATT_P, T - t0), hd = 128, Gq = a.nq / a.nkv;
+  const size_t cb = (((size_t)l * a.Bc + a.seq0 + n) * a.nkv + j) * (size_t)a.cap * hd * 2;
+  k_issue_mfma(kbuf, a.kc + cb, t0, np);
+  kv_issue(vbuf, a.vc + cb, t0, np, 256);
+  const float qscale = 1.0f / sqrtf((float)hd);
+  for (int i = tid; i < 4 * hd; i += BNT)
+    qs[i] = i < Gq * hd ? gp(a.q)[(size_t)n * a.nq * hd + (size_t)j * Gq * hd + i] * qscale : 0.f;
+  wait_vmem();
+  __syncthreads();
+  {  // scores: D[position][head] = K[16 positions x 32 dims] . Q^T[32 dims x 16 heads]
+    const int hcol = lane & 15, kq = (lane >> 4) * 8;
+    bf16x8_t qh[4], ql[4];
+#pragma unroll
+    for (int sk = 0; sk < 4; ++sk)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float qv = hcol < Gq ? qs[hcol * hd + sk * 32 + kq + e] : 0.f;
+        const uint32_t hb = f2bf(qv);
+        qh[sk][e] = __builtin_bit_cast(__bf16, (uint16_t)hb);
+        ql[sk][e] = __builtin_bit_cast(__bf16, (uint16_t)f2bf(qv - bf2f(hb)));
+      }
+    for (int b = wave; b < (np + 15) / 16; b += BNW) {
+      f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int sk = 0; sk < 4; ++sk) {
+        const bf16x8_t kop = as_bf16x8(kbuf[(b * 4 + sk) * 64 + lane]);
+        acc = mfma(kop, qh[sk], acc);
+        acc = mfma(kop, ql[sk], acc);
+      }
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int pr = b * 16 + (lane >> 4) * 4 + r;
+        if (hcol < Gq && pr < np) sc[hcol * ATT_P + pr] = acc[r];
+      }
+    }
+  }
+  __syncthreads();
+  for (int h = wave; h < 4; h += BNW) {  // softmax of head h (padding heads: zero probabilities)
+    if (h >= Gq) {
+      for (int i = lane; i < np; i += 64) pt[i * 4 + h] = 0.f;
+      continue;
+    }
+    float mx = -INFINITY;
+    for (int i = lane; i < np; i += 64) mx = fmaxf(mx, sc[h * ATT_P + i]);
+    mx = wave_max(mx);
+    float ls = 0.f;
+    for (int i = lane; i < np; i += 64) {
+      const float p = __expf(sc[h * ATT_P + i] - mx);
+      pt[i * 4 + h] = p;
+      ls += p;
+    }
+    ls = wave_sum(ls);
+    if (lane == 0) {
+      mst[h] = mx;
+      lst[h] = ls;
+    }
+  }
+  __syncthreads();
+  // P.V: wave w takes positions w, w + 8, ...; lane: dims 2 lane, 2 lane + 1 of every head
+  float o[4][2] = {{0.f, 0.f}, {0.f, 0.f}, {0.f, 0.f}, {0.f, 0.f}};
+  const uint32_t* vb = reinterpret_cast<const uint32_t*>(vbuf);
+#pragma unroll 4
+  for (int i = wave; i < np; i += BNW) {
+    const float4 p = *reinterpret_cast<const float4*>(pt + i * 4);
+    const uint32_t v2 = vb[i * 64 + lane];
+    const float v0 = bf2f(v2 & 0xFFFFu), v1 = bf2f(v2 >> 16);
+    o[0][0] = fmaf(p.x, v0, o[0][0]);
+    o[0][1] = fmaf(p.x, v1, o[0][1]);
+    o[1][0] = fmaf(p.y, v0, o[1][0]);
+    o[1][1] = fmaf(p.y, v1, o[1][1]);
+    o[2][0] = fmaf(p.z, v0, o[2][0]);
+    o[2][1] = fmaf(p.z, v1, o[2][1]);
+    o[3][0] = fmaf(p.w, v0, o[3][0]);
+    o[3][1] = fmaf(p.w, v1, o[3][1]);
+  }
+  float* red = reinterpret_cast<float*>(kbuf);  // the K rows are dead since the softmax's barrier
+#pragma unroll
+  for (int h = 0; h < 4; ++h) {
+    red[(wave * 4 + h) * hd + 2 * lane] = o[h][0];
+    red[(wave * 4 + h) * hd + 2 * lane + 1] = o[h][1];
+  }
+  __syncthreads();
+  float* dst = a.part + (((size_t)n * a.nq + (size_t)j * Gq) * a.nsmax + s) * (hd + 2);
+  const size_t hstep = (size_t)a.nsmax * (hd + 2);  // between query heads
+  for (int idx = tid; idx < Gq * hd; idx += BNT) {
+    const int h = idx / hd, e = idx % hd;
+    float t = 0.f;
+#pragma unroll
+    for (int w = 0; w < BNW; ++w) t += red[(w * 4 + h) * hd + e];
+    gp(dst)[h * hstep + 2 + e] = t;
+  }
+  if (tid < 2 * Gq) gp(dst)[(tid >> 1) * hstep + (tid & 1)] = (tid & 1) ? lst[tid >> 1] : mst[tid >> 1];
+}
+
+// Merge the splits of (query head h, sequence n): o = sum_s e^(m_s - M) o_s / sum_s e^(m_s - M) l_s, as the
+// o_proj input.  One thread per dim.
+template <int WT>
+__global__ void bk_merge(const BArgs a) {
+  const int h = blockIdx.x, n = blockIdx.y, d = threadIdx.x, hd = a.hd;
+  const int T = gp(a.len)[a.seq0 + n] + 1, ns = (T + ATT_P - 1) / ATT_P;
+  const float* p = a.part + ((size_t)n * a.nq + h) * a.nsmax * (hd + 2);
+  float M = -INFINITY;
+  for (int s = 0; s < ns; ++s) M = fmaxf(M, gp(p)[(size_t)s * (hd + 2)]);
+  float Ls = 0.f, O = 0.f;
+  for (int s = 0; s < ns; ++s) {
+    const float* ps = p + (size_t)s * (hd + 2);
+    const float w = __expf(gp(ps)[0] - M);
+    Ls = fmaf(w, gp(ps)[1], Ls);
+    O = fmaf(w, gp(ps)[2 + d], O);
+  }
+  gp(a.act)[(size_t)n * a.astride + act_pos<WT>(h * hd + d)] = (uint16_t)f2bf(O / Ls);
+}
+
+// o_proj rows t*16 .. t*16 + 15 over input chunk kc: partial sums, added to the residual by the next norm.
+template <int WT>
+__global__ void __launch_bounds__(BNT) bk_oproj(const BArgs a, int l) {
+  __shared__ f32x4_t red[BNW * 64];
+  const int t = blockIdx.x, kc = blockIdx.y, lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int QD = a.nq * a.hd, G = QD / 64, gb = part(G, OKC, kc), ge = part(G, OKC, kc + 1);
+  const int n = lane & 15, kg = lane >> 4;
+  auto rowmap = [&](int m) -> long long { return (long long)l * a.H + t * 16 + m; };
+  const uint16_t* col = n < a.B ? a.act + (size_t)n * a.astride : nullptr;
+  f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+  mma_groups<WT>(acc, a.o, QD, rowmap, col, gb + part(ge - gb, BNW, wave), gb + part(ge - gb, BNW, wave + 1));
+  acc = sum_waves(acc, red);
+  if (wave != 0 || n >= a.B) return;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) gp(a.opart)[((size_t)kc * BT + n) * a.H + t * 16 + 4 * kg + r] = acc[r];
+}
+
+// Gate and up rows t*64 .. t*64 + 63 of expert e (dense layers: of the dense MLP) for the sequences that
+// selected it, then SwiGLU into h[sequence][slot * expert_inter + row].  Wave w: 16-row tile w % 4 of
+// the gate (w < 4) or up (w >= 4) matrix over all inputs.
+template <int WT>
+__global__ void __launch_bounds__(BNT) bk_gateup(const BArgs a, int l) {
+  __shared__ float gu[2][64][BT + 1];
+  __shared__ int slot[BT];
+  const int t = blockIdx.x, e = blockIdx.y, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const bool dense = l < a.n_dense;
+  if (tid < BT) {
+    int sl = -1;
+    if (tid < a.B) {
+      if (dense) sl = 0;
+      else
+        for (int k = 0; k < a.K; ++k)
+          if (gp(a.sel)[tid * a.K + k] == e) sl = k;
+    }
+    slot[tid] = sl;
+  }
+  __syncthreads();
+  bool any = false;
+#pragma unroll
+  for (int i = 0; i < BT; ++i) any |= slot[i] >= 0;
+  if (!any) return;  // no sequence picked this expert
+  const int tt = wave & 3, mat = wave >> 2, n = lane & 15, kg = lane >> 4;
+  const Mat& M = dense ? (mat ? a.du : a.dg) : (mat ? a.eu : a.eg);
+  const long long base = dense ? (long long)l * a.DI : ((long long)(l - a.n_dense) * a.E + e) * a.EI;
+  auto rowmap = [&](int m) -> long long { return base + t * 64 + tt * 16 + m; };
+  const uint16_t* col = slot[n] >= 0 ? a.act + (size_t)n * a.astride : nullptr;
+  f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+  mma_groups<WT>(acc, M, a.H, rowmap, col, 0, a.H / 64);
+#pragma unroll
+  for (int r = 0; r < 4; ++r) gu[mat][tt * 16 + 4 * kg + r][n] = acc[r];
+  __syncthreads();
+  const int inner = dense ? a.DI : a.EI;
+  for (int idx = tid; idx < 64 * BT; idx += BNT) {
+    const int q = idx >> 6, rr = idx & 63, sl = slot[q];
+    if (sl < 0) continue;
+    const float g = gu[0][rr][q], u = gu[1][rr][q];
+    const int ei = sl * inner + t * 64 + rr;
+    gp(a.h)[(size_t)q * a.hstride + act_pos<WT>(ei)] = (uint16_t)f2bf(g / (1.0f + __expf(-g)) * u);
+  }
+}
+
+// Down rows t*16 .. t*16 + 15.  MoE: the selected experts of chunk c (of DKC), wave w taking every 8th,
+// each product weighted per sequence by its routing weight; dense: input chunk c.  Partial sums, added to
+// the residual by the next norm (every workgroup writes its chunk, zeros included).
+template <int WT>
+__global__ void __launch_bounds__(BNT) bk_down(const BArgs a, int l) {
+  __shared__ f32x4_t red[BNW * 64];
+  __shared__ int sel_s[BT * MAX_K];
+  __shared__ unsigned long long emask;
+  const int t = blockIdx.x, c = blockIdx.y, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int n = lane & 15, kg = lane >> 4;
+  const bool dense = l < a.n_dense;
+  f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+  if (dense) {
+    const int G = a.DI / 64, gb = part(G, DKC, c), ge = part(G, DKC, c + 1);
+    auto rowmap = [&](int m) -> long long { return (long long)l * a.H + t * 16 + m; };
+    const uint16_t* col = n < a.B ? a.h + (size_t)n * a.hstride : nullptr;
+    mma_groups<WT>(acc, a.dd, a.DI, rowmap, col, gb + part(ge - gb, BNW, wave), gb + part(ge - gb, BNW, wave + 1));
+  } else {
+    const int eb = part(a.E, DKC, c), ee = part(a.E, DKC, c + 1);
+    if (tid == 0) emask = 0ull;
+    for (int i = tid; i < a.B * a.K; i += BNT) sel_s[i] = gp(a.sel)[i];
+    __syncthreads();
+    for (int i = tid; i < a.B * a.K; i += BNT) atomicOr(&emask, 1ull << sel_s[i]);
+    __syncthreads();
+    // the chunk's experts that some sequence picked, in index order; wave w takes every 8th
+    unsigned long long mk = emask & ((ee >= 64 ? ~0ull : (1ull << ee) - 1ull) & ~((1ull << eb) - 1ull));
+    const int lm = l - a.n_dense;
+    for (int i = 0; mk; ++i, mk &= mk - 1) {
+      if (i % BNW != wave) continue;
+      const int e = __builtin_ctzll(mk);
+      int sl = -1;
+      if (n < a.B)
+        for (int k = 0; k < a.K; ++k)
+          if (sel_s[n * a.K + k] == e) sl = k;
+      const float wn = sl >= 0 ? gp(a.wsel)[n * a.K + sl] : 0.f;
+      const uint16_t* col = sl >= 0 ? a.h + (size_t)n * a.hstride + (size_t)sl * a.EI : nullptr;
+      auto rowmap = [&](int m) -> long long { return ((long long)lm * a.E + e) * a.H + t * 16 + m; };
+      f32x4_t d = {0.f, 0.f, 0.f, 0.f};
+      mma_groups<WT>(d, a.ed, a.EI, rowmap, col, 0, a.EI / 64);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) acc[r] = fmaf(wn, d[r], acc[r]);
+    }
+  }
+  acc = sum_waves(acc, red);
+  if (wave != 0 || n >= a.B) return;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) gp(a.dpart)[((size_t)c * BT + n) * a.H + t * 16 + 4 * kg + r] = acc[r];
+}
+
+// lm_head (bf16) rows of this workgroup, 16-row tiles, wave w taking tiles w, w + 8, ...; per sequence the
+// largest logit (lowest id on ties) goes into a packed atomic maximum; the last workgroup publishes.
+__global__ void __launch_bounds__(BNT) bk_head(const BArgs a) {
+  __shared__ float bv_s[BNW][BT];
+  __shared__ int bi_s[BNW][BT];
+  const int W = blockIdx.x, G = gridDim.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int n = lane & 15, kg = lane >> 4, ntl = a.V / 16;
+  const int tb = part(ntl, G, W), te = part(ntl, G, W + 1);
+  const Mat lm{a.lmhead, nullptr};
+  const uint16_t* col = n < a.B ? a.act + (size_t)n * a.astride : nullptr;
+  float bv = -INFINITY;
+  int bi = 0x7FFFFFFF;
+  for (int tl = tb + wave; tl < te; tl += BNW) {
+    auto rowmap = [&](int m) -> long long { return (long long)tl * 16 + m; };
+    f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+    mma_groups<W_BF16>(acc, lm, a.H, rowmap, col, 0, a.H / 64);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int row = tl * 16 + 4 * kg + r;
+      if (a.dbg_logits && n < a.B) gp(a.dbg_logits)[(size_t)(a.seq0 + n) * a.V + row] = acc[r];
+      if (acc[r] > bv || (acc[r] == bv && row < bi)) {
+        bv = acc[r];
+        bi = row;
+      }
+    }
+  }
+  // lanes n, n + 16, n + 32, n + 48 hold the same sequence
+#define FLINT_BEST(MOVV, MOVI)            \
+  {                                       \
+    const float ov = MOVV;                \
+    const int oi = MOVI;                  \
+    if (ov > bv || (ov == bv && oi < bi)) { \
+      bv = ov;                            \
+      bi = oi;                            \
+    }                                     \
+  }
+  FLINT_BEST(swap16(bv), swap16i(bi))
+  FLINT_BEST(swap32(bv), swap32i(bi))
+#undef FLINT_BEST
+  if (lane < BT) {
+    bv_s[wave][lane] = bv;
+    bi_s[wave][lane] = bi;
+  }
+  __syncthreads();
+  if (tid == 0) {
+    for (int q = 0; q < a.B; ++q) {
+      float v = -INFINITY;
+      int id = 0x7FFFFFFF;
+      for (int w = 0; w < BNW; ++w)
+        if (bv_s[w][q] > v || (bv_s[w][q] == v && bi_s[w][q] < id)) {
+          v = bv_s[w][q];
+          id = bi_s[w][q];
+        }
+      if (id == 0x7FFFFFFF) continue;  // no rows in this workgroup
+      const uint32_t u = __float_as_uint(v);
+      const uint32_t ord = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+      const unsigned long long key = ((unsigned long long)ord << 32) | (0xFFFFFFFFu - (uint32_t)id);
+      __hip_atomic_fetch_max(gp(a.amax + q), key, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    const uint32_t prev = __hip_atomic_fetch_add(gp(a.done), 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+    if (prev == (uint32_t)G - 1) {  // last workgroup: publish the ids, advance the lengths, reset
+      for (int q = 0; q < a.B; ++q) {
+        const unsigned long long fin = __hip_atomic_exchange(gp(a.amax + q), 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        gp(a.out_ids)[a.seq0 + q] = (int32_t)(0xFFFFFFFFu - (uint32_t)(fin & 0xFFFFFFFFull));
+        gp(a.len)[a.seq0 + q] += 1;
+      }
+      __hip_atomic_store(gp(a.done), 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+  }
+}
+
+template <int WT> hipError_t run_pass(const BArgs& a, hipStream_t st) {
+  const int QR = (a.nq + 2 * a.nkv) * a.hd;
+  for (int l = 0; l < a.L; ++l) {
+    hipLaunchKernelGGL(bk_norm<WT>, dim3(a.B), dim3(BNT), 0, st, a, l, l == 0 ? (int)NORM_EMBED : (int)NORM_INPUT);
+    hipLaunchKernelGGL(bk_qkv<WT>, dim3(QR / 16), dim3(BNT), 0, st, a, l);
+    hipLaunchKernelGGL(bk_attn, dim3(a.nsmax, a.nkv, a.B), dim3(BNT), 0, st, a, l);
+    hipLaunchKernelGGL(bk_merge<WT>, dim3(a.nq, a.B), dim3(a.hd), 0, st, a);
+    hipLaunchKernelGGL(bk_oproj<WT>, dim3(a.H / 16, OKC), dim3(BNT), 0, st, a, l);
+    hipLaunchKernelGGL(bk_norm<WT>, dim3(a.B), dim3(BNT), 0, st, a, l, (int)NORM_POST);
+    const bool dense = l < a.n_dense;
+    hipLaunchKernelGGL(bk_gateup<WT>, dense ? dim3(a.DI / 64, 1) : dim3(a.EI / 64, a.E), dim3(BNT), 0, st, a, l);
+    hipLaunchKernelGGL(bk_down<WT>, dim3(a.H / 16, DKC), dim3(BNT), 0, st, a, l);
+  }
+  hipLaunchKernelGGL(bk_norm<WT>, dim3(a.B), dim3(BNT), 0, st, a, a.L, (int)NORM_FINAL);
+  hipLaunchKernelGGL(bk_head, dim3(std::min(256, a.V / 16)), dim3(BNT), 0, st, a);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_batch_pass(int wt, const BArgs& a, hipStream_t stream) {
+  return wt == W_I4 ? run_pass<W_I4>(a, stream) : run_pass<W_BF16>(a, stream);
+}
+
+}  // namespace flint

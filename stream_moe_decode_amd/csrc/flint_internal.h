@@ -80,6 +80,60 @@ struct KDyn {
   uint64_t* dbg_ts;
 };
 
+// Batched decode: up to BT sequences per pass go through a sequence of
+// ordinary kernels per layer whose contractions run on MFMA with the
+// sequences as the 16 columns.
+constexpr int BT = 16;                  // sequences per pass (MFMA columns)
+constexpr int ATT_P = 128;              // cached positions per attention split of the batched path
+constexpr int OKC = 2;                  // o_proj input chunks (partial sums added by the next norm)
+constexpr int DKC = 4;                  // MoE down expert chunks / dense down input chunks
+
+struct BArgs {
+  // model
+  int H, nq, nkv, hd, V, L, n_dense, DI, E, K, EI, renorm;
+  float eps;
+  const uint8_t* embed;
+  const uint8_t* lmhead;
+  const float* fnorm;
+  const float* anorm;
+  const float* pnorm;
+  Mat qkv, o, dg, du, dd, router, eg, eu, ed;
+  // this pass: sequences seq0 .. seq0 + B - 1 of a cache of Bc sequences
+  int B, seq0, Bc, cap;
+  uint8_t* kc;           // [L][Bc][nkv][cap][hd] bf16
+  uint8_t* vc;
+  const float2* rope;    // [cap][hd/2] (cos, sin)
+  int32_t* len;          // [Bc]
+  const int32_t* tokens; // [Bc]
+  int32_t* out_ids;      // [Bc]
+  uint32_t* err;         // device error word
+  uint32_t* herr;        // host-mapped error word
+  // scratch of the pass (device, owned by the cache)
+  float* x;              // [BT][H] residual
+  uint16_t* act;         // [BT][astride] bf16 GEMM input (int4 models: 8-element groups permuted)
+  int astride;
+  float* q;              // [BT][nq * hd] queries after RoPE
+  float* part;           // [BT][nq][nsmax][hd + 2] attention partials (m, l, o)
+  int nsmax;
+  float* opart;          // [OKC][BT][H]
+  float* dpart;          // [DKC][BT][H]
+  uint16_t* h;           // [BT][hstride] SwiGLU output (same layout rule as act)
+  int hstride;
+  int32_t* sel;          // [BT][K] selected experts
+  float* wsel;           // [BT][K] their weights
+  unsigned long long* amax;  // [BT] packed argmax keys
+  uint32_t* done;        // workgroups finished with lm_head
+  // debug outputs (indexed by cache sequence), or null
+  float* dbg_logits;
+  int32_t* dbg_routes;
+  float* dbg_rw;
+  float* dbg_resid;
+  int dbg_resid_layer;
+};
+
+// Enqueue one batched decode pass (every layer and the head) on `stream`.
+hipError_t launch_batch_pass(int wt, const BArgs& a, hipStream_t stream);
+
 // True if the compile-time 2048-wide shape (and a 256-workgroup grid) matches.
 bool shape_is_static(const KStatic& k, int grid);
 // Launch the persistent kernel for weight type wt on `stream` (stat: the compile-time shape).

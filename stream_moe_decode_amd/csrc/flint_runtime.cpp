@@ -58,6 +58,7 @@ struct flint_ctx {
   KStatic base;               // weights, dimensions and scratch (host copy)
   KStatic* kdev;              // the same, in device memory, read by the kernel
   bool stat;                  // the compile-time 2048-wide kernel applies
+  bool batch_ok;              // batches of several sequences take the batched MFMA path
   uint32_t* herr_host;        // host-mapped error word
   uint64_t* xbuf;
   size_t xbuf_words;
@@ -73,6 +74,8 @@ struct flint_kv {
   int32_t* len;
   float* rope;
   std::vector<int32_t> hlen;
+  void* bscratch;             // scratch of the batched path (batch > 1), null otherwise
+  BArgs bargs;                // its buffers and the pass-invariant arguments
 };
 
 namespace {
@@ -228,6 +231,86 @@ int launch(flint_ctx* c, flint_kv* kv, const int32_t* tokens, int tok_idx, int s
   return FLINT_OK;
 }
 
+// Scratch of the batched path, one allocation carved into the buffers of BArgs, plus the arguments
+// that stay the same for every pass.
+int batch_scratch(flint_ctx* c, flint_kv* kv) {
+  const flint_config& cfg = c->cfg;
+  const KStatic& k = c->base;
+  BArgs& a = kv->bargs;
+  memset(&a, 0, sizeof a);
+  a.H = cfg.hidden;
+  a.nq = cfg.n_q_heads;
+  a.nkv = cfg.n_kv_heads;
+  a.hd = cfg.head_dim;
+  a.V = cfg.vocab;
+  a.L = cfg.n_layers;
+  a.n_dense = cfg.n_dense_layers;
+  a.DI = cfg.dense_inter;
+  a.E = cfg.n_experts;
+  a.K = cfg.top_k;
+  a.EI = cfg.expert_inter;
+  a.renorm = cfg.router_renorm;
+  a.eps = cfg.rms_eps;
+  a.embed = k.embed;
+  a.lmhead = k.lmhead;
+  a.fnorm = k.fnorm;
+  a.anorm = k.anorm;
+  a.pnorm = k.pnorm;
+  a.qkv = k.qkv;
+  a.o = k.o;
+  a.dg = k.dg;
+  a.du = k.du;
+  a.dd = k.dd;
+  a.router = k.router;
+  a.eg = k.eg;
+  a.eu = k.eu;
+  a.ed = k.ed;
+  a.Bc = kv->batch;
+  a.cap = kv->max_tokens;
+  a.kc = (uint8_t*)kv->k;
+  a.vc = (uint8_t*)kv->v;
+  a.rope = (const float2*)kv->rope;
+  a.len = kv->len;
+  a.err = k.err;
+  a.herr = k.herr;
+  const size_t H = cfg.hidden, QD = (size_t)cfg.n_q_heads * cfg.head_dim;
+  a.astride = (int)std::max(H, QD);
+  a.nsmax = (kv->max_tokens + ATT_P - 1) / ATT_P;
+  const size_t ND = cfg.n_dense_layers, NM = cfg.n_layers - ND;
+  a.hstride = (int)std::max(ND ? (size_t)cfg.dense_inter : 0, NM ? (size_t)cfg.top_k * cfg.expert_inter : 0);
+  // byte sizes, each rounded up to 256
+  auto r256 = [](size_t b) { return (b + 255) & ~(size_t)255; };
+  const size_t sx = r256(BT * H * 4), sact = r256(BT * (size_t)a.astride * 2), sq = r256(BT * QD * 4);
+  const size_t spart = r256((size_t)BT * cfg.n_q_heads * a.nsmax * (cfg.head_dim + 2) * 4);
+  const size_t sop = r256(OKC * BT * H * 4), sdp = r256(DKC * BT * H * 4), sh = r256(BT * (size_t)a.hstride * 2);
+  const size_t ssel = r256(BT * MAX_K * 4), sam = r256(BT * 8 + 64);
+  const size_t total = sx + sact + sq + spart + sop + sdp + sh + 2 * ssel + sam;
+  if (hipMalloc(&kv->bscratch, total) != hipSuccess) {
+    kv->bscratch = nullptr;
+    return fail(FLINT_ENOMEM, "batched-path scratch of %zu bytes", total);
+  }
+  char* p = (char*)kv->bscratch;
+  auto take = [&](size_t b) {
+    char* q = p;
+    p += b;
+    return q;
+  };
+  a.x = (float*)take(sx);
+  a.act = (uint16_t*)take(sact);
+  a.q = (float*)take(sq);
+  a.part = (float*)take(spart);
+  a.opart = (float*)take(sop);
+  a.dpart = (float*)take(sdp);
+  a.h = (uint16_t*)take(sh);
+  a.sel = (int32_t*)take(ssel);
+  a.wsel = (float*)take(ssel);
+  a.amax = (unsigned long long*)take(sam);
+  a.done = (uint32_t*)(a.amax + BT);
+  if (hipMemsetAsync(kv->bscratch, 0, total, c->stream) != hipSuccess || hipStreamSynchronize(c->stream) != hipSuccess)
+    return fail(FLINT_EHIP, "batched-path scratch initialisation failed");
+  return FLINT_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -342,6 +425,11 @@ int flint_decode_init(const flint_config* cfg, const flint_weights* w, void* hip
     return bail(fail(FLINT_EHIP, "hipHostGetDevicePointer failed"));
   a.herr = (uint32_t*)herr_dev;
   c->stat = cfg->weight_type != FLINT_W_F32 && shape_is_static(a, c->grid) && !getenv("FLINT_GENERIC_KERNEL");
+  // the batched path: bf16 activations, 128-dim heads with at most 4 query heads per kv head (attention
+  // scores on MFMA), row counts in whole 16-row tiles and 64-row gate/up blocks
+  c->batch_ok = cfg->weight_type != FLINT_W_F32 && hd == 128 && cfg->n_q_heads / cfg->n_kv_heads <= 4 &&
+                QD % 64 == 0 && (ND == 0 || DI % 64 == 0) && (NM == 0 || EI % 64 == 0) && V % 16 == 0 &&
+                !getenv("FLINT_NO_BATCH_PATH");
   void* kd;
   if ((rc = dalloc(c, &kd, sizeof(KStatic)))) return bail(rc);
   c->kdev = (KStatic*)kd;
@@ -382,11 +470,13 @@ int flint_kv_alloc(flint_ctx* c, int32_t batch, int32_t max_tokens, flint_kv** o
   kv->k = kv->v = nullptr;
   kv->len = nullptr;
   kv->rope = nullptr;
+  kv->bscratch = nullptr;
   auto bail = [&](int code) {
     if (kv->k) (void)hipFree(kv->k);
     if (kv->v) (void)hipFree(kv->v);
     if (kv->len) (void)hipFree(kv->len);
     if (kv->rope) (void)hipFree(kv->rope);
+    if (kv->bscratch) (void)hipFree(kv->bscratch);
     delete kv;
     return code;
   };
@@ -409,6 +499,11 @@ int flint_kv_alloc(flint_ctx* c, int32_t batch, int32_t max_tokens, flint_kv** o
       hipStreamSynchronize(c->stream) != hipSuccess)
     return bail(fail(FLINT_EHIP, "KV cache initialisation failed"));
   kv->hlen.assign(batch, 0);
+  kv->bscratch = nullptr;
+  if (batch > 1 && c->batch_ok) {
+    int rc2 = batch_scratch(c, kv);
+    if (rc2) return bail(rc2);
+  }
   c->live_kv++;
   *out = kv;
   return FLINT_OK;
@@ -417,6 +512,7 @@ int flint_kv_alloc(flint_ctx* c, int32_t batch, int32_t max_tokens, flint_kv** o
 int flint_kv_free(flint_kv* kv) {
   if (!kv) return FLINT_OK;
   (void)hipStreamSynchronize(kv->ctx->stream);
+  if (kv->bscratch) (void)hipFree(kv->bscratch);
   (void)hipFree(kv->k);
   (void)hipFree(kv->v);
   (void)hipFree(kv->len);
@@ -464,6 +560,23 @@ int flint_decode_step_debug(flint_ctx* c, const int32_t* tokens, flint_kv* kv, i
   for (int b = 0; b < kv->batch; ++b)
     if (kv->hlen[b] + 1 > kv->max_tokens)
       return fail(FLINT_ECAPACITY, "sequence %d: length %d + 1 exceeds max_tokens %d", b, kv->hlen[b], kv->max_tokens);
+  if (kv->bscratch) {  // batched path: passes of up to BT sequences
+    BArgs a = kv->bargs;
+    a.tokens = tokens;
+    a.out_ids = out_ids;
+    a.dbg_logits = dbg ? dbg->logits : nullptr;
+    a.dbg_routes = dbg ? dbg->routes : nullptr;
+    a.dbg_rw = dbg ? dbg->route_w : nullptr;
+    a.dbg_resid = dbg ? dbg->resid : nullptr;
+    a.dbg_resid_layer = dbg ? dbg->resid_layer : -1;
+    for (int s0 = 0; s0 < kv->batch; s0 += BT) {
+      a.seq0 = s0;
+      a.B = std::min(BT, kv->batch - s0);
+      HIPCHECK(launch_batch_pass(c->cfg.weight_type, a, c->stream));
+    }
+    for (int b = 0; b < kv->batch; ++b) kv->hlen[b]++;
+    return FLINT_OK;
+  }
   for (int b = 0; b < kv->batch; ++b) {
     rc = launch(c, kv, tokens, b, b, out_ids, b, dbg);
     if (rc) return rc;
