@@ -60,6 +60,140 @@ def step_bytes(cfg, pos: int) -> int:
     return weight_bytes_per_step(cfg) + kv_bytes_per_position(cfg) * (pos + 1)
 
 
+def batch_step_bytes(cfg, lens, routes) -> int:
+    """Algorithmic HBM bytes of one batched step: the weights of every layer once (for each MoE layer the
+    union of the experts any sequence picked, from routes [batch][layers][top_k]), one embedding row and
+    the K/V reads and writes of each sequence at its own length."""
+    import synth
+    H, V = cfg.hidden, cfg.vocab
+
+    def mat(rows, cols):
+        if cfg.weight_type == synth.INT4G64:
+            return rows * cols // 2 + rows * (cols // 64) * 2
+        return rows * cols * (4 if cfg.weight_type == synth.F32 else 2)
+
+    eb = 4 if cfg.weight_type == synth.F32 else 2
+    b = len(lens) * H * eb + V * H * eb + H * 4
+    for l in range(cfg.n_layers):
+        b += 2 * H * 4 + mat(cfg.qkv_rows, H) + mat(H, cfg.q_dim)
+        if l < cfg.n_dense_layers:
+            b += 2 * mat(cfg.dense_inter, H) + mat(H, cfg.dense_inter)
+        else:
+            union = len(set(int(e) for e in routes[:, l, :].ravel()))
+            b += mat(cfg.n_experts, H) + union * (2 * mat(cfg.expert_inter, H) + mat(H, cfg.expert_inter))
+    return b + sum(kv_bytes_per_position(cfg) * (int(p) + 1) for p in lens)
+
+
+def bench_batch(args, cfg):
+    """The batched path on a ragged batch (one JSON line of its own; not the default workload)."""
+    import numpy as np
+    import torch
+    import synth
+    from stream_moe_decode_amd import decode_step, decode_step_debug, kv_set_lengths, lib, sync
+    from stream_moe_decode_amd.loader import DeviceModel, make_debug
+
+    lib()
+    B = cfg.batch
+    lens = [int(x) for x in synth.lengths(cfg)]
+    t_gen = time.perf_counter()
+    cache = {}
+
+    def layer_fn(l):
+        d = synth.layer(cfg, l)
+        if not args.no_cpu_baseline:
+            cache[l] = d
+        return d
+
+    head = synth.head(cfg)
+    model = DeviceModel(cfg, layer_fn, head)
+    cap = max(lens) + args.warmup + args.steps + 8
+    kv = model.kv(B, cap)
+    for b in range(B):
+        for l in range(cfg.n_layers):
+            k, v = synth.resident_kv(cfg, l, b, lens[b])
+            kv.load_resident(l, b, k, v)
+        log(f"resident KV of sequence {b} ({lens[b]} positions) loaded ({time.perf_counter() - t_gen:.0f} s)")
+    dev = model.device
+    first = torch.from_numpy(synth.tokens(cfg, B, stream=11)).to(dev)
+    tok = first.clone()
+
+    def reset():
+        kv.set_lengths(lens)
+        tok.copy_(first)
+        torch.cuda.synchronize()
+
+    reset()
+    for _ in range(args.warmup):
+        decode_step(model.ctx, tok.data_ptr(), kv.handle, tok.data_ptr())
+    sync(model.ctx)
+    reset()
+    K = args.steps
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(K):
+        decode_step(model.ctx, tok.data_ptr(), kv.handle, tok.data_ptr())
+    e1.record()
+    torch.cuda.synchronize()
+    sync(model.ctx)
+    total_ms = e0.elapsed_time(e1)
+    # the same steps again with the routes recorded: the union of picked experts per layer and step
+    reset()
+    dbgs = [make_debug(cfg, B, dev, logits=(i == 0)) for i in range(K)]
+    for i in range(K):
+        decode_step_debug(model.ctx, tok.data_ptr(), kv.handle, tok.data_ptr(), dbgs[i][0])
+    sync(model.ctx)
+    bytes_total = 0
+    unions = []
+    for i in range(K):
+        r = dbgs[i][1]["routes"].cpu().numpy()
+        unions.append(np.mean([len(set(r[:, l, :].ravel())) for l in range(cfg.n_dense_layers, cfg.n_layers)]))
+        bytes_total += batch_step_bytes(cfg, [p + i for p in lens], r)
+    g_logits = dbgs[0][1]["logits"].cpu().numpy()
+    g_routes0 = dbgs[0][1]["routes"].cpu().numpy()
+    model.free()
+    achieved = bytes_total / (total_ms / 1e3) / 1e9
+    log(f"{K} batched steps of {B}: {total_ms:.2f} ms total, {total_ms / K * 1e3:.1f} us/step, "
+        f"experts per MoE layer (union) {np.mean(unions):.2f}, {achieved:.1f} GB/s")
+
+    cpu_baseline = None
+    if not args.no_cpu_baseline:  # the oracle on the shortest sequence's first step, checked against the GPU
+        import oracle
+        b = int(np.argmin(lens))
+        orc = oracle.Oracle(cfg, lambda l: cache[l], head, cap=lens[b] + 4)
+        for l in range(cfg.n_layers):
+            k, v = synth.resident_kv(cfg, l, b, lens[b])
+            orc.set_resident(0, l, k, v)
+        orc.len[0] = lens[b]
+        t0 = time.perf_counter()
+        r = orc.forward(0, first[b:b + 1].cpu().numpy(), ref_routes=g_routes0[b][None])
+        dt = time.perf_counter() - t0
+        err = float(np.max(np.abs(g_logits[b] - r["logits"][0])) / np.max(np.abs(r["logits"][0])))
+        cores = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+        cpu_baseline = {"value": round(1.0 / dt, 4), "unit": "tok/s", "cores": cores, "kind": "oracle",
+                        "sample": f"one decode step of sequence {b} ({lens[b]} resident positions; the oracle "
+                                  f"decodes one sequence at a time), {dt:.1f} s",
+                        "parity_first_step": {"sequence": b, "logits_max_rel_err": err,
+                                              "routes_flagged": int((r["route_flags"] == 2).sum())}}
+        log(f"oracle: {dt:.1f} s for one step of sequence {b}; logits rel err {err:.3g}")
+
+    out = {
+        "metric": "batch-16 ragged decode tok/s (aggregate) + achieved HBM GB/s (% of peak), 49-layer int4",
+        "value": round(B * K / (total_ms / 1e3), 2), "unit": "tok/s", "n_gpus": 1, "steps": K,
+        "warmup": args.warmup, "ms_per_step": round(total_ms / K, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": f"{cfg.name}: {B} sequences, resident lengths uniform in [{cfg.ragged[0]}, "
+                               f"{cfg.ragged[1]}] (mean {np.mean(lens):.0f}), {cfg.n_layers} layers, int4-g64 "
+                               f"weights, {K} greedy steps", "global_batch": B, "seq_len": max(lens) + K,
+                   "parallelism": "none (one GPU)"},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "bytes_per_step": int(bytes_total / K), "experts_per_moe_layer": round(float(np.mean(unions)), 2),
+                     "scope": "whole step (every kernel of the pass)"},
+        "cpu_baseline": cpu_baseline,
+    }
+    print(json.dumps(out), flush=True)
+
+
 def measured_traffic():
     """HBM bytes per launch from the committed counter summary, if it was taken on this kernel source."""
     import hashlib
@@ -104,7 +238,8 @@ def main():
 
     lib()
     cfg = synth.CONFIGS[args.config]
-    assert cfg.batch == 1, "single-stream workloads only"
+    if cfg.batch > 1:
+        return bench_batch(args, cfg)
     cpu = not args.no_cpu_baseline
     t_gen = time.perf_counter()
     cache = {} if cpu else None

@@ -145,7 +145,29 @@ __global__ void __launch_bounds__(BNT) bk_norm(const BArgs a, int l, int mode) {
   __shared__ float z[MAX_E];
   __shared__ float wred[BNW];
   const int n = blockIdx.x, seq = a.seq0 + n, tid = threadIdx.x, H = a.H;
+  const int lane = tid & 63, wave = tid >> 6, E = a.E, lm = l - a.n_dense;
   float* xg = a.x + (size_t)n * H;
+  // router rows of this wave (e = wave + 8 i; lanes over 16-byte chunks), loaded before the norm so that
+  // their latency overlaps it
+  constexpr int CE = WT == W_I4 ? 32 : 8;               // inputs per 16-byte chunk
+  constexpr int RPW = MAX_E / BNW, CPL = (MAX_H / CE + 63) / 64;
+  const int C = H / CE;
+  const bool route = mode == NORM_POST && l >= a.n_dense;
+  uint4 rw[RPW][CPL];
+  float rs[RPW][CPL];
+  if (route) {
+#pragma unroll
+    for (int i = 0; i < RPW; ++i)
+#pragma unroll
+      for (int j = 0; j < CPL; ++j) {
+        const int e = wave + BNW * i, c = lane + 64 * j;
+        rs[i][j] = 1.f;
+        if (e < E && c < C) {
+          rw[i][j] = ld16(a.router.w + ((long long)lm * E + e) * row_bytes<WT>(H) + 16ll * c);
+          if constexpr (WT == W_I4) rs[i][j] = bf2f(gp(a.router.s)[((long long)lm * E + e) * (H / 64) + c / 2]);
+        }
+      }
+  }
   if (mode == NORM_EMBED) {
     int tok = gp(a.tokens)[seq];
     if (tok < 0 || tok >= a.V) {
@@ -188,20 +210,19 @@ __global__ void __launch_bounds__(BNT) bk_norm(const BArgs a, int l, int mode) {
     return;
   }
 
-  // router: wave w computes logits w, w + 8, ...; lanes over 16-byte weight chunks
+  // router logits from the staged rows
   __syncthreads();
-  const int lane = tid & 63, wave = tid >> 6, E = a.E;
-  const int lm = l - a.n_dense;
   const I4K k4 = i4k();
-  constexpr int CE = WT == W_I4 ? 32 : 8;  // inputs per 16-byte chunk
-  const int C = H / CE;
-  for (int e = wave; e < E; e += BNW) {
-    const uint8_t* row = a.router.w + ((long long)lm * E + e) * row_bytes<WT>(H);
+#pragma unroll
+  for (int i = 0; i < RPW; ++i) {
+    const int e = wave + BNW * i;
+    if (e >= E) break;
     float acc = 0.f;
-    for (int c = lane; c < C; c += 64) {
-      const uint4 w = ld16(row + 16ll * c);
+#pragma unroll
+    for (int j = 0; j < CPL; ++j) {
+      const int c = lane + 64 * j;
+      if (c >= C) continue;
       ActC<WT> x;
-      float scale = 1.f;
       if constexpr (WT == W_I4) {
         const uint4* p = reinterpret_cast<const uint4*>(an + 32 * c);
         x.a[0] = p[0];
@@ -209,12 +230,11 @@ __global__ void __launch_bounds__(BNT) bk_norm(const BArgs a, int l, int mode) {
         x.a[2] = p[2];
         x.a[3] = p[3];
         x.s = chunk_sum(x.a[0], x.a[1], x.a[2], x.a[3]);
-        scale = bf2f(gp(a.router.s)[((long long)lm * E + e) * (H / 64) + c / 2]);
       } else {
         x.a[0] = *reinterpret_cast<const uint4*>(an + 8 * c);
         x.s = 0.f;
       }
-      acc += chunk_dot<WT>(w, x, scale, k4);
+      acc += chunk_dot<WT>(rw[i][j], x, rs[i][j], k4);
     }
     acc = wave_sum(acc);
     if (lane == 0) z[e] = acc;
@@ -396,22 +416,45 @@ __global__ void __launch_bounds__(BNT) bk_attn(const BArgs a, int l) {
 }
 
 // Merge the splits of (query head h, sequence n): o = sum_s e^(m_s - M) o_s / sum_s e^(m_s - M) l_s, as the
-// o_proj input.  One thread per dim.
+// o_proj input.  The splits' (m, l) are read once into LDS (one thread each), then every thread (one per
+// dim) sums its dim over the splits with 8 loads in flight.
 template <int WT>
-__global__ void bk_merge(const BArgs a) {
+__global__ void __launch_bounds__(128) bk_merge(const BArgs a) {
+  __shared__ float ws[MAX_SPLITS];
+  __shared__ float wm[2], wl[2];
   const int h = blockIdx.x, n = blockIdx.y, d = threadIdx.x, hd = a.hd;
-  const int T = gp(a.len)[a.seq0 + n] + 1, ns = (T + ATT_P - 1) / ATT_P;
+  const int T = gp(a.len)[a.seq0 + n] + 1, ns = min((T + ATT_P - 1) / ATT_P, MAX_SPLITS);
   const float* p = a.part + ((size_t)n * a.nq + h) * a.nsmax * (hd + 2);
-  float M = -INFINITY;
-  for (int s = 0; s < ns; ++s) M = fmaxf(M, gp(p)[(size_t)s * (hd + 2)]);
-  float Ls = 0.f, O = 0.f;
-  for (int s = 0; s < ns; ++s) {
-    const float* ps = p + (size_t)s * (hd + 2);
-    const float w = __expf(gp(ps)[0] - M);
-    Ls = fmaf(w, gp(ps)[1], Ls);
-    O = fmaf(w, gp(ps)[2 + d], O);
+  float mloc = -INFINITY;
+  for (int s = d; s < ns; s += 128) {
+    ws[s] = gp(p)[(size_t)s * (hd + 2)];
+    mloc = fmaxf(mloc, ws[s]);
   }
-  gp(a.act)[(size_t)n * a.astride + act_pos<WT>(h * hd + d)] = (uint16_t)f2bf(O / Ls);
+  mloc = wave_max(mloc);
+  if ((d & 63) == 0) wm[d >> 6] = mloc;
+  __syncthreads();
+  const float M = fmaxf(wm[0], wm[1]);
+  float lp = 0.f;
+  for (int s = d; s < ns; s += 128) {
+    const float w = __expf(ws[s] - M);
+    ws[s] = w;
+    lp = fmaf(w, gp(p)[(size_t)s * (hd + 2) + 1], lp);
+  }
+  lp = wave_sum(lp);
+  if ((d & 63) == 0) wl[d >> 6] = lp;
+  __syncthreads();
+  const float lsum = wl[0] + wl[1];
+  float O = 0.f;
+  int s = 0;
+  for (; s + 8 <= ns; s += 8) {
+    float v[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) v[k] = gp(p)[(size_t)(s + k) * (hd + 2) + 2 + d];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) O = fmaf(ws[s + k], v[k], O);
+  }
+  for (; s < ns; ++s) O = fmaf(ws[s], gp(p)[(size_t)s * (hd + 2) + 2 + d], O);
+  gp(a.act)[(size_t)n * a.astride + act_pos<WT>(h * hd + d)] = (uint16_t)f2bf(O / lsum);
 }
 
 // o_proj rows t*16 .. t*16 + 15 over input chunk kc: partial sums, added to the residual by the next norm.

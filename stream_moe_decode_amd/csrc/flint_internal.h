@@ -85,6 +85,7 @@ struct KDyn {
 // sequences as the 16 columns.
 constexpr int BT = 16;                  // sequences per pass (MFMA columns)
 constexpr int ATT_P = 128;              // cached positions per attention split of the batched path
+constexpr int MAX_SPLITS = 1024;        // attention splits per sequence (max_tokens <= ATT_P * MAX_SPLITS)
 constexpr int OKC = 2;                  // o_proj input chunks (partial sums added by the next norm)
 constexpr int DKC = 4;                  // MoE down expert chunks / dense down input chunks
 

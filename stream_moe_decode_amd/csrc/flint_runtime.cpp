@@ -500,7 +500,7 @@ int flint_kv_alloc(flint_ctx* c, int32_t batch, int32_t max_tokens, flint_kv** o
     return bail(fail(FLINT_EHIP, "KV cache initialisation failed"));
   kv->hlen.assign(batch, 0);
   kv->bscratch = nullptr;
-  if (batch > 1 && c->batch_ok) {
+  if (batch > 1 && c->batch_ok && max_tokens <= ATT_P * MAX_SPLITS) {
     int rc2 = batch_scratch(c, kv);
     if (rc2) return bail(rc2);
   }
