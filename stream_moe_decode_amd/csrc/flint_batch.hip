@@ -47,41 +47,44 @@ __device__ __forceinline__ void latch(const BArgs& a, uint32_t bits) {
   __hip_atomic_store(gp(a.herr), bits, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
 }
 
-// acc += W[the tile's 16 rows] . x over the 64-input groups [g0, g1), for 16 sequence columns.
-// Lane L supplies row L % 16 of the tile (matrix row rowmap(L % 16)) and column L % 16 (`col`: that
-// sequence's input row, null for a zero column), inputs (L / 16) * 16 + [0, 16) of each group; it
-// accumulates rows (L / 16) * 4 + r of column L % 16.  int4: codes enter as 128 + u, and two MFMAs
-// with the constant -136 as the weight operand remove the offset before the group's scale applies.
-template <int WT, class RowMap>
-__device__ __forceinline__ void mma_groups(f32x4_t& acc, const Mat& m, int in, RowMap rowmap, const uint16_t* col,
-                                           int g0, int g1) {
-  const int lane = threadIdx.x & 63, mr = lane & 15, kg = lane >> 4;
-  const uint8_t* wr = m.w + rowmap(mr) * row_bytes<WT>(in);
-  const uint16_t* sp[4];
-  if constexpr (WT == W_I4) {
+// acc[t] += W[tile t's 16 rows] . x over the 64-input groups [g0, g1) for 16 sequence columns, the input
+// operand of a group loaded once for all NT tiles.  Lane L supplies row L % 16 of each tile (matrix row
+// rowmap(t, L % 16)) and column L % 16 (`col`: that sequence's input row, null for a zero column), inputs
+// (L / 16) * 16 + [0, 16) of each group, and accumulates rows (L / 16) * 4 + r of column L % 16; rows
+// rowmap(t, 4 k) .. + 3 are consecutive from a multiple of 4.  int4: codes enter as 128 + u, two MFMAs
+// with the constant -136 as the weight operand remove the offset, then the group's scale of each row
+// (four rows in one 8-byte load of the regrouped scales) multiplies the group's fp32 result.  Every load
+// of U groups is issued before their products.
+template <int WT, int NT, class RowMap>
+__device__ __forceinline__ void mma_tiles(f32x4_t (&acc)[NT], const Mat& m, int in, RowMap rowmap,
+                                          const uint16_t* col, int g0, int g1) {
+  const int lane = threadIdx.x & 63, mr = lane & 15, kg = lane >> 4, G = in / 64;
+  const uint8_t* wr[NT];
+  const uint16_t* s4[NT];
 #pragma unroll
-    for (int r = 0; r < 4; ++r) sp[r] = m.s + rowmap(4 * kg + r) * (in / 64);
+  for (int t = 0; t < NT; ++t) {
+    wr[t] = m.w + rowmap(t, mr) * row_bytes<WT>(in);
+    if constexpr (WT == W_I4) s4[t] = m.s4 + (size_t)(rowmap(t, 4 * kg) >> 2) * G * 4;
   }
   const I4K k4 = i4k();
   const bf16x8_t bias = as_bf16x8(make_uint4(0xC308C308u, 0xC308C308u, 0xC308C308u, 0xC308C308u));  // bf16 -136
-  constexpr int U = 4;
+  constexpr int U = NT >= 4 ? 2 : 4;
   for (int g = g0; g < g1; g += U) {
-    uint32_t wq[U][2];
-    uint4 wb[U][2], b0[U], b1[U];
-    float sc[U][4];
+    u32x2_t wq[U][NT], sq[U][NT];
+    uint4 wb[U][NT][2], b0[U], b1[U];
 #pragma unroll
-    for (int u = 0; u < U; ++u) {  // every load of U groups first
-      const int gg = min(g + u, g1 - 1);
+    for (int u = 0; u < U; ++u) {
+      const int gg = min(g + u, g1 - 1);  // past the end: the last group again, not used
       const int e0 = gg * 64 + kg * 16;
-      if constexpr (WT == W_I4) {
-        const u32x2_t w2 = *(GLOBAL const u32x2_t*)(wr + e0 / 2);
-        wq[u][0] = w2.x;
-        wq[u][1] = w2.y;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) sc[u][r] = bf2f(gp(sp[r])[gg]);
-      } else {
-        wb[u][0] = ld16(wr + 2 * e0);
-        wb[u][1] = ld16(wr + 2 * e0 + 16);
+      for (int t = 0; t < NT; ++t) {
+        if constexpr (WT == W_I4) {
+          wq[u][t] = *(GLOBAL const u32x2_t*)(wr[t] + e0 / 2);
+          sq[u][t] = *(GLOBAL const u32x2_t*)(s4[t] + (size_t)gg * 4);
+        } else {
+          wb[u][t][0] = ld16(wr[t] + 2 * e0);
+          wb[u][t][1] = ld16(wr[t] + 2 * e0 + 16);
+        }
       }
       if (col) {
         b0[u] = ld16(col + e0);
@@ -92,18 +95,22 @@ __device__ __forceinline__ void mma_groups(f32x4_t& acc, const Mat& m, int in, R
     }
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      if (g + u < g1) {
+      if (g + u >= g1) break;
+#pragma unroll
+      for (int t = 0; t < NT; ++t) {
         if constexpr (WT == W_I4) {
           f32x4_t d = {0.f, 0.f, 0.f, 0.f};
-          d = mfma(unpack8(wq[u][0], k4), as_bf16x8(b0[u]), d);
-          d = mfma(unpack8(wq[u][1], k4), as_bf16x8(b1[u]), d);
+          d = mfma(unpack8(wq[u][t].x, k4), as_bf16x8(b0[u]), d);
+          d = mfma(unpack8(wq[u][t].y, k4), as_bf16x8(b1[u]), d);
           d = mfma(bias, as_bf16x8(b0[u]), d);
           d = mfma(bias, as_bf16x8(b1[u]), d);
-#pragma unroll
-          for (int r = 0; r < 4; ++r) acc[r] = fmaf(sc[u][r], d[r], acc[r]);
+          acc[t][0] = fmaf(bf2f(sq[u][t].x & 0xFFFFu), d[0], acc[t][0]);
+          acc[t][1] = fmaf(bf2f(sq[u][t].x >> 16), d[1], acc[t][1]);
+          acc[t][2] = fmaf(bf2f(sq[u][t].y & 0xFFFFu), d[2], acc[t][2]);
+          acc[t][3] = fmaf(bf2f(sq[u][t].y >> 16), d[3], acc[t][3]);
         } else {
-          acc = mfma(as_bf16x8(wb[u][0]), as_bf16x8(b0[u]), acc);
-          acc = mfma(as_bf16x8(wb[u][1]), as_bf16x8(b1[u]), acc);
+          acc[t] = mfma(as_bf16x8(wb[u][t][0]), as_bf16x8(b0[u]), acc[t]);
+          acc[t] = mfma(as_bf16x8(wb[u][t][1]), as_bf16x8(b1[u]), acc[t]);
         }
       }
     }
@@ -134,6 +141,21 @@ __device__ __forceinline__ float bsum(float v, float* wred) {
 }
 
 enum { NORM_EMBED = 0, NORM_INPUT = 1, NORM_POST = 2, NORM_FINAL = 3 };
+
+// xs[e] = x[e] + sum of the NP partial rows of sequence n (every load of a thread issued before the sums).
+template <int NP>
+__device__ __forceinline__ void add_parts(float* xs, const float* xg, const float* parts, int n, int H) {
+  for (int e = threadIdx.x; e < H; e += BNT) {
+    float v[NP + 1];
+    v[0] = gp(xg)[e];
+#pragma unroll
+    for (int p = 0; p < NP; ++p) v[p + 1] = gp(parts)[((size_t)p * BT + n) * H + e];
+    float t = v[0];
+#pragma unroll
+    for (int p = 0; p < NP; ++p) t += v[p + 1];
+    xs[e] = t;
+  }
+}
 
 // RMSNorm of one sequence's residual (grid: one workgroup per sequence).  The residual first takes the
 // pending partial sums (down of the previous layer, or o_proj); the normalised row becomes the next
@@ -176,14 +198,10 @@ __global__ void __launch_bounds__(BNT) bk_norm(const BArgs a, int l, int mode) {
     }
     const uint16_t* er = reinterpret_cast<const uint16_t*>(a.embed) + (size_t)tok * H;
     for (int e = tid; e < H; e += BNT) xs[e] = bf2f(gp(er)[e]);
+  } else if (mode == NORM_POST) {
+    add_parts<OKC>(xs, xg, a.opart, n, H);
   } else {
-    const float* pp = mode == NORM_POST ? a.opart : a.dpart;
-    const int np = mode == NORM_POST ? OKC : DKC;
-    for (int e = tid; e < H; e += BNT) {
-      float v = gp(xg)[e];
-      for (int p = 0; p < np; ++p) v += gp(pp)[((size_t)p * BT + n) * H + e];
-      xs[e] = v;
-    }
+    add_parts<DKC>(xs, xg, a.dpart, n, H);
   }
   for (int e = tid; e < H; e += BNT) gp(xg)[e] = xs[e];
   // the residual after layer dbg_resid_layer is complete when the next layer's input norm (or the final norm) adds it up
@@ -271,14 +289,14 @@ __global__ void __launch_bounds__(BNT) bk_qkv(const BArgs a, int l) {
   const int hd = a.hd, half = hd / 2, tph = hd / 16;
   const int hh = t / tph, i0 = (t % tph) * 8;
   const int QR = (a.nq + 2 * a.nkv) * hd;
-  auto rowmap = [&](int m) -> long long { return (long long)l * QR + hh * hd + (m < 8 ? i0 + m : half + i0 + m - 8); };
+  auto rowmap = [&](int, int m) -> long long { return (long long)l * QR + hh * hd + (m < 8 ? i0 + m : half + i0 + m - 8); };
   const int G = a.H / 64, n = lane & 15, kg = lane >> 4;
   const uint16_t* col = n < a.B ? a.act + (size_t)n * a.astride : nullptr;
-  f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-  mma_groups<WT>(acc, a.qkv, a.H, rowmap, col, part(G, BNW, wave), part(G, BNW, wave + 1));
-  acc = sum_waves(acc, red);
+  f32x4_t acc[1] = {{0.f, 0.f, 0.f, 0.f}};
+  mma_tiles<WT, 1>(acc, a.qkv, a.H, rowmap, col, part(G, BNW, wave), part(G, BNW, wave + 1));
+  const f32x4_t sum = sum_waves(acc[0], red);
   if (wave != 0) return;
-  float y[4] = {acc[0], acc[1], acc[2], acc[3]};
+  float y[4] = {sum[0], sum[1], sum[2], sum[3]};
   const int pos = n < a.B ? gp(a.len)[a.seq0 + n] : 0;
   if (hh < a.nq + a.nkv) {  // RoPE on q and k heads: (y_i, y_{i + hd/2}) rotated by the angle of pair i
     float p[4];
@@ -464,22 +482,22 @@ __global__ void __launch_bounds__(BNT) bk_oproj(const BArgs a, int l) {
   const int t = blockIdx.x, kc = blockIdx.y, lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int QD = a.nq * a.hd, G = QD / 64, gb = part(G, OKC, kc), ge = part(G, OKC, kc + 1);
   const int n = lane & 15, kg = lane >> 4;
-  auto rowmap = [&](int m) -> long long { return (long long)l * a.H + t * 16 + m; };
+  auto rowmap = [&](int, int m) -> long long { return (long long)l * a.H + t * 16 + m; };
   const uint16_t* col = n < a.B ? a.act + (size_t)n * a.astride : nullptr;
-  f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-  mma_groups<WT>(acc, a.o, QD, rowmap, col, gb + part(ge - gb, BNW, wave), gb + part(ge - gb, BNW, wave + 1));
-  acc = sum_waves(acc, red);
+  f32x4_t acc[1] = {{0.f, 0.f, 0.f, 0.f}};
+  mma_tiles<WT, 1>(acc, a.o, QD, rowmap, col, gb + part(ge - gb, BNW, wave), gb + part(ge - gb, BNW, wave + 1));
+  const f32x4_t sum = sum_waves(acc[0], red);
   if (wave != 0 || n >= a.B) return;
 #pragma unroll
-  for (int r = 0; r < 4; ++r) gp(a.opart)[((size_t)kc * BT + n) * a.H + t * 16 + 4 * kg + r] = acc[r];
+  for (int r = 0; r < 4; ++r) gp(a.opart)[((size_t)kc * BT + n) * a.H + t * 16 + 4 * kg + r] = sum[r];
 }
 
 // Gate and up rows t*64 .. t*64 + 63 of expert e (dense layers: of the dense MLP) for the sequences that
-// selected it, then SwiGLU into h[sequence][slot * expert_inter + row].  Wave w: 16-row tile w % 4 of
-// the gate (w < 4) or up (w >= 4) matrix over all inputs.
+// selected it, then SwiGLU into h[sequence][slot * expert_inter + row].  Every wave computes all eight
+// 16-row tiles (gate 0-3, up 4-7) over its eighth of the inputs; the partial tiles meet in LDS.
 template <int WT>
 __global__ void __launch_bounds__(BNT) bk_gateup(const BArgs a, int l) {
-  __shared__ float gu[2][64][BT + 1];
+  __shared__ f32x4_t red[BNW][8][64];
   __shared__ int slot[BT];
   const int t = blockIdx.x, e = blockIdx.y, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const bool dense = l < a.n_dense;
@@ -498,43 +516,61 @@ __global__ void __launch_bounds__(BNT) bk_gateup(const BArgs a, int l) {
 #pragma unroll
   for (int i = 0; i < BT; ++i) any |= slot[i] >= 0;
   if (!any) return;  // no sequence picked this expert
-  const int tt = wave & 3, mat = wave >> 2, n = lane & 15, kg = lane >> 4;
-  const Mat& M = dense ? (mat ? a.du : a.dg) : (mat ? a.eu : a.eg);
+  const int n = lane & 15;
+  const Mat& Mg = dense ? a.dg : a.eg;
+  const Mat& Mu = dense ? a.du : a.eu;
   const long long base = dense ? (long long)l * a.DI : ((long long)(l - a.n_dense) * a.E + e) * a.EI;
-  auto rowmap = [&](int m) -> long long { return base + t * 64 + tt * 16 + m; };
   const uint16_t* col = slot[n] >= 0 ? a.act + (size_t)n * a.astride : nullptr;
-  f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-  mma_groups<WT>(acc, M, a.H, rowmap, col, 0, a.H / 64);
+  const int G = a.H / 64, g0 = part(G, BNW, wave), g1 = part(G, BNW, wave + 1);
+  f32x4_t acc[4];
+  // gate tiles, then up tiles (same rows; the two matrices share the layout and the scales' regrouping)
 #pragma unroll
-  for (int r = 0; r < 4; ++r) gu[mat][tt * 16 + 4 * kg + r][n] = acc[r];
+  for (int mat = 0; mat < 2; ++mat) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) acc[q] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    auto rowmap = [&](int q, int m) -> long long { return base + t * 64 + q * 16 + m; };
+    mma_tiles<WT, 4>(acc, mat ? Mu : Mg, a.H, rowmap, col, g0, g1);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) red[wave][mat * 4 + q][lane] = acc[q];
+  }
   __syncthreads();
   const int inner = dense ? a.DI : a.EI;
   for (int idx = tid; idx < 64 * BT; idx += BNT) {
     const int q = idx >> 6, rr = idx & 63, sl = slot[q];
     if (sl < 0) continue;
-    const float g = gu[0][rr][q], u = gu[1][rr][q];
+    const int tile = rr >> 4, m = rr & 15, ln = (m >> 2) * 16 + q, r = m & 3;
+    float g = 0.f, u = 0.f;
+#pragma unroll
+    for (int w = 0; w < BNW; ++w) {
+      g += red[w][tile][ln][r];
+      u += red[w][4 + tile][ln][r];
+    }
     const int ei = sl * inner + t * 64 + rr;
     gp(a.h)[(size_t)q * a.hstride + act_pos<WT>(ei)] = (uint16_t)f2bf(g / (1.0f + __expf(-g)) * u);
   }
 }
 
-// Down rows t*16 .. t*16 + 15.  MoE: the selected experts of chunk c (of DKC), wave w taking every 8th,
-// each product weighted per sequence by its routing weight; dense: input chunk c.  Partial sums, added to
-// the residual by the next norm (every workgroup writes its chunk, zeros included).
+// Down rows t*64 .. t*64 + 63 (four 16-row tiles) for chunk c.  MoE: the experts of chunk c (of DKC) that
+// some sequence picked; the work items are (expert, pair of 64-input groups), wave w taking every 8th, each
+// product weighted per sequence by its routing weight (zero for sequences that did not pick the expert).
+// Dense: the pairs of 64-input groups of input chunk c.  Partial sums, added to the residual by the next norm (every
+// workgroup writes its chunk, zeros included).
 template <int WT>
 __global__ void __launch_bounds__(BNT) bk_down(const BArgs a, int l) {
-  __shared__ f32x4_t red[BNW * 64];
+  __shared__ f32x4_t red[BNW][4][64];
   __shared__ int sel_s[BT * MAX_K];
   __shared__ unsigned long long emask;
   const int t = blockIdx.x, c = blockIdx.y, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int n = lane & 15, kg = lane >> 4;
   const bool dense = l < a.n_dense;
-  f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+  f32x4_t acc[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) acc[q] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   if (dense) {
     const int G = a.DI / 64, gb = part(G, DKC, c), ge = part(G, DKC, c + 1);
-    auto rowmap = [&](int m) -> long long { return (long long)l * a.H + t * 16 + m; };
+    auto rowmap = [&](int q, int m) -> long long { return (long long)l * a.H + t * 64 + q * 16 + m; };
     const uint16_t* col = n < a.B ? a.h + (size_t)n * a.hstride : nullptr;
-    mma_groups<WT>(acc, a.dd, a.DI, rowmap, col, gb + part(ge - gb, BNW, wave), gb + part(ge - gb, BNW, wave + 1));
+    for (int g = gb + 2 * wave; g < ge; g += 2 * BNW) mma_tiles<WT, 4>(acc, a.dd, a.DI, rowmap, col, g, min(g + 2, ge));
   } else {
     const int eb = part(a.E, DKC, c), ee = part(a.E, DKC, c + 1);
     if (tid == 0) emask = 0ull;
@@ -542,80 +578,119 @@ __global__ void __launch_bounds__(BNT) bk_down(const BArgs a, int l) {
     __syncthreads();
     for (int i = tid; i < a.B * a.K; i += BNT) atomicOr(&emask, 1ull << sel_s[i]);
     __syncthreads();
-    // the chunk's experts that some sequence picked, in index order; wave w takes every 8th
-    unsigned long long mk = emask & ((ee >= 64 ? ~0ull : (1ull << ee) - 1ull) & ~((1ull << eb) - 1ull));
-    const int lm = l - a.n_dense;
-    for (int i = 0; mk; ++i, mk &= mk - 1) {
-      if (i % BNW != wave) continue;
-      const int e = __builtin_ctzll(mk);
-      int sl = -1;
-      if (n < a.B)
-        for (int k = 0; k < a.K; ++k)
-          if (sel_s[n * a.K + k] == e) sl = k;
-      const float wn = sl >= 0 ? gp(a.wsel)[n * a.K + sl] : 0.f;
+    // the chunk's experts that some sequence picked, in index order
+    const unsigned long long mk = emask & ((ee >= 64 ? ~0ull : (1ull << ee) - 1ull) & ~((1ull << eb) - 1ull));
+    const int ne = __builtin_popcountll(mk), G = a.EI / 64, G2 = (G + 1) / 2, lm = l - a.n_dense;
+    int e = -1, ei = -1, sl = -1;
+    float wn = 0.f;
+    for (int it = wave; it < ne * G2; it += BNW) {
+      const int want = it / G2, g = 2 * (it - want * G2);
+      if (want != ei) {  // next expert of this wave: its index, this lane's sequence slot and weight
+        unsigned long long mm = mk;
+        for (int k = 0; k < want; ++k) mm &= mm - 1;
+        e = __builtin_ctzll(mm);
+        ei = want;
+        sl = -1;
+        if (n < a.B)
+          for (int k = 0; k < a.K; ++k)
+            if (sel_s[n * a.K + k] == e) sl = k;
+        wn = sl >= 0 ? gp(a.wsel)[n * a.K + sl] : 0.f;
+      }
       const uint16_t* col = sl >= 0 ? a.h + (size_t)n * a.hstride + (size_t)sl * a.EI : nullptr;
-      auto rowmap = [&](int m) -> long long { return ((long long)lm * a.E + e) * a.H + t * 16 + m; };
-      f32x4_t d = {0.f, 0.f, 0.f, 0.f};
-      mma_groups<WT>(d, a.ed, a.EI, rowmap, col, 0, a.EI / 64);
+      auto rowmap = [&](int q, int m) -> long long { return ((long long)lm * a.E + e) * a.H + t * 64 + q * 16 + m; };
+      f32x4_t d[4];
 #pragma unroll
-      for (int r = 0; r < 4; ++r) acc[r] = fmaf(wn, d[r], acc[r]);
+      for (int q = 0; q < 4; ++q) d[q] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      mma_tiles<WT, 4>(d, a.ed, a.EI, rowmap, col, g, min(g + 2, G));
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) acc[q][r] = fmaf(wn, d[q][r], acc[q][r]);
     }
   }
-  acc = sum_waves(acc, red);
-  if (wave != 0 || n >= a.B) return;
 #pragma unroll
-  for (int r = 0; r < 4; ++r) gp(a.dpart)[((size_t)c * BT + n) * a.H + t * 16 + 4 * kg + r] = acc[r];
+  for (int q = 0; q < 4; ++q) red[wave][q][lane] = acc[q];
+  __syncthreads();
+  // 64 rows x 16 sequences: thread -> (row, sequence)
+  for (int idx = tid; idx < 64 * BT; idx += BNT) {
+    const int q = idx >> 6, rr = idx & 63;
+    if (q >= a.B) continue;
+    const int tile = rr >> 4, m = rr & 15, ln = (m >> 2) * 16 + q, r = m & 3;
+    float v = 0.f;
+#pragma unroll
+    for (int w = 0; w < BNW; ++w) v += red[w][tile][ln][r];
+    gp(a.dpart)[((size_t)c * BT + q) * a.H + t * 64 + rr] = v;
+  }
 }
 
-// lm_head (bf16) rows of this workgroup, 16-row tiles, wave w taking tiles w, w + 8, ...; per sequence the
-// largest logit (lowest id on ties) goes into a packed atomic maximum; the last workgroup publishes.
+// lm_head (bf16) rows of this workgroup in 16-row tiles; wave w computes four tiles over half of the
+// inputs (waves w and w + 4 share tiles), the halves meet in LDS.  Per sequence the largest logit (lowest
+// id on ties) goes into a packed atomic maximum; the last workgroup publishes the ids.
 __global__ void __launch_bounds__(BNT) bk_head(const BArgs a) {
-  __shared__ float bv_s[BNW][BT];
-  __shared__ int bi_s[BNW][BT];
+  __shared__ f32x4_t red[BNW][4][64];
+  __shared__ float bv_s[4][BT];
+  __shared__ int bi_s[4][BT];
   const int W = blockIdx.x, G = gridDim.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int n = lane & 15, kg = lane >> 4, ntl = a.V / 16;
   const int tb = part(ntl, G, W), te = part(ntl, G, W + 1);
-  const Mat lm{a.lmhead, nullptr};
+  const Mat lm{a.lmhead, nullptr, nullptr};
   const uint16_t* col = n < a.B ? a.act + (size_t)n * a.astride : nullptr;
+  const int half = wave >> 2, grp = wave & 3, NG = a.H / 64;
   float bv = -INFINITY;
   int bi = 0x7FFFFFFF;
-  for (int tl = tb + wave; tl < te; tl += BNW) {
-    auto rowmap = [&](int m) -> long long { return (long long)tl * 16 + m; };
-    f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-    mma_groups<W_BF16>(acc, lm, a.H, rowmap, col, 0, a.H / 64);
+  for (int t0 = tb; t0 < te; t0 += 16) {  // 16 tiles per round: wave group grp takes tiles t0 + 4 grp .. + 3
+    f32x4_t acc[4];
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int row = tl * 16 + 4 * kg + r;
-      if (a.dbg_logits && n < a.B) gp(a.dbg_logits)[(size_t)(a.seq0 + n) * a.V + row] = acc[r];
-      if (acc[r] > bv || (acc[r] == bv && row < bi)) {
-        bv = acc[r];
-        bi = row;
+    for (int q = 0; q < 4; ++q) acc[q] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    auto rowmap = [&](int q, int m) -> long long { return (long long)min(t0 + 4 * grp + q, te - 1) * 16 + m; };
+    mma_tiles<W_BF16, 4>(acc, lm, a.H, rowmap, col, half ? NG / 2 : 0, half ? NG : NG / 2);
+    __syncthreads();  // the previous round's reads of red are done
+#pragma unroll
+    for (int q = 0; q < 4; ++q) red[wave][q][lane] = acc[q];
+    __syncthreads();
+    if (half == 0) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int tl = t0 + 4 * grp + q;
+        if (tl >= te) break;
+        const f32x4_t v = acc[q] + red[wave + 4][q][lane];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int row = tl * 16 + 4 * kg + r;
+          if (a.dbg_logits && n < a.B) gp(a.dbg_logits)[(size_t)(a.seq0 + n) * a.V + row] = v[r];
+          if (v[r] > bv || (v[r] == bv && row < bi)) {
+            bv = v[r];
+            bi = row;
+          }
+        }
       }
     }
   }
-  // lanes n, n + 16, n + 32, n + 48 hold the same sequence
-#define FLINT_BEST(MOVV, MOVI)            \
-  {                                       \
-    const float ov = MOVV;                \
-    const int oi = MOVI;                  \
+  if (half == 0) {
+    // lanes n, n + 16, n + 32, n + 48 hold the same sequence
+#define FLINT_BEST(MOVV, MOVI)              \
+  {                                         \
+    const float ov = MOVV;                  \
+    const int oi = MOVI;                    \
     if (ov > bv || (ov == bv && oi < bi)) { \
-      bv = ov;                            \
-      bi = oi;                            \
-    }                                     \
+      bv = ov;                              \
+      bi = oi;                              \
+    }                                       \
   }
-  FLINT_BEST(swap16(bv), swap16i(bi))
-  FLINT_BEST(swap32(bv), swap32i(bi))
+    FLINT_BEST(swap16(bv), swap16i(bi))
+    FLINT_BEST(swap32(bv), swap32i(bi))
 #undef FLINT_BEST
-  if (lane < BT) {
-    bv_s[wave][lane] = bv;
-    bi_s[wave][lane] = bi;
+    if (lane < BT) {
+      bv_s[grp][lane] = bv;
+      bi_s[grp][lane] = bi;
+    }
   }
   __syncthreads();
   if (tid == 0) {
     for (int q = 0; q < a.B; ++q) {
       float v = -INFINITY;
       int id = 0x7FFFFFFF;
-      for (int w = 0; w < BNW; ++w)
+      for (int w = 0; w < 4; ++w)
         if (bv_s[w][q] > v || (bv_s[w][q] == v && bi_s[w][q] < id)) {
           v = bv_s[w][q];
           id = bi_s[w][q];
@@ -638,6 +713,15 @@ __global__ void __launch_bounds__(BNT) bk_head(const BArgs a) {
   }
 }
 
+// Scales regrouped by four rows for the batched contractions.
+__global__ void regroup_scales_kernel(const uint16_t* s, uint16_t* s4, size_t rows, int G) {
+  const size_t total = rows * (size_t)G;
+  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < total; i += (size_t)gridDim.x * blockDim.x) {
+    const size_t r = i / G, g = i - r * G;
+    s4[((r >> 2) * G + g) * 4 + (r & 3)] = s[i];
+  }
+}
+
 template <int WT> hipError_t run_pass(const BArgs& a, hipStream_t st) {
   const int QR = (a.nq + 2 * a.nkv) * a.hd;
   for (int l = 0; l < a.L; ++l) {
@@ -649,7 +733,7 @@ template <int WT> hipError_t run_pass(const BArgs& a, hipStream_t st) {
     hipLaunchKernelGGL(bk_norm<WT>, dim3(a.B), dim3(BNT), 0, st, a, l, (int)NORM_POST);
     const bool dense = l < a.n_dense;
     hipLaunchKernelGGL(bk_gateup<WT>, dense ? dim3(a.DI / 64, 1) : dim3(a.EI / 64, a.E), dim3(BNT), 0, st, a, l);
-    hipLaunchKernelGGL(bk_down<WT>, dim3(a.H / 16, DKC), dim3(BNT), 0, st, a, l);
+    hipLaunchKernelGGL(bk_down<WT>, dim3(a.H / 64, DKC), dim3(BNT), 0, st, a, l);
   }
   hipLaunchKernelGGL(bk_norm<WT>, dim3(a.B), dim3(BNT), 0, st, a, a.L, (int)NORM_FINAL);
   hipLaunchKernelGGL(bk_head, dim3(std::min(256, a.V / 16)), dim3(BNT), 0, st, a);
@@ -660,6 +744,13 @@ template <int WT> hipError_t run_pass(const BArgs& a, hipStream_t st) {
 
 hipError_t launch_batch_pass(int wt, const BArgs& a, hipStream_t stream) {
   return wt == W_I4 ? run_pass<W_I4>(a, stream) : run_pass<W_BF16>(a, stream);
+}
+
+hipError_t launch_regroup_scales(const uint16_t* s, uint16_t* s4, size_t rows, int G, hipStream_t stream) {
+  const size_t total = rows * (size_t)G;
+  const int blocks = (int)std::min<size_t>((total + 255) / 256, 65536);
+  hipLaunchKernelGGL(regroup_scales_kernel, dim3(blocks), dim3(256), 0, stream, s, s4, rows, G);
+  return hipGetLastError();
 }
 
 }  // namespace flint

@@ -31,6 +31,7 @@ enum { ERR_TIMEOUT = 1u, ERR_TOKEN = 2u, ERR_POS = 4u };
 struct Mat {
   const uint8_t* w;      // row-major [rows][in] (fp32 / bf16) or int4 codes [rows][in/2]
   const uint16_t* s;     // int4 only: bf16 scales [rows][in/64]
+  const uint16_t* s4;    // int4, batched path: the same scales as [rows/4][in/64][4] (4 rows per 8 bytes)
 };
 
 // Per-context constants, kept in device memory for the kernel's lifetime.
@@ -87,7 +88,7 @@ constexpr int BT = 16;                  // sequences per pass (MFMA columns)
 constexpr int ATT_P = 128;              // cached positions per attention split of the batched path
 constexpr int MAX_SPLITS = 1024;        // attention splits per sequence (max_tokens <= ATT_P * MAX_SPLITS)
 constexpr int OKC = 2;                  // o_proj input chunks (partial sums added by the next norm)
-constexpr int DKC = 4;                  // MoE down expert chunks / dense down input chunks
+constexpr int DKC = 16;                 // MoE down expert chunks / dense down input chunks
 
 struct BArgs {
   // model
@@ -134,6 +135,8 @@ struct BArgs {
 
 // Enqueue one batched decode pass (every layer and the head) on `stream`.
 hipError_t launch_batch_pass(int wt, const BArgs& a, hipStream_t stream);
+// s4[((r / 4) * G + g) * 4 + r % 4] = s[r * G + g] for r < rows (a multiple of 4), g < G.
+hipError_t launch_regroup_scales(const uint16_t* s, uint16_t* s4, size_t rows, int G, hipStream_t stream);
 
 // True if the compile-time 2048-wide shape (and a 256-workgroup grid) matches.
 bool shape_is_static(const KStatic& k, int grid);

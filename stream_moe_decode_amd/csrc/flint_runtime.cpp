@@ -430,6 +430,21 @@ int flint_decode_init(const flint_config* cfg, const flint_weights* w, void* hip
   c->batch_ok = cfg->weight_type != FLINT_W_F32 && hd == 128 && cfg->n_q_heads / cfg->n_kv_heads <= 4 &&
                 QD % 64 == 0 && (ND == 0 || DI % 64 == 0) && (NM == 0 || EI % 64 == 0) && V % 16 == 0 &&
                 !getenv("FLINT_NO_BATCH_PATH");
+  if (c->batch_ok && wt == FLINT_W_INT4G64) {  // int4 scales regrouped by 4 rows for the batched contractions
+    struct R {
+      Mat* m;
+      size_t rows, in;
+    } regs[] = {{&a.qkv, L * QR, H}, {&a.o, L * H, QD}, {&a.dg, ND * DI, H}, {&a.du, ND * DI, H},
+                {&a.dd, ND * H, DI}, {&a.eg, NM * E * EI, H}, {&a.eu, NM * E * EI, H}, {&a.ed, NM * E * H, EI}};
+    for (const R& r : regs) {
+      if (!r.rows || !r.m->s) continue;
+      void* p4;
+      if ((rc = dalloc(c, &p4, r.rows * (r.in / 64) * 2))) return bail(rc);
+      if (launch_regroup_scales(r.m->s, (uint16_t*)p4, r.rows, (int)(r.in / 64), c->stream) != hipSuccess)
+        return bail(fail(FLINT_EHIP, "scale regrouping failed"));
+      r.m->s4 = (const uint16_t*)p4;
+    }
+  }
   void* kd;
   if ((rc = dalloc(c, &kd, sizeof(KStatic)))) return bail(rc);
   c->kdev = (KStatic*)kd;
