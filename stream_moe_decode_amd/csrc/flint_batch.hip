@@ -34,6 +34,8 @@ template <int WT> __device__ __forceinline__ int act_pos(int e) {
   return WT == W_I4 ? (e & ~7) | ((e & 3) << 1) | ((e >> 2) & 1) : e;
 }
 __device__ __forceinline__ bf16x8_t as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8_t, v); }
+// inputs per 1 KB chunk of a tile of the tiled weights
+template <int WT> constexpr int kChunkIn = WT == W_I4 ? 128 : 32;
 __device__ __forceinline__ f32x4_t mfma(bf16x8_t a, bf16x8_t b, f32x4_t c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
@@ -47,70 +49,106 @@ __device__ __forceinline__ void latch(const BArgs& a, uint32_t bits) {
   __hip_atomic_store(gp(a.herr), bits, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
 }
 
-// acc[t] += W[tile t's 16 rows] . x over the 64-input groups [g0, g1) for 16 sequence columns, the input
-// operand of a group loaded once for all NT tiles.  Lane L supplies row L % 16 of each tile (matrix row
-// rowmap(t, L % 16)) and column L % 16 (`col`: that sequence's input row, null for a zero column), inputs
-// (L / 16) * 16 + [0, 16) of each group, and accumulates rows (L / 16) * 4 + r of column L % 16; rows
-// rowmap(t, 4 k) .. + 3 are consecutive from a multiple of 4.  int4: codes enter as 128 + u, two MFMAs
-// with the constant -136 as the weight operand remove the offset, then the group's scale of each row
-// (four rows in one 8-byte load of the regrouped scales) multiplies the group's fp32 result.  Every load
-// of U groups is issued before their products.
-template <int WT, int NT, class RowMap>
-__device__ __forceinline__ void mma_tiles(f32x4_t (&acc)[NT], const Mat& m, int in, RowMap rowmap,
-                                          const uint16_t* col, int g0, int g1) {
-  const int lane = threadIdx.x & 63, mr = lane & 15, kg = lane >> 4, G = in / 64;
-  const uint8_t* wr[NT];
+// Row of the matrix at row m (< 16) of tile T: rows in order, or, for the fused QKV rows of heads of rope_hd
+// dims, 8 rotate-half pairs of one head (rows i0 + m and rope_hd/2 + i0 + m), so that a row and its RoPE
+// partner meet in one MFMA result.
+__host__ __device__ __forceinline__ long long tile_row(long long T, int m, int rope_hd) {
+  if (rope_hd == 0) return T * 16 + m;
+  const int tph = rope_hd / 16, half = rope_hd / 2, i0 = (int)(T % tph) * 8;
+  return T / tph * rope_hd + (m < 8 ? i0 + m : half + i0 + m - 8);
+}
+
+// Tiled weights of the batched path: tile T (16 rows), chunk c, lane L hold, at ((T * C + c) * 64 + L) * 16,
+// the 16 bytes that lane L feeds to the MFMAs of chunk c: row tile_row(T, L % 16), k-slice L / 16.
+//   int4 (C = in / 128): inputs (2c + h) * 64 + (L / 16) * 16 + j * 8 + [0, 8) in dword 2h + j (h, j < 2);
+//   bf16 (C = in / 32): inputs c * 32 + (L / 16) * 8 + [0, 8).
+// A wave's load of one chunk of one tile is then 1 KB of contiguous memory.
+template <int WT>
+__global__ void tile_weights_kernel(const uint8_t* w, uint8_t* dst, size_t rows, int in, int rope_hd) {
+  const int C = WT == W_I4 ? in / 128 : in / 32;
+  const size_t total = rows / 16 * (size_t)C * 64;
+  for (size_t u = (size_t)blockIdx.x * blockDim.x + threadIdx.x; u < total; u += (size_t)gridDim.x * blockDim.x) {
+    const int L = (int)(u & 63), kg = L >> 4;
+    const size_t tc = u >> 6, T = tc / C;
+    const int c = (int)(tc - T * C);
+    const long long r = tile_row((long long)T, L & 15, rope_hd);
+    uint4 v;
+    if constexpr (WT == W_I4) {
+      const uint8_t* row = w + r * (in / 2);
+      const uint32_t* pa = reinterpret_cast<const uint32_t*>(row + (2 * c) * 32 + kg * 8);
+      const uint32_t* pb = reinterpret_cast<const uint32_t*>(row + (2 * c + 1) * 32 + kg * 8);
+      v = make_uint4(gp(pa)[0], gp(pa)[1], gp(pb)[0], gp(pb)[1]);
+    } else {
+      v = ld16(w + (r * in + c * 32 + kg * 8) * 2);
+    }
+    *(GLOBAL u32x4_t*)(dst + u * 16) = u32x4_t{v.x, v.y, v.z, v.w};
+  }
+}
+
+// acc[t] += W[tile t] . x over the chunks [c0, c1) (int4: 128 inputs, bf16: 32) for 16 sequence columns,
+// the input operand of a chunk loaded once for all NT tiles.  tile_of(t): the tile's index in m.wt;
+// rowmap(t, m): its rows (for the int4 scales; rows rowmap(t, 4 k) .. + 3 are consecutive from a
+// multiple of 4).  Lane L accumulates rows (L / 16) * 4 + r of column L % 16 (`col`: that sequence's
+// input row, null for a zero column).  int4: codes enter as 128 + u, two MFMAs with the constant -136 as
+// the weight operand remove the offset, then each row's group scale (four rows in one 8-byte load of the
+// regrouped scales) multiplies the group's fp32 result.  Every load of U chunks is issued first.
+template <int WT, int NT, class TileOf, class RowMap>
+__device__ __forceinline__ void mma_tiles(f32x4_t (&acc)[NT], const Mat& m, int in, TileOf tile_of, RowMap rowmap,
+                                          const uint16_t* col, int c0, int c1) {
+  const int lane = threadIdx.x & 63, kg = lane >> 4, G = in / 64;
+  const int C = in / kChunkIn<WT>;
+  const uint8_t* tp[NT];
   const uint16_t* s4[NT];
 #pragma unroll
   for (int t = 0; t < NT; ++t) {
-    wr[t] = m.w + rowmap(t, mr) * row_bytes<WT>(in);
+    tp[t] = m.wt + ((size_t)tile_of(t) * C * 64 + lane) * 16;
     if constexpr (WT == W_I4) s4[t] = m.s4 + (size_t)(rowmap(t, 4 * kg) >> 2) * G * 4;
   }
   const I4K k4 = i4k();
   const bf16x8_t bias = as_bf16x8(make_uint4(0xC308C308u, 0xC308C308u, 0xC308C308u, 0xC308C308u));  // bf16 -136
-  constexpr int U = NT >= 4 ? 2 : 4;
-  for (int g = g0; g < g1; g += U) {
-    u32x2_t wq[U][NT], sq[U][NT];
-    uint4 wb[U][NT][2], b0[U], b1[U];
+  constexpr int U = WT == W_I4 ? (NT >= 4 ? 2 : 4) : (NT >= 4 ? 4 : 8);
+  constexpr int NB = WT == W_I4 ? 4 : 1;  // 16-byte input loads per chunk
+  for (int c = c0; c < c1; c += U) {
+    uint4 wv[U][NT], b[U][NB];
+    u32x2_t sa[U][NT], sb[U][NT];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const int gg = min(g + u, g1 - 1);  // past the end: the last group again, not used
-      const int e0 = gg * 64 + kg * 16;
+      const int cc = min(c + u, c1 - 1);  // past the end: the last chunk again, not used
 #pragma unroll
       for (int t = 0; t < NT; ++t) {
+        wv[u][t] = ld16(tp[t] + (size_t)cc * 1024);
         if constexpr (WT == W_I4) {
-          wq[u][t] = *(GLOBAL const u32x2_t*)(wr[t] + e0 / 2);
-          sq[u][t] = *(GLOBAL const u32x2_t*)(s4[t] + (size_t)gg * 4);
-        } else {
-          wb[u][t][0] = ld16(wr[t] + 2 * e0);
-          wb[u][t][1] = ld16(wr[t] + 2 * e0 + 16);
+          sa[u][t] = *(GLOBAL const u32x2_t*)(s4[t] + (size_t)(2 * cc) * 4);
+          sb[u][t] = *(GLOBAL const u32x2_t*)(s4[t] + (size_t)(2 * cc + 1) * 4);
         }
       }
-      if (col) {
-        b0[u] = ld16(col + e0);
-        b1[u] = ld16(col + e0 + 8);
-      } else {
-        b0[u] = b1[u] = make_uint4(0u, 0u, 0u, 0u);
+#pragma unroll
+      for (int q = 0; q < NB; ++q) {
+        const int e = WT == W_I4 ? (2 * cc + (q >> 1)) * 64 + kg * 16 + (q & 1) * 8 : cc * 32 + kg * 8;
+        b[u][q] = col ? ld16(col + e) : make_uint4(0u, 0u, 0u, 0u);
       }
     }
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      if (g + u >= g1) break;
+      if (c + u >= c1) break;
 #pragma unroll
       for (int t = 0; t < NT; ++t) {
         if constexpr (WT == W_I4) {
-          f32x4_t d = {0.f, 0.f, 0.f, 0.f};
-          d = mfma(unpack8(wq[u][t].x, k4), as_bf16x8(b0[u]), d);
-          d = mfma(unpack8(wq[u][t].y, k4), as_bf16x8(b1[u]), d);
-          d = mfma(bias, as_bf16x8(b0[u]), d);
-          d = mfma(bias, as_bf16x8(b1[u]), d);
-          acc[t][0] = fmaf(bf2f(sq[u][t].x & 0xFFFFu), d[0], acc[t][0]);
-          acc[t][1] = fmaf(bf2f(sq[u][t].x >> 16), d[1], acc[t][1]);
-          acc[t][2] = fmaf(bf2f(sq[u][t].y & 0xFFFFu), d[2], acc[t][2]);
-          acc[t][3] = fmaf(bf2f(sq[u][t].y >> 16), d[3], acc[t][3]);
+          f32x4_t da = {0.f, 0.f, 0.f, 0.f}, db = {0.f, 0.f, 0.f, 0.f};
+          da = mfma(unpack8(wv[u][t].x, k4), as_bf16x8(b[u][0]), da);
+          da = mfma(unpack8(wv[u][t].y, k4), as_bf16x8(b[u][1]), da);
+          da = mfma(bias, as_bf16x8(b[u][0]), da);
+          da = mfma(bias, as_bf16x8(b[u][1]), da);
+          db = mfma(unpack8(wv[u][t].z, k4), as_bf16x8(b[u][2]), db);
+          db = mfma(unpack8(wv[u][t].w, k4), as_bf16x8(b[u][3]), db);
+          db = mfma(bias, as_bf16x8(b[u][2]), db);
+          db = mfma(bias, as_bf16x8(b[u][3]), db);
+          acc[t][0] = fmaf(bf2f(sa[u][t].x & 0xFFFFu), da[0], fmaf(bf2f(sb[u][t].x & 0xFFFFu), db[0], acc[t][0]));
+          acc[t][1] = fmaf(bf2f(sa[u][t].x >> 16), da[1], fmaf(bf2f(sb[u][t].x >> 16), db[1], acc[t][1]));
+          acc[t][2] = fmaf(bf2f(sa[u][t].y & 0xFFFFu), da[2], fmaf(bf2f(sb[u][t].y & 0xFFFFu), db[2], acc[t][2]));
+          acc[t][3] = fmaf(bf2f(sa[u][t].y >> 16), da[3], fmaf(bf2f(sb[u][t].y >> 16), db[3], acc[t][3]));
         } else {
-          acc[t] = mfma(as_bf16x8(wb[u][t][0]), as_bf16x8(b0[u]), acc[t]);
-          acc[t] = mfma(as_bf16x8(wb[u][t][1]), as_bf16x8(b1[u]), acc[t]);
+          acc[t] = mfma(as_bf16x8(wv[u][t]), as_bf16x8(b[u][0]), acc[t]);
         }
       }
     }
@@ -290,10 +328,11 @@ __global__ void __launch_bounds__(BNT) bk_qkv(const BArgs a, int l) {
   const int hh = t / tph, i0 = (t % tph) * 8;
   const int QR = (a.nq + 2 * a.nkv) * hd;
   auto rowmap = [&](int, int m) -> long long { return (long long)l * QR + hh * hd + (m < 8 ? i0 + m : half + i0 + m - 8); };
-  const int G = a.H / 64, n = lane & 15, kg = lane >> 4;
+  const int C = a.H / kChunkIn<WT>, n = lane & 15, kg = lane >> 4;
   const uint16_t* col = n < a.B ? a.act + (size_t)n * a.astride : nullptr;
   f32x4_t acc[1] = {{0.f, 0.f, 0.f, 0.f}};
-  mma_tiles<WT, 1>(acc, a.qkv, a.H, rowmap, col, part(G, BNW, wave), part(G, BNW, wave + 1));
+  auto tile_of = [&](int) -> long long { return (long long)l * (QR / 16) + t; };  // tiled with rope_hd = hd
+  mma_tiles<WT, 1>(acc, a.qkv, a.H, tile_of, rowmap, col, part(C, BNW, wave), part(C, BNW, wave + 1));
   const f32x4_t sum = sum_waves(acc[0], red);
   if (wave != 0) return;
   float y[4] = {sum[0], sum[1], sum[2], sum[3]};
@@ -480,12 +519,13 @@ template <int WT>
 __global__ void __launch_bounds__(BNT) bk_oproj(const BArgs a, int l) {
   __shared__ f32x4_t red[BNW * 64];
   const int t = blockIdx.x, kc = blockIdx.y, lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int QD = a.nq * a.hd, G = QD / 64, gb = part(G, OKC, kc), ge = part(G, OKC, kc + 1);
+  const int QD = a.nq * a.hd, C = QD / kChunkIn<WT>, cb = part(C, OKC, kc), ce = part(C, OKC, kc + 1);
   const int n = lane & 15, kg = lane >> 4;
   auto rowmap = [&](int, int m) -> long long { return (long long)l * a.H + t * 16 + m; };
+  auto tile_of = [&](int) -> long long { return ((long long)l * a.H >> 4) + t; };
   const uint16_t* col = n < a.B ? a.act + (size_t)n * a.astride : nullptr;
   f32x4_t acc[1] = {{0.f, 0.f, 0.f, 0.f}};
-  mma_tiles<WT, 1>(acc, a.o, QD, rowmap, col, gb + part(ge - gb, BNW, wave), gb + part(ge - gb, BNW, wave + 1));
+  mma_tiles<WT, 1>(acc, a.o, QD, tile_of, rowmap, col, cb + part(ce - cb, BNW, wave), cb + part(ce - cb, BNW, wave + 1));
   const f32x4_t sum = sum_waves(acc[0], red);
   if (wave != 0 || n >= a.B) return;
 #pragma unroll
@@ -501,16 +541,9 @@ __global__ void __launch_bounds__(BNT) bk_gateup(const BArgs a, int l) {
   __shared__ int slot[BT];
   const int t = blockIdx.x, e = blockIdx.y, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const bool dense = l < a.n_dense;
-  if (tid < BT) {
-    int sl = -1;
-    if (tid < a.B) {
-      if (dense) sl = 0;
-      else
-        for (int k = 0; k < a.K; ++k)
-          if (gp(a.sel)[tid * a.K + k] == e) sl = k;
-    }
-    slot[tid] = sl;
-  }
+  if (tid < BT) slot[tid] = dense && tid < a.B ? 0 : -1;
+  __syncthreads();
+  if (!dense && tid < a.B * a.K && gp(a.sel)[tid] == e) slot[tid / a.K] = tid % a.K;  // one load per thread
   __syncthreads();
   bool any = false;
 #pragma unroll
@@ -521,7 +554,7 @@ __global__ void __launch_bounds__(BNT) bk_gateup(const BArgs a, int l) {
   const Mat& Mu = dense ? a.du : a.eu;
   const long long base = dense ? (long long)l * a.DI : ((long long)(l - a.n_dense) * a.E + e) * a.EI;
   const uint16_t* col = slot[n] >= 0 ? a.act + (size_t)n * a.astride : nullptr;
-  const int G = a.H / 64, g0 = part(G, BNW, wave), g1 = part(G, BNW, wave + 1);
+  const int C = a.H / kChunkIn<WT>, c0 = part(C, BNW, wave), c1 = part(C, BNW, wave + 1);
   f32x4_t acc[4];
   // gate tiles, then up tiles (same rows; the two matrices share the layout and the scales' regrouping)
 #pragma unroll
@@ -529,7 +562,8 @@ __global__ void __launch_bounds__(BNT) bk_gateup(const BArgs a, int l) {
 #pragma unroll
     for (int q = 0; q < 4; ++q) acc[q] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     auto rowmap = [&](int q, int m) -> long long { return base + t * 64 + q * 16 + m; };
-    mma_tiles<WT, 4>(acc, mat ? Mu : Mg, a.H, rowmap, col, g0, g1);
+    auto tile_of = [&](int q) -> long long { return (base >> 4) + t * 4 + q; };
+    mma_tiles<WT, 4>(acc, mat ? Mu : Mg, a.H, tile_of, rowmap, col, c0, c1);
 #pragma unroll
     for (int q = 0; q < 4; ++q) red[wave][mat * 4 + q][lane] = acc[q];
   }
@@ -559,6 +593,7 @@ template <int WT>
 __global__ void __launch_bounds__(BNT) bk_down(const BArgs a, int l) {
   __shared__ f32x4_t red[BNW][4][64];
   __shared__ int sel_s[BT * MAX_K];
+  __shared__ float wsel_s[BT * MAX_K];
   __shared__ unsigned long long emask;
   const int t = blockIdx.x, c = blockIdx.y, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int n = lane & 15, kg = lane >> 4;
@@ -567,24 +602,32 @@ __global__ void __launch_bounds__(BNT) bk_down(const BArgs a, int l) {
 #pragma unroll
   for (int q = 0; q < 4; ++q) acc[q] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   if (dense) {
-    const int G = a.DI / 64, gb = part(G, DKC, c), ge = part(G, DKC, c + 1);
+    // items of 128 inputs (int4: one chunk, bf16: four)
+    constexpr int IC = 128 / kChunkIn<WT>;
+    const int NI = a.DI / 128, ib = part(NI, DKC, c), ie = part(NI, DKC, c + 1);
     auto rowmap = [&](int q, int m) -> long long { return (long long)l * a.H + t * 64 + q * 16 + m; };
+    auto tile_of = [&](int q) -> long long { return ((long long)l * a.H >> 4) + t * 4 + q; };
     const uint16_t* col = n < a.B ? a.h + (size_t)n * a.hstride : nullptr;
-    for (int g = gb + 2 * wave; g < ge; g += 2 * BNW) mma_tiles<WT, 4>(acc, a.dd, a.DI, rowmap, col, g, min(g + 2, ge));
+    for (int i = ib + wave; i < ie; i += BNW) mma_tiles<WT, 4>(acc, a.dd, a.DI, tile_of, rowmap, col, i * IC, (i + 1) * IC);
   } else {
     const int eb = part(a.E, DKC, c), ee = part(a.E, DKC, c + 1);
     if (tid == 0) emask = 0ull;
-    for (int i = tid; i < a.B * a.K; i += BNT) sel_s[i] = gp(a.sel)[i];
+    for (int i = tid; i < a.B * a.K; i += BNT) {
+      sel_s[i] = gp(a.sel)[i];
+      wsel_s[i] = gp(a.wsel)[i];
+    }
     __syncthreads();
     for (int i = tid; i < a.B * a.K; i += BNT) atomicOr(&emask, 1ull << sel_s[i]);
     __syncthreads();
     // the chunk's experts that some sequence picked, in index order
     const unsigned long long mk = emask & ((ee >= 64 ? ~0ull : (1ull << ee) - 1ull) & ~((1ull << eb) - 1ull));
-    const int ne = __builtin_popcountll(mk), G = a.EI / 64, G2 = (G + 1) / 2, lm = l - a.n_dense;
+    // items of 128 inputs (int4: one chunk, bf16: four) of each picked expert
+    constexpr int IC = 128 / kChunkIn<WT>;
+    const int ne = __builtin_popcountll(mk), NI = a.EI / 128, lm = l - a.n_dense;
     int e = -1, ei = -1, sl = -1;
     float wn = 0.f;
-    for (int it = wave; it < ne * G2; it += BNW) {
-      const int want = it / G2, g = 2 * (it - want * G2);
+    for (int it = wave; it < ne * NI; it += BNW) {
+      const int want = it / NI, ic = it - want * NI;
       if (want != ei) {  // next expert of this wave: its index, this lane's sequence slot and weight
         unsigned long long mm = mk;
         for (int k = 0; k < want; ++k) mm &= mm - 1;
@@ -594,14 +637,15 @@ __global__ void __launch_bounds__(BNT) bk_down(const BArgs a, int l) {
         if (n < a.B)
           for (int k = 0; k < a.K; ++k)
             if (sel_s[n * a.K + k] == e) sl = k;
-        wn = sl >= 0 ? gp(a.wsel)[n * a.K + sl] : 0.f;
+        wn = sl >= 0 ? wsel_s[n * a.K + sl] : 0.f;
       }
       const uint16_t* col = sl >= 0 ? a.h + (size_t)n * a.hstride + (size_t)sl * a.EI : nullptr;
       auto rowmap = [&](int q, int m) -> long long { return ((long long)lm * a.E + e) * a.H + t * 64 + q * 16 + m; };
+      auto tile_of = [&](int q) -> long long { return (((long long)lm * a.E + e) * a.H >> 4) + t * 4 + q; };
       f32x4_t d[4];
 #pragma unroll
       for (int q = 0; q < 4; ++q) d[q] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-      mma_tiles<WT, 4>(d, a.ed, a.EI, rowmap, col, g, min(g + 2, G));
+      mma_tiles<WT, 4>(d, a.ed, a.EI, tile_of, rowmap, col, ic * IC, (ic + 1) * IC);
 #pragma unroll
       for (int q = 0; q < 4; ++q)
 #pragma unroll
@@ -633,17 +677,18 @@ __global__ void __launch_bounds__(BNT) bk_head(const BArgs a) {
   const int W = blockIdx.x, G = gridDim.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int n = lane & 15, kg = lane >> 4, ntl = a.V / 16;
   const int tb = part(ntl, G, W), te = part(ntl, G, W + 1);
-  const Mat lm{a.lmhead, nullptr, nullptr};
+  const Mat lm{a.lmhead, nullptr, nullptr, a.lmt};
   const uint16_t* col = n < a.B ? a.act + (size_t)n * a.astride : nullptr;
-  const int half = wave >> 2, grp = wave & 3, NG = a.H / 64;
+  const int half = wave >> 2, grp = wave & 3, NC = a.H / kChunkIn<W_BF16>;
   float bv = -INFINITY;
   int bi = 0x7FFFFFFF;
   for (int t0 = tb; t0 < te; t0 += 16) {  // 16 tiles per round: wave group grp takes tiles t0 + 4 grp .. + 3
     f32x4_t acc[4];
 #pragma unroll
     for (int q = 0; q < 4; ++q) acc[q] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    auto rowmap = [&](int q, int m) -> long long { return (long long)min(t0 + 4 * grp + q, te - 1) * 16 + m; };
-    mma_tiles<W_BF16, 4>(acc, lm, a.H, rowmap, col, half ? NG / 2 : 0, half ? NG : NG / 2);
+    auto tile_of = [&](int q) -> long long { return min(t0 + 4 * grp + q, te - 1); };
+    auto rowmap = [&](int q, int m) -> long long { return tile_of(q) * 16 + m; };
+    mma_tiles<W_BF16, 4>(acc, lm, a.H, tile_of, rowmap, col, half ? NC / 2 : 0, half ? NC : NC / 2);
     __syncthreads();  // the previous round's reads of red are done
 #pragma unroll
     for (int q = 0; q < 4; ++q) red[wave][q][lane] = acc[q];
@@ -744,6 +789,17 @@ template <int WT> hipError_t run_pass(const BArgs& a, hipStream_t st) {
 
 hipError_t launch_batch_pass(int wt, const BArgs& a, hipStream_t stream) {
   return wt == W_I4 ? run_pass<W_I4>(a, stream) : run_pass<W_BF16>(a, stream);
+}
+
+hipError_t launch_tile_weights(int wt, const uint8_t* w, uint8_t* dst, size_t rows, int in, int rope_hd,
+                               hipStream_t stream) {
+  const size_t units = rows / 16 * (size_t)(wt == W_I4 ? in / 128 : in / 32) * 64;
+  const int blocks = (int)std::min<size_t>((units + 255) / 256, 65536);
+  if (wt == W_I4)
+    hipLaunchKernelGGL(tile_weights_kernel<W_I4>, dim3(blocks), dim3(256), 0, stream, w, dst, rows, in, rope_hd);
+  else
+    hipLaunchKernelGGL(tile_weights_kernel<W_BF16>, dim3(blocks), dim3(256), 0, stream, w, dst, rows, in, rope_hd);
+  return hipGetLastError();
 }
 
 hipError_t launch_regroup_scales(const uint16_t* s, uint16_t* s4, size_t rows, int G, hipStream_t stream) {

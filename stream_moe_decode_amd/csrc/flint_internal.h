@@ -32,6 +32,7 @@ struct Mat {
   const uint8_t* w;      // row-major [rows][in] (fp32 / bf16) or int4 codes [rows][in/2]
   const uint16_t* s;     // int4 only: bf16 scales [rows][in/64]
   const uint16_t* s4;    // int4, batched path: the same scales as [rows/4][in/64][4] (4 rows per 8 bytes)
+  const uint8_t* wt;     // batched path: the weights in 16-row tiles of 1 KB MFMA operand chunks (see tile_map)
 };
 
 // Per-context constants, kept in device memory for the kernel's lifetime.
@@ -96,6 +97,7 @@ struct BArgs {
   float eps;
   const uint8_t* embed;
   const uint8_t* lmhead;
+  const uint8_t* lmt;    // lm_head in the tiled layout
   const float* fnorm;
   const float* anorm;
   const float* pnorm;
@@ -137,6 +139,11 @@ struct BArgs {
 hipError_t launch_batch_pass(int wt, const BArgs& a, hipStream_t stream);
 // s4[((r / 4) * G + g) * 4 + r % 4] = s[r * G + g] for r < rows (a multiple of 4), g < G.
 hipError_t launch_regroup_scales(const uint16_t* s, uint16_t* s4, size_t rows, int G, hipStream_t stream);
+// Copy a [rows][in] weight matrix into the tiled layout of the batched path (rows a multiple of 16).  Tile
+// T holds rows tile_row(T, m), m < 16: the rows in order (rope_hd == 0), or, for the fused QKV rows of
+// rope_hd-dim heads, 8 rotate-half pairs per tile (rows i0 + m and rope_hd/2 + i0 + m of one head).
+hipError_t launch_tile_weights(int wt, const uint8_t* w, uint8_t* dst, size_t rows, int in, int rope_hd,
+                               hipStream_t stream);
 
 // True if the compile-time 2048-wide shape (and a 256-workgroup grid) matches.
 bool shape_is_static(const KStatic& k, int grid);

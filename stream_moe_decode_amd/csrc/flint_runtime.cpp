@@ -59,6 +59,8 @@ struct flint_ctx {
   KStatic* kdev;              // the same, in device memory, read by the kernel
   bool stat;                  // the compile-time 2048-wide kernel applies
   bool batch_ok;              // batches of several sequences take the batched MFMA path
+  bool tiled;                 // the batched path's tiled weight copies exist
+  const uint8_t* lmt;         // lm_head in the tiled layout (with `tiled`)
   uint32_t* herr_host;        // host-mapped error word
   uint64_t* xbuf;
   size_t xbuf_words;
@@ -231,10 +233,49 @@ int launch(flint_ctx* c, flint_kv* kv, const int32_t* tokens, int tok_idx, int s
   return FLINT_OK;
 }
 
+// The batched path's weight copies in 16-row tiles of MFMA operand chunks (made once per context, on
+// the first cache of several sequences).
+int tile_weights(flint_ctx* c) {
+  if (c->tiled) return FLINT_OK;
+  const flint_config& cfg = c->cfg;
+  KStatic& k = c->base;
+  const int wt = cfg.weight_type;
+  const size_t L = cfg.n_layers, ND = cfg.n_dense_layers, NM = L - ND, H = cfg.hidden, hd = cfg.head_dim;
+  const size_t QR = (cfg.n_q_heads + 2 * cfg.n_kv_heads) * hd, QD = cfg.n_q_heads * hd;
+  const size_t DI = cfg.dense_inter, E = cfg.n_experts, EI = cfg.expert_inter;
+  struct T {
+    Mat* m;
+    size_t rows, in;
+    int rope;
+  } mats[] = {{&k.qkv, L * QR, H, (int)hd}, {&k.o, L * H, QD, 0},        {&k.dg, ND * DI, H, 0},
+              {&k.du, ND * DI, H, 0},       {&k.dd, ND * H, DI, 0},       {&k.eg, NM * E * EI, H, 0},
+              {&k.eu, NM * E * EI, H, 0},   {&k.ed, NM * E * H, EI, 0}};
+  int rc;
+  for (const T& t : mats) {
+    if (!t.rows) continue;
+    void* p;
+    if ((rc = dalloc(c, &p, mat_bytes(wt, t.rows, t.in)))) return rc;
+    if (launch_tile_weights(wt == FLINT_W_INT4G64 ? W_I4 : W_BF16, t.m->w, (uint8_t*)p, t.rows, (int)t.in, t.rope,
+                            c->stream) != hipSuccess)
+      return fail(FLINT_EHIP, "weight tiling failed");
+    t.m->wt = (const uint8_t*)p;
+  }
+  void* p;
+  if ((rc = dalloc(c, &p, (size_t)cfg.vocab * H * 2))) return rc;
+  if (launch_tile_weights(W_BF16, k.lmhead, (uint8_t*)p, cfg.vocab, (int)H, 0, c->stream) != hipSuccess)
+    return fail(FLINT_EHIP, "lm_head tiling failed");
+  c->lmt = (const uint8_t*)p;
+  if (hipStreamSynchronize(c->stream) != hipSuccess) return fail(FLINT_EHIP, "weight tiling failed");
+  c->tiled = true;
+  return FLINT_OK;
+}
+
 // Scratch of the batched path, one allocation carved into the buffers of BArgs, plus the arguments
 // that stay the same for every pass.
 int batch_scratch(flint_ctx* c, flint_kv* kv) {
   const flint_config& cfg = c->cfg;
+  int trc = tile_weights(c);
+  if (trc) return trc;
   const KStatic& k = c->base;
   BArgs& a = kv->bargs;
   memset(&a, 0, sizeof a);
@@ -253,6 +294,7 @@ int batch_scratch(flint_ctx* c, flint_kv* kv) {
   a.eps = cfg.rms_eps;
   a.embed = k.embed;
   a.lmhead = k.lmhead;
+  a.lmt = c->lmt;
   a.fnorm = k.fnorm;
   a.anorm = k.anorm;
   a.pnorm = k.pnorm;
@@ -428,7 +470,8 @@ int flint_decode_init(const flint_config* cfg, const flint_weights* w, void* hip
   // the batched path: bf16 activations, 128-dim heads with at most 4 query heads per kv head (attention
   // scores on MFMA), row counts in whole 16-row tiles and 64-row gate/up blocks
   c->batch_ok = cfg->weight_type != FLINT_W_F32 && hd == 128 && cfg->n_q_heads / cfg->n_kv_heads <= 4 &&
-                QD % 64 == 0 && (ND == 0 || DI % 64 == 0) && (NM == 0 || EI % 64 == 0) && V % 16 == 0 &&
+                H % 128 == 0 && QD % 128 == 0 && (ND == 0 || DI % 128 == 0) && (NM == 0 || EI % 128 == 0) &&
+                V % 16 == 0 &&
                 !getenv("FLINT_NO_BATCH_PATH");
   if (c->batch_ok && wt == FLINT_W_INT4G64) {  // int4 scales regrouped by 4 rows for the batched contractions
     struct R {
