@@ -113,7 +113,8 @@ __device__ __forceinline__ void mma_tiles(f32x4_t (&acc)[NT], const Mat& m, int 
     u32x2_t sa[U][NT], sb[U][NT];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const int cc = min(c + u, c1 - 1);  // past the end: the last chunk again, not used
+      if (c + u >= c1) break;
+      const int cc = c + u;
 #pragma unroll
       for (int t = 0; t < NT; ++t) {
         wv[u][t] = ld16(tp[t] + (size_t)cc * 1024);
@@ -180,29 +181,51 @@ __device__ __forceinline__ float bsum(float v, float* wred) {
 
 enum { NORM_EMBED = 0, NORM_INPUT = 1, NORM_POST = 2, NORM_FINAL = 3 };
 
-// xs[e] = x[e] + sum of the NP partial rows of sequence n (every load of a thread issued before the sums).
+// Partial sums cross workgroups (and XCDs) through memory: written with system-scope stores, which go
+// through the writer's L2, and read back with system-scope loads, which do not take a stale line from the
+// reader's L2.
+__device__ __forceinline__ void pstore(float* p, float v) {
+  __hip_atomic_store(gp(p), v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+}
+__device__ __forceinline__ float pload(const float* p) {
+  return __hip_atomic_load(gp(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+}
+
+// The last of the NP workgroups that wrote partial sums for rows [r0, r0 + nr) adds them to the residual
+// (in partial order, so the result does not depend on which workgroup is last) and re-arms the counter.
+// Called by the whole workgroup after its partial rows are stored (pstore).
 template <int NP>
-__device__ __forceinline__ void add_parts(float* xs, const float* xg, const float* parts, int n, int H) {
-  for (int e = threadIdx.x; e < H; e += BNT) {
+__device__ __forceinline__ void fold_parts(const BArgs& a, const float* parts, uint32_t* cnt, int r0, int nr) {
+  __shared__ int last;
+  wait_vmem();  // this thread's partial stores have completed
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const uint32_t prev = __hip_atomic_fetch_add(gp(cnt), 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    last = prev == (uint32_t)NP - 1;
+    if (last) __hip_atomic_store(gp(cnt), 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  __syncthreads();
+  if (!last) return;
+  for (int idx = threadIdx.x; idx < nr * a.B; idx += BNT) {
+    const int n = idx / nr, r = r0 + idx - n * nr;
     float v[NP + 1];
-    v[0] = gp(xg)[e];
+    v[0] = gp(a.x)[(size_t)n * a.H + r];
 #pragma unroll
-    for (int p = 0; p < NP; ++p) v[p + 1] = gp(parts)[((size_t)p * BT + n) * H + e];
+    for (int p = 0; p < NP; ++p) v[p + 1] = pload(parts + ((size_t)p * BT + n) * a.H + r);
     float t = v[0];
 #pragma unroll
     for (int p = 0; p < NP; ++p) t += v[p + 1];
-    xs[e] = t;
+    gp(a.x)[(size_t)n * a.H + r] = t;
   }
 }
 
-// RMSNorm of one sequence's residual (grid: one workgroup per sequence).  The residual first takes the
-// pending partial sums (down of the previous layer, or o_proj); the normalised row becomes the next
-// GEMM input.  NORM_POST of a MoE layer also computes the router logits and the top-k.
+// RMSNorm of one sequence's residual (grid: one workgroup per sequence); the normalised row becomes the
+// next GEMM input.  NORM_POST of a MoE layer also computes the router logits and the top-k.
 template <int WT>
 __global__ void __launch_bounds__(BNT) bk_norm(const BArgs a, int l, int mode) {
-  __shared__ float xs[MAX_H];
   __shared__ __attribute__((aligned(16))) uint16_t an[MAX_H];
   __shared__ float z[MAX_E];
+  __shared__ int rk[BNW][64];
   __shared__ float wred[BNW];
   const int n = blockIdx.x, seq = a.seq0 + n, tid = threadIdx.x, H = a.H;
   const int lane = tid & 63, wave = tid >> 6, E = a.E, lm = l - a.n_dense;
@@ -214,20 +237,23 @@ __global__ void __launch_bounds__(BNT) bk_norm(const BArgs a, int l, int mode) {
   const int C = H / CE;
   const bool route = mode == NORM_POST && l >= a.n_dense;
   uint4 rw[RPW][CPL];
-  float rs[RPW][CPL];
-  if (route) {
+  uint32_t rs[RPW][CPL];  // int4: the 32-bit word holding the chunk's bf16 scale (groups 2k, 2k + 1)
+  if (route) {  // no conditions around the loads (indices clamped), so all of them are in flight at once
 #pragma unroll
     for (int i = 0; i < RPW; ++i)
 #pragma unroll
       for (int j = 0; j < CPL; ++j) {
-        const int e = wave + BNW * i, c = lane + 64 * j;
-        rs[i][j] = 1.f;
-        if (e < E && c < C) {
-          rw[i][j] = ld16(a.router.w + ((long long)lm * E + e) * row_bytes<WT>(H) + 16ll * c);
-          if constexpr (WT == W_I4) rs[i][j] = bf2f(gp(a.router.s)[((long long)lm * E + e) * (H / 64) + c / 2]);
-        }
+        const int e = min(wave + BNW * i, E - 1), c = min(lane + 64 * j, C - 1);
+        rw[i][j] = ld16(a.router.w + ((long long)lm * E + e) * row_bytes<WT>(H) + 16ll * c);
+        if constexpr (WT == W_I4)
+          rs[i][j] = gp(reinterpret_cast<const uint32_t*>(a.router.s))[(((long long)lm * E + e) * (H / 64) + c / 2) >> 1];
       }
   }
+  // the residual row (layer 0: the embedding row; later: complete, the last o_proj / down workgroup of each
+  // row block having added the partial sums) and the norm weights, every load in flight at once
+  constexpr int EPT = MAX_H / BNT;
+  const float* g = mode == NORM_POST ? a.pnorm + (size_t)l * H : (mode == NORM_FINAL ? a.fnorm : a.anorm + (size_t)l * H);
+  float xv[EPT], gv[EPT];
   if (mode == NORM_EMBED) {
     int tok = gp(a.tokens)[seq];
     if (tok < 0 || tok >= a.V) {
@@ -235,24 +261,39 @@ __global__ void __launch_bounds__(BNT) bk_norm(const BArgs a, int l, int mode) {
       tok = 0;
     }
     const uint16_t* er = reinterpret_cast<const uint16_t*>(a.embed) + (size_t)tok * H;
-    for (int e = tid; e < H; e += BNT) xs[e] = bf2f(gp(er)[e]);
-  } else if (mode == NORM_POST) {
-    add_parts<OKC>(xs, xg, a.opart, n, H);
+#pragma unroll
+    for (int k = 0; k < EPT; ++k) {
+      const int e = tid + k * BNT;
+      xv[k] = e < H ? bf2f(gp(er)[e]) : 0.f;
+      gv[k] = e < H ? gp(g)[e] : 0.f;
+    }
+#pragma unroll
+    for (int k = 0; k < EPT; ++k)
+      if (tid + k * BNT < H) gp(xg)[tid + k * BNT] = xv[k];
   } else {
-    add_parts<DKC>(xs, xg, a.dpart, n, H);
+#pragma unroll
+    for (int k = 0; k < EPT; ++k) {
+      const int e = tid + k * BNT;
+      xv[k] = e < H ? gp(xg)[e] : 0.f;
+      gv[k] = e < H ? gp(g)[e] : 0.f;
+    }
   }
-  for (int e = tid; e < H; e += BNT) gp(xg)[e] = xs[e];
-  // the residual after layer dbg_resid_layer is complete when the next layer's input norm (or the final norm) adds it up
+  // the residual after layer dbg_resid_layer is complete at the next layer's input norm (or the final norm)
   if (a.dbg_resid && ((mode == NORM_INPUT && l - 1 == a.dbg_resid_layer) || (mode == NORM_FINAL && a.L - 1 == a.dbg_resid_layer)))
-    for (int e = tid; e < H; e += BNT) gp(a.dbg_resid)[(size_t)seq * H + e] = xs[e];
+#pragma unroll
+    for (int k = 0; k < EPT; ++k)
+      if (tid + k * BNT < H) gp(a.dbg_resid)[(size_t)seq * H + tid + k * BNT] = xv[k];
   float ss = 0.f;
-  for (int e = tid; e < H; e += BNT) ss += xs[e] * xs[e];
+#pragma unroll
+  for (int k = 0; k < EPT; ++k) ss += xv[k] * xv[k];
   ss = bsum(ss, wred);
   const float inv = 1.0f / sqrtf(ss / (float)H + a.eps);
-  const float* g = mode == NORM_POST ? a.pnorm + (size_t)l * H : (mode == NORM_FINAL ? a.fnorm : a.anorm + (size_t)l * H);
   uint16_t* ag = a.act + (size_t)n * a.astride;
-  for (int e = tid; e < H; e += BNT) {
-    const uint16_t v = (uint16_t)f2bf(xs[e] * inv * gp(g)[e]);
+#pragma unroll
+  for (int k = 0; k < EPT; ++k) {
+    const int e = tid + k * BNT;
+    if (e >= H) break;
+    const uint16_t v = (uint16_t)f2bf(xv[k] * inv * gv[k]);
     const int p = mode == NORM_FINAL ? e : act_pos<WT>(e);  // the lm_head is bf16: natural order
     an[p] = v;
     gp(ag)[p] = v;
@@ -266,44 +307,57 @@ __global__ void __launch_bounds__(BNT) bk_norm(const BArgs a, int l, int mode) {
     return;
   }
 
-  // router logits from the staged rows
+  // router logits from the staged rows: each lane's activation chunks read once for all its rows
   __syncthreads();
   const I4K k4 = i4k();
+  float racc[RPW];
+#pragma unroll
+  for (int i = 0; i < RPW; ++i) racc[i] = 0.f;
+#pragma unroll
+  for (int j = 0; j < CPL; ++j) {
+    const int c = lane + 64 * j;
+    if (c >= C) break;
+    ActC<WT> x;
+    if constexpr (WT == W_I4) {
+      const uint4* p = reinterpret_cast<const uint4*>(an + 32 * c);
+      x.a[0] = p[0];
+      x.a[1] = p[1];
+      x.a[2] = p[2];
+      x.a[3] = p[3];
+      x.s = chunk_sum(x.a[0], x.a[1], x.a[2], x.a[3]);
+    } else {
+      x.a[0] = *reinterpret_cast<const uint4*>(an + 8 * c);
+      x.s = 0.f;
+    }
+#pragma unroll
+    for (int i = 0; i < RPW; ++i)
+      racc[i] += chunk_dot<WT>(rw[i][j], x, WT == W_I4 ? bf2f(((c >> 1) & 1) ? rs[i][j] >> 16 : rs[i][j] & 0xFFFFu) : 1.f, k4);
+  }
 #pragma unroll
   for (int i = 0; i < RPW; ++i) {
+    const float v = wave_sum(racc[i]);
     const int e = wave + BNW * i;
-    if (e >= E) break;
-    float acc = 0.f;
+    if (lane == 0 && e < E) z[e] = v;
+  }
+  __syncthreads();
+  // top-k by rank (larger logit first, equal logits: lower index first): wave w counts the experts
+  // 8 w .. 8 w + 7 that beat lane e's, the counts meet in LDS; weights: softmax over all experts
+  const float zl = lane < E ? z[lane] : -INFINITY;
+  {
+    int part = 0;
 #pragma unroll
-    for (int j = 0; j < CPL; ++j) {
-      const int c = lane + 64 * j;
-      if (c >= C) continue;
-      ActC<WT> x;
-      if constexpr (WT == W_I4) {
-        const uint4* p = reinterpret_cast<const uint4*>(an + 32 * c);
-        x.a[0] = p[0];
-        x.a[1] = p[1];
-        x.a[2] = p[2];
-        x.a[3] = p[3];
-        x.s = chunk_sum(x.a[0], x.a[1], x.a[2], x.a[3]);
-      } else {
-        x.a[0] = *reinterpret_cast<const uint4*>(an + 8 * c);
-        x.s = 0.f;
-      }
-      acc += chunk_dot<WT>(rw[i][j], x, rs[i][j], k4);
+    for (int jj = 0; jj < MAX_E / BNW; ++jj) {
+      const int j = wave * (MAX_E / BNW) + jj;
+      const float zj = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(zl), j));
+      part += j < E && (zj > zl || (zj == zl && j < lane));
     }
-    acc = wave_sum(acc);
-    if (lane == 0) z[e] = acc;
+    rk[wave][lane] = part;
   }
   __syncthreads();
   if (wave != 0) return;
-  // top-k by rank (larger logit first, equal logits: lower index first), weights softmax over all experts
-  const float zl = lane < E ? z[lane] : -INFINITY;
   int rank = 0;
-  for (int j = 0; j < E; ++j) {
-    const float zj = z[j];
-    rank += zj > zl || (zj == zl && j < lane);
-  }
+#pragma unroll
+  for (int w = 0; w < BNW; ++w) rank += rk[w][lane];
   const float zmax = wave_max(zl);
   const float pe = lane < E ? __expf(zl - zmax) : 0.f;
   const float w = pe / wave_sum(pe);
@@ -527,9 +581,10 @@ __global__ void __launch_bounds__(BNT) bk_oproj(const BArgs a, int l) {
   f32x4_t acc[1] = {{0.f, 0.f, 0.f, 0.f}};
   mma_tiles<WT, 1>(acc, a.o, QD, tile_of, rowmap, col, cb + part(ce - cb, BNW, wave), cb + part(ce - cb, BNW, wave + 1));
   const f32x4_t sum = sum_waves(acc[0], red);
-  if (wave != 0 || n >= a.B) return;
+  if (wave == 0 && n < a.B)
 #pragma unroll
-  for (int r = 0; r < 4; ++r) gp(a.opart)[((size_t)kc * BT + n) * a.H + t * 16 + 4 * kg + r] = sum[r];
+    for (int r = 0; r < 4; ++r) pstore(a.opart + ((size_t)kc * BT + n) * a.H + t * 16 + 4 * kg + r, sum[r]);
+  fold_parts<OKC>(a, a.opart, a.cnt + t, t * 16, 16);
 }
 
 // Gate and up rows t*64 .. t*64 + 63 of expert e (dense layers: of the dense MLP) for the sequences that
@@ -663,8 +718,9 @@ __global__ void __launch_bounds__(BNT) bk_down(const BArgs a, int l) {
     float v = 0.f;
 #pragma unroll
     for (int w = 0; w < BNW; ++w) v += red[w][tile][ln][r];
-    gp(a.dpart)[((size_t)c * BT + q) * a.H + t * 64 + rr] = v;
+    pstore(a.dpart + ((size_t)c * BT + q) * a.H + t * 64 + rr, v);
   }
+  fold_parts<DKC>(a, a.dpart, a.cnt + a.H / 16 + t, t * 64, 64);
 }
 
 // lm_head (bf16) rows of this workgroup in 16-row tiles; wave w computes four tiles over half of the

@@ -86,7 +86,7 @@ struct KDyn {
 // ordinary kernels per layer whose contractions run on MFMA with the
 // sequences as the 16 columns.
 constexpr int BT = 16;                  // sequences per pass (MFMA columns)
-constexpr int ATT_P = 128;              // cached positions per attention split of the batched path
+constexpr int ATT_P = 64;               // cached positions per attention split of the batched path
 constexpr int MAX_SPLITS = 1024;        // attention splits per sequence (max_tokens <= ATT_P * MAX_SPLITS)
 constexpr int OKC = 2;                  // o_proj input chunks (partial sums added by the next norm)
 constexpr int DKC = 16;                 // MoE down expert chunks / dense down input chunks
@@ -127,6 +127,7 @@ struct BArgs {
   float* wsel;           // [BT][K] their weights
   unsigned long long* amax;  // [BT] packed argmax keys
   uint32_t* done;        // workgroups finished with lm_head
+  uint32_t* cnt;         // [H/16 + H/64] workgroups finished per o_proj row tile, then per down row block
   // debug outputs (indexed by cache sequence), or null
   float* dbg_logits;
   int32_t* dbg_routes;

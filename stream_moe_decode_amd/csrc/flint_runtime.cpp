@@ -325,8 +325,8 @@ int batch_scratch(flint_ctx* c, flint_kv* kv) {
   const size_t sx = r256(BT * H * 4), sact = r256(BT * (size_t)a.astride * 2), sq = r256(BT * QD * 4);
   const size_t spart = r256((size_t)BT * cfg.n_q_heads * a.nsmax * (cfg.head_dim + 2) * 4);
   const size_t sop = r256(OKC * BT * H * 4), sdp = r256(DKC * BT * H * 4), sh = r256(BT * (size_t)a.hstride * 2);
-  const size_t ssel = r256(BT * MAX_K * 4), sam = r256(BT * 8 + 64);
-  const size_t total = sx + sact + sq + spart + sop + sdp + sh + 2 * ssel + sam;
+  const size_t ssel = r256(BT * MAX_K * 4), sam = r256(BT * 8 + 64), scnt = r256((H / 16 + H / 64) * 4);
+  const size_t total = sx + sact + sq + spart + sop + sdp + sh + 2 * ssel + sam + scnt;
   if (hipMalloc(&kv->bscratch, total) != hipSuccess) {
     kv->bscratch = nullptr;
     return fail(FLINT_ENOMEM, "batched-path scratch of %zu bytes", total);
@@ -348,6 +348,7 @@ int batch_scratch(flint_ctx* c, flint_kv* kv) {
   a.wsel = (float*)take(ssel);
   a.amax = (unsigned long long*)take(sam);
   a.done = (uint32_t*)(a.amax + BT);
+  a.cnt = (uint32_t*)take(scnt);
   if (hipMemsetAsync(kv->bscratch, 0, total, c->stream) != hipSuccess || hipStreamSynchronize(c->stream) != hipSuccess)
     return fail(FLINT_EHIP, "batched-path scratch initialisation failed");
   return FLINT_OK;
