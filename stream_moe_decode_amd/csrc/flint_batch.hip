@@ -657,9 +657,9 @@ __global__ void __launch_bounds__(BNT) bk_down(const BArgs a, int l) {
 #pragma unroll
   for (int q = 0; q < 4; ++q) acc[q] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   if (dense) {
-    // items of 128 inputs (int4: one chunk, bf16: four)
-    constexpr int IC = 128 / kChunkIn<WT>;
-    const int NI = a.DI / 128, ib = part(NI, DKC, c), ie = part(NI, DKC, c + 1);
+    // items of 256 inputs (int4: two chunks, bf16: eight)
+    constexpr int IC = 256 / kChunkIn<WT>;
+    const int NI = a.DI / 256, ib = part(NI, DKC, c), ie = part(NI, DKC, c + 1);
     auto rowmap = [&](int q, int m) -> long long { return (long long)l * a.H + t * 64 + q * 16 + m; };
     auto tile_of = [&](int q) -> long long { return ((long long)l * a.H >> 4) + t * 4 + q; };
     const uint16_t* col = n < a.B ? a.h + (size_t)n * a.hstride : nullptr;
@@ -676,9 +676,9 @@ __global__ void __launch_bounds__(BNT) bk_down(const BArgs a, int l) {
     __syncthreads();
     // the chunk's experts that some sequence picked, in index order
     const unsigned long long mk = emask & ((ee >= 64 ? ~0ull : (1ull << ee) - 1ull) & ~((1ull << eb) - 1ull));
-    // items of 128 inputs (int4: one chunk, bf16: four) of each picked expert
-    constexpr int IC = 128 / kChunkIn<WT>;
-    const int ne = __builtin_popcountll(mk), NI = a.EI / 128, lm = l - a.n_dense;
+    // items of 256 inputs (int4: two chunks, bf16: eight) of each picked expert
+    constexpr int IC = 256 / kChunkIn<WT>;
+    const int ne = __builtin_popcountll(mk), NI = a.EI / 256, lm = l - a.n_dense;
     int e = -1, ei = -1, sl = -1;
     float wn = 0.f;
     for (int it = wave; it < ne * NI; it += BNW) {

@@ -471,7 +471,7 @@ int flint_decode_init(const flint_config* cfg, const flint_weights* w, void* hip
   // the batched path: bf16 activations, 128-dim heads with at most 4 query heads per kv head (attention
   // scores on MFMA), row counts in whole 16-row tiles and 64-row gate/up blocks
   c->batch_ok = cfg->weight_type != FLINT_W_F32 && hd == 128 && cfg->n_q_heads / cfg->n_kv_heads <= 4 &&
-                H % 128 == 0 && QD % 128 == 0 && (ND == 0 || DI % 128 == 0) && (NM == 0 || EI % 128 == 0) &&
+                H % 128 == 0 && QD % 128 == 0 && (ND == 0 || DI % 256 == 0) && (NM == 0 || EI % 256 == 0) &&
                 V % 16 == 0 &&
                 !getenv("FLINT_NO_BATCH_PATH");
   if (c->batch_ok && wt == FLINT_W_INT4G64) {  // int4 scales regrouped by 4 rows for the batched contractions
