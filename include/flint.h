@@ -120,7 +120,9 @@ typedef struct flint_debug {
                            3 q gathered, 4 attention partial published, 5 splits merged, 6 merged
                            output gathered, 7 o_proj published, 8 residual gathered, 9 post norm,
                            10 router, 11 top-k (10 and 11 are 0 on dense layers), 12 SwiGLU
-                           published, 13 SwiGLU gathered, 14 MLP residual published, 15 gathered */
+                           published, 13 SwiGLU gathered, 14 MLP residual published, 15 gathered.
+                           The persistent kernel only (several sequences: not written) */
+  float* router_logits; /* [batch][n_layers][n_experts] router logits (0 on dense layers) */
 } flint_debug;
 
 /* ------------------------------------------------------------- entry points */

@@ -73,7 +73,7 @@ def lib():
         L.oracle_argmax.argtypes = [vp, i64]
         L.oracle_argmax.restype = i32
         L.oracle_attention_head.argtypes = [vp, vp, vp, i32, i32, i64, vp]
-        L.oracle_layer.argtypes = [vp, vp, vp, vp, i32, i32, i32, vp, vp, dbl, vp, vp, vp, vp]
+        L.oracle_layer.argtypes = [vp, vp, vp, vp, i32, i32, i32, vp, vp, dbl, vp, vp, vp, vp, vp]
         L.oracle_layer.restype = i32
         L.oracle_embed.argtypes = [vp, vp, i32, vp]
         L.oracle_head.argtypes = [vp, vp, vp, vp, i32, vp, vp, vp]
@@ -260,8 +260,11 @@ class Oracle:
         lib().oracle_embed(ctypes.byref(E), _p(toks), toks.size, _p(x))
         return x
 
-    def layer(self, l: int, seq: int, x: np.ndarray, p0: int, ref_routes=None, tie_eps: float = 1e-3):
-        """Run layer l over the block x ([n][hidden], modified) at positions p0.. of sequence seq."""
+    def layer(self, l: int, seq: int, x: np.ndarray, p0: int, ref_routes=None, tie_eps: float = 1e-3, ref_z=None):
+        """Run layer l over the block x ([n][hidden], modified) at positions p0.. of sequence seq.
+
+        ref_routes [n][top_k] / ref_z [n][n_experts]: another implementation's routes and router logits
+        (see ``oracle_layer``: a different set is adopted when it is a valid top-k within the tolerance)."""
         n = x.shape[0]
         keep = []
         L = self._olayer(l, keep)
@@ -271,8 +274,10 @@ class Oracle:
         flags = np.zeros(n, np.int32)
         gap = np.full(n, np.inf, np.float32)
         ref = None if ref_routes is None else np.ascontiguousarray(ref_routes, np.int32).reshape(n, K)
+        rz = None if ref_z is None else np.ascontiguousarray(ref_z, np.float32).reshape(n, self.cfg.n_experts)
         rc = lib().oracle_layer(ctypes.byref(self.ocfg), ctypes.byref(L), _p(self.K[l][seq]), _p(self.V[l][seq]),
-                                self.cap, p0, n, _p(x), _p(ref), tie_eps, _p(routes), _p(rw), _p(flags), _p(gap))
+                                self.cap, p0, n, _p(x), _p(ref), tie_eps, _p(rz), _p(routes), _p(rw), _p(flags),
+                                _p(gap))
         if rc != 0:
             raise ValueError("oracle_layer: capacity exceeded")
         return routes, rw, flags, gap
@@ -289,7 +294,7 @@ class Oracle:
         return logits, ids, gap
 
     def forward(self, seq: int, toks, ref_routes=None, tie_eps: float = 1e-3, want_logits: bool = True,
-                resid_layer: int | None = None):
+                resid_layer: int | None = None, ref_z=None):
         """Block pass over known tokens at positions len..len+n-1; advances len.
 
         ref_routes: [n][n_layers][top_k] candidate routes (see ``oracle_layer``).
@@ -310,7 +315,8 @@ class Oracle:
         resid = None
         for l in range(Ln):
             ref = None if ref_routes is None else np.ascontiguousarray(np.asarray(ref_routes)[:, l, :])
-            r, w, f, g = self.layer(l, seq, x, p0, ref, tie_eps)
+            rz = None if ref_z is None else np.ascontiguousarray(np.asarray(ref_z)[:, l, :])
+            r, w, f, g = self.layer(l, seq, x, p0, ref, tie_eps, rz)
             routes[:, l], rw[:, l], flags[:, l], rgap[:, l] = r, w, f, g
             if resid_layer is not None and l == resid_layer:
                 resid = x.copy()

@@ -189,15 +189,19 @@ static double silu(double u) { return u / (1.0 + exp(-u)); }
  *
  * Routing (MoE layers): the oracle selects its own top-k.  If ref_routes
  * ([n][top_k]) is given and names a different set, that set is accepted only
- * when it is a valid top-k within tie_eps: min over the set >= max outside the
- * set - tie_eps * max|z|.  Then it is adopted (flag 1); otherwise the oracle
- * keeps its own set (flag 2).  Equal sets: flag 0.
+ * when it is a valid top-k within eps: min over the set >= max outside the
+ * set - eps * max|z|.  Then it is adopted (flag 1); otherwise the oracle
+ * keeps its own set (flag 2).  Equal sets: flag 0.  eps = tie_eps, or, when the
+ * reference's own router logits ref_z ([n][n_experts]) are given, the larger of
+ * tie_eps and twice their largest deviation from the oracle's, max|ref_z - z| /
+ * max|z| (a set that is a top-k of the reference's logits is then accepted
+ * exactly when it is one within the measured disagreement).
  * routes_out [n][top_k], rw_out [n][top_k], flags_out [n], gap_out [n]
  * ((z_(k) - z_(k+1)) / max|z|) may each be NULL.
  */
 int32_t oracle_layer(const OCfg* cfg, const OLayer* L, float* Kc, float* Vc, int32_t cap, int32_t p0, int32_t n,
-                     double* x, const int32_t* ref_routes, double tie_eps, int32_t* routes_out, float* rw_out,
-                     int32_t* flags_out, float* gap_out) {
+                     double* x, const int32_t* ref_routes, double tie_eps, const float* ref_z, int32_t* routes_out,
+                     float* rw_out, int32_t* flags_out, float* gap_out) {
   const int32_t H = cfg->hidden, d = cfg->head_dim, nq = cfg->n_q_heads, nkv = cfg->n_kv_heads;
   const int32_t group = nq / nkv, bf = cfg->act_bf16;
   if (p0 + n > cap) return 1;
@@ -269,7 +273,13 @@ int32_t oracle_layer(const OCfg* cfg, const OLayer* L, float* Kc, float* Vc, int
               if (in_ref[e]) min_in = std::min(min_in, z[e]);
               else max_out = std::max(max_out, z[e]);
             }
-            valid = min_in >= max_out - tie_eps * zmax;
+            double eps = tie_eps;
+            if (ref_z) {
+              double dz = 0.0;
+              for (int32_t e = 0; e < E; ++e) dz = std::max(dz, fabs((double)ref_z[(size_t)i * E + e] - z[e]));
+              eps = std::max(eps, zmax > 0 ? 2.0 * dz / zmax : 0.0);
+            }
+            valid = min_in >= max_out - eps * zmax;
           }
           if (valid) {
             flag = 1;

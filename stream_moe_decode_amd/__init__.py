@@ -55,7 +55,7 @@ class Weights(ctypes.Structure):
 class Debug(ctypes.Structure):
     _fields_ = [("logits", ctypes.c_void_p), ("routes", ctypes.c_void_p), ("route_w", ctypes.c_void_p),
                 ("resid", ctypes.c_void_p), ("resid_layer", ctypes.c_int32), ("pad", ctypes.c_int32),
-                ("phase_ts", ctypes.c_void_p)]
+                ("phase_ts", ctypes.c_void_p), ("router_logits", ctypes.c_void_p)]
 
 
 _lib = None

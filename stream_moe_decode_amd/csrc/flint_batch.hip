@@ -300,6 +300,7 @@ __global__ void __launch_bounds__(BNT) bk_norm(const BArgs a, int l, int mode) {
   }
   if (mode != NORM_POST) return;
   if (l < a.n_dense) {  // dense layer: no routing
+    if (a.dbg_z && tid < E) gp(a.dbg_z)[((size_t)seq * a.L + l) * E + tid] = 0.f;
     if (tid < a.K) {
       if (a.dbg_routes) gp(a.dbg_routes)[((size_t)seq * a.L + l) * a.K + tid] = -1;
       if (a.dbg_rw) gp(a.dbg_rw)[((size_t)seq * a.L + l) * a.K + tid] = 0.f;
@@ -343,6 +344,7 @@ __global__ void __launch_bounds__(BNT) bk_norm(const BArgs a, int l, int mode) {
   // top-k by rank (larger logit first, equal logits: lower index first): wave w counts the experts
   // 8 w .. 8 w + 7 that beat lane e's, the counts meet in LDS; weights: softmax over all experts
   const float zl = lane < E ? z[lane] : -INFINITY;
+  if (a.dbg_z && wave == 0 && lane < E) gp(a.dbg_z)[((size_t)seq * a.L + l) * E + lane] = zl;
   {
     int part = 0;
 #pragma unroll

@@ -60,6 +60,27 @@ template <int N> __device__ __forceinline__ void wait_vmem_n() {
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
 }
 __device__ __forceinline__ void wait_vmem() { wait_vmem_n<0>(); }
+// vmcnt(n) for a run-time n (waits for everything when n is outside 0..15)
+__device__ __forceinline__ void wait_vmem_dyn(int n) {
+  switch (n) {
+    case 1: wait_vmem_n<1>(); break;
+    case 2: wait_vmem_n<2>(); break;
+    case 3: wait_vmem_n<3>(); break;
+    case 4: wait_vmem_n<4>(); break;
+    case 5: wait_vmem_n<5>(); break;
+    case 6: wait_vmem_n<6>(); break;
+    case 7: wait_vmem_n<7>(); break;
+    case 8: wait_vmem_n<8>(); break;
+    case 9: wait_vmem_n<9>(); break;
+    case 10: wait_vmem_n<10>(); break;
+    case 11: wait_vmem_n<11>(); break;
+    case 12: wait_vmem_n<12>(); break;
+    case 13: wait_vmem_n<13>(); break;
+    case 14: wait_vmem_n<14>(); break;
+    case 15: wait_vmem_n<15>(); break;
+    default: wait_vmem_n<0>(); break;
+  }
+}
 // wait until this wave's LDS operations have completed (lgkmcnt(0))
 __device__ __forceinline__ void wait_lds() { __builtin_amdgcn_s_waitcnt(0xC07F); }
 __device__ __forceinline__ void dma16(const void* g, void* l) {

@@ -80,6 +80,7 @@ struct KDyn {
   float* dbg_resid;
   int dbg_resid_layer;
   uint64_t* dbg_ts;
+  float* dbg_z;          // [n_layers][n_experts] router logits of this sequence
 };
 
 // Batched decode: up to BT sequences per pass go through a sequence of
@@ -134,6 +135,7 @@ struct BArgs {
   float* dbg_rw;
   float* dbg_resid;
   int dbg_resid_layer;
+  float* dbg_z;
 };
 
 // Enqueue one batched decode pass (every layer and the head) on `stream`.

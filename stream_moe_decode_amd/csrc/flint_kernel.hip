@@ -143,10 +143,11 @@ template <int WT> __device__ __forceinline__ void act_sums(const uint32_t* act, 
 }
 // RMSNorm of the residual with the weights sm.gn (brought in by this
 // workgroup's DMA), as the next GEMV input actA in the layout of OW.
+// later: vector memory operations this wave issued after the norm weights' DMA (they may stay in flight).
 template <int WT, int OW = WT>
-__device__ __forceinline__ void rmsnorm_act(Smem& sm, int H, float eps, bool sums) {
+__device__ __forceinline__ void rmsnorm_act(Smem& sm, int H, float eps, bool sums, int later = 0) {
   const int tid = threadIdx.x;
-  wait_vmem();  // this wave's part of sm.gn has landed; block_sum's barrier publishes it
+  wait_vmem_dyn(later);  // this wave's part of sm.gn has landed; block_sum's barrier publishes it
   float ss = 0.f;
   for (int e = tid; e < H; e += NT) ss += sm.xres[e] * sm.xres[e];
   ss = block_sum(sm, ss);
@@ -462,12 +463,13 @@ __device__ __forceinline__ void compute_static_rows(const LStage& st, const Geo&
   }
 }
 
-// A staged GEMV of the static shape whose items fit one round of NIS items per wave.
+// A staged GEMV of the static shape whose items fit one round of NIS items per wave; later: vector
+// memory operations this wave issued after the stage's DMA (they may stay in flight).
 template <int WT, int CPLR, int NIS, class RowFn, class OutFn>
 __device__ __forceinline__ void gemv_static(const LStage& st, const Geo& g, bool issued, const ActRegs<WT, CPLR>& ar,
-                                            RowFn rowfn, OutFn outfn) {
+                                            RowFn rowfn, OutFn outfn, int later = 0) {
   if (!issued) lstage_issue_static<WT, NIS>(st, g, 0, rowfn, g.wave);
-  wait_vmem();
+  wait_vmem_dyn(issued ? later : 0);
   compute_static<WT, CPLR, NIS>(st, g, 0, ar, outfn);
 }
 
@@ -475,11 +477,11 @@ __device__ __forceinline__ void gemv_static(const LStage& st, const Geo& g, bool
 // time, 0 = not) fit the capacity CAP, else the general rounds.
 template <int WT, int CPLR, int NIS, int CAP, class RowFn, class OutFn>
 __device__ __forceinline__ void gemv_auto(const LStage& st, const Geo& g, bool issued, const ActRegs<WT, CPLR>& ar,
-                                          RowFn rowfn, OutFn outfn) {
+                                          RowFn rowfn, OutFn outfn, int later = 0) {
   if constexpr (CPLR > 0 && NIS > 0 && NIS <= CAP && NIS / CPLR <= 16)
-    gemv_static<WT, CPLR, NIS>(st, g, issued, ar, rowfn, outfn);
+    gemv_static<WT, CPLR, NIS>(st, g, issued, ar, rowfn, outfn, later);
   else
-    gemv_lds<WT, CPLR>(st, g, issued, ar, rowfn, outfn);
+    gemv_lds<WT, CPLR>(st, g, issued, ar, rowfn, outfn);  // waits for everything (later ignored)
 }
 
 // Compute round `round` of this wave's items.  CPLR > 0: every row has CPLR
@@ -827,19 +829,25 @@ __global__ void __launch_bounds__(NT, 1) decode_kernel(const KStatic* __restrict
   const int dpb = part(DI_ / 2, G, W), dpe = part(DI_ / 2, G, W + 1);  // dense SwiGLU pairs
   const int xpb = part(K_ * EI_ / 2, G, W), xpe = part(K_ * EI_ / 2, G, W + 1);  // expert pairs
   const float inv_ei = 1.0f / (float)EI_, inv_k = 1.0f / (float)K_;
-  // QKV weights and the first attention chunk of layer l (into the shared region)
-  auto issue_attn_front = [&](int l) {
-    issue_auto<WT, NI_QKV, QKV_CAP>(lstage(sm.u.att.sq), gq, qkv_rowfn(l));
-    if (attn && t1 > t0) {
-      const size_t cb = (((size_t)l * B + seq) * nkv + aj) * kvstride * ebytes;
-      const int np0 = min(CHP, t1 - t0);
-      if constexpr (MFMA_QK) k_issue_mfma(sm.u.att.kbuf, kc + cb, t0, np0);
-      else kv_issue(sm.u.att.kbuf, kc + cb, t0, np0, rowb);
-      kv_issue(sm.u.att.vbuf, vc + cb, t0, np0, rowb);
-    }
+  // QKV weights of layer l and the first attention chunk of layer l (into the shared region); the chunk's
+  // issue returns the number of DMA instructions this wave issued (waits that need only earlier loads
+  // leave them in flight)
+  auto issue_qkv = [&](int l) { issue_auto<WT, NI_QKV, QKV_CAP>(lstage(sm.u.att.sq), gq, qkv_rowfn(l)); };
+  auto issue_kv_front = [&](int l) -> int {
+    if (!attn || t1 <= t0) return 0;
+    const size_t cb = (((size_t)l * B + seq) * nkv + aj) * kvstride * ebytes;
+    const int np0 = min(CHP, t1 - t0);
+    if constexpr (MFMA_QK) k_issue_mfma(sm.u.att.kbuf, kc + cb, t0, np0);
+    else kv_issue(sm.u.att.kbuf, kc + cb, t0, np0, rowb);
+    kv_issue(sm.u.att.vbuf, vc + cb, t0, np0, rowb);
+    auto per_wave = [&](int n) { return n > wave ? (n - wave + NW - 1) / NW : 0; };
+    const int nk = MFMA_QK ? (np0 + 15) / 16 * 4 : (np0 * rowb / 16 + 63) / 64;
+    return per_wave(nk) + per_wave((np0 * rowb / 16 + 63) / 64);
   };
+  int kv_later = 0;  // this layer's front chunk DMAs, issued after the previous layer's last exchange
 
-  issue_attn_front(0);
+  issue_qkv(0);
+  issue_kv_front(0);
   gn_issue(sm, p_anorm, H);
   for (int e = tid; e < H; e += NT) {  // embedding row -> residual
     if constexpr (kAct32<WT>)
@@ -863,14 +871,14 @@ __global__ void __launch_bounds__(NT, 1) decode_kernel(const KStatic* __restrict
     const int lmoe = l - ks.n_dense;
 
     // ---------------- input RMSNorm (recomputed by every workgroup)
-    rmsnorm_act<WT>(sm, H, ks.eps, ASUM_A);
+    rmsnorm_act<WT>(sm, H, ks.eps, ASUM_A, kv_later);
     if (stamp) stamp[0] = now();
 
     // ---------------- QKV rows (staged during the previous layer), RoPE, publish, KV append
     {
       const auto ar = act_regs<WT, CP_QKV>(gq, sm.actA, sm.asumA);
       gemv_auto<WT, CP_QKV, NI_QKV, QKV_CAP>(lstage(sm.u.att.sq), gq, true, ar, qkv_rowfn(l),
-                                             [&](int q, float v) { sm.ytmp[q] = v; });
+                                             [&](int q, float v) { sm.ytmp[q] = v; }, kv_later);
     }
     __syncthreads();
     if (stamp) stamp[1] = now();
@@ -1302,6 +1310,8 @@ __global__ void __launch_bounds__(NT, 1) decode_kernel(const KStatic* __restrict
       ok = gather_flat(sm, copy_of(x_z, E_, par), E_, tag + 6, [&](int i, uint32_t p) { sm.z[i] = __uint_as_float(p); },
                        wt);
       if (!ok) break;
+      if (d.dbg_z && W == 0)
+        for (int e = tid; e < E_; e += NT) gp(d.dbg_z)[(size_t)l * E_ + e] = sm.z[e];
       if (stamp) stamp[10] = now();
       // top-k by rank, in every wave (identical results; a wave reads only its own writes):
       // lane e counts the experts that beat it (larger logit, or equal logit and lower index)
@@ -1470,12 +1480,14 @@ __global__ void __launch_bounds__(NT, 1) decode_kernel(const KStatic* __restrict
       }
       return __float_as_uint(sm.xres[drb + q] + y);
     });
-    // the shared region is free: the next layer's QKV weights and first attention chunk load during the exchange
-    if (l + 1 < L) issue_attn_front(l + 1);
+    // the shared region is free: the next layer's QKV weights load during the exchange; its first
+    // attention chunk after it (the exchange's loads would otherwise return only after the chunk)
+    if (l + 1 < L) issue_qkv(l + 1);
     if (stamp) stamp[14] = now();
     ok = gather_flat(sm, copy_of(x_res2, H, par), H, tag + 5,
                      [&](int i, uint32_t p) { sm.xres[i] = __uint_as_float(p); }, wt);
     if (!ok) break;
+    kv_later = l + 1 < L ? issue_kv_front(l + 1) : 0;
     if (stamp) stamp[15] = now();
     if (d.dbg_resid && W == 0 && l == d.dbg_resid_layer)
       for (int e = tid; e < H; e += NT) gp(d.dbg_resid)[e] = sm.xres[e];

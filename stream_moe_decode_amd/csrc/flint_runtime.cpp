@@ -227,6 +227,7 @@ int launch(flint_ctx* c, flint_kv* kv, const int32_t* tokens, int tok_idx, int s
     a.dbg_resid = dbg->resid ? dbg->resid + (size_t)seq * H : nullptr;
     a.dbg_resid_layer = dbg->resid_layer;
     a.dbg_ts = seq == 0 ? dbg->phase_ts : nullptr;
+    a.dbg_z = dbg->router_logits ? dbg->router_logits + (size_t)seq * L * c->cfg.n_experts : nullptr;
   }
   HIPCHECK(launch_decode(c->cfg.weight_type, c->stat, c->kdev, a, c->grid, c->stream));
   c->launches++;
@@ -628,6 +629,7 @@ int flint_decode_step_debug(flint_ctx* c, const int32_t* tokens, flint_kv* kv, i
     a.dbg_rw = dbg ? dbg->route_w : nullptr;
     a.dbg_resid = dbg ? dbg->resid : nullptr;
     a.dbg_resid_layer = dbg ? dbg->resid_layer : -1;
+    a.dbg_z = dbg ? dbg->router_logits : nullptr;
     for (int s0 = 0; s0 < kv->batch; s0 += BT) {
       a.seq0 = s0;
       a.B = std::min(BT, kv->batch - s0);

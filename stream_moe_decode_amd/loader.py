@@ -174,7 +174,8 @@ class DeviceKV:
             self.handle = None
 
 
-def make_debug(cfg, batch: int, device, logits=True, routes=True, resid_layer=None, phase_ts=False) -> tuple:
+def make_debug(cfg, batch: int, device, logits=True, routes=True, resid_layer=None, phase_ts=False,
+               router_logits=None) -> tuple:
     """Allocate the optional outputs of decode_step_debug; returns (Debug, dict of tensors)."""
     t = {}
     dbg = Debug()
@@ -192,4 +193,7 @@ def make_debug(cfg, batch: int, device, logits=True, routes=True, resid_layer=No
     if phase_ts:
         t["phase_ts"] = torch.zeros((cfg.n_layers + 1, 16), dtype=torch.int64, device=device)
         dbg.phase_ts = t["phase_ts"].data_ptr()
+    if router_logits if router_logits is not None else routes:  # with the routes unless asked otherwise
+        t["router_logits"] = torch.zeros((batch, cfg.n_layers, cfg.n_experts), dtype=torch.float32, device=device)
+        dbg.router_logits = t["router_logits"].data_ptr()
     return dbg, t

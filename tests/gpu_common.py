@@ -66,14 +66,18 @@ class Stepper:
         g_logits = self.t["logits"][self.seq].cpu().numpy()
         g_routes = self.t["routes"][self.seq].cpu().numpy()
         g_id = int(self.out[self.seq].item())
-        self.report.append(check_step(cfg, self.orc, self.seq, token, g_logits, g_routes, g_id))
+        g_z = self.t["router_logits"][self.seq].cpu().numpy() if "router_logits" in self.t else None
+        self.report.append(check_step(cfg, self.orc, self.seq, token, g_logits, g_routes, g_id, g_z=g_z))
         return g_id
 
 
-def check_step(cfg, orc, seq, token, g_logits, g_routes, g_id, what=""):
+def check_step(cfg, orc, seq, token, g_logits, g_routes, g_id, what="", g_z=None):
     """The oracle's step of sequence `seq` on `token` (following the GPU's routes and token where the
-    oracle's own margin is below TIE_EPS) against the GPU's logits, routes and id; returns a report."""
-    r = orc.forward(seq, np.array([token], np.int32), ref_routes=g_routes[None], tie_eps=TIE_EPS)
+    oracle's own margin is below the tolerance) against the GPU's logits, routes and id; returns a report.
+    g_z: the GPU's router logits [n_layers][n_experts], which widen the route tolerance of a layer to
+    twice their measured deviation from the oracle's."""
+    r = orc.forward(seq, np.array([token], np.int32), ref_routes=g_routes[None], tie_eps=TIE_EPS,
+                    ref_z=None if g_z is None else g_z[None])
     err = rel_err(g_logits, r["logits"][0])
     moe = [l for l in range(cfg.n_layers) if l >= cfg.n_dense_layers]
     flags = r["route_flags"][0, moe] if moe else np.zeros(0)

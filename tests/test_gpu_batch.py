@@ -48,10 +48,10 @@ def _run(cfg, batch, steps):
         decode_step_debug(model.ctx, tok.data_ptr(), kv.handle, out.data_ptr(), dbg)
         sync(model.ctx)
         g_logits, g_routes = t["logits"].cpu().numpy(), t["routes"].cpu().numpy()
-        g_ids, toks = out.cpu().numpy(), tok.cpu().numpy()
+        g_ids, toks, g_z = out.cpu().numpy(), tok.cpu().numpy(), t["router_logits"].cpu().numpy()
         for b in range(batch):
             reports.append(check_step(cfg, orc, b, int(toks[b]), g_logits[b], g_routes[b], int(g_ids[b]),
-                                      what=f"step {step} seq {b}: "))
+                                      what=f"step {step} seq {b}: ", g_z=g_z[b]))
         tok.copy_(out)
     got = np.array(kv_get_lengths(kv.handle, batch))
     model.free()

@@ -110,7 +110,8 @@ def test_int4_batch16_fullsize_sampled():
     sync(model.ctx)
     g_logits, g_routes, g_ids, toks = (t["logits"].cpu().numpy(), t["routes"].cpu().numpy(), out.cpu().numpy(),
                                        tok.cpu().numpy())
+    g_z = t["router_logits"].cpu().numpy()
     for b in check:
         check_step(cfg, orc, int(b), int(toks[b]), g_logits[b], g_routes[b], int(g_ids[b]),
-                   what=f"sequence {b} ({lens[b]} positions): ")
+                   what=f"sequence {b} ({lens[b]} positions): ", g_z=g_z[b])
     model.free()
