@@ -167,9 +167,14 @@ int flint_kv_layer_ptrs(flint_kv* kv, int32_t layer, void** k, void** v);
  * tokens[b] at position len[b], append its K/V, write the argmax token id to
  * out_ids[b] (device) and increment len[b].  tokens and out_ids may alias,
  * so out_ids can be fed back as the next step's tokens without a host round
- * trip.  Errors: FLINT_EINVAL, FLINT_ECAPACITY (len[b] + 1 > max_tokens, from
- * the host mirror), FLINT_EHIP, and FLINT_ETIMEOUT / FLINT_EDEVICE latched by
- * an earlier step (reported once, then cleared).
+ * trip.  One sequence: the persistent kernel.  Several (bf16 / int4 models
+ * with 128-dim heads): passes of up to 16 sequences on the batched MFMA path,
+ * which on the first such cache makes the context's tiled weight copies (the
+ * "batch-16 ragged" step of the pages' concurrent-client workload, section 4
+ * of "Flint Inference on Apple Silicon: rec Megakernel and Tempo9 Compared").
+ * Errors: FLINT_EINVAL, FLINT_ENOMEM, FLINT_ECAPACITY (len[b] + 1 > max_tokens,
+ * from the host mirror), FLINT_EHIP, and FLINT_ETIMEOUT / FLINT_EDEVICE latched
+ * by an earlier step (reported once, then cleared).
  */
 int flint_decode_step(flint_ctx* ctx, const int32_t* tokens, flint_kv* kv, int32_t* out_ids);
 
@@ -181,8 +186,10 @@ int flint_decode_step_debug(flint_ctx* ctx, const int32_t* tokens, flint_kv* kv,
  * Process n (1 <= n <= 4096) known device tokens of sequence seq at positions
  * len[seq] .. len[seq] + n - 1 (causal attention over the cache and the
  * chunk), append their K/V, write the greedy id after the last position to
- * out_id[0] (device) and add n to len[seq].  Errors: FLINT_EINVAL,
- * FLINT_ECAPACITY, FLINT_EHIP.
+ * out_id[0] (device) and add n to len[seq].  bf16 / int4 models with 128-dim
+ * heads run 16 tokens per batched MFMA pass (the first call makes the tiled
+ * weight copies and the cache's scratch); others, one persistent launch per
+ * token.  Errors: FLINT_EINVAL, FLINT_ENOMEM, FLINT_ECAPACITY, FLINT_EHIP.
  */
 int flint_prefill_chunk(flint_ctx* ctx, flint_kv* kv, int32_t seq, const int32_t* tokens, int32_t n,
                         int32_t* out_id);

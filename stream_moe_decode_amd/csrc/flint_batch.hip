@@ -181,6 +181,13 @@ __device__ __forceinline__ float bsum(float v, float* wred) {
 
 enum { NORM_EMBED = 0, NORM_INPUT = 1, NORM_POST = 2, NORM_FINAL = 3 };
 
+// Cache sequence and position of column n of the pass (decode: sequence seq0 + n at its length;
+// prefill: sequence seq0 at its length + n).
+__device__ __forceinline__ int col_seq(const BArgs& a, int n) { return a.prefill ? a.seq0 : a.seq0 + n; }
+__device__ __forceinline__ int col_pos(const BArgs& a, int n) {
+  return a.prefill ? gp(a.len)[a.seq0] + n : gp(a.len)[a.seq0 + n];
+}
+
 // Partial sums cross workgroups (and XCDs) through memory: written with system-scope stores, which go
 // through the writer's L2, and read back with system-scope loads, which do not take a stale line from the
 // reader's L2.
@@ -255,7 +262,7 @@ __global__ void __launch_bounds__(BNT) bk_norm(const BArgs a, int l, int mode) {
   const float* g = mode == NORM_POST ? a.pnorm + (size_t)l * H : (mode == NORM_FINAL ? a.fnorm : a.anorm + (size_t)l * H);
   float xv[EPT], gv[EPT];
   if (mode == NORM_EMBED) {
-    int tok = gp(a.tokens)[seq];
+    int tok = gp(a.tokens)[a.prefill ? a.tok0 + n : seq];
     if (tok < 0 || tok >= a.V) {
       if (tid == 0) latch(a, ERR_TOKEN);
       tok = 0;
@@ -392,7 +399,7 @@ __global__ void __launch_bounds__(BNT) bk_qkv(const BArgs a, int l) {
   const f32x4_t sum = sum_waves(acc[0], red);
   if (wave != 0) return;
   float y[4] = {sum[0], sum[1], sum[2], sum[3]};
-  const int pos = n < a.B ? gp(a.len)[a.seq0 + n] : 0;
+  const int pos = n < a.B ? col_pos(a, n) : 0;
   if (hh < a.nq + a.nkv) {  // RoPE on q and k heads: (y_i, y_{i + hd/2}) rotated by the angle of pair i
     float p[4];
 #pragma unroll
@@ -414,7 +421,7 @@ __global__ void __launch_bounds__(BNT) bk_qkv(const BArgs a, int l) {
     } else {
       const bool isk = hh < a.nq + a.nkv;
       const int j = isk ? hh - a.nq : hh - a.nq - a.nkv;
-      const size_t off = ((((size_t)l * a.Bc + a.seq0 + n) * a.nkv + j) * a.cap + pos) * hd + d;
+      const size_t off = ((((size_t)l * a.Bc + col_seq(a, n)) * a.nkv + j) * a.cap + pos) * hd + d;
       gp(reinterpret_cast<uint16_t*>(isk ? a.kc : a.vc))[off] = (uint16_t)f2bf(y[r]);
     }
   }
@@ -432,10 +439,10 @@ __global__ void __launch_bounds__(BNT) bk_attn(const BArgs a, int l) {
   __shared__ float mst[4], lst[4];
   const int s = blockIdx.x, j = blockIdx.y, n = blockIdx.z;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int T = gp(a.len)[a.seq0 + n] + 1, t0 = s * ATT_P;
+  const int T = col_pos(a, n) + 1, t0 = s * ATT_P;
   if (t0 >= T) return;
   const int np = min(ATT_P, T - t0), hd = 128, Gq = a.nq / a.nkv;
-  const size_t cb = (((size_t)l * a.Bc + a.seq0 + n) * a.nkv + j) * (size_t)a.cap * hd * 2;
+  const size_t cb = (((size_t)l * a.Bc + col_seq(a, n)) * a.nkv + j) * (size_t)a.cap * hd * 2;
   k_issue_mfma(kbuf, a.kc + cb, t0, np);
   kv_issue(vbuf, a.vc + cb, t0, np, 256);
   const float qscale = 1.0f / sqrtf((float)hd);
@@ -536,7 +543,7 @@ __global__ void __launch_bounds__(128) bk_merge(const BArgs a) {
   __shared__ float ws[MAX_SPLITS];
   __shared__ float wm[2], wl[2];
   const int h = blockIdx.x, n = blockIdx.y, d = threadIdx.x, hd = a.hd;
-  const int T = gp(a.len)[a.seq0 + n] + 1, ns = min((T + ATT_P - 1) / ATT_P, MAX_SPLITS);
+  const int T = col_pos(a, n) + 1, ns = min((T + ATT_P - 1) / ATT_P, MAX_SPLITS);
   const float* p = a.part + ((size_t)n * a.nq + h) * a.nsmax * (hd + 2);
   float mloc = -INFINITY;
   for (int s = d; s < ns; s += 128) {
@@ -808,8 +815,14 @@ __global__ void __launch_bounds__(BNT) bk_head(const BArgs a) {
     if (prev == (uint32_t)G - 1) {  // last workgroup: publish the ids, advance the lengths, reset
       for (int q = 0; q < a.B; ++q) {
         const unsigned long long fin = __hip_atomic_exchange(gp(a.amax + q), 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        gp(a.out_ids)[a.seq0 + q] = (int32_t)(0xFFFFFFFFu - (uint32_t)(fin & 0xFFFFFFFFull));
-        gp(a.len)[a.seq0 + q] += 1;
+        const int32_t id = (int32_t)(0xFFFFFFFFu - (uint32_t)(fin & 0xFFFFFFFFull));
+        if (!a.prefill) {
+          gp(a.out_ids)[a.seq0 + q] = id;
+          gp(a.len)[a.seq0 + q] += 1;
+        } else if (q == a.B - 1) {  // prefill: the id after the last prompt token of the pass
+          gp(a.out_ids)[0] = id;
+          gp(a.len)[a.seq0] += a.B;
+        }
       }
       __hip_atomic_store(gp(a.done), 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }

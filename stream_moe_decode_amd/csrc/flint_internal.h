@@ -103,8 +103,10 @@ struct BArgs {
   const float* anorm;
   const float* pnorm;
   Mat qkv, o, dg, du, dd, router, eg, eu, ed;
-  // this pass: sequences seq0 .. seq0 + B - 1 of a cache of Bc sequences
-  int B, seq0, Bc, cap;
+  // this pass: sequences seq0 .. seq0 + B - 1 of a cache of Bc sequences, each at its own length; or
+  // (prefill) B consecutive prompt tokens tokens[tok0 ..] of sequence seq0 at positions len[seq0] ..,
+  // the greedy id after the last one written to out_ids[0]
+  int B, seq0, Bc, cap, prefill, tok0;
   uint8_t* kc;           // [L][Bc][nkv][cap][hd] bf16
   uint8_t* vc;
   const float2* rope;    // [cap][hd/2] (cos, sin)

@@ -620,7 +620,7 @@ int flint_decode_step_debug(flint_ctx* c, const int32_t* tokens, flint_kv* kv, i
   for (int b = 0; b < kv->batch; ++b)
     if (kv->hlen[b] + 1 > kv->max_tokens)
       return fail(FLINT_ECAPACITY, "sequence %d: length %d + 1 exceeds max_tokens %d", b, kv->hlen[b], kv->max_tokens);
-  if (kv->bscratch) {  // batched path: passes of up to BT sequences
+  if (kv->bscratch && kv->batch > 1) {  // batched path: passes of up to BT sequences
     BArgs a = kv->bargs;
     a.tokens = tokens;
     a.out_ids = out_ids;
@@ -660,6 +660,24 @@ int flint_prefill_chunk(flint_ctx* c, flint_kv* kv, int32_t seq, const int32_t* 
   if (kv->hlen[seq] + n > kv->max_tokens)
     return fail(FLINT_ECAPACITY, "sequence %d: length %d + %d exceeds max_tokens %d", seq, kv->hlen[seq], n,
                 kv->max_tokens);
+  if (c->batch_ok && !kv->bscratch && kv->max_tokens <= ATT_P * MAX_SPLITS) {
+    rc = batch_scratch(c, kv);
+    if (rc) return rc;
+  }
+  if (kv->bscratch) {  // batched path: up to BT prompt tokens per pass, causal over the shared cache
+    BArgs a = kv->bargs;
+    a.prefill = 1;
+    a.seq0 = seq;
+    a.tokens = tokens;
+    a.out_ids = out_id;
+    for (int i0 = 0; i0 < n; i0 += BT) {
+      a.tok0 = i0;
+      a.B = std::min(BT, n - i0);
+      HIPCHECK(launch_batch_pass(c->cfg.weight_type, a, c->stream));
+      kv->hlen[seq] += a.B;
+    }
+    return FLINT_OK;
+  }
   // positions in order; each launch writes its greedy id to out_id[0], the
   // last one is the id after the chunk
   for (int i = 0; i < n; ++i) {

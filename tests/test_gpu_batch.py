@@ -103,3 +103,38 @@ def test_batch_equals_single_sequence_steps():
         k1.free()
         model.kvs.remove(k1)
     model.free()
+
+
+def test_prefill_passes_match_oracle():
+    # a 40-token prompt through flint_prefill_chunk on the batched path (passes of 16, 16 and 8 tokens of
+    # one sequence, causal over the shared cache) after 100 resident positions, then 3 greedy steps
+    from gpu_common import Stepper
+    from stream_moe_decode_amd import prefill_chunk
+    cfg = SMALL
+    model = build(cfg)
+    res, n = 100, 40
+    cap = res + n + 8
+    kv = model.kv(1, cap)
+    orc = make_oracle(cfg, cap)
+    for l in range(cfg.n_layers):
+        k, v = synth.resident_kv(cfg, l, 0, res)
+        kv.load_resident(l, 0, k, v)
+        orc.set_resident(0, l, k, v)
+    kv.set_lengths([res])
+    orc.len[0] = res
+    prompt = synth.tokens(cfg, n, stream=13)
+    dev = model.device
+    toks = torch.from_numpy(prompt).to(dev)
+    out = torch.zeros(1, dtype=torch.int32, device=dev)
+    prefill_chunk(model.ctx, kv.handle, 0, toks.data_ptr(), n, out.data_ptr())
+    sync(model.ctx)
+    r = orc.forward(0, prompt)
+    gpu_id = int(out.item())
+    print("prefill: gpu id", gpu_id, "oracle id", int(r["ids"][-1]), "oracle gap", float(r["gap"][-1]))
+    assert gpu_id == int(r["ids"][-1]) or float(r["gap"][-1]) < 1e-2
+    assert kv_get_lengths(kv.handle, 1) == [res + n]
+    st = Stepper(cfg, model, kv, orc)
+    tok = gpu_id
+    for _ in range(3):
+        tok = st.step(tok)
+    model.free()
