@@ -194,6 +194,50 @@ def bench_batch(args, cfg):
     print(json.dumps(out), flush=True)
 
 
+def bench_prefill(args, cfg):
+    """Prompt processing: `--prefill N` tokens of one sequence through flint_prefill_chunk (chunks of at
+    most 4,096 tokens) on the model of `cfg` (one JSON line of its own; not the default workload)."""
+    import numpy as np
+    import torch
+    import synth
+    from stream_moe_decode_amd import kv_set_lengths, lib, prefill_chunk, sync
+    from stream_moe_decode_amd.loader import DeviceModel
+
+    lib()
+    n = args.prefill
+    t_gen = time.perf_counter()
+    model = DeviceModel(cfg, lambda l: synth.layer(cfg, l), synth.head(cfg))
+    kv = model.kv(1, n + 8)
+    log(f"model ready in {time.perf_counter() - t_gen:.1f} s")
+    dev = model.device
+    prompt = torch.from_numpy(synth.tokens(cfg, n, stream=17)).to(dev)
+    out = torch.zeros(1, dtype=torch.int32, device=dev)
+
+    def run():
+        kv.set_lengths([0])
+        for i0 in range(0, n, 4096):
+            m = min(4096, n - i0)
+            prefill_chunk(model.ctx, kv.handle, 0, prompt.data_ptr() + 4 * i0, m, out.data_ptr())
+
+    run()  # warm-up (also makes the batched path's tiled weights)
+    sync(model.ctx)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    run()
+    e1.record()
+    torch.cuda.synchronize()
+    sync(model.ctx)
+    ms = e0.elapsed_time(e1)
+    model.free()
+    log(f"prefill of {n} tokens: {ms:.1f} ms")
+    print(json.dumps({
+        "metric": "prefill tok/s (one sequence, cold cache)", "value": round(n / (ms / 1e3), 1), "unit": "tok/s",
+        "n_gpus": 1, "higher_is_better": True, "ms_total": round(ms, 2), "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": f"{cfg.name}: {n}-token prompt from an empty cache", "prompt": n},
+    }), flush=True)
+
+
 def measured_traffic():
     """HBM bytes per launch from the committed counter summary, if it was taken on this kernel source."""
     import hashlib
@@ -221,6 +265,7 @@ def main():
     ap.add_argument("--config", default="int4_49")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-steps", type=int, default=4, help="decode steps the oracle is timed on")
+    ap.add_argument("--prefill", type=int, default=0, help="time a prompt of this many tokens instead")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run one 1 GiB device copy (counter calibration under rocprofv3 --pmc)")
     args = ap.parse_args()
@@ -238,6 +283,8 @@ def main():
 
     lib()
     cfg = synth.CONFIGS[args.config]
+    if args.prefill:
+        return bench_prefill(args, cfg)
     if cfg.batch > 1:
         return bench_batch(args, cfg)
     cpu = not args.no_cpu_baseline
