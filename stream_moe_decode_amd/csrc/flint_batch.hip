@@ -85,6 +85,34 @@ __global__ void tile_weights_kernel(const uint8_t* w, uint8_t* dst, size_t rows,
   }
 }
 
+// One int4 chunk (128 inputs) of one tile: wv = this lane's 16 bytes of the tiled weights, sa / sb = the
+// scales of its 4 rows for the chunk's two groups, b = this lane's inputs of the chunk.
+__device__ __forceinline__ void i4_chunk(f32x4_t& acc, uint4 wv, u32x2_t sa, u32x2_t sb, const uint4 (&b)[4],
+                                         const I4K& k4, bf16x8_t bias) {
+  f32x4_t da = {0.f, 0.f, 0.f, 0.f}, db = {0.f, 0.f, 0.f, 0.f};
+  da = mfma(unpack8(wv.x, k4), as_bf16x8(b[0]), da);
+  da = mfma(unpack8(wv.y, k4), as_bf16x8(b[1]), da);
+  da = mfma(bias, as_bf16x8(b[0]), da);
+  da = mfma(bias, as_bf16x8(b[1]), da);
+  db = mfma(unpack8(wv.z, k4), as_bf16x8(b[2]), db);
+  db = mfma(unpack8(wv.w, k4), as_bf16x8(b[3]), db);
+  db = mfma(bias, as_bf16x8(b[2]), db);
+  db = mfma(bias, as_bf16x8(b[3]), db);
+  acc[0] = fmaf(bf2f(sa.x & 0xFFFFu), da[0], fmaf(bf2f(sb.x & 0xFFFFu), db[0], acc[0]));
+  acc[1] = fmaf(bf2f(sa.x >> 16), da[1], fmaf(bf2f(sb.x >> 16), db[1], acc[1]));
+  acc[2] = fmaf(bf2f(sa.y & 0xFFFFu), da[2], fmaf(bf2f(sb.y & 0xFFFFu), db[2], acc[2]));
+  acc[3] = fmaf(bf2f(sa.y >> 16), da[3], fmaf(bf2f(sb.y >> 16), db[3], acc[3]));
+}
+__device__ __forceinline__ bf16x8_t bias136() {  // bf16 -136 in every element
+  return as_bf16x8(make_uint4(0xC308C308u, 0xC308C308u, 0xC308C308u, 0xC308C308u));
+}
+// This lane's inputs of int4 chunk c (both groups, both 32-input halves), or zeros for a null column.
+__device__ __forceinline__ void i4_inputs(uint4 (&b)[4], const uint16_t* col, int c, int kg) {
+#pragma unroll
+  for (int q = 0; q < 4; ++q)
+    b[q] = col ? ld16(col + (2 * c + (q >> 1)) * 64 + kg * 16 + (q & 1) * 8) : make_uint4(0u, 0u, 0u, 0u);
+}
+
 // acc[t] += W[tile t] . x over the chunks [c0, c1) (int4: 128 inputs, bf16: 32) for 16 sequence columns,
 // the input operand of a chunk loaded once for all NT tiles.  tile_of(t): the tile's index in m.wt;
 // rowmap(t, m): its rows (for the int4 scales; rows rowmap(t, 4 k) .. + 3 are consecutive from a
@@ -105,7 +133,7 @@ __device__ __forceinline__ void mma_tiles(f32x4_t (&acc)[NT], const Mat& m, int 
     if constexpr (WT == W_I4) s4[t] = m.s4 + (size_t)(rowmap(t, 4 * kg) >> 2) * G * 4;
   }
   const I4K k4 = i4k();
-  const bf16x8_t bias = as_bf16x8(make_uint4(0xC308C308u, 0xC308C308u, 0xC308C308u, 0xC308C308u));  // bf16 -136
+  const bf16x8_t bias = bias136();
   constexpr int U = WT == W_I4 ? (NT >= 4 ? 2 : 4) : (NT >= 4 ? 4 : 8);
   constexpr int NB = WT == W_I4 ? 4 : 1;  // 16-byte input loads per chunk
   for (int c = c0; c < c1; c += U) {
@@ -135,19 +163,7 @@ __device__ __forceinline__ void mma_tiles(f32x4_t (&acc)[NT], const Mat& m, int 
 #pragma unroll
       for (int t = 0; t < NT; ++t) {
         if constexpr (WT == W_I4) {
-          f32x4_t da = {0.f, 0.f, 0.f, 0.f}, db = {0.f, 0.f, 0.f, 0.f};
-          da = mfma(unpack8(wv[u][t].x, k4), as_bf16x8(b[u][0]), da);
-          da = mfma(unpack8(wv[u][t].y, k4), as_bf16x8(b[u][1]), da);
-          da = mfma(bias, as_bf16x8(b[u][0]), da);
-          da = mfma(bias, as_bf16x8(b[u][1]), da);
-          db = mfma(unpack8(wv[u][t].z, k4), as_bf16x8(b[u][2]), db);
-          db = mfma(unpack8(wv[u][t].w, k4), as_bf16x8(b[u][3]), db);
-          db = mfma(bias, as_bf16x8(b[u][2]), db);
-          db = mfma(bias, as_bf16x8(b[u][3]), db);
-          acc[t][0] = fmaf(bf2f(sa[u][t].x & 0xFFFFu), da[0], fmaf(bf2f(sb[u][t].x & 0xFFFFu), db[0], acc[t][0]));
-          acc[t][1] = fmaf(bf2f(sa[u][t].x >> 16), da[1], fmaf(bf2f(sb[u][t].x >> 16), db[1], acc[t][1]));
-          acc[t][2] = fmaf(bf2f(sa[u][t].y & 0xFFFFu), da[2], fmaf(bf2f(sb[u][t].y & 0xFFFFu), db[2], acc[t][2]));
-          acc[t][3] = fmaf(bf2f(sa[u][t].y >> 16), da[3], fmaf(bf2f(sb[u][t].y >> 16), db[3], acc[t][3]));
+          i4_chunk(acc[t], wv[u][t], sa[u][t], sb[u][t], b[u], k4, bias);
         } else {
           acc[t] = mfma(as_bf16x8(wv[u][t]), as_bf16x8(b[u][0]), acc[t]);
         }
@@ -601,7 +617,7 @@ __global__ void __launch_bounds__(BNT) bk_oproj(const BArgs a, int l) {
 // 16-row tiles (gate 0-3, up 4-7) over its eighth of the inputs; the partial tiles meet in LDS.
 template <int WT>
 __global__ void __launch_bounds__(BNT) bk_gateup(const BArgs a, int l) {
-  __shared__ f32x4_t red[BNW][8][64];
+  __shared__ f32x4_t red[BNW * 8 * 64];  // the waves' partial tiles [wave][tile][lane]
   __shared__ int slot[BT];
   const int t = blockIdx.x, e = blockIdx.y, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const bool dense = l < a.n_dense;
@@ -619,17 +635,19 @@ __global__ void __launch_bounds__(BNT) bk_gateup(const BArgs a, int l) {
   const long long base = dense ? (long long)l * a.DI : ((long long)(l - a.n_dense) * a.E + e) * a.EI;
   const uint16_t* col = slot[n] >= 0 ? a.act + (size_t)n * a.astride : nullptr;
   const int C = a.H / kChunkIn<WT>, c0 = part(C, BNW, wave), c1 = part(C, BNW, wave + 1);
-  f32x4_t acc[4];
-  // gate tiles, then up tiles (same rows; the two matrices share the layout and the scales' regrouping)
+  {
+    f32x4_t acc[4];
+    // gate tiles, then up tiles (same rows; the two matrices share the layout)
 #pragma unroll
-  for (int mat = 0; mat < 2; ++mat) {
+    for (int mat = 0; mat < 2; ++mat) {
 #pragma unroll
-    for (int q = 0; q < 4; ++q) acc[q] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    auto rowmap = [&](int q, int m) -> long long { return base + t * 64 + q * 16 + m; };
-    auto tile_of = [&](int q) -> long long { return (base >> 4) + t * 4 + q; };
-    mma_tiles<WT, 4>(acc, mat ? Mu : Mg, a.H, tile_of, rowmap, col, c0, c1);
+      for (int q = 0; q < 4; ++q) acc[q] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      auto rowmap = [&](int q, int m) -> long long { return base + t * 64 + q * 16 + m; };
+      auto tile_of = [&](int q) -> long long { return (base >> 4) + t * 4 + q; };
+      mma_tiles<WT, 4>(acc, mat ? Mu : Mg, a.H, tile_of, rowmap, col, c0, c1);
 #pragma unroll
-    for (int q = 0; q < 4; ++q) red[wave][mat * 4 + q][lane] = acc[q];
+      for (int q = 0; q < 4; ++q) red[(wave * 8 + mat * 4 + q) * 64 + lane] = acc[q];
+    }
   }
   __syncthreads();
   const int inner = dense ? a.DI : a.EI;
@@ -640,8 +658,8 @@ __global__ void __launch_bounds__(BNT) bk_gateup(const BArgs a, int l) {
     float g = 0.f, u = 0.f;
 #pragma unroll
     for (int w = 0; w < BNW; ++w) {
-      g += red[w][tile][ln][r];
-      u += red[w][4 + tile][ln][r];
+      g += red[(w * 8 + tile) * 64 + ln][r];
+      u += red[(w * 8 + 4 + tile) * 64 + ln][r];
     }
     const int ei = sl * inner + t * 64 + rr;
     gp(a.h)[(size_t)q * a.hstride + act_pos<WT>(ei)] = (uint16_t)f2bf(g / (1.0f + __expf(-g)) * u);
