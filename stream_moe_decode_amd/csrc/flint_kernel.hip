@@ -63,6 +63,8 @@ struct AttnLds {                         // QKV and attention
   uint4 kbuf[KV_LDS / 16];               // K rows of a chunk
   uint4 vbuf[KV_LDS / 16];               // V rows of a chunk
   float qs[MAX_GQ * MAX_HD];             // queries of the kv-head group, pre-scaled
+  uint16_t qop[2][4 * 64 * 8];           // MFMA scores: the same as B operands (bf16 high, low parts) for
+                                         // 128-dim heads: [dims / 32][lane (head + 16 * k-slice)][8]
   float kn[MAX_HD], vn[MAX_HD];          // the new token's k, v (activation-rounded)
   float sc[MAX_GQ * MAX_CHUNK_POS];      // scores of a chunk, [head][position]
   float pt[MAX_GQ * MAX_CHUNK_POS];      // probabilities of a chunk, [position][head (padded to 4 or 8)]
@@ -930,11 +932,24 @@ __global__ void __launch_bounds__(NT, 1) decode_kernel(const KStatic* __restrict
             [=](int k, int m) { return (int)(((long long)(k + 1) * n) / m) - 1; }, ns,
             [&](int i, uint32_t p) {
               const float v = __uint_as_float(p);
-              if (i < nqs) at.qs[i] = v * qscale;
+              if (i < nqs) {
+                at.qs[i] = v * qscale;
+                if constexpr (MFMA_QK) {  // query dim d of head h goes to lane 16 ((d / 8) % 4) + h, slot d % 8
+                  const float qv = v * qscale;
+                  const uint32_t hb = f2bf(qv);
+                  const int h = i >> 7, dd = i & 127;
+                  const int idx = ((dd >> 5) * 64 + ((dd >> 3) & 3) * 16 + h) * 8 + (dd & 7);
+                  at.qop[0][idx] = (uint16_t)hb;
+                  at.qop[1][idx] = (uint16_t)f2bf(qv - bf2f(hb));
+                }
+              }
               else if (i < nqs + hd) at.kn[i - nqs] = act_round<WT>(v);
               else at.vn[i - nqs - hd] = act_round<WT>(v);
             },
             wt);
+        if constexpr (MFMA_QK)  // the operand lanes of heads Gq .. 15 are zero
+          for (int idx = tid; idx < 4 * 64 * 8; idx += NT)
+            if (((idx >> 3) & 15) >= Gq) at.qop[0][idx] = at.qop[1][idx] = 0;
       } else {
         ok = sync_ok(sm, wt);
       }
@@ -988,17 +1003,13 @@ __global__ void __launch_bounds__(NT, 1) decode_kernel(const KStatic* __restrict
           // query split into bf16 high and low parts (q = hi + lo to about 16 bits) so the product keeps
           // fp32-level accuracy; lane L supplies head L % 16 (zero past Gq) and gets positions
           // (L / 16) * 4 + r of the block
-          const int n = lane & 15, kg = (lane >> 4) * 8;
+          const int n = lane & 15;
           bf16x8_t qh[4], ql[4];
 #pragma unroll
-          for (int sk = 0; sk < 4; ++sk)
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-              const float qv = n < Gq ? at.qs[n * hd + sk * 32 + kg + e] : 0.f;
-              const uint32_t hb = f2bf(qv);
-              qh[sk][e] = __builtin_bit_cast(__bf16, (uint16_t)hb);
-              ql[sk][e] = __builtin_bit_cast(__bf16, (uint16_t)f2bf(qv - bf2f(hb)));
-            }
+          for (int sk = 0; sk < 4; ++sk) {
+            qh[sk] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(&at.qop[0][(sk * 64 + lane) * 8]));
+            ql[sk] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(&at.qop[1][(sk * 64 + lane) * 8]));
+          }
           const int nb = (np + 15) / 16;
           for (int b = wave; b < nb; b += NW) {
             f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
