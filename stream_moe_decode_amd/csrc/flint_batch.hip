@@ -200,8 +200,12 @@ enum { NORM_EMBED = 0, NORM_INPUT = 1, NORM_POST = 2, NORM_FINAL = 3 };
 // Cache sequence and position of column n of the pass (decode: sequence seq0 + n at its length;
 // prefill: sequence seq0 at its length + n).
 __device__ __forceinline__ int col_seq(const BArgs& a, int n) { return a.prefill ? a.seq0 : a.seq0 + n; }
+// Position of column n; n may differ between lanes (a select over the kernel argument array, no load).
 __device__ __forceinline__ int col_pos(const BArgs& a, int n) {
-  return a.prefill ? gp(a.len)[a.seq0] + n : gp(a.len)[a.seq0 + n];
+  int p = 0;
+#pragma unroll
+  for (int m = 0; m < BT; ++m) p = n == m ? a.pos[m] : p;
+  return p;
 }
 
 // Partial sums cross workgroups (and XCDs) through memory: written with system-scope stores, which go
@@ -443,154 +447,218 @@ __global__ void __launch_bounds__(BNT) bk_qkv(const BArgs a, int l) {
   }
 }
 
-// Attention partial of (split s, kv head j, sequence n) over positions [s P, min(s P + P, len + 1)) of the
-// sequence's own cache (the new token's K/V already appended): scores on MFMA (the query split into bf16 high
-// and low parts), softmax, P.V on the vector units.  Writes (m, l, o) of each query head of the group.
-__global__ void __launch_bounds__(BNT) bk_attn(const BArgs a, int l) {
-  __shared__ uint4 kbuf[ATT_P * 16];   // K rows in the A-operand layout of v_mfma_f32_16x16x32_bf16
-  __shared__ uint4 vbuf[ATT_P * 16];   // V rows
-  __shared__ float qs[4 * 128];
-  __shared__ float sc[4 * ATT_P];      // [head][position]
-  __shared__ float pt[ATT_P * 4];      // [position][head]
-  __shared__ float mst[4], lst[4];
-  const int s = blockIdx.x, j = blockIdx.y, n = blockIdx.z;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int T = col_pos(a, n) + 1, t0 = s * ATT_P;
-  if (t0 >= T) return;
-  const int np = min(ATT_P, T - t0), hd = 128, Gq = a.nq / a.nkv;
+// Attention of the batched path: a workgroup of ATT_NW waves takes ATT_P cached positions of one (column,
+// kv head); wave w takes the chunks of ATT_C positions w, w + ATT_NW, ... and keeps its own online softmax,
+// with the K and V rows of a chunk loaded straight into registers one chunk ahead of the math, so the loop
+// has no barrier.  One exchange through LDS at the end folds the waves into the split's partial.
+constexpr int ATT_NW = 4, ATT_NT = ATT_NW * 64, ATT_K = ATT_P / (ATT_NW * ATT_C);  // chunks per wave
+static_assert(ATT_C == 16 && ATT_K * ATT_NW * ATT_C == ATT_P, "attention split shape");
+
+// Rows of one chunk: k[sk] is the A operand of v_mfma_f32_16x16x32_bf16 for dims sk * 32 .. + 32 (lane L:
+// position c0 + L % 16, dims sk * 32 + (L / 16) * 8 .. + 8); v[r] holds dims (L % 16) * 8 .. + 8 of position
+// c0 + (L / 16) * 4 + r, the position whose score lands in element r of lane L's score fragment.  Positions
+// past tl re-read row tl.
+struct AttChunk {
+  uint4 k[4], v[4];
+};
+__device__ __forceinline__ void att_load(AttChunk& c, const uint8_t* kbase, const uint8_t* vbase, int c0, int tl,
+                                         int lane) {
+  const size_t pk = min(c0 + (lane & 15), tl);
+#pragma unroll
+  for (int sk = 0; sk < 4; ++sk) c.k[sk] = ld16(kbase + pk * 256 + sk * 64 + (lane >> 4) * 16);
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const size_t pv = min(c0 + (lane >> 4) * 4 + r, tl);
+    c.v[r] = ld16(vbase + pv * 256 + (lane & 15) * 16);
+  }
+}
+
+// Attention of (split s, kv head j, column n) over positions [s P, min(s P + P, pos + 1)) of the column's
+// own cache (the new token's K/V already appended): scores on MFMA (the query split into bf16 high and low
+// parts), online softmax, P.V on the vector units.  The grid holds only real splits: workgroup x is split
+// x - asp[n] of column n.  Writes (m, l, o) of each query head of the group.
+__global__ void __launch_bounds__(ATT_NT) bk_attn(const BArgs a, int l) {
+  __shared__ __align__(16) float ow[ATT_NW][4][128];
+  __shared__ float mw[ATT_NW][4], lw[ATT_NW][4];
+  __shared__ uint4 qop[4][2][64];  // [dims / 32][high, low][lane]
+  const int j = blockIdx.y, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  int n = 0;
+  while (n + 1 < a.B && a.asp[n + 1] <= (int)blockIdx.x) ++n;
+  const int s = blockIdx.x - a.asp[n];
+  const int T = a.pos[n] + 1, t0 = s * ATT_P;  // t0 < T: the host counts ceil(T / P) splits
+  const int t1 = min(t0 + ATT_P, T), tl = t1 - 1, hd = 128, Gq = a.nq / a.nkv;
   const size_t cb = (((size_t)l * a.Bc + col_seq(a, n)) * a.nkv + j) * (size_t)a.cap * hd * 2;
-  k_issue_mfma(kbuf, a.kc + cb, t0, np);
-  kv_issue(vbuf, a.vc + cb, t0, np, 256);
-  const float qscale = 1.0f / sqrtf((float)hd);
-  for (int i = tid; i < 4 * hd; i += BNT)
-    qs[i] = i < Gq * hd ? gp(a.q)[(size_t)n * a.nq * hd + (size_t)j * Gq * hd + i] * qscale : 0.f;
-  wait_vmem();
-  __syncthreads();
-  {  // scores: D[position][head] = K[16 positions x 32 dims] . Q^T[32 dims x 16 heads]
-    const int hcol = lane & 15, kq = (lane >> 4) * 8;
-    bf16x8_t qh[4], ql[4];
+  const uint8_t* const kbase = a.kc + cb;
+  const uint8_t* const vbase = a.vc + cb;
+  AttChunk buf[2];
+  att_load(buf[0], kbase, vbase, t0 + wave * ATT_C, tl, lane);
+  // the query as MFMA B operands (lane: head L % 16, dims (L / 16) * 8 ..), bf16 high and low parts, built by
+  // wave 0 into LDS
+  const int hcol = lane & 15, grp = lane >> 4;
+  if (wave == 0) {
+    const float* qp = a.q + (size_t)n * a.nq * hd + ((size_t)j * Gq + min(hcol, Gq - 1)) * hd + grp * 8;
+    const float qm = hcol < Gq ? 1.0f / sqrtf((float)hd) : 0.f;
 #pragma unroll
-    for (int sk = 0; sk < 4; ++sk)
+    for (int sk = 0; sk < 4; ++sk) {
+      const f32x4_t x0 = *(GLOBAL const f32x4_t*)(qp + sk * 32), x1 = *(GLOBAL const f32x4_t*)(qp + sk * 32 + 4);
+      uint32_t hw[4], lw4[4];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const float qv = hcol < Gq ? qs[hcol * hd + sk * 32 + kq + e] : 0.f;
-        const uint32_t hb = f2bf(qv);
-        qh[sk][e] = __builtin_bit_cast(__bf16, (uint16_t)hb);
-        ql[sk][e] = __builtin_bit_cast(__bf16, (uint16_t)f2bf(qv - bf2f(hb)));
+      for (int e = 0; e < 4; ++e) {
+        uint32_t hb[2], lb[2];
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          const float qv = (2 * e + u < 4 ? x0[2 * e + u] : x1[2 * e + u - 4]) * qm;
+          hb[u] = f2bf(qv);
+          lb[u] = f2bf(qv - bf2f(hb[u]));
+        }
+        hw[e] = hb[0] | hb[1] << 16;
+        lw4[e] = lb[0] | lb[1] << 16;
       }
-    for (int b = wave; b < (np + 15) / 16; b += BNW) {
-      f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+      qop[sk][0][lane] = make_uint4(hw[0], hw[1], hw[2], hw[3]);
+      qop[sk][1][lane] = make_uint4(lw4[0], lw4[1], lw4[2], lw4[3]);
+    }
+  }
+  __syncthreads();
+  float m = -INFINITY, lsum = 0.f;  // running max and sum of head hcol
+  float o[4][8];                    // head h, dims hcol * 8 + e, over this lane's positions
+#pragma unroll
+  for (int h = 0; h < 4; ++h)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) o[h][e] = 0.f;
+#pragma unroll
+  for (int k = 0; k < ATT_K; ++k) {
+    const int c0 = t0 + (k * ATT_NW + wave) * ATT_C;
+    if (k + 1 < ATT_K) att_load(buf[(k + 1) & 1], kbase, vbase, c0 + ATT_NW * ATT_C, tl, lane);
+    if (c0 < t1) {
+      const AttChunk& c = buf[k & 1];
+      f32x4_t acc = {0.f, 0.f, 0.f, 0.f};  // D[position][head]
 #pragma unroll
       for (int sk = 0; sk < 4; ++sk) {
-        const bf16x8_t kop = as_bf16x8(kbuf[(b * 4 + sk) * 64 + lane]);
-        acc = mfma(kop, qh[sk], acc);
-        acc = mfma(kop, ql[sk], acc);
+        acc = mfma(as_bf16x8(c.k[sk]), as_bf16x8(qop[sk][0][lane]), acc);
+        acc = mfma(as_bf16x8(c.k[sk]), as_bf16x8(qop[sk][1][lane]), acc);
+      }
+      float sv[4], mx = -INFINITY;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        sv[r] = c0 + grp * 4 + r < t1 ? acc[r] : -INFINITY;
+        mx = fmaxf(mx, sv[r]);
+      }
+      mx = fmaxf(mx, swap16(mx));
+      mx = fmaxf(mx, swap32(mx));
+      const float mn = fmaxf(m, mx);  // finite: position c0 is in range
+      const float alpha = __expf(m - mn);
+      float p[4], ps = 0.f;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        p[r] = __expf(sv[r] - mn);
+        ps += p[r];
+      }
+      ps += swap16(ps);
+      ps += swap32(ps);
+      lsum = lsum * alpha + ps;
+      m = mn;
+#pragma unroll
+      for (int h = 0; h < 4; ++h) {
+        const float ah = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(alpha), h));
+#pragma unroll
+        for (int e = 0; e < 8; ++e) o[h][e] *= ah;
       }
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const int pr = b * 16 + (lane >> 4) * 4 + r;
-        if (hcol < Gq && pr < np) sc[hcol * ATT_P + pr] = acc[r];
+        const uint32_t w4[4] = {c.v[r].x, c.v[r].y, c.v[r].z, c.v[r].w};
+        float vv[8];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          vv[2 * e] = bf2f(w4[e] & 0xFFFFu);
+          vv[2 * e + 1] = bf2f(w4[e] >> 16);
+        }
+#pragma unroll
+        for (int h = 0; h < 4; ++h) {
+          const float ph =
+              __int_as_float(__builtin_amdgcn_ds_bpermute(((lane & 48) + h) * 4, __float_as_int(p[r])));
+#pragma unroll
+          for (int e = 0; e < 8; ++e) o[h][e] = fmaf(ph, vv[e], o[h][e]);
+        }
       }
     }
   }
-  __syncthreads();
-  for (int h = wave; h < 4; h += BNW) {  // softmax of head h (padding heads: zero probabilities)
-    if (h >= Gq) {
-      for (int i = lane; i < np; i += 64) pt[i * 4 + h] = 0.f;
-      continue;
-    }
-    float mx = -INFINITY;
-    for (int i = lane; i < np; i += 64) mx = fmaxf(mx, sc[h * ATT_P + i]);
-    mx = wave_max(mx);
-    float ls = 0.f;
-    for (int i = lane; i < np; i += 64) {
-      const float p = __expf(sc[h * ATT_P + i] - mx);
-      pt[i * 4 + h] = p;
-      ls += p;
-    }
-    ls = wave_sum(ls);
-    if (lane == 0) {
-      mst[h] = mx;
-      lst[h] = ls;
-    }
-  }
-  __syncthreads();
-  // P.V: wave w takes positions w, w + 8, ...; lane: dims 2 lane, 2 lane + 1 of every head
-  float o[4][2] = {{0.f, 0.f}, {0.f, 0.f}, {0.f, 0.f}, {0.f, 0.f}};
-  const uint32_t* vb = reinterpret_cast<const uint32_t*>(vbuf);
-#pragma unroll 4
-  for (int i = wave; i < np; i += BNW) {
-    const float4 p = *reinterpret_cast<const float4*>(pt + i * 4);
-    const uint32_t v2 = vb[i * 64 + lane];
-    const float v0 = bf2f(v2 & 0xFFFFu), v1 = bf2f(v2 >> 16);
-    o[0][0] = fmaf(p.x, v0, o[0][0]);
-    o[0][1] = fmaf(p.x, v1, o[0][1]);
-    o[1][0] = fmaf(p.y, v0, o[1][0]);
-    o[1][1] = fmaf(p.y, v1, o[1][1]);
-    o[2][0] = fmaf(p.z, v0, o[2][0]);
-    o[2][1] = fmaf(p.z, v1, o[2][1]);
-    o[3][0] = fmaf(p.w, v0, o[3][0]);
-    o[3][1] = fmaf(p.w, v1, o[3][1]);
-  }
-  float* red = reinterpret_cast<float*>(kbuf);  // the K rows are dead since the softmax's barrier
+  // fold the four lane groups (their positions), then the waves
 #pragma unroll
-  for (int h = 0; h < 4; ++h) {
-    red[(wave * 4 + h) * hd + 2 * lane] = o[h][0];
-    red[(wave * 4 + h) * hd + 2 * lane + 1] = o[h][1];
+  for (int h = 0; h < 4; ++h)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      o[h][e] += swap16(o[h][e]);
+      o[h][e] += swap32(o[h][e]);
+    }
+  if (lane < 16)
+#pragma unroll
+    for (int h = 0; h < 4; ++h) {
+      *reinterpret_cast<float4*>(&ow[wave][h][lane * 8]) = make_float4(o[h][0], o[h][1], o[h][2], o[h][3]);
+      *reinterpret_cast<float4*>(&ow[wave][h][lane * 8 + 4]) = make_float4(o[h][4], o[h][5], o[h][6], o[h][7]);
+    }
+  if (lane < 4) {
+    mw[wave][lane] = m;
+    lw[wave][lane] = lsum;
   }
   __syncthreads();
-  float* dst = a.part + (((size_t)n * a.nq + (size_t)j * Gq) * a.nsmax + s) * (hd + 2);
+  float* const dst = a.part + (((size_t)n * a.nq + (size_t)j * Gq) * a.nsmax + s) * (hd + 2);
   const size_t hstep = (size_t)a.nsmax * (hd + 2);  // between query heads
-  for (int idx = tid; idx < Gq * hd; idx += BNT) {
+  for (int idx = tid; idx < Gq * hd; idx += ATT_NT) {
     const int h = idx / hd, e = idx % hd;
+    float M = mw[0][h];  // wave 0 always has position t0
+#pragma unroll
+    for (int w = 1; w < ATT_NW; ++w) M = fmaxf(M, mw[w][h]);
     float t = 0.f;
 #pragma unroll
-    for (int w = 0; w < BNW; ++w) t += red[(w * 4 + h) * hd + e];
+    for (int w = 0; w < ATT_NW; ++w) t += __expf(mw[w][h] - M) * ow[w][h][e];
     gp(dst)[h * hstep + 2 + e] = t;
   }
-  if (tid < 2 * Gq) gp(dst)[(tid >> 1) * hstep + (tid & 1)] = (tid & 1) ? lst[tid >> 1] : mst[tid >> 1];
+  if (tid < Gq) {
+    float M = mw[0][tid];
+#pragma unroll
+    for (int w = 1; w < ATT_NW; ++w) M = fmaxf(M, mw[w][tid]);
+    float L = 0.f;
+#pragma unroll
+    for (int w = 0; w < ATT_NW; ++w) L += __expf(mw[w][tid] - M) * lw[w][tid];
+    gp(dst)[tid * hstep] = M;
+    gp(dst)[tid * hstep + 1] = L;
+  }
 }
 
-// Merge the splits of (query head h, sequence n): o = sum_s e^(m_s - M) o_s / sum_s e^(m_s - M) l_s, as the
-// o_proj input.  The splits' (m, l) are read once into LDS (one thread each), then every thread (one per
-// dim) sums its dim over the splits with 8 loads in flight.
+// Merge the splits of (query head h, column n): o = sum_s e^(m_s - M) o_s / sum_s e^(m_s - M) l_s, as the
+// o_proj input.  Thread d owns dim d; the splits are taken MB at a time with every load of a block (m, l
+// and o of each split) issued before any is used, and the blocks are folded by the running-max rule.
+constexpr int MB = 32;
 template <int WT>
 __global__ void __launch_bounds__(128) bk_merge(const BArgs a) {
-  __shared__ float ws[MAX_SPLITS];
-  __shared__ float wm[2], wl[2];
   const int h = blockIdx.x, n = blockIdx.y, d = threadIdx.x, hd = a.hd;
-  const int T = col_pos(a, n) + 1, ns = min((T + ATT_P - 1) / ATT_P, MAX_SPLITS);
+  const int ns = a.asp[n + 1] - a.asp[n];
   const float* p = a.part + ((size_t)n * a.nq + h) * a.nsmax * (hd + 2);
-  float mloc = -INFINITY;
-  for (int s = d; s < ns; s += 128) {
-    ws[s] = gp(p)[(size_t)s * (hd + 2)];
-    mloc = fmaxf(mloc, ws[s]);
-  }
-  mloc = wave_max(mloc);
-  if ((d & 63) == 0) wm[d >> 6] = mloc;
-  __syncthreads();
-  const float M = fmaxf(wm[0], wm[1]);
-  float lp = 0.f;
-  for (int s = d; s < ns; s += 128) {
-    const float w = __expf(ws[s] - M);
-    ws[s] = w;
-    lp = fmaf(w, gp(p)[(size_t)s * (hd + 2) + 1], lp);
-  }
-  lp = wave_sum(lp);
-  if ((d & 63) == 0) wl[d >> 6] = lp;
-  __syncthreads();
-  const float lsum = wl[0] + wl[1];
-  float O = 0.f;
-  int s = 0;
-  for (; s + 8 <= ns; s += 8) {
-    float v[8];
+  float M = -INFINITY, L = 0.f, O = 0.f;
+  for (int s0 = 0; s0 < ns; s0 += MB) {
+    float m[MB], lv[MB], o[MB];
 #pragma unroll
-    for (int k = 0; k < 8; ++k) v[k] = gp(p)[(size_t)(s + k) * (hd + 2) + 2 + d];
+    for (int u = 0; u < MB; ++u) {  // past the last split: re-read it with weight 0
+      const float* q = p + (size_t)min(s0 + u, ns - 1) * (hd + 2);
+      m[u] = gp(q)[0];
+      lv[u] = gp(q)[1];
+      o[u] = gp(q)[2 + d];
+    }
+    float mb = M;
 #pragma unroll
-    for (int k = 0; k < 8; ++k) O = fmaf(ws[s + k], v[k], O);
+    for (int u = 0; u < MB; ++u) mb = s0 + u < ns ? fmaxf(mb, m[u]) : mb;
+    const float sc = __expf(M - mb);  // M = -inf on the first block: 0
+    L *= sc;
+    O *= sc;
+#pragma unroll
+    for (int u = 0; u < MB; ++u) {
+      const float w = s0 + u < ns ? __expf(m[u] - mb) : 0.f;
+      L = fmaf(w, lv[u], L);
+      O = fmaf(w, o[u], O);
+    }
+    M = mb;
   }
-  for (; s < ns; ++s) O = fmaf(ws[s], gp(p)[(size_t)s * (hd + 2) + 2 + d], O);
-  gp(a.act)[(size_t)n * a.astride + act_pos<WT>(h * hd + d)] = (uint16_t)f2bf(O / lsum);
+  gp(a.act)[(size_t)n * a.astride + act_pos<WT>(h * hd + d)] = (uint16_t)f2bf(O / L);
 }
 
 // o_proj rows t*16 .. t*16 + 15 over input chunk kc: partial sums, added to the residual by the next norm.
@@ -861,7 +929,7 @@ template <int WT> hipError_t run_pass(const BArgs& a, hipStream_t st) {
   for (int l = 0; l < a.L; ++l) {
     hipLaunchKernelGGL(bk_norm<WT>, dim3(a.B), dim3(BNT), 0, st, a, l, l == 0 ? (int)NORM_EMBED : (int)NORM_INPUT);
     hipLaunchKernelGGL(bk_qkv<WT>, dim3(QR / 16), dim3(BNT), 0, st, a, l);
-    hipLaunchKernelGGL(bk_attn, dim3(a.nsmax, a.nkv, a.B), dim3(BNT), 0, st, a, l);
+    hipLaunchKernelGGL(bk_attn, dim3(a.asp[a.B], a.nkv), dim3(ATT_NT), 0, st, a, l);
     hipLaunchKernelGGL(bk_merge<WT>, dim3(a.nq, a.B), dim3(a.hd), 0, st, a);
     hipLaunchKernelGGL(bk_oproj<WT>, dim3(a.H / 16, OKC), dim3(BNT), 0, st, a, l);
     hipLaunchKernelGGL(bk_norm<WT>, dim3(a.B), dim3(BNT), 0, st, a, l, (int)NORM_POST);

@@ -87,7 +87,8 @@ struct KDyn {
 // ordinary kernels per layer whose contractions run on MFMA with the
 // sequences as the 16 columns.
 constexpr int BT = 16;                  // sequences per pass (MFMA columns)
-constexpr int ATT_P = 64;               // cached positions per attention split of the batched path
+constexpr int ATT_P = 256;              // cached positions per attention split of the batched path
+constexpr int ATT_C = 16;               // positions per chunk of a split (one MFMA score tile)
 constexpr int MAX_SPLITS = 1024;        // attention splits per sequence (max_tokens <= ATT_P * MAX_SPLITS)
 constexpr int OKC = 2;                  // o_proj input chunks (partial sums added by the next norm)
 constexpr int DKC = 16;                 // MoE down expert chunks / dense down input chunks
@@ -107,6 +108,10 @@ struct BArgs {
   // (prefill) B consecutive prompt tokens tokens[tok0 ..] of sequence seq0 at positions len[seq0] ..,
   // the greedy id after the last one written to out_ids[0]
   int B, seq0, Bc, cap, prefill, tok0;
+  // position of column n (its sequence's length, or len + n in prefill), taken from the host's mirror of
+  // the lengths so that no kernel waits on a load to know it; asp[n] = attention splits of columns 0 .. n - 1
+  int pos[BT];
+  int asp[BT + 1];
   uint8_t* kc;           // [L][Bc][nkv][cap][hd] bf16
   uint8_t* vc;
   const float2* rope;    // [cap][hd/2] (cos, sin)

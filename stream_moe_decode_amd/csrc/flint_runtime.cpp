@@ -355,6 +355,15 @@ int batch_scratch(flint_ctx* c, flint_kv* kv) {
   return FLINT_OK;
 }
 
+// Positions of a pass's columns from the host's mirror of the lengths, and the attention splits per column.
+void set_positions(BArgs& a, const std::vector<int32_t>& hlen) {
+  a.asp[0] = 0;
+  for (int n = 0; n < BT; ++n) {
+    a.pos[n] = n < a.B ? (a.prefill ? hlen[a.seq0] + n : hlen[a.seq0 + n]) : 0;
+    a.asp[n + 1] = a.asp[n] + (n < a.B ? (a.pos[n] + 1 + ATT_P - 1) / ATT_P : 0);
+  }
+}
+
 }  // namespace
 
 extern "C" {
@@ -633,6 +642,7 @@ int flint_decode_step_debug(flint_ctx* c, const int32_t* tokens, flint_kv* kv, i
     for (int s0 = 0; s0 < kv->batch; s0 += BT) {
       a.seq0 = s0;
       a.B = std::min(BT, kv->batch - s0);
+      set_positions(a, kv->hlen);
       HIPCHECK(launch_batch_pass(c->cfg.weight_type, a, c->stream));
     }
     for (int b = 0; b < kv->batch; ++b) kv->hlen[b]++;
@@ -673,6 +683,7 @@ int flint_prefill_chunk(flint_ctx* c, flint_kv* kv, int32_t seq, const int32_t* 
     for (int i0 = 0; i0 < n; i0 += BT) {
       a.tok0 = i0;
       a.B = std::min(BT, n - i0);
+      set_positions(a, kv->hlen);
       HIPCHECK(launch_batch_pass(c->cfg.weight_type, a, c->stream));
       kv->hlen[seq] += a.B;
     }
