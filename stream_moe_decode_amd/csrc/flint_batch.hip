@@ -120,7 +120,7 @@ __device__ __forceinline__ void i4_inputs(uint4 (&b)[4], const uint16_t* col, in
 // input row, null for a zero column).  int4: codes enter as 128 + u, two MFMAs with the constant -136 as
 // the weight operand remove the offset, then each row's group scale (four rows in one 8-byte load of the
 // regrouped scales) multiplies the group's fp32 result.  Every load of U chunks is issued first.
-template <int WT, int NT, class TileOf, class RowMap>
+template <int WT, int NT, int UF = 0, class TileOf, class RowMap>
 __device__ __forceinline__ void mma_tiles(f32x4_t (&acc)[NT], const Mat& m, int in, TileOf tile_of, RowMap rowmap,
                                           const uint16_t* col, int c0, int c1) {
   const int lane = threadIdx.x & 63, kg = lane >> 4, G = in / 64;
@@ -134,7 +134,7 @@ __device__ __forceinline__ void mma_tiles(f32x4_t (&acc)[NT], const Mat& m, int 
   }
   const I4K k4 = i4k();
   const bf16x8_t bias = bias136();
-  constexpr int U = WT == W_I4 ? (NT >= 4 ? 2 : 4) : (NT >= 4 ? 4 : 8);
+  constexpr int U = UF ? UF : (WT == W_I4 ? (NT >= 4 ? 2 : 4) : (NT >= 4 ? 4 : 8));
   constexpr int NB = WT == W_I4 ? 4 : 1;  // 16-byte input loads per chunk
   for (int c = c0; c < c1; c += U) {
     uint4 wv[U][NT], b[U][NB];
@@ -712,7 +712,8 @@ __global__ void __launch_bounds__(BNT) bk_gateup(const BArgs a, int l) {
       for (int q = 0; q < 4; ++q) acc[q] = f32x4_t{0.f, 0.f, 0.f, 0.f};
       auto rowmap = [&](int q, int m) -> long long { return base + t * 64 + q * 16 + m; };
       auto tile_of = [&](int q) -> long long { return (base >> 4) + t * 4 + q; };
-      mma_tiles<WT, 4>(acc, mat ? Mu : Mg, a.H, tile_of, rowmap, col, c0, c1);
+      // one chunk per load round keeps the kernel within two workgroups per compute unit
+      mma_tiles<WT, 4, 1>(acc, mat ? Mu : Mg, a.H, tile_of, rowmap, col, c0, c1);
 #pragma unroll
       for (int q = 0; q < 4; ++q) red[(wave * 8 + mat * 4 + q) * 64 + lane] = acc[q];
     }
