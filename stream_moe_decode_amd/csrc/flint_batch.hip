@@ -473,30 +473,24 @@ __device__ __forceinline__ void att_load(AttChunk& c, const uint8_t* kbase, cons
   }
 }
 
-// Attention of (split s, kv head j, column n) over positions [s P, min(s P + P, pos + 1)) of the column's
-// own cache (the new token's K/V already appended): scores on MFMA (the query split into bf16 high and low
-// parts), online softmax, P.V on the vector units.  The grid holds only real splits: workgroup x is split
-// x - asp[n] of column n.  Writes (m, l, o) of each query head of the group.
-__global__ void __launch_bounds__(ATT_NT) bk_attn(const BArgs a, int l) {
+// Attention of one split: kv head j of one column over cached positions [t0, t1) (t0 < t1) of the cache
+// slice at kbase / vbase, for the Gq query heads at qcol (fp32, head-major): scores on MFMA (the query split
+// into bf16 high and low parts), online softmax, P.V on the vector units.  Writes (m, l, o) of each query
+// head to dst + h * hstep.
+__device__ __forceinline__ void attn_split(const BArgs& a, const uint8_t* const kbase, const uint8_t* const vbase,
+                                           const float* qcol, int t0, int t1, float* const dst, size_t hstep) {
   __shared__ __align__(16) float ow[ATT_NW][4][128];
   __shared__ float mw[ATT_NW][4], lw[ATT_NW][4];
   __shared__ uint4 qop[4][2][64];  // [dims / 32][high, low][lane]
-  const int j = blockIdx.y, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  int n = 0;
-  while (n + 1 < a.B && a.asp[n + 1] <= (int)blockIdx.x) ++n;
-  const int s = blockIdx.x - a.asp[n];
-  const int T = a.pos[n] + 1, t0 = s * ATT_P;  // t0 < T: the host counts ceil(T / P) splits
-  const int t1 = min(t0 + ATT_P, T), tl = t1 - 1, hd = 128, Gq = a.nq / a.nkv;
-  const size_t cb = (((size_t)l * a.Bc + col_seq(a, n)) * a.nkv + j) * (size_t)a.cap * hd * 2;
-  const uint8_t* const kbase = a.kc + cb;
-  const uint8_t* const vbase = a.vc + cb;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tl = t1 - 1, hd = 128, Gq = a.nq / a.nkv;
   AttChunk buf[2];
   att_load(buf[0], kbase, vbase, t0 + wave * ATT_C, tl, lane);
   // the query as MFMA B operands (lane: head L % 16, dims (L / 16) * 8 ..), bf16 high and low parts, built by
   // wave 0 into LDS
   const int hcol = lane & 15, grp = lane >> 4;
   if (wave == 0) {
-    const float* qp = a.q + (size_t)n * a.nq * hd + ((size_t)j * Gq + min(hcol, Gq - 1)) * hd + grp * 8;
+    const float* qp = qcol + (size_t)min(hcol, Gq - 1) * hd + grp * 8;
     const float qm = hcol < Gq ? 1.0f / sqrtf((float)hd) : 0.f;
 #pragma unroll
     for (int sk = 0; sk < 4; ++sk) {
@@ -601,8 +595,6 @@ __global__ void __launch_bounds__(ATT_NT) bk_attn(const BArgs a, int l) {
     lw[wave][lane] = lsum;
   }
   __syncthreads();
-  float* const dst = a.part + (((size_t)n * a.nq + (size_t)j * Gq) * a.nsmax + s) * (hd + 2);
-  const size_t hstep = (size_t)a.nsmax * (hd + 2);  // between query heads
   for (int idx = tid; idx < Gq * hd; idx += ATT_NT) {
     const int h = idx / hd, e = idx % hd;
     float M = mw[0][h];  // wave 0 always has position t0
@@ -625,15 +617,28 @@ __global__ void __launch_bounds__(ATT_NT) bk_attn(const BArgs a, int l) {
   }
 }
 
-// Merge the splits of (query head h, column n): o = sum_s e^(m_s - M) o_s / sum_s e^(m_s - M) l_s, as the
-// o_proj input.  Thread d owns dim d; the splits are taken MB at a time with every load of a block (m, l
-// and o of each split) issued before any is used, and the blocks are folded by the running-max rule.
+// Attention of (split s, kv head j, column n) over positions [s P, min(s P + P, pos + 1)) of the column's
+// own cache (the new token's K/V already appended).  The grid holds only real splits: workgroup x is split
+// x - asp[n] of column n.
+__global__ void __launch_bounds__(ATT_NT) bk_attn(const BArgs a, int l) {
+  const int j = blockIdx.y, hd = 128, Gq = a.nq / a.nkv;
+  int n = 0;
+  while (n + 1 < a.B && a.asp[n + 1] <= (int)blockIdx.x) ++n;
+  const int s = blockIdx.x - a.asp[n];
+  const int T = a.pos[n] + 1, t0 = s * ATT_P;  // t0 < T: the host counts ceil(T / P) splits
+  const size_t cb = (((size_t)l * a.Bc + col_seq(a, n)) * a.nkv + j) * (size_t)a.cap * hd * 2;
+  attn_split(a, a.kc + cb, a.vc + cb, a.q + (size_t)n * a.nq * hd + (size_t)j * Gq * hd, t0, min(t0 + ATT_P, T),
+             a.part + (((size_t)n * a.nq + (size_t)j * Gq) * a.nsmax + s) * (hd + 2), (size_t)a.nsmax * (hd + 2));
+}
+
+// Merge of the ns splits at p (one query head of one column): o = sum_s e^(m_s - M) o_s / sum_s e^(m_s - M)
+// l_s, written in bf16 to out[act_pos(d)] (the o_proj input).  Thread d owns dim d; the splits are taken MB
+// at a time with every load of a block (m, l and o of each split) issued before any is used, and the
+// blocks are folded by the running-max rule.
 constexpr int MB = 32;
 template <int WT>
-__global__ void __launch_bounds__(128) bk_merge(const BArgs a) {
-  const int h = blockIdx.x, n = blockIdx.y, d = threadIdx.x, hd = a.hd;
-  const int ns = a.asp[n + 1] - a.asp[n];
-  const float* p = a.part + ((size_t)n * a.nq + h) * a.nsmax * (hd + 2);
+__device__ __forceinline__ void merge_head(const float* p, int ns, int hd, uint16_t* out) {
+  const int d = threadIdx.x;
   float M = -INFINITY, L = 0.f, O = 0.f;
   for (int s0 = 0; s0 < ns; s0 += MB) {
     float m[MB], lv[MB], o[MB];
@@ -658,7 +663,13 @@ __global__ void __launch_bounds__(128) bk_merge(const BArgs a) {
     }
     M = mb;
   }
-  gp(a.act)[(size_t)n * a.astride + act_pos<WT>(h * hd + d)] = (uint16_t)f2bf(O / L);
+  gp(out)[act_pos<WT>(d)] = (uint16_t)f2bf(O / L);
+}
+template <int WT>
+__global__ void __launch_bounds__(128) bk_merge(const BArgs a) {
+  const int h = blockIdx.x, n = blockIdx.y, hd = a.hd;
+  merge_head<WT>(a.part + ((size_t)n * a.nq + h) * a.nsmax * (hd + 2), a.asp[n + 1] - a.asp[n], hd,
+                 a.act + (size_t)n * a.astride + h * hd);
 }
 
 // o_proj rows t*16 .. t*16 + 15 over input chunk kc: partial sums, added to the residual by the next norm.
@@ -908,7 +919,7 @@ __global__ void __launch_bounds__(BNT) bk_head(const BArgs a) {
           gp(a.len)[a.seq0 + q] += 1;
         } else if (q == a.B - 1) {  // prefill: the id after the last prompt token of the pass
           gp(a.out_ids)[0] = id;
-          gp(a.len)[a.seq0] += a.B;
+          gp(a.len)[a.seq0] += a.lenadd;
         }
       }
       __hip_atomic_store(gp(a.done), 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -923,6 +934,338 @@ __global__ void regroup_scales_kernel(const uint16_t* s, uint16_t* s4, size_t ro
     const size_t r = i / G, g = i - r * G;
     s4[((r >> 2) * G + g) * 4 + (r & 3)] = s[i];
   }
+}
+
+// ---------------------------------------------------------------- prefill of long chunks
+// A chunk of n > BT prompt tokens of one sequence: the contractions run over 64 tokens per workgroup so
+// that every weight byte loaded feeds 64 tokens; attention runs per token over its own causal range
+// through the split / merge kernels; the experts run on the tokens that picked them, grouped by expert.
+
+constexpr int PF_T = 64;     // tokens per contraction workgroup
+constexpr int PF_NT = 256;   // its threads: 4 waves, each one 16-row weight tile against the 64 tokens
+constexpr int PF_PB = 512;   // columns per attention batch (bounds the partial-result buffer)
+enum { PF_QKV = 0, PF_ADD = 1, PF_SWIGLU = 2, PF_DOWNG = 3 };
+
+struct PfJob {
+  Mat m, m2;           // weights; m2: the up matrix of a SwiGLU job (waves 2 and 3)
+  long long tile0;     // first 16-row tile of the job's rows (grouped jobs: of expert 0 of the layer)
+  long long etiles;    // grouped jobs: tiles per expert
+  int K;               // inputs, a multiple of 128
+  const uint16_t* A;   // input rows, bf16 in GEMM input order
+  int lda;
+  int M;               // input rows of an ungrouped job
+  int grouped;         // 0: rows 0 .. M-1; 1: the token row of each list entry; 2: one input row per list entry
+  int l;               // layer
+  uint16_t* hout;      // SwiGLU output rows
+  int ldh;
+};
+
+// Output tile (64 rows x 64 tokens) of one job.  Wave w owns weight tile w (SwiGLU: gate tiles 0, 1 and up
+// tiles 2, 3 of 32 rows) and all four 16-token tiles; the tokens' inputs go to LDS 128 inputs at a time
+// (direct-to-LDS loads, wave w bringing token tile w), double-buffered against the MFMAs of the previous
+// 128, and each wave's weight chunk and scales are loaded into registers one stage ahead.  int4: the codes
+// are unpacked once per stage for the four token tiles; arithmetic as in the batched path (codes 128 + u,
+// the constant -136 operand, the group scale on each group's fp32 result).
+template <int WT, int EPI>
+__global__ void __launch_bounds__(PF_NT) pf_gemm(const BArgs a, const PfJob j) {
+  __shared__ uint4 abuf[2][16 * 64];  // [token tile][k-slice q][lane]
+  __shared__ f32x4_t upx[2][4][64];   // SwiGLU: the up tiles' results
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, n = lane & 15, kg = lane >> 4;
+  const int rb = blockIdx.x;
+  int r0, r1, e = 0;  // input rows (list entries of grouped jobs) [r0, r1) of this token block
+  if (j.grouped) {
+    if ((int)blockIdx.y >= gp(a.nblk)[0]) return;
+    const int32_t* bk = a.blk + 3 * blockIdx.y;
+    e = gp(bk)[0];
+    r0 = gp(bk)[1];
+    r1 = min(r0 + PF_T, gp(bk)[2]);
+  } else {
+    r0 = blockIdx.y * PF_T;
+    r1 = min(r0 + PF_T, j.M);
+  }
+  // input row of this lane in token tile `wave` (rows past r1 repeat the last one)
+  const int ri = min(r0 + wave * 16 + n, r1 - 1);
+  const int arow = j.grouped == 1 ? (gp(a.lst)[ri] >> 3) : ri;
+  const uint16_t* ap = j.A + (size_t)arow * j.lda;
+  constexpr bool SWI = EPI == PF_SWIGLU;
+  const Mat& M = SWI && wave >= 2 ? j.m2 : j.m;
+  const long long T = j.tile0 + (long long)e * j.etiles + (SWI ? rb * 2 + (wave & 1) : rb * 4 + wave);
+  const int C = j.K / kChunkIn<WT>, S = j.K / 128, G = j.K / 64;
+  const uint8_t* wp = M.wt + ((size_t)T * C * 64 + lane) * 16;
+  const long long srow = EPI == PF_QKV ? tile_row(T, 4 * kg, a.hd) : T * 16 + 4 * kg;  // rows 4 kg .. + 3
+  const uint16_t* sp = WT == W_I4 ? M.s4 + (size_t)(srow >> 2) * G * 4 : nullptr;
+  constexpr int NW4 = WT == W_I4 ? 1 : 4;  // weight chunks per stage
+  auto issue = [&](int s, uint4* buf) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int e0 = WT == W_I4 ? (2 * s + (q >> 1)) * 64 + kg * 16 + (q & 1) * 8 : (4 * s + q) * 32 + kg * 8;
+      dma16(ap + e0, &buf[(wave * 4 + q) * 64]);
+    }
+  };
+  uint4 wc[NW4], wn[NW4], sc = make_uint4(0u, 0u, 0u, 0u), sn = sc;
+  auto wload = [&](int s, uint4 (&w)[NW4], uint4& sv) {
+#pragma unroll
+    for (int q = 0; q < NW4; ++q) w[q] = ld16(wp + (size_t)(NW4 * s + q) * 1024);
+    if constexpr (WT == W_I4) sv = ld16(sp + (size_t)(2 * s) * 4);
+  };
+  f32x4_t acc[4];
+#pragma unroll
+  for (int t = 0; t < 4; ++t) acc[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  const I4K k4 = i4k();
+  const bf16x8_t bias = bias136();
+  wload(0, wc, sc);
+  issue(0, abuf[0]);
+  for (int s = 0; s < S; ++s) {
+    int later = 0;
+    if (s + 1 < S) {
+      wload(s + 1, wn, sn);
+      issue(s + 1, abuf[(s + 1) & 1]);
+      later = NW4 + (WT == W_I4 ? 1 : 0) + 4;
+    }
+    wait_vmem_dyn(later);  // stage s has landed (every wave's part of it, after the barrier)
+    __syncthreads();
+    const uint4* buf = abuf[s & 1];
+    if constexpr (WT == W_I4) {
+      const bf16x8_t c0 = unpack8(wc[0].x, k4), c1 = unpack8(wc[0].y, k4), c2 = unpack8(wc[0].z, k4),
+                     c3 = unpack8(wc[0].w, k4);
+      const float sa[4] = {bf2f(sc.x & 0xFFFFu), bf2f(sc.x >> 16), bf2f(sc.y & 0xFFFFu), bf2f(sc.y >> 16)};
+      const float sb[4] = {bf2f(sc.z & 0xFFFFu), bf2f(sc.z >> 16), bf2f(sc.w & 0xFFFFu), bf2f(sc.w >> 16)};
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const bf16x8_t b0 = as_bf16x8(buf[(t * 4 + 0) * 64 + lane]), b1 = as_bf16x8(buf[(t * 4 + 1) * 64 + lane]);
+        const bf16x8_t b2 = as_bf16x8(buf[(t * 4 + 2) * 64 + lane]), b3 = as_bf16x8(buf[(t * 4 + 3) * 64 + lane]);
+        f32x4_t da = {0.f, 0.f, 0.f, 0.f}, db = {0.f, 0.f, 0.f, 0.f};
+        da = mfma(bias, b0, da);
+        da = mfma(bias, b1, da);
+        db = mfma(bias, b2, db);
+        db = mfma(bias, b3, db);
+        da = mfma(c0, b0, da);
+        da = mfma(c1, b1, da);
+        db = mfma(c2, b2, db);
+        db = mfma(c3, b3, db);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) acc[t][r] = fmaf(sa[r], da[r], fmaf(sb[r], db[r], acc[t][r]));
+      }
+    } else {
+#pragma unroll
+      for (int t = 0; t < 4; ++t)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) acc[t] = mfma(as_bf16x8(wc[q]), as_bf16x8(buf[(t * 4 + q) * 64 + lane]), acc[t]);
+    }
+    __syncthreads();  // every wave is done with this buffer before stage s + 2 is loaded into it
+#pragma unroll
+    for (int q = 0; q < NW4; ++q) wc[q] = wn[q];
+    sc = sn;
+  }
+  // epilogue: lane holds rows 4 kg .. 4 kg + 3 of its tile for token n of each token tile
+  if constexpr (EPI == PF_SWIGLU) {
+    if (wave >= 2)
+#pragma unroll
+      for (int t = 0; t < 4; ++t) upx[wave - 2][t][lane] = acc[t];
+    __syncthreads();
+    if (wave >= 2) return;
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const int rr = r0 + t * 16 + n;
+      if (rr >= r1) continue;
+      const f32x4_t u = upx[wave][t][lane];
+      uint16_t* hr = j.hout + (size_t)rr * j.ldh;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float g = acc[t][r];
+        gp(hr)[act_pos<WT>(rb * 32 + wave * 16 + 4 * kg + r)] = (uint16_t)f2bf(g / (1.0f + __expf(-g)) * u[r]);
+      }
+    }
+  } else if constexpr (EPI == PF_ADD) {
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const int rr = r0 + t * 16 + n;
+      if (rr >= r1) continue;
+      f32x4_t* xp = reinterpret_cast<f32x4_t*>(a.x + (size_t)rr * a.H + rb * 64 + wave * 16 + 4 * kg);
+      gp(xp)[0] = gp(xp)[0] + acc[t];
+    }
+  } else if constexpr (EPI == PF_DOWNG) {
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const int rr = r0 + t * 16 + n;
+      if (rr >= r1) continue;
+      const int ent = gp(a.lst)[rr];
+      f32x4_t* yp = reinterpret_cast<f32x4_t*>(a.y + ((size_t)(ent >> 3) * a.K + (ent & 7)) * a.H + rb * 64 +
+                                                wave * 16 + 4 * kg);
+      gp(yp)[0] = acc[t];
+    }
+  } else {  // PF_QKV: RoPE on q and k heads (partner rows in lane ^ 32), q kept in fp32, K/V appended
+    const int hd = a.hd, half = hd / 2, tph = hd / 16;
+    const int tl = (int)(T - j.tile0), hh = tl / tph, i0 = (tl % tph) * 8;
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const int rr = min(r0 + t * 16 + n, r1 - 1), pos = a.p0 + rr;
+      float y[4] = {acc[t][0], acc[t][1], acc[t][2], acc[t][3]};
+      if (hh < a.nq + a.nkv) {
+        float pr[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) pr[r] = swap32(y[r]);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const f32x2_t cs = *(GLOBAL const f32x2_t*)(a.rope + (size_t)pos * half + i0 + 4 * (kg & 1) + r);
+          y[r] = kg < 2 ? y[r] * cs.x - pr[r] * cs.y : y[r] * cs.x + pr[r] * cs.y;
+        }
+      }
+      if (r0 + t * 16 + n >= r1) continue;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int m = 4 * kg + r, d = m < 8 ? i0 + m : half + i0 + m - 8;
+        if (hh < a.nq) {
+          gp(a.q)[((size_t)rr * a.nq + hh) * hd + d] = y[r];
+        } else {
+          const bool isk = hh < a.nq + a.nkv;
+          const int jh = isk ? hh - a.nq : hh - a.nq - a.nkv;
+          const size_t off = ((((size_t)j.l * a.Bc + a.seq0) * a.nkv + jh) * a.cap + pos) * hd + d;
+          gp(reinterpret_cast<uint16_t*>(isk ? a.kc : a.vc))[off] = (uint16_t)f2bf(y[r]);
+        }
+      }
+    }
+  }
+}
+
+// Entries per expert among the chunk's n K (token, slot) picks.
+__global__ void __launch_bounds__(256) pf_count(const BArgs a, int n) {
+  __shared__ float wred[4];
+  const int e = blockIdx.x;
+  int c = 0;
+  for (int i = threadIdx.x; i < n * a.K; i += 256) c += gp(a.sel)[i] == e;
+  float v = wave_sum((float)c);
+  if ((threadIdx.x & 63) == 0) wred[threadIdx.x >> 6] = v;
+  __syncthreads();
+  if (threadIdx.x == 0) gp(a.ecnt)[e] = (int)(wred[0] + wred[1] + wred[2] + wred[3]);
+}
+
+// Expert e's entries (token << 3 | slot) in token order at the sum of the earlier experts' counts, and its
+// blocks of up to 64 entries in the block table after the earlier experts' blocks.
+__global__ void __launch_bounds__(256) pf_fill(const BArgs a, int n) {
+  __shared__ int wc[4];
+  __shared__ int base[2];
+  const int e = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, nk = n * a.K;
+  if (wave == 0) {
+    const int c = lane < a.E ? gp(a.ecnt)[lane] : 0, nb = (c + PF_T - 1) / PF_T;
+    const int off = (int)wave_sum(lane < e ? (float)c : 0.f), boff = (int)wave_sum(lane < e ? (float)nb : 0.f);
+    const int tot = (int)wave_sum((float)nb);
+    if (lane == 0) {
+      base[0] = off;
+      base[1] = boff;
+      if (e == 0) gp(a.nblk)[0] = tot;
+    }
+    if (lane == e)
+      for (int b = 0; b < nb; ++b) {
+        gp(a.blk)[3 * (boff + b)] = e;
+        gp(a.blk)[3 * (boff + b) + 1] = off + b * PF_T;
+        gp(a.blk)[3 * (boff + b) + 2] = off + c;
+      }
+  }
+  __syncthreads();
+  int run = base[0];
+  for (int i0 = 0; i0 < nk; i0 += 256) {
+    const int i = i0 + tid;
+    const bool m = i < nk && gp(a.sel)[i] == e;
+    const unsigned long long bal = __ballot(m);
+    if (lane == 0) wc[wave] = __popcll(bal);
+    __syncthreads();
+    int pre = run;
+    for (int w = 0; w < wave; ++w) pre += wc[w];
+    if (m) gp(a.lst)[pre + __popcll(bal & ((1ull << lane) - 1ull))] = ((i / a.K) << 3) | (i % a.K);
+    run += wc[0] + wc[1] + wc[2] + wc[3];
+    __syncthreads();
+  }
+}
+
+// x[t] += sum over slots k (in order) of wsel[t][k] y[t][k].
+__global__ void __launch_bounds__(256) pf_combine(const BArgs a) {
+  const int t = blockIdx.x;
+  for (int r = threadIdx.x * 4; r < a.H; r += 1024) {
+    f32x4_t* xp = reinterpret_cast<f32x4_t*>(a.x + (size_t)t * a.H + r);
+    f32x4_t v = gp(xp)[0];
+    for (int k = 0; k < a.K; ++k)
+      v += gp(a.wsel)[t * a.K + k] * gp(reinterpret_cast<const f32x4_t*>(a.y + ((size_t)t * a.K + k) * a.H + r))[0];
+    gp(xp)[0] = v;
+  }
+}
+
+// Splits of the columns before n: the sum over t in (p0 + c0, p0 + n] of ceil(t / P), from
+// g(T) = sum_{t <= T} ceil(t / P) = P q (q + 1) / 2 + r (q + 1) with T = q P + r.
+__host__ __device__ __forceinline__ long long pf_splits_upto(long long T) {
+  const long long q = T / ATT_P, r = T - q * ATT_P;
+  return ATT_P * q * (q + 1) / 2 + r * (q + 1);
+}
+// Attention of the chunk's columns [c0, c1) (token n at position p0 + n sees positions 0 .. p0 + n):
+// workgroup x is the split of the column found by bisection on the closed form above.
+__global__ void __launch_bounds__(ATT_NT) pf_attn(const BArgs a, int l, int c0, int c1) {
+  const int j = blockIdx.y, hd = 128, Gq = a.nq / a.nkv;
+  const long long x = blockIdx.x, g0 = pf_splits_upto((long long)a.p0 + c0);
+  int lo = c0, hi = c1 - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (pf_splits_upto((long long)a.p0 + mid) - g0 <= x) lo = mid;
+    else hi = mid - 1;
+  }
+  const int n = lo, s = (int)(x - (pf_splits_upto((long long)a.p0 + n) - g0));
+  const int T = a.p0 + n + 1, t0 = s * ATT_P;
+  const size_t cb = (((size_t)l * a.Bc + a.seq0) * a.nkv + j) * (size_t)a.cap * hd * 2;
+  attn_split(a, a.kc + cb, a.vc + cb, a.q + (size_t)n * a.nq * hd + (size_t)j * Gq * hd, t0, min(t0 + ATT_P, T),
+             a.part + (((size_t)(n - c0) * a.nq + (size_t)j * Gq) * a.nsmax + s) * (hd + 2),
+             (size_t)a.nsmax * (hd + 2));
+}
+template <int WT>
+__global__ void __launch_bounds__(128) pf_merge(const BArgs a, int c0) {
+  const int h = blockIdx.x, n = c0 + blockIdx.y, hd = a.hd;
+  merge_head<WT>(a.part + ((size_t)blockIdx.y * a.nq + h) * a.nsmax * (hd + 2), (a.p0 + n + ATT_P) / ATT_P, hd,
+                 a.act + (size_t)n * a.astride + h * hd);
+}
+
+template <int WT> hipError_t run_prefill(const BArgs& a0, int n, hipStream_t st) {
+  BArgs a = a0;
+  a.B = n;
+  a.prefill = 1;
+  a.tok0 = 0;
+  const int QR = (a.nq + 2 * a.nkv) * a.hd, QD = a.nq * a.hd, TB = (n + PF_T - 1) / PF_T;
+  const int NBM = (n * a.K + PF_T - 1) / PF_T + a.E;
+  const Mat none{};
+  for (int l = 0; l < a.L; ++l) {
+    hipLaunchKernelGGL(bk_norm<WT>, dim3(n), dim3(BNT), 0, st, a, l, l == 0 ? (int)NORM_EMBED : (int)NORM_INPUT);
+    const PfJob jq{a.qkv, none, (long long)l * (QR / 16), 0, a.H, a.act, a.astride, n, 0, l, nullptr, 0};
+    hipLaunchKernelGGL((pf_gemm<WT, PF_QKV>), dim3(QR / 64, TB), dim3(PF_NT), 0, st, a, jq);
+    for (int c0 = 0; c0 < n; c0 += PF_PB) {
+      const int c1 = std::min(n, c0 + PF_PB);
+      const long long ns = pf_splits_upto((long long)a.p0 + c1) - pf_splits_upto((long long)a.p0 + c0);
+      hipLaunchKernelGGL(pf_attn, dim3((unsigned)ns, a.nkv), dim3(ATT_NT), 0, st, a, l, c0, c1);
+      hipLaunchKernelGGL(pf_merge<WT>, dim3(a.nq, c1 - c0), dim3(a.hd), 0, st, a, c0);
+    }
+    const PfJob jo{a.o, none, (long long)l * (a.H / 16), 0, QD, a.act, a.astride, n, 0, l, nullptr, 0};
+    hipLaunchKernelGGL((pf_gemm<WT, PF_ADD>), dim3(a.H / 64, TB), dim3(PF_NT), 0, st, a, jo);
+    hipLaunchKernelGGL(bk_norm<WT>, dim3(n), dim3(BNT), 0, st, a, l, (int)NORM_POST);
+    if (l < a.n_dense) {
+      const PfJob jg{a.dg, a.du, (long long)l * (a.DI / 16), 0, a.H, a.act, a.astride, n, 0, l, a.h, a.DI};
+      hipLaunchKernelGGL((pf_gemm<WT, PF_SWIGLU>), dim3(a.DI / 32, TB), dim3(PF_NT), 0, st, a, jg);
+      const PfJob jd{a.dd, none, (long long)l * (a.H / 16), 0, a.DI, a.h, a.DI, n, 0, l, nullptr, 0};
+      hipLaunchKernelGGL((pf_gemm<WT, PF_ADD>), dim3(a.H / 64, TB), dim3(PF_NT), 0, st, a, jd);
+    } else {
+      const long long lm = l - a.n_dense;
+      hipLaunchKernelGGL(pf_count, dim3(a.E), dim3(256), 0, st, a, n);
+      hipLaunchKernelGGL(pf_fill, dim3(a.E), dim3(256), 0, st, a, n);
+      const PfJob jg{a.eg, a.eu, lm * a.E * (a.EI / 16), a.EI / 16, a.H, a.act, a.astride, 0, 1, l, a.h, a.EI};
+      hipLaunchKernelGGL((pf_gemm<WT, PF_SWIGLU>), dim3(a.EI / 32, NBM), dim3(PF_NT), 0, st, a, jg);
+      const PfJob jd{a.ed, none, lm * a.E * (a.H / 16), a.H / 16, a.EI, a.h, a.EI, 0, 2, l, nullptr, 0};
+      hipLaunchKernelGGL((pf_gemm<WT, PF_DOWNG>), dim3(a.H / 64, NBM), dim3(PF_NT), 0, st, a, jd);
+      hipLaunchKernelGGL(pf_combine, dim3(n), dim3(256), 0, st, a);
+    }
+  }
+  // the last token: final norm, lm_head, argmax; the length advances by n
+  BArgs f = a;
+  f.B = 1;
+  f.x = a.x + (size_t)(n - 1) * a.H;
+  f.lenadd = n;
+  hipLaunchKernelGGL(bk_norm<WT>, dim3(1), dim3(BNT), 0, st, f, a.L, (int)NORM_FINAL);
+  hipLaunchKernelGGL(bk_head, dim3(std::min(256, a.V / 16)), dim3(BNT), 0, st, f);
+  return hipGetLastError();
 }
 
 template <int WT> hipError_t run_pass(const BArgs& a, hipStream_t st) {
@@ -948,6 +1291,12 @@ template <int WT> hipError_t run_pass(const BArgs& a, hipStream_t st) {
 hipError_t launch_batch_pass(int wt, const BArgs& a, hipStream_t stream) {
   return wt == W_I4 ? run_pass<W_I4>(a, stream) : run_pass<W_BF16>(a, stream);
 }
+
+hipError_t launch_prefill(int wt, const BArgs& a, int n, hipStream_t stream) {
+  return wt == W_I4 ? run_prefill<W_I4>(a, n, stream) : run_prefill<W_BF16>(a, n, stream);
+}
+
+size_t prefill_part_floats(int nq, int nsmax, int hd) { return (size_t)PF_PB * nq * nsmax * (hd + 2); }
 
 hipError_t launch_tile_weights(int wt, const uint8_t* w, uint8_t* dst, size_t rows, int in, int rope_hd,
                                hipStream_t stream) {

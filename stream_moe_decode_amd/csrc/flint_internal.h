@@ -133,6 +133,14 @@ struct BArgs {
   int hstride;
   int32_t* sel;          // [BT][K] selected experts
   float* wsel;           // [BT][K] their weights
+  // prefill of a chunk of n > BT tokens of sequence seq0 at positions p0 .. p0 + n - 1 (the buffers above then
+  // hold n rows); the head adds lenadd to the length (batched prefill passes: B)
+  int p0, lenadd;
+  float* y;              // [n][K][H] expert down products per (token, slot)
+  int32_t* lst;          // [n K] (token << 3 | slot), grouped by expert in expert order, tokens ascending
+  int32_t* ecnt;         // [E] entries per expert
+  int32_t* blk;          // [n K / 64 + E][3] token blocks: (expert, first entry, end of the expert's entries)
+  int32_t* nblk;         // [1] token blocks in use
   unsigned long long* amax;  // [BT] packed argmax keys
   uint32_t* done;        // workgroups finished with lm_head
   uint32_t* cnt;         // [H/16 + H/64] workgroups finished per o_proj row tile, then per down row block
@@ -147,6 +155,10 @@ struct BArgs {
 
 // Enqueue one batched decode pass (every layer and the head) on `stream`.
 hipError_t launch_batch_pass(int wt, const BArgs& a, hipStream_t stream);
+// Prefill of n (BT < n <= 4096) tokens of sequence a.seq0 at positions a.p0 .. through the long-chunk
+// kernels; a's buffers hold n rows (a.part: prefill_part_floats floats).
+hipError_t launch_prefill(int wt, const BArgs& a, int n, hipStream_t stream);
+size_t prefill_part_floats(int nq, int nsmax, int hd);
 // s4[((r / 4) * G + g) * 4 + r % 4] = s[r * G + g] for r < rows (a multiple of 4), g < G.
 hipError_t launch_regroup_scales(const uint16_t* s, uint16_t* s4, size_t rows, int G, hipStream_t stream);
 // Copy a [rows][in] weight matrix into the tiled layout of the batched path (rows a multiple of 16).  Tile

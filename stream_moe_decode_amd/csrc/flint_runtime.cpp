@@ -78,6 +78,8 @@ struct flint_kv {
   std::vector<int32_t> hlen;
   void* bscratch;             // scratch of the batched path (batch > 1), null otherwise
   BArgs bargs;                // its buffers and the pass-invariant arguments
+  void* pscratch;             // scratch of the long-chunk prefill (made by its first use), null otherwise
+  BArgs pargs;                // bargs with the buffers pointed at pscratch
 };
 
 namespace {
@@ -355,6 +357,48 @@ int batch_scratch(flint_ctx* c, flint_kv* kv) {
   return FLINT_OK;
 }
 
+// Scratch of the long-chunk prefill (chunks of up to PF_MAXN tokens), carved like batch_scratch.
+constexpr int PF_MAXN = 4096;
+int prefill_scratch(flint_ctx* c, flint_kv* kv) {
+  const flint_config& cfg = c->cfg;
+  BArgs a = kv->bargs;
+  const size_t N = PF_MAXN, H = cfg.hidden, QD = (size_t)cfg.n_q_heads * cfg.head_dim, K = cfg.top_k;
+  const size_t ND = cfg.n_dense_layers, NM = cfg.n_layers - ND;
+  const size_t hw = std::max(ND ? (size_t)cfg.dense_inter : 0, NM ? K * cfg.expert_inter : 0);
+  auto r256 = [](size_t b) { return (b + 255) & ~(size_t)255; };
+  const size_t sx = r256(N * H * 4), sact = r256(N * a.astride * 2), sq = r256(N * QD * 4);
+  const size_t spart = r256(prefill_part_floats(cfg.n_q_heads, a.nsmax, cfg.head_dim) * 4);
+  const size_t sh = r256(N * hw * 2), ssel = r256(N * K * 4), sy = r256(N * K * H * 4);
+  const size_t secnt = r256(((size_t)cfg.n_experts + 1) * 4), sblk = r256(((N * K + 63) / 64 + cfg.n_experts) * 3 * 4);
+  const size_t total = sx + sact + sq + spart + sh + 3 * ssel + sy + secnt + sblk;
+  if (hipMalloc(&kv->pscratch, total) != hipSuccess) {
+    kv->pscratch = nullptr;
+    return fail(FLINT_ENOMEM, "prefill scratch of %zu bytes", total);
+  }
+  char* p = (char*)kv->pscratch;
+  auto take = [&](size_t b) {
+    char* q = p;
+    p += b;
+    return q;
+  };
+  a.x = (float*)take(sx);
+  a.act = (uint16_t*)take(sact);
+  a.q = (float*)take(sq);
+  a.part = (float*)take(spart);
+  a.h = (uint16_t*)take(sh);
+  a.sel = (int32_t*)take(ssel);
+  a.wsel = (float*)take(ssel);
+  a.lst = (int32_t*)take(ssel);
+  a.y = (float*)take(sy);
+  a.ecnt = (int32_t*)take(secnt);
+  a.nblk = a.ecnt + cfg.n_experts;
+  a.blk = (int32_t*)take(sblk);
+  kv->pargs = a;
+  if (hipMemsetAsync(kv->pscratch, 0, total, c->stream) != hipSuccess || hipStreamSynchronize(c->stream) != hipSuccess)
+    return fail(FLINT_EHIP, "prefill scratch initialisation failed");
+  return FLINT_OK;
+}
+
 // Positions of a pass's columns from the host's mirror of the lengths, and the attention splits per column.
 void set_positions(BArgs& a, const std::vector<int32_t>& hlen) {
   a.asp[0] = 0;
@@ -540,6 +584,7 @@ int flint_kv_alloc(flint_ctx* c, int32_t batch, int32_t max_tokens, flint_kv** o
   kv->len = nullptr;
   kv->rope = nullptr;
   kv->bscratch = nullptr;
+  kv->pscratch = nullptr;
   auto bail = [&](int code) {
     if (kv->k) (void)hipFree(kv->k);
     if (kv->v) (void)hipFree(kv->v);
@@ -582,6 +627,7 @@ int flint_kv_free(flint_kv* kv) {
   if (!kv) return FLINT_OK;
   (void)hipStreamSynchronize(kv->ctx->stream);
   if (kv->bscratch) (void)hipFree(kv->bscratch);
+  if (kv->pscratch) (void)hipFree(kv->pscratch);
   (void)hipFree(kv->k);
   (void)hipFree(kv->v);
   (void)hipFree(kv->len);
@@ -674,6 +720,20 @@ int flint_prefill_chunk(flint_ctx* c, flint_kv* kv, int32_t seq, const int32_t* 
     rc = batch_scratch(c, kv);
     if (rc) return rc;
   }
+  if (kv->bscratch && n > BT) {  // long chunk: contractions over 64 tokens per workgroup
+    if (!kv->pscratch) {
+      rc = prefill_scratch(c, kv);
+      if (rc) return rc;
+    }
+    BArgs a = kv->pargs;
+    a.seq0 = seq;
+    a.tokens = tokens;
+    a.out_ids = out_id;
+    a.p0 = kv->hlen[seq];
+    HIPCHECK(launch_prefill(c->cfg.weight_type, a, n, c->stream));
+    kv->hlen[seq] += n;
+    return FLINT_OK;
+  }
   if (kv->bscratch) {  // batched path: up to BT prompt tokens per pass, causal over the shared cache
     BArgs a = kv->bargs;
     a.prefill = 1;
@@ -683,6 +743,7 @@ int flint_prefill_chunk(flint_ctx* c, flint_kv* kv, int32_t seq, const int32_t* 
     for (int i0 = 0; i0 < n; i0 += BT) {
       a.tok0 = i0;
       a.B = std::min(BT, n - i0);
+      a.lenadd = a.B;
       set_positions(a, kv->hlen);
       HIPCHECK(launch_batch_pass(c->cfg.weight_type, a, c->stream));
       kv->hlen[seq] += a.B;

@@ -138,3 +138,46 @@ def test_prefill_passes_match_oracle():
     for _ in range(3):
         tok = st.step(tok)
     model.free()
+
+
+def _prefill_then_steps(cfg, chunks, steps=2):
+    # prompt chunks through flint_prefill_chunk from an empty cache (each chunk after the previous ones), the
+    # greedy id after each chunk against the oracle's, then greedy steps checked like decode steps
+    from gpu_common import Stepper
+    from stream_moe_decode_amd import prefill_chunk
+    model = build(cfg)
+    total = sum(chunks)
+    cap = total + steps + 8
+    kv = model.kv(1, cap)
+    orc = make_oracle(cfg, cap)
+    prompt = synth.tokens(cfg, total, stream=19)
+    dev = model.device
+    toks = torch.from_numpy(prompt).to(dev)
+    out = torch.zeros(1, dtype=torch.int32, device=dev)
+    i0 = 0
+    for n in chunks:
+        print(f"{cfg.name}: prefill of tokens {i0} .. {i0 + n - 1}", flush=True)
+        prefill_chunk(model.ctx, kv.handle, 0, toks.data_ptr() + 4 * i0, n, out.data_ptr())
+        sync(model.ctx)
+        r = orc.forward(0, prompt[i0:i0 + n])
+        gpu_id, o_id, gap = int(out.item()), int(r["ids"][-1]), float(r["gap"][-1])
+        print(f"  gpu id {gpu_id} oracle id {o_id} oracle gap {gap:.3g}", flush=True)
+        assert gpu_id == o_id or gap < TIE_EPS
+        i0 += n
+        assert kv_get_lengths(kv.handle, 1) == [i0]
+    st = Stepper(cfg, model, kv, orc)
+    tok = int(out.item())
+    for _ in range(steps):
+        tok = st.step(tok)
+    model.free()
+
+
+def test_long_prefill_chunks_match_oracle():
+    # 700 prompt tokens as chunks of 600 (two attention column batches, ragged 64-token blocks, uneven
+    # expert loads) and 100 (positions after 600 cached ones) through the long-chunk kernels
+    _prefill_then_steps(SMALL, [600, 100])
+
+
+def test_long_prefill_bf16():
+    # the same kernels with bf16 weights: 200 tokens, then 70 more
+    _prefill_then_steps(SMALL.replace(name="bf16_b16_small", weight_type=synth.BF16), [200, 70])
