@@ -938,8 +938,8 @@ __global__ void regroup_scales_kernel(const uint16_t* s, uint16_t* s4, size_t ro
 
 // ---------------------------------------------------------------- prefill of long chunks
 // A chunk of n > BT prompt tokens of one sequence: the contractions run over 64 tokens per workgroup so
-// that every weight byte loaded feeds 64 tokens; attention runs per token over its own causal range
-// through the split / merge kernels; the experts run on the tokens that picked them, grouped by expert.
+// that every weight byte loaded feeds 64 tokens; attention runs on MFMA per block of 16 tokens and split of
+// cached positions, merged per token; the experts run on the tokens that picked them, grouped by expert.
 
 constexpr int PF_T = 64;     // tokens per contraction workgroup
 constexpr int PF_NT = 256;   // its threads: 4 waves, each one 16-row weight tile against the 64 tokens
@@ -1190,29 +1190,139 @@ __global__ void __launch_bounds__(256) pf_combine(const BArgs a) {
   }
 }
 
-// Splits of the columns before n: the sum over t in (p0 + c0, p0 + n] of ceil(t / P), from
-// g(T) = sum_{t <= T} ceil(t / P) = P q (q + 1) / 2 + r (q + 1) with T = q P + r.
-__host__ __device__ __forceinline__ long long pf_splits_upto(long long T) {
-  const long long q = T / ATT_P, r = T - q * ATT_P;
-  return ATT_P * q * (q + 1) / 2 + r * (q + 1);
+// Prefill attention, flash style: workgroup (query block b of 16 tokens, key split s of ATT_P positions,
+// kv head j); wave w is query head j Gq + w over the block's tokens.  Scores are computed transposed,
+// S^T = K Q^T on v_mfma_f32_16x16x32_bf16 (K as the A operand, the query's bf16 high and low parts as B), so
+// that a lane holds 4 keys of one query row: the online softmax of a row stays in its lane group, and the
+// probabilities are already the B operand of O^T += V^T P^T on v_mfma_f32_16x16x16_bf16 (high and low
+// parts again).  V^T comes from row-major V in LDS through the transposing LDS read (ds_read_b64_tr_b16);
+// V's 16-byte units are XOR-swizzled by row so that those reads spread over the banks.  K and V go to LDS
+// 64 keys at a time, double-buffered.  Writes the split's (m, l, o) per token and head; a token's splits
+// past its own causal range are written but never merged.
+constexpr int FA_Q = 16, FA_KS = 64;
+typedef short s16x4_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ f32x4_t mfma16(s16x4_t a, s16x4_t b, f32x4_t c) {
+  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
 }
-// Attention of the chunk's columns [c0, c1) (token n at position p0 + n sees positions 0 .. p0 + n):
-// workgroup x is the split of the column found by bisection on the closed form above.
-__global__ void __launch_bounds__(ATT_NT) pf_attn(const BArgs a, int l, int c0, int c1) {
-  const int j = blockIdx.y, hd = 128, Gq = a.nq / a.nkv;
-  const long long x = blockIdx.x, g0 = pf_splits_upto((long long)a.p0 + c0);
-  int lo = c0, hi = c1 - 1;
-  while (lo < hi) {
-    const int mid = (lo + hi + 1) >> 1;
-    if (pf_splits_upto((long long)a.p0 + mid) - g0 <= x) lo = mid;
-    else hi = mid - 1;
-  }
-  const int n = lo, s = (int)(x - (pf_splits_upto((long long)a.p0 + n) - g0));
-  const int T = a.p0 + n + 1, t0 = s * ATT_P;
+__global__ void __launch_bounds__(256) pf_fattn(const BArgs a, int l, int c0, int c1) {
+  __shared__ uint4 kl[2][FA_KS * 16];  // [chunk of 16 keys][dims / 32][lane]: the A operand of S^T
+  __shared__ uint4 vl[2][FA_KS * 16];  // [key][16-byte unit ^ (key & 15)]
+  const int b = blockIdx.x, s = blockIdx.y, j = blockIdx.z;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, i = lane & 15, g = lane >> 4;
+  const int t0 = c0 + b * FA_Q, tq1 = min(t0 + FA_Q, c1);
+  const int k0 = s * ATT_P, kend = a.p0 + tq1;  // keys [0, kend) are visible to some token of the block
+  if (t0 >= c1 || k0 >= kend) return;
+  const int k1 = min(k0 + ATT_P, kend), hd = 128, Gq = a.nq / a.nkv;
   const size_t cb = (((size_t)l * a.Bc + a.seq0) * a.nkv + j) * (size_t)a.cap * hd * 2;
-  attn_split(a, a.kc + cb, a.vc + cb, a.q + (size_t)n * a.nq * hd + (size_t)j * Gq * hd, t0, min(t0 + ATT_P, T),
-             a.part + (((size_t)(n - c0) * a.nq + (size_t)j * Gq) * a.nsmax + s) * (hd + 2),
-             (size_t)a.nsmax * (hd + 2));
+  const uint8_t* const kb = a.kc + cb;
+  const uint8_t* const vb = a.vc + cb;
+  auto issue = [&](int ks, int buf) {  // keys [ks, ks + 64), past k1 re-reading k1 - 1: 8 loads per wave
+#pragma unroll
+    for (int q = wave; q < 16; q += 4) {
+      const int c = q >> 2, sk = q & 3, key = min(ks + 16 * c + i, k1 - 1);
+      dma16(kb + (size_t)key * 256 + sk * 64 + g * 16, &kl[buf][q * 64]);
+    }
+#pragma unroll
+    for (int q = wave; q < 16; q += 4) {
+      const int row = 4 * q + g, key = min(ks + row, k1 - 1);
+      dma16(vb + (size_t)key * 256 + (i ^ (row & 15)) * 16, &vl[buf][q * 64]);
+    }
+  };
+  issue(k0, 0);
+  // this wave's query rows as B operands of S^T: token t0 + i, dims 32 sk + 8 g .. + 8, high and low parts
+  const bool act = wave < Gq;
+  const int head = j * Gq + min(wave, Gq - 1), tq = min(t0 + i, tq1 - 1), qpos = a.p0 + t0 + i;
+  const float* qp = a.q + ((size_t)tq * a.nq + head) * hd + g * 8;
+  const float qm = 1.0f / sqrtf((float)hd);
+  bf16x8_t qh[4], ql[4];
+#pragma unroll
+  for (int sk = 0; sk < 4; ++sk) {
+    const f32x4_t x0 = *(GLOBAL const f32x4_t*)(qp + sk * 32), x1 = *(GLOBAL const f32x4_t*)(qp + sk * 32 + 4);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float qv = (e < 4 ? x0[e] : x1[e - 4]) * qm;
+      const uint32_t hb = f2bf(qv);
+      qh[sk][e] = __builtin_bit_cast(__bf16, (uint16_t)hb);
+      ql[sk][e] = __builtin_bit_cast(__bf16, (uint16_t)f2bf(qv - bf2f(hb)));
+    }
+  }
+  float m = -INFINITY, lsum = 0.f;  // of query row i
+  f32x4_t o[8];                     // O^T: dims 16 db + 4 g + r of query row i
+#pragma unroll
+  for (int db = 0; db < 8; ++db) o[db] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  const int nst = (k1 - k0 + FA_KS - 1) / FA_KS;
+  for (int st = 0; st < nst; ++st) {
+    const int ks = k0 + st * FA_KS, buf = st & 1;
+    int later = 0;
+    if (st + 1 < nst) {
+      issue(ks + FA_KS, buf ^ 1);
+      later = 8;
+    }
+    wait_vmem_dyn(later);
+    __syncthreads();
+    if (act) {
+      const uint8_t* vlb = reinterpret_cast<const uint8_t*>(vl[buf]);
+      for (int c = 0; c < FA_KS / 16; ++c) {
+        const int kc0 = ks + 16 * c;
+        if (kc0 >= k1) break;
+        f32x4_t sc = {0.f, 0.f, 0.f, 0.f};  // S^T: keys kc0 + 4 g + r, query row i
+#pragma unroll
+        for (int sk = 0; sk < 4; ++sk) {
+          const bf16x8_t kop = as_bf16x8(kl[buf][(c * 4 + sk) * 64 + lane]);
+          sc = mfma(kop, qh[sk], sc);
+          sc = mfma(kop, ql[sk], sc);
+        }
+        float sv[4], mx = -INFINITY;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int kp = kc0 + 4 * g + r;
+          sv[r] = kp < k1 && kp <= qpos ? sc[r] : -INFINITY;
+          mx = fmaxf(mx, sv[r]);
+        }
+        mx = fmaxf(mx, swap16(mx));
+        mx = fmaxf(mx, swap32(mx));
+        const float mn = fmaxf(m, mx), mref = mn == -INFINITY ? 0.f : mn;
+        const float alpha = __expf(m - mref);
+        float p[4], ps = 0.f;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          p[r] = __expf(sv[r] - mref);
+          ps += p[r];
+        }
+        ps += swap16(ps);
+        ps += swap32(ps);
+        lsum = lsum * alpha + ps;
+        m = mn;
+        s16x4_t ph, pl;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const uint32_t hb = f2bf(p[r]);
+          ph[r] = (short)hb;
+          pl[r] = (short)f2bf(p[r] - bf2f(hb));
+        }
+        // V^T operand of dims 16 db .. + 16: this lane passes key row 16 c + 4 g + i / 4, dims 16 db + 4 (i & 3)
+        const int row = 16 * c + 4 * g + (i >> 2);
+#pragma unroll
+        for (int db = 0; db < 8; ++db) {
+          const int u = 2 * db + ((i & 3) >> 1);
+          const s16x4_t vt = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (__attribute__((address_space(3))) s16x4_t*)(vlb + row * 256 + ((u ^ (row & 15)) * 16) + (i & 1) * 8));
+          o[db] *= alpha;
+          o[db] = mfma16(vt, ph, o[db]);
+          o[db] = mfma16(vt, pl, o[db]);
+        }
+      }
+    }
+    __syncthreads();  // every wave is done with this buffer before it is refilled
+  }
+  if (!act || t0 + i >= tq1) return;
+  float* dst = a.part + (((size_t)(t0 + i - c0) * a.nq + head) * a.nsmax + s) * (hd + 2);
+#pragma unroll
+  for (int db = 0; db < 8; ++db) *(GLOBAL f32x4_t*)(dst + 2 + 16 * db + 4 * g) = o[db];
+  if (g == 0) {
+    gp(dst)[0] = m;
+    gp(dst)[1] = lsum;
+  }
 }
 template <int WT>
 __global__ void __launch_bounds__(128) pf_merge(const BArgs a, int c0) {
@@ -1235,8 +1345,8 @@ template <int WT> hipError_t run_prefill(const BArgs& a0, int n, hipStream_t st)
     hipLaunchKernelGGL((pf_gemm<WT, PF_QKV>), dim3(QR / 64, TB), dim3(PF_NT), 0, st, a, jq);
     for (int c0 = 0; c0 < n; c0 += PF_PB) {
       const int c1 = std::min(n, c0 + PF_PB);
-      const long long ns = pf_splits_upto((long long)a.p0 + c1) - pf_splits_upto((long long)a.p0 + c0);
-      hipLaunchKernelGGL(pf_attn, dim3((unsigned)ns, a.nkv), dim3(ATT_NT), 0, st, a, l, c0, c1);
+      hipLaunchKernelGGL(pf_fattn, dim3((c1 - c0 + FA_Q - 1) / FA_Q, (a.p0 + c1 + ATT_P - 1) / ATT_P, a.nkv),
+                         dim3(256), 0, st, a, l, c0, c1);
       hipLaunchKernelGGL(pf_merge<WT>, dim3(a.nq, c1 - c0), dim3(a.hd), 0, st, a, c0);
     }
     const PfJob jo{a.o, none, (long long)l * (a.H / 16), 0, QD, a.act, a.astride, n, 0, l, nullptr, 0};
