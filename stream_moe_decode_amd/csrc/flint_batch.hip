@@ -968,7 +968,7 @@ struct PfJob {
 // the constant -136 operand, the group scale on each group's fp32 result).
 template <int WT, int EPI>
 __global__ void __launch_bounds__(PF_NT) pf_gemm(const BArgs a, const PfJob j) {
-  __shared__ uint4 abuf[2][16 * 64];  // [token tile][k-slice q][lane]
+  __shared__ uint4 abuf[2][PF_T * 16];  // [token][16-byte unit ^ (token & 15)] of 128 inputs
   __shared__ f32x4_t upx[2][4][64];   // SwiGLU: the up tiles' results
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, n = lane & 15, kg = lane >> 4;
   const int rb = blockIdx.x;
@@ -983,10 +983,15 @@ __global__ void __launch_bounds__(PF_NT) pf_gemm(const BArgs a, const PfJob j) {
     r0 = blockIdx.y * PF_T;
     r1 = min(r0 + PF_T, j.M);
   }
-  // input row of this lane in token tile `wave` (rows past r1 repeat the last one)
-  const int ri = min(r0 + wave * 16 + n, r1 - 1);
-  const int arow = j.grouped == 1 ? (gp(a.lst)[ri] >> 3) : ri;
-  const uint16_t* ap = j.A + (size_t)arow * j.lda;
+  // wave w brings tokens 16 w .. 16 w + 15 of the block, 4 rows of 256 contiguous bytes per load: this
+  // lane's rows 16 w + 4 k + L / 16 (rows past r1 repeat the last one), 16-byte unit L % 16 of the LDS row
+  const uint16_t* ap[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const int ri = min(r0 + wave * 16 + 4 * k + kg, r1 - 1);
+    const int arow = j.grouped == 1 ? (gp(a.lst)[ri] >> 3) : ri;
+    ap[k] = j.A + (size_t)arow * j.lda + (n ^ ((4 * k + kg) & 15)) * 8;
+  }
   constexpr bool SWI = EPI == PF_SWIGLU;
   const Mat& M = SWI && wave >= 2 ? j.m2 : j.m;
   const long long T = j.tile0 + (long long)e * j.etiles + (SWI ? rb * 2 + (wave & 1) : rb * 4 + wave);
@@ -997,10 +1002,13 @@ __global__ void __launch_bounds__(PF_NT) pf_gemm(const BArgs a, const PfJob j) {
   constexpr int NW4 = WT == W_I4 ? 1 : 4;  // weight chunks per stage
   auto issue = [&](int s, uint4* buf) {
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int e0 = WT == W_I4 ? (2 * s + (q >> 1)) * 64 + kg * 16 + (q & 1) * 8 : (4 * s + q) * 32 + kg * 8;
-      dma16(ap + e0, &buf[(wave * 4 + q) * 64]);
-    }
+    for (int k = 0; k < 4; ++k) dma16(ap[k] + (size_t)s * 128, &buf[(wave * 16 + 4 * k) * 16]);
+  };
+  // the MFMA input operand of token tile t, 32-input slice q: token 16 t + n, 16-byte unit
+  // int4: (q / 2) * 8 + 2 kg + (q & 1) (groups of 64 in the code order); bf16: 4 q + kg
+  auto bop = [&](const uint4* buf, int t, int q) -> bf16x8_t {
+    const int u = WT == W_I4 ? (q >> 1) * 8 + 2 * kg + (q & 1) : 4 * q + kg;
+    return as_bf16x8(buf[(16 * t + n) * 16 + (u ^ n)]);
   };
   uint4 wc[NW4], wn[NW4], sc = make_uint4(0u, 0u, 0u, 0u), sn = sc;
   auto wload = [&](int s, uint4 (&w)[NW4], uint4& sv) {
@@ -1032,8 +1040,7 @@ __global__ void __launch_bounds__(PF_NT) pf_gemm(const BArgs a, const PfJob j) {
       const float sb[4] = {bf2f(sc.z & 0xFFFFu), bf2f(sc.z >> 16), bf2f(sc.w & 0xFFFFu), bf2f(sc.w >> 16)};
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
-        const bf16x8_t b0 = as_bf16x8(buf[(t * 4 + 0) * 64 + lane]), b1 = as_bf16x8(buf[(t * 4 + 1) * 64 + lane]);
-        const bf16x8_t b2 = as_bf16x8(buf[(t * 4 + 2) * 64 + lane]), b3 = as_bf16x8(buf[(t * 4 + 3) * 64 + lane]);
+        const bf16x8_t b0 = bop(buf, t, 0), b1 = bop(buf, t, 1), b2 = bop(buf, t, 2), b3 = bop(buf, t, 3);
         f32x4_t da = {0.f, 0.f, 0.f, 0.f}, db = {0.f, 0.f, 0.f, 0.f};
         da = mfma(bias, b0, da);
         da = mfma(bias, b1, da);
@@ -1050,7 +1057,7 @@ __global__ void __launch_bounds__(PF_NT) pf_gemm(const BArgs a, const PfJob j) {
 #pragma unroll
       for (int t = 0; t < 4; ++t)
 #pragma unroll
-        for (int q = 0; q < 4; ++q) acc[t] = mfma(as_bf16x8(wc[q]), as_bf16x8(buf[(t * 4 + q) * 64 + lane]), acc[t]);
+        for (int q = 0; q < 4; ++q) acc[t] = mfma(as_bf16x8(wc[q]), bop(buf, t, q), acc[t]);
     }
     __syncthreads();  // every wave is done with this buffer before stage s + 2 is loaded into it
 #pragma unroll
