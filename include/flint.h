@@ -187,9 +187,15 @@ int flint_decode_step_debug(flint_ctx* ctx, const int32_t* tokens, flint_kv* kv,
  * len[seq] .. len[seq] + n - 1 (causal attention over the cache and the
  * chunk), append their K/V, write the greedy id after the last position to
  * out_id[0] (device) and add n to len[seq].  bf16 / int4 models with 128-dim
- * heads run 16 tokens per batched MFMA pass (the first call makes the tiled
- * weight copies and the cache's scratch); others, one persistent launch per
- * token.  Errors: FLINT_EINVAL, FLINT_ENOMEM, FLINT_ECAPACITY, FLINT_EHIP.
+ * heads: up to 16 tokens as one batched MFMA pass; longer chunks layer by layer
+ * over all n tokens (MFMA contractions over 64 tokens per workgroup, experts
+ * run on the tokens that picked them, attention per 16 tokens and split of
+ * 256 cached positions).  The first call makes the tiled weight copies and the
+ * cache's scratch; the first long chunk on a cache allocates the long-chunk
+ * scratch, sized for 4,096 tokens (about 0.65 GB for the 49-layer shape at
+ * 9,300 positions), held until flint_kv_free.  Other models: one persistent
+ * launch per token.  Errors: FLINT_EINVAL, FLINT_ENOMEM, FLINT_ECAPACITY,
+ * FLINT_EHIP.
  */
 int flint_prefill_chunk(flint_ctx* ctx, flint_kv* kv, int32_t seq, const int32_t* tokens, int32_t n,
                         int32_t* out_id);
