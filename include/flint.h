@@ -192,7 +192,7 @@ int flint_decode_step_debug(flint_ctx* ctx, const int32_t* tokens, flint_kv* kv,
  * run on the tokens that picked them, attention per 16 tokens and split of
  * 256 cached positions).  The first call makes the tiled weight copies and the
  * cache's scratch; the first long chunk on a cache allocates the long-chunk
- * scratch, sized for 4,096 tokens (about 0.65 GB for the 49-layer shape at
+ * scratch, sized for 4,096 tokens (about 0.5 GB for the 49-layer shape at
  * 9,300 positions), held until flint_kv_free.  Other models: one persistent
  * launch per token.  Errors: FLINT_EINVAL, FLINT_ENOMEM, FLINT_ECAPACITY,
  * FLINT_EHIP.
