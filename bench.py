@@ -122,6 +122,8 @@ def bench_batch(args, cfg):
         tok.copy_(first)
         torch.cuda.synchronize()
 
+    if args.concurrency:
+        return bench_concurrency(args, cfg, model, kv, lens, first)
     reset()
     for _ in range(args.warmup):
         decode_step(model.ctx, tok.data_ptr(), kv.handle, tok.data_ptr())
@@ -192,6 +194,40 @@ def bench_batch(args, cfg):
         "cpu_baseline": cpu_baseline,
     }
     print(json.dumps(out), flush=True)
+
+
+def bench_concurrency(args, cfg, model, kv, lens, first):
+    """Continuous batching: each step decodes only the first C of the cache's sequences
+    (flint_decode_step_seqs; C = 1 runs the persistent kernel); one JSON line per C."""
+    import torch
+    from stream_moe_decode_amd import decode_step_seqs, sync
+    for C in [int(x) for x in args.concurrency.split(",")]:
+        seqs = list(range(C))
+        tok = first[:C].clone()
+        kv.set_lengths(lens)
+        for _ in range(args.warmup):
+            decode_step_seqs(model.ctx, kv.handle, seqs, tok.data_ptr(), tok.data_ptr())
+        sync(model.ctx)
+        kv.set_lengths(lens)
+        tok.copy_(first[:C])
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(args.steps):
+            decode_step_seqs(model.ctx, kv.handle, seqs, tok.data_ptr(), tok.data_ptr())
+        e1.record()
+        torch.cuda.synchronize()
+        sync(model.ctx)
+        ms = e0.elapsed_time(e1)
+        print(json.dumps({
+            "metric": "concurrent decode tok/s (aggregate over the active sequences)",
+            "value": round(C * args.steps / (ms / 1e3), 2), "unit": "tok/s", "n_gpus": 1, "steps": args.steps,
+            "warmup": args.warmup, "ms_per_step": round(ms / args.steps, 4), "higher_is_better": True,
+            "dtype": "bf16", "data": "synthetic",
+            "config": {"workload": f"{cfg.name}: the first {C} of {len(lens)} cached sequences (resident lengths "
+                                   f"{lens[:C]}) decode each step", "concurrency": C},
+        }), flush=True)
+    model.free()
 
 
 def bench_prefill(args, cfg):
@@ -266,6 +302,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-steps", type=int, default=4, help="decode steps the oracle is timed on")
     ap.add_argument("--prefill", type=int, default=0, help="time a prompt of this many tokens instead")
+    ap.add_argument("--concurrency", default="",
+                    help="with a batched config: comma-separated counts of active sequences to time instead")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run one 1 GiB device copy (counter calibration under rocprofv3 --pmc)")
     args = ap.parse_args()

@@ -167,8 +167,9 @@ int flint_kv_layer_ptrs(flint_kv* kv, int32_t layer, void** k, void** v);
  * tokens[b] at position len[b], append its K/V, write the argmax token id to
  * out_ids[b] (device) and increment len[b].  tokens and out_ids may alias,
  * so out_ids can be fed back as the next step's tokens without a host round
- * trip.  One sequence: the persistent kernel.  Several (bf16 / int4 models
- * with 128-dim heads): passes of up to 16 sequences on the batched MFMA path,
+ * trip.  One or two sequences: the persistent kernel per sequence.  Three or
+ * more (bf16 / int4 models with 128-dim heads): passes of up to 16 sequences on
+ * the batched MFMA path,
  * which on the first such cache makes the context's tiled weight copies (the
  * "batch-16 ragged" step of the pages' concurrent-client workload, section 4
  * of "Flint Inference on Apple Silicon: rec Megakernel and Tempo9 Compared").
@@ -177,6 +178,22 @@ int flint_kv_layer_ptrs(flint_kv* kv, int32_t layer, void** k, void** v);
  * by an earlier step (reported once, then cleared).
  */
 int flint_decode_step(flint_ctx* ctx, const int32_t* tokens, flint_kv* kv, int32_t* out_ids);
+
+/*
+ * One greedy decode step for the n distinct sequences seqs[0 .. n-1] (host
+ * array, 1 <= n <= batch) of kv and no other: sequence seqs[i] consumes the
+ * device token tokens[i] at position len[seqs[i]], appends its K/V, gets its
+ * argmax id in out_ids[i] (device; may alias tokens) and len[seqs[i]] += 1.
+ * Sequences may join, leave and come back between calls (each keeps its own
+ * cache), the continuous-batching use of the batch-16 step of "Flint Inference
+ * on Apple Silicon: rec Megakernel and Tempo9 Compared", section 4.  Three or
+ * more sequences take the batched path (when the cache has one), one or two the
+ * persistent kernel per sequence.  Errors: FLINT_EINVAL (NULL pointer, n out of range,
+ * a sequence out of range or listed twice), FLINT_ECAPACITY, FLINT_EHIP, and
+ * errors latched by an earlier step.
+ */
+int flint_decode_step_seqs(flint_ctx* ctx, flint_kv* kv, const int32_t* seqs, int32_t n, const int32_t* tokens,
+                           int32_t* out_ids);
 
 /* flint_decode_step with the optional outputs of `dbg` (may be NULL). */
 int flint_decode_step_debug(flint_ctx* ctx, const int32_t* tokens, flint_kv* kv, int32_t* out_ids,

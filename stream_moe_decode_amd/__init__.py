@@ -24,8 +24,8 @@ STATUS_NAMES = {0: "FLINT_OK", 1: "FLINT_EINVAL", 2: "FLINT_ENOMEM", 3: "FLINT_E
 
 # every symbol include/flint.h declares
 EXPORTS = ("flint_decode_init", "flint_decode_free", "flint_kv_alloc", "flint_kv_free", "flint_kv_set_lengths",
-           "flint_kv_get_lengths", "flint_kv_layer_ptrs", "flint_decode_step", "flint_decode_step_debug",
-           "flint_prefill_chunk", "flint_sync", "flint_device_info", "flint_last_error")
+           "flint_kv_get_lengths", "flint_kv_layer_ptrs", "flint_decode_step", "flint_decode_step_seqs",
+           "flint_decode_step_debug", "flint_prefill_chunk", "flint_sync", "flint_device_info", "flint_last_error")
 
 
 class FlintError(RuntimeError):
@@ -82,6 +82,7 @@ def lib():
             "flint_kv_get_lengths": [vp, vp],
             "flint_kv_layer_ptrs": [vp, i32, P(vp), P(vp)],
             "flint_decode_step": [vp, vp, vp, vp],
+            "flint_decode_step_seqs": [vp, vp, P(i32), i32, vp, vp],
             "flint_decode_step_debug": [vp, vp, vp, vp, P(Debug)],
             "flint_prefill_chunk": [vp, vp, i32, vp, i32, vp],
             "flint_sync": [vp],
@@ -146,6 +147,12 @@ def kv_layer_ptrs(kv: int, layer: int):
 
 def decode_step(ctx: int, tokens_ptr: int, kv: int, out_ptr: int):
     _check(lib().flint_decode_step(ctx, tokens_ptr, kv, out_ptr))
+
+
+def decode_step_seqs(ctx: int, kv: int, seqs, tokens_ptr: int, out_ptr: int):
+    """One greedy step for the listed sequences only (tokens / out_ids indexed by list position)."""
+    arr = (ctypes.c_int32 * len(seqs))(*[int(x) for x in seqs])
+    _check(lib().flint_decode_step_seqs(ctx, kv, arr, len(seqs), tokens_ptr, out_ptr))
 
 
 def decode_step_debug(ctx: int, tokens_ptr: int, kv: int, out_ptr: int, dbg: Debug | None):

@@ -197,9 +197,16 @@ __device__ __forceinline__ float bsum(float v, float* wred) {
 
 enum { NORM_EMBED = 0, NORM_INPUT = 1, NORM_POST = 2, NORM_FINAL = 3 };
 
-// Cache sequence and position of column n of the pass (decode: sequence seq0 + n at its length;
-// prefill: sequence seq0 at its length + n).
-__device__ __forceinline__ int col_seq(const BArgs& a, int n) { return a.prefill ? a.seq0 : a.seq0 + n; }
+// Cache sequence and position of column n of the pass (decode: sequence cseq[n] at its length;
+// prefill: sequence seq0 at its length + n); n may differ between lanes (selects over the kernel
+// argument arrays, no loads).
+__device__ __forceinline__ int col_seq(const BArgs& a, int n) {
+  if (a.prefill) return a.seq0;
+  int q = 0;
+#pragma unroll
+  for (int m = 0; m < BT; ++m) q = n == m ? a.cseq[m] : q;
+  return q;
+}
 // Position of column n; n may differ between lanes (a select over the kernel argument array, no load).
 __device__ __forceinline__ int col_pos(const BArgs& a, int n) {
   int p = 0;
@@ -254,7 +261,7 @@ __global__ void __launch_bounds__(BNT) bk_norm(const BArgs a, int l, int mode) {
   __shared__ float z[MAX_E];
   __shared__ int rk[BNW][64];
   __shared__ float wred[BNW];
-  const int n = blockIdx.x, seq = a.seq0 + n, tid = threadIdx.x, H = a.H;
+  const int n = blockIdx.x, seq = col_seq(a, n), tid = threadIdx.x, H = a.H;
   const int lane = tid & 63, wave = tid >> 6, E = a.E, lm = l - a.n_dense;
   float* xg = a.x + (size_t)n * H;
   // router rows of this wave (e = wave + 8 i; lanes over 16-byte chunks), loaded before the norm so that
@@ -282,7 +289,7 @@ __global__ void __launch_bounds__(BNT) bk_norm(const BArgs a, int l, int mode) {
   const float* g = mode == NORM_POST ? a.pnorm + (size_t)l * H : (mode == NORM_FINAL ? a.fnorm : a.anorm + (size_t)l * H);
   float xv[EPT], gv[EPT];
   if (mode == NORM_EMBED) {
-    int tok = gp(a.tokens)[a.prefill ? a.tok0 + n : seq];
+    int tok = gp(a.tokens)[a.prefill ? a.tok0 + n : n];
     if (tok < 0 || tok >= a.V) {
       if (tid == 0) latch(a, ERR_TOKEN);
       tok = 0;
@@ -865,7 +872,7 @@ __global__ void __launch_bounds__(BNT) bk_head(const BArgs a) {
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const int row = tl * 16 + 4 * kg + r;
-          if (a.dbg_logits && n < a.B) gp(a.dbg_logits)[(size_t)(a.seq0 + n) * a.V + row] = v[r];
+          if (a.dbg_logits && n < a.B) gp(a.dbg_logits)[(size_t)col_seq(a, n) * a.V + row] = v[r];
           if (v[r] > bv || (v[r] == bv && row < bi)) {
             bv = v[r];
             bi = row;
@@ -915,8 +922,8 @@ __global__ void __launch_bounds__(BNT) bk_head(const BArgs a) {
         const unsigned long long fin = __hip_atomic_exchange(gp(a.amax + q), 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         const int32_t id = (int32_t)(0xFFFFFFFFu - (uint32_t)(fin & 0xFFFFFFFFull));
         if (!a.prefill) {
-          gp(a.out_ids)[a.seq0 + q] = id;
-          gp(a.len)[a.seq0 + q] += 1;
+          gp(a.out_ids)[q] = id;
+          gp(a.len)[col_seq(a, q)] += 1;
         } else if (q == a.B - 1) {  // prefill: the id after the last prompt token of the pass
           gp(a.out_ids)[0] = id;
           gp(a.len)[a.seq0] += a.lenadd;

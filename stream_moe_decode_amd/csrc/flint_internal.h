@@ -104,10 +104,12 @@ struct BArgs {
   const float* anorm;
   const float* pnorm;
   Mat qkv, o, dg, du, dd, router, eg, eu, ed;
-  // this pass: sequences seq0 .. seq0 + B - 1 of a cache of Bc sequences, each at its own length; or
-  // (prefill) B consecutive prompt tokens tokens[tok0 ..] of sequence seq0 at positions len[seq0] ..,
+  // this pass: columns n < B are the cache's sequences cseq[n] (of Bc), each at its own length, with
+  // tokens[n] and out_ids[n] their token and next id; or (prefill) B consecutive prompt tokens
+  // tokens[tok0 ..] of sequence seq0 at positions len[seq0] ..,
   // the greedy id after the last one written to out_ids[0]
   int B, seq0, Bc, cap, prefill, tok0;
+  int cseq[BT];
   // position of column n (its sequence's length, or len + n in prefill), taken from the host's mirror of
   // the lengths so that no kernel waits on a load to know it; asp[n] = attention splits of columns 0 .. n - 1
   int pos[BT];

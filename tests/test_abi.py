@@ -124,6 +124,7 @@ def test_null_arguments_are_rejected():
     assert lib.flint_kv_free(None) == fl.FLINT_OK
     assert lib.flint_kv_alloc(None, 1, 16, ctypes.byref(out)) == fl.FLINT_EINVAL
     assert lib.flint_decode_step(None, None, None, None) == fl.FLINT_EINVAL
+    assert lib.flint_decode_step_seqs(None, None, None, 0, None, None) == fl.FLINT_EINVAL
     assert lib.flint_prefill_chunk(None, None, 0, None, 1, None) == fl.FLINT_EINVAL
     assert lib.flint_sync(None) == fl.FLINT_EINVAL
     assert lib.flint_kv_set_lengths(None, None) == fl.FLINT_EINVAL

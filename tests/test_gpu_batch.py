@@ -181,3 +181,40 @@ def test_long_prefill_chunks_match_oracle():
 def test_long_prefill_bf16():
     # the same kernels with bf16 weights: 200 tokens, then 70 more
     _prefill_then_steps(SMALL.replace(name="bf16_b16_small", weight_type=synth.BF16), [200, 70])
+
+
+def test_sequence_subsets_join_and_leave():
+    # continuous batching on one cache of 6 ragged sequences: steps over subsets (one sequence, a few,
+    # all, a returning one), each listed sequence's id against the oracle, unlisted lengths unchanged; a
+    # final full step with logits checks every sequence's cache as the subset steps left it
+    from stream_moe_decode_amd import decode_step_seqs
+    cfg = SMALL
+    batch = 6
+    model, kv, orc, lens = _setup(cfg, batch, 8)
+    dev = model.device
+    cur = [int(x) for x in synth.tokens(cfg, batch, stream=23)]
+    length = [int(x) for x in lens]
+    schedule = [[0], [0], [3], [0], [2, 4, 0], [0, 1, 2, 3, 4, 5], [5, 1], [3]]
+    for seqs in schedule:
+        toks = torch.tensor([cur[b] for b in seqs], dtype=torch.int32, device=dev)
+        out = torch.zeros(len(seqs), dtype=torch.int32, device=dev)
+        decode_step_seqs(model.ctx, kv.handle, seqs, toks.data_ptr(), out.data_ptr())
+        sync(model.ctx)
+        ids = out.cpu().numpy()
+        for i, b in enumerate(seqs):
+            r = orc.forward(b, np.array([cur[b]], np.int32), tie_eps=TIE_EPS)
+            o_id, gap = int(r["ids"][0]), float(r["gap"][0])
+            print(f"subset {seqs}: sequence {b} gpu id {int(ids[i])} oracle id {o_id} gap {gap:.3g}", flush=True)
+            assert int(ids[i]) == o_id or gap < TIE_EPS
+            cur[b] = int(ids[i])
+            length[b] += 1
+        assert kv_get_lengths(kv.handle, batch) == length
+    tok = torch.tensor(cur, dtype=torch.int32, device=dev)
+    out = torch.zeros(batch, dtype=torch.int32, device=dev)
+    dbg, t = make_debug(cfg, batch, dev)
+    decode_step_debug(model.ctx, tok.data_ptr(), kv.handle, out.data_ptr(), dbg)
+    sync(model.ctx)
+    for b in range(batch):
+        check_step(cfg, orc, b, cur[b], t["logits"][b].cpu().numpy(), t["routes"][b].cpu().numpy(),
+                   int(out[b].item()), what=f"sequence {b}: ", g_z=t["router_logits"][b].cpu().numpy())
+    model.free()
