@@ -158,6 +158,26 @@ int flint_kv_set_lengths(flint_kv* kv, const int32_t* lengths);
 /* Copy the device lengths into a host array [batch] (synchronises the stream). */
 int flint_kv_get_lengths(flint_kv* kv, int32_t* lengths);
 
+/*
+ * The token ids a sequence's cache holds: tokens[p] for p < n <= len[seq] is
+ * the token consumed at position p (by flint_decode_step*, flint_prefill_chunk),
+ * -1 for positions whose K/V were written otherwise (flint_kv_layer_ptrs).
+ * Host output; synchronizes the context's stream.  Errors: FLINT_EINVAL,
+ * FLINT_EHIP.
+ */
+int flint_kv_tokens(flint_kv* kv, int32_t seq, int32_t* tokens, int32_t n);
+
+/*
+ * Prefix reuse within one sequence: *matched = the number of leading entries of
+ * the host array tokens[0 .. n-1] equal to the sequence's cached tokens (at
+ * most len[seq]).  The caller keeps that prefix with flint_kv_set_lengths
+ * (rollback truncates; generated tokens that were consumed are part of the
+ * cache) and prefills the rest, the single-session prompt cache of "Flint
+ * Inference on Apple Silicon: rec Megakernel and Tempo9 Compared", section 1.
+ * Synchronizes the context's stream.  Errors: FLINT_EINVAL, FLINT_EHIP.
+ */
+int flint_kv_prefix_match(flint_kv* kv, int32_t seq, const int32_t* tokens, int32_t n, int32_t* matched);
+
 /* Device pointers to layer `layer`'s K and V ([batch][n_kv][max_tokens][head_dim]),
  * e.g. to load a resident cache.  Errors: FLINT_EINVAL. */
 int flint_kv_layer_ptrs(flint_kv* kv, int32_t layer, void** k, void** v);

@@ -24,7 +24,8 @@ STATUS_NAMES = {0: "FLINT_OK", 1: "FLINT_EINVAL", 2: "FLINT_ENOMEM", 3: "FLINT_E
 
 # every symbol include/flint.h declares
 EXPORTS = ("flint_decode_init", "flint_decode_free", "flint_kv_alloc", "flint_kv_free", "flint_kv_set_lengths",
-           "flint_kv_get_lengths", "flint_kv_layer_ptrs", "flint_decode_step", "flint_decode_step_seqs",
+           "flint_kv_get_lengths", "flint_kv_tokens", "flint_kv_prefix_match", "flint_kv_layer_ptrs",
+           "flint_decode_step", "flint_decode_step_seqs",
            "flint_decode_step_debug", "flint_prefill_chunk", "flint_sync", "flint_device_info", "flint_last_error")
 
 
@@ -80,6 +81,8 @@ def lib():
             "flint_kv_free": [vp],
             "flint_kv_set_lengths": [vp, vp],
             "flint_kv_get_lengths": [vp, vp],
+            "flint_kv_tokens": [vp, i32, P(i32), i32],
+            "flint_kv_prefix_match": [vp, i32, P(i32), i32, P(i32)],
             "flint_kv_layer_ptrs": [vp, i32, P(vp), P(vp)],
             "flint_decode_step": [vp, vp, vp, vp],
             "flint_decode_step_seqs": [vp, vp, P(i32), i32, vp, vp],
@@ -147,6 +150,21 @@ def kv_layer_ptrs(kv: int, layer: int):
 
 def decode_step(ctx: int, tokens_ptr: int, kv: int, out_ptr: int):
     _check(lib().flint_decode_step(ctx, tokens_ptr, kv, out_ptr))
+
+
+def kv_tokens(kv: int, seq: int, n: int):
+    """The first n token ids the sequence's cache holds (-1 where unknown)."""
+    arr = (ctypes.c_int32 * max(n, 1))()
+    _check(lib().flint_kv_tokens(kv, seq, arr, n))
+    return list(arr)[:n]
+
+
+def kv_prefix_match(kv: int, seq: int, tokens) -> int:
+    """Leading tokens of `tokens` that the sequence's cache already holds."""
+    arr = (ctypes.c_int32 * max(len(tokens), 1))(*[int(x) for x in tokens])
+    out = ctypes.c_int32()
+    _check(lib().flint_kv_prefix_match(kv, seq, arr, len(tokens), ctypes.byref(out)))
+    return out.value
 
 
 def decode_step_seqs(ctx: int, kv: int, seqs, tokens_ptr: int, out_ptr: int):

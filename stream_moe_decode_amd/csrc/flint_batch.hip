@@ -294,6 +294,7 @@ __global__ void __launch_bounds__(BNT) bk_norm(const BArgs a, int l, int mode) {
       if (tid == 0) latch(a, ERR_TOKEN);
       tok = 0;
     }
+    if (tid == 0) gp(a.hist)[(size_t)seq * a.cap + (a.prefill ? a.p0 + n : col_pos(a, n))] = tok;
     const uint16_t* er = reinterpret_cast<const uint16_t*>(a.embed) + (size_t)tok * H;
 #pragma unroll
     for (int k = 0; k < EPT; ++k) {

@@ -71,6 +71,7 @@ struct KDyn {
   int32_t* len;          // [B] device lengths
   const int32_t* tokens;
   int tok_idx, seq;
+  int32_t* hist;         // [B][cap] token consumed at each position
   int32_t* out_ids;
   int out_idx;
   uint32_t epoch;
@@ -138,6 +139,7 @@ struct BArgs {
   // prefill of a chunk of n > BT tokens of sequence seq0 at positions p0 .. p0 + n - 1 (the buffers above then
   // hold n rows); the head adds lenadd to the length (batched prefill passes: B)
   int p0, lenadd;
+  int32_t* hist;         // [Bc][cap] token consumed at each position (written at the embedding)
   float* y;              // [n][K][H] expert down products per (token, slot)
   int32_t* lst;          // [n K] (token << 3 | slot), grouped by expert in expert order, tokens ascending
   int32_t* ecnt;         // [E] entries per expert

@@ -797,6 +797,7 @@ __global__ void __launch_bounds__(NT, 1) decode_kernel(const KStatic* __restrict
     if (W == 0 && tid == 0) raise_error(wt, ERR_TOKEN);
     tok = 0;
   }
+  if (W == 0 && tid == 0) gp(d.hist)[(size_t)seq * cap + pos] = tok;  // the cache's token record
   if (stamps) {
     stamps[0] = now();
     stamps[3] = __builtin_amdgcn_s_memtime();  // shader clock, to relate the stamps to cycles

@@ -74,6 +74,7 @@ struct flint_kv {
   void* k;
   void* v;
   int32_t* len;
+  int32_t* hist;              // [batch][max_tokens] token consumed at each position, -1 where unknown
   float* rope;
   std::vector<int32_t> hlen;
   void* bscratch;             // scratch of the batched path (batch > 1), null otherwise
@@ -215,6 +216,7 @@ int launch(flint_ctx* c, flint_kv* kv, const int32_t* tokens, int tok_idx, int s
   a.cap = kv->max_tokens;
   a.rope = (const float2*)kv->rope;
   a.len = kv->len;
+  a.hist = kv->hist;
   a.tokens = tokens;
   a.tok_idx = tok_idx;
   a.seq = seq;
@@ -316,6 +318,7 @@ int batch_scratch(flint_ctx* c, flint_kv* kv) {
   a.vc = (uint8_t*)kv->v;
   a.rope = (const float2*)kv->rope;
   a.len = kv->len;
+  a.hist = kv->hist;
   a.err = k.err;
   a.herr = k.herr;
   const size_t H = cfg.hidden, QD = (size_t)cfg.n_q_heads * cfg.head_dim;
@@ -406,6 +409,7 @@ constexpr int BATCH_MIN = 3;
 
 // Positions of a pass's columns from the host's mirror of the lengths, and the attention splits per column.
 void set_positions(BArgs& a, const std::vector<int32_t>& hlen) {
+  if (a.prefill) a.p0 = hlen[a.seq0];
   a.asp[0] = 0;
   for (int n = 0; n < BT; ++n) {
     a.pos[n] = n < a.B ? (a.prefill ? hlen[a.seq0] + n : hlen[a.cseq[n]]) : 0;
@@ -587,6 +591,7 @@ int flint_kv_alloc(flint_ctx* c, int32_t batch, int32_t max_tokens, flint_kv** o
   kv->max_tokens = max_tokens;
   kv->k = kv->v = nullptr;
   kv->len = nullptr;
+  kv->hist = nullptr;
   kv->rope = nullptr;
   kv->bscratch = nullptr;
   kv->pscratch = nullptr;
@@ -594,6 +599,7 @@ int flint_kv_alloc(flint_ctx* c, int32_t batch, int32_t max_tokens, flint_kv** o
     if (kv->k) (void)hipFree(kv->k);
     if (kv->v) (void)hipFree(kv->v);
     if (kv->len) (void)hipFree(kv->len);
+    if (kv->hist) (void)hipFree(kv->hist);
     if (kv->rope) (void)hipFree(kv->rope);
     if (kv->bscratch) (void)hipFree(kv->bscratch);
     delete kv;
@@ -602,6 +608,8 @@ int flint_kv_alloc(flint_ctx* c, int32_t batch, int32_t max_tokens, flint_kv** o
   if (hipMalloc(&kv->k, per) != hipSuccess || hipMalloc(&kv->v, per) != hipSuccess)
     return bail(fail(FLINT_ENOMEM, "KV cache of 2 x %zu bytes", per));
   if (hipMalloc((void**)&kv->len, sizeof(int32_t) * batch) != hipSuccess) return bail(fail(FLINT_ENOMEM, "lengths"));
+  const size_t hist_bytes = sizeof(int32_t) * (size_t)batch * max_tokens;
+  if (hipMalloc((void**)&kv->hist, hist_bytes) != hipSuccess) return bail(fail(FLINT_ENOMEM, "token record"));
   // RoPE table: cos, sin of p * theta^(-2i/d) in double, stored fp32 [max_tokens][d/2][2]
   const int half = cfg.head_dim / 2;
   std::vector<float> tab((size_t)max_tokens * half * 2);
@@ -614,6 +622,7 @@ int flint_kv_alloc(flint_ctx* c, int32_t batch, int32_t max_tokens, flint_kv** o
   if (hipMalloc((void**)&kv->rope, tab.size() * 4) != hipSuccess) return bail(fail(FLINT_ENOMEM, "RoPE table"));
   if (hipMemsetAsync(kv->k, 0, per, c->stream) != hipSuccess || hipMemsetAsync(kv->v, 0, per, c->stream) != hipSuccess ||
       hipMemsetAsync(kv->len, 0, sizeof(int32_t) * batch, c->stream) != hipSuccess ||
+      hipMemsetAsync(kv->hist, 0xFF, hist_bytes, c->stream) != hipSuccess ||
       hipMemcpyAsync(kv->rope, tab.data(), tab.size() * 4, hipMemcpyHostToDevice, c->stream) != hipSuccess ||
       hipStreamSynchronize(c->stream) != hipSuccess)
     return bail(fail(FLINT_EHIP, "KV cache initialisation failed"));
@@ -636,6 +645,7 @@ int flint_kv_free(flint_kv* kv) {
   (void)hipFree(kv->k);
   (void)hipFree(kv->v);
   (void)hipFree(kv->len);
+  (void)hipFree(kv->hist);
   (void)hipFree(kv->rope);
   kv->ctx->live_kv--;
   delete kv;
@@ -657,6 +667,30 @@ int flint_kv_get_lengths(flint_kv* kv, int32_t* lengths) {
   if (!kv || !lengths) return fail(FLINT_EINVAL, "kv or lengths is NULL");
   HIPCHECK(hipMemcpyAsync(lengths, kv->len, sizeof(int32_t) * kv->batch, hipMemcpyDeviceToHost, kv->ctx->stream));
   HIPCHECK(hipStreamSynchronize(kv->ctx->stream));
+  return FLINT_OK;
+}
+
+int flint_kv_tokens(flint_kv* kv, int32_t seq, int32_t* tokens, int32_t n) {
+  if (!kv || !tokens) return fail(FLINT_EINVAL, "NULL argument");
+  if (seq < 0 || seq >= kv->batch) return fail(FLINT_EINVAL, "seq %d not in [0, %d)", seq, kv->batch);
+  if (n < 0 || n > kv->hlen[seq]) return fail(FLINT_EINVAL, "n %d not in [0, %d]", n, kv->hlen[seq]);
+  if (n == 0) return FLINT_OK;
+  HIPCHECK(hipStreamSynchronize(kv->ctx->stream));
+  HIPCHECK(hipMemcpy(tokens, kv->hist + (size_t)seq * kv->max_tokens, sizeof(int32_t) * n, hipMemcpyDeviceToHost));
+  return FLINT_OK;
+}
+
+int flint_kv_prefix_match(flint_kv* kv, int32_t seq, const int32_t* tokens, int32_t n, int32_t* matched) {
+  if (!kv || !matched || (n > 0 && !tokens)) return fail(FLINT_EINVAL, "NULL argument");
+  if (seq < 0 || seq >= kv->batch) return fail(FLINT_EINVAL, "seq %d not in [0, %d)", seq, kv->batch);
+  if (n < 0) return fail(FLINT_EINVAL, "n %d < 0", n);
+  const int m = std::min<int>(n, kv->hlen[seq]);
+  std::vector<int32_t> rec(m);
+  int rc = flint_kv_tokens(kv, seq, rec.data(), m);
+  if (rc) return rc;
+  int k = 0;
+  while (k < m && rec[k] == tokens[k]) ++k;
+  *matched = k;
   return FLINT_OK;
 }
 

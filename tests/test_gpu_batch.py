@@ -218,3 +218,50 @@ def test_sequence_subsets_join_and_leave():
         check_step(cfg, orc, b, cur[b], t["logits"][b].cpu().numpy(), t["routes"][b].cpu().numpy(),
                    int(out[b].item()), what=f"sequence {b}: ", g_z=t["router_logits"][b].cpu().numpy())
     model.free()
+
+
+def test_prefix_reuse_after_generation():
+    # single-session prompt cache: a 300-token prompt, 4 greedy steps; the cache's token record is the
+    # prompt plus the consumed tokens; a new request sharing the prompt and 2 generated tokens matches
+    # 302 positions, the cache is cut back to them and the 40 new tokens are prefilled; the next id and
+    # greedy steps against the oracle taking the same path
+    from gpu_common import Stepper
+    from stream_moe_decode_amd import kv_prefix_match, kv_set_lengths, kv_tokens, prefill_chunk
+    cfg = SMALL
+    model = build(cfg)
+    cap = 400
+    kv = model.kv(1, cap)
+    orc = make_oracle(cfg, cap)
+    dev = model.device
+    prompt = synth.tokens(cfg, 300, stream=29)
+    toks = torch.from_numpy(prompt).to(dev)
+    out = torch.zeros(1, dtype=torch.int32, device=dev)
+    prefill_chunk(model.ctx, kv.handle, 0, toks.data_ptr(), 300, out.data_ptr())
+    sync(model.ctx)
+    orc.forward(0, prompt, want_logits=False)
+    st = Stepper(cfg, model, kv, orc)
+    tok = int(out.item())
+    consumed = []
+    for _ in range(4):
+        consumed.append(tok)
+        tok = st.step(tok)
+    rec = kv_tokens(kv.handle, 0, 304)
+    assert rec == [int(x) for x in prompt] + consumed
+    new = synth.tokens(cfg, 40, stream=31)
+    request = [int(x) for x in prompt] + consumed[:2] + [int(x) for x in new]
+    m = kv_prefix_match(kv.handle, 0, request)
+    assert m == 302
+    kv_set_lengths(kv.handle, [m])
+    orc.len[0] = m
+    rest = torch.tensor(request[m:], dtype=torch.int32, device=dev)
+    prefill_chunk(model.ctx, kv.handle, 0, rest.data_ptr(), len(request) - m, out.data_ptr())
+    sync(model.ctx)
+    r = orc.forward(0, np.array(request[m:], np.int32))
+    gpu_id, o_id, gap = int(out.item()), int(r["ids"][-1]), float(r["gap"][-1])
+    print(f"after the reused prefix: gpu id {gpu_id} oracle id {o_id} gap {gap:.3g}", flush=True)
+    assert gpu_id == o_id or gap < TIE_EPS
+    assert kv_get_lengths(kv.handle, 1) == [len(request)]
+    tok = gpu_id
+    for _ in range(2):
+        tok = st.step(tok)
+    model.free()
