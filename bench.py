@@ -429,6 +429,8 @@ def main():
               "moe_us_per_layer": round(float(np.mean(moe)), 2) if moe else None,
               "head_us": round(float(head_us), 2), "source": "workgroup-0 s_memrealtime stamps, one step at "
                                                              f"position {resident}"}
+    from stream_moe_decode_amd import micro
+    micro_out = micro(model.ctx)  # the measurement helpers, beside the decode numbers
     model.free()
 
     cpu_baseline = None
@@ -478,6 +480,7 @@ def main():
                      "kernel_mean_us": round(1e6 * mean_kern_s, 2),
                      "roofline_tok_s": round(HBM_PEAK_GBS * 1e9 / (bytes_total / K), 1)},
         "phases": phases,
+        "micro": dict(micro_out, decode_frac_of_stream_read=round(achieved / micro_out["stream_read_gbs"], 4)),
         "cpu_baseline": cpu_baseline,
     }
     print(json.dumps(out), flush=True)

@@ -188,8 +188,9 @@ int flint_kv_layer_ptrs(flint_kv* kv, int32_t layer, void** k, void** v);
  * out_ids[b] (device) and increment len[b].  tokens and out_ids may alias,
  * so out_ids can be fed back as the next step's tokens without a host round
  * trip.  One or two sequences: the persistent kernel per sequence.  Three or
- * more (bf16 / int4 models with 128-dim heads): passes of up to 16 sequences on
- * the batched MFMA path,
+ * more (the environment variable FLINT_BATCH_MIN, read at flint_decode_init,
+ * changes the threshold) on bf16 / int4 models with 128-dim heads: passes of up
+ * to 16 sequences on the batched MFMA path,
  * which on the first such cache makes the context's tiled weight copies (the
  * "batch-16 ragged" step of the pages' concurrent-client workload, section 4
  * of "Flint Inference on Apple Silicon: rec Megakernel and Tempo9 Compared").
@@ -236,6 +237,24 @@ int flint_decode_step_debug(flint_ctx* ctx, const int32_t* tokens, flint_kv* kv,
  */
 int flint_prefill_chunk(flint_ctx* ctx, flint_kv* kv, int32_t seq, const int32_t* tokens, int32_t n,
                         int32_t* out_id);
+
+/*
+ * Measurement helpers (outside the decode path; each synchronizes the
+ * context's stream and allocates and frees its own device memory), the
+ * microbenchmarks that "Flint Inference on Apple Silicon: rec Megakernel and
+ * Tempo9 Compared" reports beside its decode numbers (section 3):
+ *  - flint_micro_stream_read: GB/s of reading `bytes` (>= 1 MiB) of device
+ *    memory once per launch, `reps` launches (the practical HBM ceiling);
+ *  - flint_micro_exchange: microseconds per round of an all-to-all exchange
+ *    among `workgroups` (2 .. compute units) co-resident workgroups through
+ *    tagged system-scope slots, as the decode kernel hands data between
+ *    workgroups; FLINT_ETIMEOUT if a bounded wait ran out;
+ *  - flint_micro_launch: microseconds per back-to-back empty kernel launch.
+ * Errors: FLINT_EINVAL, FLINT_ENOMEM, FLINT_EHIP (and FLINT_ETIMEOUT above).
+ */
+int flint_micro_stream_read(flint_ctx* ctx, size_t bytes, int32_t reps, float* gbps);
+int flint_micro_exchange(flint_ctx* ctx, int32_t workgroups, int32_t rounds, float* us_per_round);
+int flint_micro_launch(flint_ctx* ctx, int32_t launches, float* us_per_launch);
 
 /* Wait for the ctx stream; report and clear a latched device error. */
 int flint_sync(flint_ctx* ctx);

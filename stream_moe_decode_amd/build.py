@@ -5,7 +5,7 @@ import subprocess
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 SO = os.path.join(HERE, "libflint.so")
-SOURCES = [os.path.join(HERE, "csrc", f) for f in ("flint_kernel.hip", "flint_batch.hip", "flint_runtime.cpp")]
+SOURCES = [os.path.join(HERE, "csrc", f) for f in ("flint_kernel.hip", "flint_batch.hip", "flint_micro.hip", "flint_runtime.cpp")]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",

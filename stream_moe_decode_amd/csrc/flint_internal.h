@@ -163,6 +163,11 @@ hipError_t launch_batch_pass(int wt, const BArgs& a, hipStream_t stream);
 // kernels; a's buffers hold n rows (a.part: prefill_part_floats floats).
 hipError_t launch_prefill(int wt, const BArgs& a, int n, hipStream_t stream);
 size_t prefill_part_floats(int nq, int nsmax, int hd);
+
+// Measurement helpers (flint_micro.hip).
+hipError_t launch_micro_read(const void* p, size_t bytes, uint32_t* sink, int blocks, hipStream_t st);
+hipError_t launch_micro_exchange(unsigned long long* slots, int workgroups, int rounds, uint32_t* err, hipStream_t st);
+hipError_t launch_micro_empty(hipStream_t st);
 // s4[((r / 4) * G + g) * 4 + r % 4] = s[r * G + g] for r < rows (a multiple of 4), g < G.
 hipError_t launch_regroup_scales(const uint16_t* s, uint16_t* s4, size_t rows, int G, hipStream_t stream);
 // Copy a [rows][in] weight matrix into the tiled layout of the batched path (rows a multiple of 16).  Tile

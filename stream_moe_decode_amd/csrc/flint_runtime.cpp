@@ -59,6 +59,7 @@ struct flint_ctx {
   KStatic* kdev;              // the same, in device memory, read by the kernel
   bool stat;                  // the compile-time 2048-wide kernel applies
   bool batch_ok;              // batches of several sequences take the batched MFMA path
+  int batch_min;              // fewest sequences of a step that take it (FLINT_BATCH_MIN overrides)
   bool tiled;                 // the batched path's tiled weight copies exist
   const uint8_t* lmt;         // lm_head in the tiled layout (with `tiled`)
   uint32_t* herr_host;        // host-mapped error word
@@ -537,6 +538,8 @@ int flint_decode_init(const flint_config* cfg, const flint_weights* w, void* hip
                 H % 128 == 0 && QD % 128 == 0 && (ND == 0 || DI % 256 == 0) && (NM == 0 || EI % 256 == 0) &&
                 V % 16 == 0 &&
                 !getenv("FLINT_NO_BATCH_PATH");
+  c->batch_min = BATCH_MIN;
+  if (const char* bm = getenv("FLINT_BATCH_MIN")) c->batch_min = std::max(1, atoi(bm));
   if (c->batch_ok && wt == FLINT_W_INT4G64) {  // int4 scales regrouped by 4 rows for the batched contractions
     struct R {
       Mat* m;
@@ -714,7 +717,7 @@ int flint_decode_step_debug(flint_ctx* c, const int32_t* tokens, flint_kv* kv, i
   for (int b = 0; b < kv->batch; ++b)
     if (kv->hlen[b] + 1 > kv->max_tokens)
       return fail(FLINT_ECAPACITY, "sequence %d: length %d + 1 exceeds max_tokens %d", b, kv->hlen[b], kv->max_tokens);
-  if (kv->bscratch && kv->batch >= BATCH_MIN) {  // batched path: passes of up to BT sequences
+  if (kv->bscratch && kv->batch >= c->batch_min) {  // batched path: passes of up to BT sequences
     BArgs a = kv->bargs;
     a.tokens = tokens;
     a.out_ids = out_ids;
@@ -763,7 +766,7 @@ int flint_decode_step_seqs(flint_ctx* c, flint_kv* kv, const int32_t* seqs, int3
   }
   int rc = latched_error(c);
   if (rc) return rc;
-  if (kv->bscratch && n >= BATCH_MIN) {  // batched passes over the listed sequences
+  if (kv->bscratch && n >= c->batch_min) {  // batched passes over the listed sequences
     BArgs a = kv->bargs;
     for (int i0 = 0; i0 < n; i0 += BT) {
       a.B = std::min(BT, n - i0);
@@ -835,6 +838,91 @@ int flint_prefill_chunk(flint_ctx* c, flint_kv* kv, int32_t seq, const int32_t* 
     if (rc) return rc;
     kv->hlen[seq]++;
   }
+  return FLINT_OK;
+}
+
+int flint_micro_stream_read(flint_ctx* c, size_t bytes, int32_t reps, float* gbps) {
+  if (!c || !gbps) return fail(FLINT_EINVAL, "NULL argument");
+  if (bytes < (1u << 20) || reps < 1) return fail(FLINT_EINVAL, "bytes %zu < 1 MiB or reps %d < 1", bytes, reps);
+  bytes &= ~(size_t)15;
+  hipDeviceProp_t prop;
+  HIPCHECK(hipGetDeviceProperties(&prop, c->device));
+  void* buf = nullptr;
+  uint32_t* sink = nullptr;
+  if (hipMalloc(&buf, bytes) != hipSuccess) return fail(FLINT_ENOMEM, "stream-read buffer of %zu bytes", bytes);
+  if (hipMalloc((void**)&sink, 64) != hipSuccess) {
+    (void)hipFree(buf);
+    return fail(FLINT_ENOMEM, "stream-read sink");
+  }
+  hipEvent_t e0 = nullptr, e1 = nullptr;
+  float ms = 0.f;
+  hipError_t e = hipMemsetAsync(buf, 0, bytes, c->stream);
+  if (e == hipSuccess) e = hipEventCreate(&e0);
+  if (e == hipSuccess) e = hipEventCreate(&e1);
+  if (e == hipSuccess) e = launch_micro_read(buf, bytes, sink, 2 * prop.multiProcessorCount, c->stream);  // warm-up
+  if (e == hipSuccess) e = hipEventRecord(e0, c->stream);
+  for (int r = 0; r < reps && e == hipSuccess; ++r) e = launch_micro_read(buf, bytes, sink, 2 * prop.multiProcessorCount, c->stream);
+  if (e == hipSuccess) e = hipEventRecord(e1, c->stream);
+  if (e == hipSuccess) e = hipEventSynchronize(e1);
+  if (e == hipSuccess) e = hipEventElapsedTime(&ms, e0, e1);
+  if (e0) (void)hipEventDestroy(e0);
+  if (e1) (void)hipEventDestroy(e1);
+  (void)hipFree(buf);
+  (void)hipFree(sink);
+  if (e != hipSuccess) return fail(FLINT_EHIP, "stream read: %s", hipGetErrorString(e));
+  const size_t read = bytes / (2 * prop.multiProcessorCount) / 1024 * 1024 * (2 * prop.multiProcessorCount);
+  *gbps = (float)((double)read * reps / (ms * 1e-3) / 1e9);
+  return FLINT_OK;
+}
+
+int flint_micro_exchange(flint_ctx* c, int32_t workgroups, int32_t rounds, float* us_per_round) {
+  if (!c || !us_per_round) return fail(FLINT_EINVAL, "NULL argument");
+  hipDeviceProp_t prop;
+  HIPCHECK(hipGetDeviceProperties(&prop, c->device));
+  if (workgroups < 2 || workgroups > prop.multiProcessorCount || rounds < 1)
+    return fail(FLINT_EINVAL, "workgroups %d not in [2, %d] or rounds %d < 1", workgroups, prop.multiProcessorCount, rounds);
+  void* mem = nullptr;
+  if (hipMalloc(&mem, 8 * (size_t)workgroups + 64) != hipSuccess) return fail(FLINT_ENOMEM, "exchange slots");
+  unsigned long long* slots = (unsigned long long*)mem;
+  uint32_t* err = (uint32_t*)(slots + workgroups);
+  hipEvent_t e0 = nullptr, e1 = nullptr;
+  float ms = 0.f;
+  uint32_t herr = 0;
+  hipError_t e = hipEventCreate(&e0);
+  if (e == hipSuccess) e = hipEventCreate(&e1);
+  if (e == hipSuccess) e = hipMemsetAsync(mem, 0, 8 * (size_t)workgroups + 64, c->stream);
+  if (e == hipSuccess) e = hipEventRecord(e0, c->stream);
+  if (e == hipSuccess) e = launch_micro_exchange(slots, workgroups, rounds, err, c->stream);
+  if (e == hipSuccess) e = hipEventRecord(e1, c->stream);
+  if (e == hipSuccess) e = hipEventSynchronize(e1);
+  if (e == hipSuccess) e = hipEventElapsedTime(&ms, e0, e1);
+  if (e == hipSuccess) e = hipMemcpy(&herr, err, 4, hipMemcpyDeviceToHost);
+  if (e0) (void)hipEventDestroy(e0);
+  if (e1) (void)hipEventDestroy(e1);
+  (void)hipFree(mem);
+  if (e != hipSuccess) return fail(FLINT_EHIP, "exchange: %s", hipGetErrorString(e));
+  if (herr) return fail(FLINT_ETIMEOUT, "exchange: a wait exceeded its bound");
+  *us_per_round = ms * 1e3f / rounds;
+  return FLINT_OK;
+}
+
+int flint_micro_launch(flint_ctx* c, int32_t launches, float* us_per_launch) {
+  if (!c || !us_per_launch) return fail(FLINT_EINVAL, "NULL argument");
+  if (launches < 1) return fail(FLINT_EINVAL, "launches %d < 1", launches);
+  hipEvent_t e0 = nullptr, e1 = nullptr;
+  float ms = 0.f;
+  hipError_t e = hipEventCreate(&e0);
+  if (e == hipSuccess) e = hipEventCreate(&e1);
+  if (e == hipSuccess) e = launch_micro_empty(c->stream);
+  if (e == hipSuccess) e = hipEventRecord(e0, c->stream);
+  for (int i = 0; i < launches && e == hipSuccess; ++i) e = launch_micro_empty(c->stream);
+  if (e == hipSuccess) e = hipEventRecord(e1, c->stream);
+  if (e == hipSuccess) e = hipEventSynchronize(e1);
+  if (e == hipSuccess) e = hipEventElapsedTime(&ms, e0, e1);
+  if (e0) (void)hipEventDestroy(e0);
+  if (e1) (void)hipEventDestroy(e1);
+  if (e != hipSuccess) return fail(FLINT_EHIP, "empty launches: %s", hipGetErrorString(e));
+  *us_per_launch = ms * 1e3f / launches;
   return FLINT_OK;
 }
 

@@ -126,6 +126,9 @@ def test_null_arguments_are_rejected():
     assert lib.flint_decode_step(None, None, None, None) == fl.FLINT_EINVAL
     assert lib.flint_decode_step_seqs(None, None, None, 0, None, None) == fl.FLINT_EINVAL
     assert lib.flint_kv_tokens(None, 0, None, 0) == fl.FLINT_EINVAL
+    assert lib.flint_micro_stream_read(None, 1 << 20, 1, None) == fl.FLINT_EINVAL
+    assert lib.flint_micro_exchange(None, 2, 1, None) == fl.FLINT_EINVAL
+    assert lib.flint_micro_launch(None, 1, None) == fl.FLINT_EINVAL
     assert lib.flint_kv_prefix_match(None, 0, None, 0, None) == fl.FLINT_EINVAL
     assert lib.flint_prefill_chunk(None, None, 0, None, 1, None) == fl.FLINT_EINVAL
     assert lib.flint_sync(None) == fl.FLINT_EINVAL
