@@ -950,7 +950,9 @@ __global__ void regroup_scales_kernel(const uint16_t* s, uint16_t* s4, size_t ro
 // cached positions, merged per token; the experts run on the tokens that picked them, grouped by expert.
 
 constexpr int PF_T = 64;     // tokens per contraction workgroup
-constexpr int PF_NT = 256;   // its threads: 4 waves, each one 16-row weight tile against the 64 tokens
+constexpr int PF_W = 8;      // its waves, each one 16-row weight tile against the 64 tokens
+constexpr int PF_NT = PF_W * 64;
+constexpr int PF_DI = 16 / PF_W;  // input loads (4 token rows of 256 bytes each) per wave and stage
 constexpr int PF_PB = 512;   // columns per attention batch (bounds the partial-result buffer)
 enum { PF_QKV = 0, PF_ADD = 1, PF_SWIGLU = 2, PF_DOWNG = 3 };
 
@@ -968,16 +970,17 @@ struct PfJob {
   int ldh;
 };
 
-// Output tile (64 rows x 64 tokens) of one job.  Wave w owns weight tile w (SwiGLU: gate tiles 0, 1 and up
-// tiles 2, 3 of 32 rows) and all four 16-token tiles; the tokens' inputs go to LDS 128 inputs at a time
-// (direct-to-LDS loads, wave w bringing token tile w), double-buffered against the MFMAs of the previous
-// 128, and each wave's weight chunk and scales are loaded into registers one stage ahead.  int4: the codes
-// are unpacked once per stage for the four token tiles; arithmetic as in the batched path (codes 128 + u,
-// the constant -136 operand, the group scale on each group's fp32 result).
+// Output tile (16 PF_W rows x 64 tokens) of one job.  Wave w owns weight tile w (SwiGLU: gate tiles in the
+// first half of the waves, the matching up tiles in the second) and all four 16-token tiles; the tokens'
+// inputs go to LDS 128 inputs at a time (direct-to-LDS loads of 256 contiguous bytes per token row, spread
+// over the waves), double-buffered against the MFMAs of the previous 128, and each wave's weight chunk and
+// scales are loaded into registers one stage ahead.  int4: the codes are unpacked once per stage for the
+// four token tiles; arithmetic as in the batched path (codes 128 + u, the constant -136 operand, the group
+// scale on each group's fp32 result).
 template <int WT, int EPI>
 __global__ void __launch_bounds__(PF_NT) pf_gemm(const BArgs a, const PfJob j) {
   __shared__ uint4 abuf[2][PF_T * 16];  // [token][16-byte unit ^ (token & 15)] of 128 inputs
-  __shared__ f32x4_t upx[2][4][64];   // SwiGLU: the up tiles' results
+  __shared__ f32x4_t upx[PF_W / 2][4][64];  // SwiGLU: the up tiles' results
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, n = lane & 15, kg = lane >> 4;
   const int rb = blockIdx.x;
   int r0, r1, e = 0;  // input rows (list entries of grouped jobs) [r0, r1) of this token block
@@ -991,18 +994,19 @@ __global__ void __launch_bounds__(PF_NT) pf_gemm(const BArgs a, const PfJob j) {
     r0 = blockIdx.y * PF_T;
     r1 = min(r0 + PF_T, j.M);
   }
-  // wave w brings tokens 16 w .. 16 w + 15 of the block, 4 rows of 256 contiguous bytes per load: this
-  // lane's rows 16 w + 4 k + L / 16 (rows past r1 repeat the last one), 16-byte unit L % 16 of the LDS row
-  const uint16_t* ap[4];
+  // load i of wave w brings token rows 4 (w PF_DI + i) .. + 3 of the block, 256 contiguous bytes each:
+  // this lane's row 4 (w PF_DI + i) + L / 16 (rows past r1 repeat the last one), 16-byte unit L % 16
+  const uint16_t* ap[PF_DI];
 #pragma unroll
-  for (int k = 0; k < 4; ++k) {
-    const int ri = min(r0 + wave * 16 + 4 * k + kg, r1 - 1);
+  for (int k = 0; k < PF_DI; ++k) {
+    const int ri = min(r0 + 4 * (wave * PF_DI + k) + kg, r1 - 1);
     const int arow = j.grouped == 1 ? (gp(a.lst)[ri] >> 3) : ri;
-    ap[k] = j.A + (size_t)arow * j.lda + (n ^ ((4 * k + kg) & 15)) * 8;
+    ap[k] = j.A + (size_t)arow * j.lda + (n ^ ((4 * (wave * PF_DI + k) + kg) & 15)) * 8;
   }
   constexpr bool SWI = EPI == PF_SWIGLU;
-  const Mat& M = SWI && wave >= 2 ? j.m2 : j.m;
-  const long long T = j.tile0 + (long long)e * j.etiles + (SWI ? rb * 2 + (wave & 1) : rb * 4 + wave);
+  constexpr int HW = PF_W / 2;  // SwiGLU: gate tiles in waves 0 .. HW - 1, up tiles in the others
+  const Mat& M = SWI && wave >= HW ? j.m2 : j.m;
+  const long long T = j.tile0 + (long long)e * j.etiles + (SWI ? rb * HW + wave % HW : rb * PF_W + wave);
   const int C = j.K / kChunkIn<WT>, S = j.K / 128, G = j.K / 64;
   const uint8_t* wp = M.wt + ((size_t)T * C * 64 + lane) * 16;
   const long long srow = EPI == PF_QKV ? tile_row(T, 4 * kg, a.hd) : T * 16 + 4 * kg;  // rows 4 kg .. + 3
@@ -1010,7 +1014,7 @@ __global__ void __launch_bounds__(PF_NT) pf_gemm(const BArgs a, const PfJob j) {
   constexpr int NW4 = WT == W_I4 ? 1 : 4;  // weight chunks per stage
   auto issue = [&](int s, uint4* buf) {
 #pragma unroll
-    for (int k = 0; k < 4; ++k) dma16(ap[k] + (size_t)s * 128, &buf[(wave * 16 + 4 * k) * 16]);
+    for (int k = 0; k < PF_DI; ++k) dma16(ap[k] + (size_t)s * 128, &buf[4 * (wave * PF_DI + k) * 16]);
   };
   // the MFMA input operand of token tile t, 32-input slice q: token 16 t + n, 16-byte unit
   // int4: (q / 2) * 8 + 2 kg + (q & 1) (groups of 64 in the code order); bf16: 4 q + kg
@@ -1036,7 +1040,7 @@ __global__ void __launch_bounds__(PF_NT) pf_gemm(const BArgs a, const PfJob j) {
     if (s + 1 < S) {
       wload(s + 1, wn, sn);
       issue(s + 1, abuf[(s + 1) & 1]);
-      later = NW4 + (WT == W_I4 ? 1 : 0) + 4;
+      later = NW4 + (WT == W_I4 ? 1 : 0) + PF_DI;
     }
     wait_vmem_dyn(later);  // stage s has landed (every wave's part of it, after the barrier)
     __syncthreads();
@@ -1074,11 +1078,11 @@ __global__ void __launch_bounds__(PF_NT) pf_gemm(const BArgs a, const PfJob j) {
   }
   // epilogue: lane holds rows 4 kg .. 4 kg + 3 of its tile for token n of each token tile
   if constexpr (EPI == PF_SWIGLU) {
-    if (wave >= 2)
+    if (wave >= HW)
 #pragma unroll
-      for (int t = 0; t < 4; ++t) upx[wave - 2][t][lane] = acc[t];
+      for (int t = 0; t < 4; ++t) upx[wave - HW][t][lane] = acc[t];
     __syncthreads();
-    if (wave >= 2) return;
+    if (wave >= HW) return;
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
       const int rr = r0 + t * 16 + n;
@@ -1088,7 +1092,7 @@ __global__ void __launch_bounds__(PF_NT) pf_gemm(const BArgs a, const PfJob j) {
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const float g = acc[t][r];
-        gp(hr)[act_pos<WT>(rb * 32 + wave * 16 + 4 * kg + r)] = (uint16_t)f2bf(g / (1.0f + __expf(-g)) * u[r]);
+        gp(hr)[act_pos<WT>(rb * 16 * HW + wave * 16 + 4 * kg + r)] = (uint16_t)f2bf(g / (1.0f + __expf(-g)) * u[r]);
       }
     }
   } else if constexpr (EPI == PF_ADD) {
@@ -1096,7 +1100,7 @@ __global__ void __launch_bounds__(PF_NT) pf_gemm(const BArgs a, const PfJob j) {
     for (int t = 0; t < 4; ++t) {
       const int rr = r0 + t * 16 + n;
       if (rr >= r1) continue;
-      f32x4_t* xp = reinterpret_cast<f32x4_t*>(a.x + (size_t)rr * a.H + rb * 64 + wave * 16 + 4 * kg);
+      f32x4_t* xp = reinterpret_cast<f32x4_t*>(a.x + (size_t)rr * a.H + rb * 16 * PF_W + wave * 16 + 4 * kg);
       gp(xp)[0] = gp(xp)[0] + acc[t];
     }
   } else if constexpr (EPI == PF_DOWNG) {
@@ -1105,8 +1109,8 @@ __global__ void __launch_bounds__(PF_NT) pf_gemm(const BArgs a, const PfJob j) {
       const int rr = r0 + t * 16 + n;
       if (rr >= r1) continue;
       const int ent = gp(a.lst)[rr];
-      f32x4_t* yp = reinterpret_cast<f32x4_t*>(a.y + ((size_t)(ent >> 3) * a.K + (ent & 7)) * a.H + rb * 64 +
-                                                wave * 16 + 4 * kg);
+      f32x4_t* yp = reinterpret_cast<f32x4_t*>(a.y + ((size_t)(ent >> 3) * a.K + (ent & 7)) * a.H +
+                                                rb * 16 * PF_W + wave * 16 + 4 * kg);
       gp(yp)[0] = acc[t];
     }
   } else {  // PF_QKV: RoPE on q and k heads (partner rows in lane ^ 32), q kept in fp32, K/V appended
@@ -1357,7 +1361,7 @@ template <int WT> hipError_t run_prefill(const BArgs& a0, int n, hipStream_t st)
   for (int l = 0; l < a.L; ++l) {
     hipLaunchKernelGGL(bk_norm<WT>, dim3(n), dim3(BNT), 0, st, a, l, l == 0 ? (int)NORM_EMBED : (int)NORM_INPUT);
     const PfJob jq{a.qkv, none, (long long)l * (QR / 16), 0, a.H, a.act, a.astride, n, 0, l, nullptr, 0};
-    hipLaunchKernelGGL((pf_gemm<WT, PF_QKV>), dim3(QR / 64, TB), dim3(PF_NT), 0, st, a, jq);
+    hipLaunchKernelGGL((pf_gemm<WT, PF_QKV>), dim3(QR / (16 * PF_W), TB), dim3(PF_NT), 0, st, a, jq);
     for (int c0 = 0; c0 < n; c0 += PF_PB) {
       const int c1 = std::min(n, c0 + PF_PB);
       hipLaunchKernelGGL(pf_fattn, dim3((c1 - c0 + FA_Q - 1) / FA_Q, (a.p0 + c1 + ATT_P - 1) / ATT_P, a.nkv),
@@ -1365,21 +1369,21 @@ template <int WT> hipError_t run_prefill(const BArgs& a0, int n, hipStream_t st)
       hipLaunchKernelGGL(pf_merge<WT>, dim3(a.nq, c1 - c0), dim3(a.hd), 0, st, a, c0);
     }
     const PfJob jo{a.o, none, (long long)l * (a.H / 16), 0, QD, a.act, a.astride, n, 0, l, nullptr, 0};
-    hipLaunchKernelGGL((pf_gemm<WT, PF_ADD>), dim3(a.H / 64, TB), dim3(PF_NT), 0, st, a, jo);
+    hipLaunchKernelGGL((pf_gemm<WT, PF_ADD>), dim3(a.H / (16 * PF_W), TB), dim3(PF_NT), 0, st, a, jo);
     hipLaunchKernelGGL(bk_norm<WT>, dim3(n), dim3(BNT), 0, st, a, l, (int)NORM_POST);
     if (l < a.n_dense) {
       const PfJob jg{a.dg, a.du, (long long)l * (a.DI / 16), 0, a.H, a.act, a.astride, n, 0, l, a.h, a.DI};
-      hipLaunchKernelGGL((pf_gemm<WT, PF_SWIGLU>), dim3(a.DI / 32, TB), dim3(PF_NT), 0, st, a, jg);
+      hipLaunchKernelGGL((pf_gemm<WT, PF_SWIGLU>), dim3(a.DI / (8 * PF_W), TB), dim3(PF_NT), 0, st, a, jg);
       const PfJob jd{a.dd, none, (long long)l * (a.H / 16), 0, a.DI, a.h, a.DI, n, 0, l, nullptr, 0};
-      hipLaunchKernelGGL((pf_gemm<WT, PF_ADD>), dim3(a.H / 64, TB), dim3(PF_NT), 0, st, a, jd);
+      hipLaunchKernelGGL((pf_gemm<WT, PF_ADD>), dim3(a.H / (16 * PF_W), TB), dim3(PF_NT), 0, st, a, jd);
     } else {
       const long long lm = l - a.n_dense;
       hipLaunchKernelGGL(pf_count, dim3(a.E), dim3(256), 0, st, a, n);
       hipLaunchKernelGGL(pf_fill, dim3(a.E), dim3(256), 0, st, a, n);
       const PfJob jg{a.eg, a.eu, lm * a.E * (a.EI / 16), a.EI / 16, a.H, a.act, a.astride, 0, 1, l, a.h, a.EI};
-      hipLaunchKernelGGL((pf_gemm<WT, PF_SWIGLU>), dim3(a.EI / 32, NBM), dim3(PF_NT), 0, st, a, jg);
+      hipLaunchKernelGGL((pf_gemm<WT, PF_SWIGLU>), dim3(a.EI / (8 * PF_W), NBM), dim3(PF_NT), 0, st, a, jg);
       const PfJob jd{a.ed, none, lm * a.E * (a.H / 16), a.H / 16, a.EI, a.h, a.EI, 0, 2, l, nullptr, 0};
-      hipLaunchKernelGGL((pf_gemm<WT, PF_DOWNG>), dim3(a.H / 64, NBM), dim3(PF_NT), 0, st, a, jd);
+      hipLaunchKernelGGL((pf_gemm<WT, PF_DOWNG>), dim3(a.H / (16 * PF_W), NBM), dim3(PF_NT), 0, st, a, jd);
       hipLaunchKernelGGL(pf_combine, dim3(n), dim3(256), 0, st, a);
     }
   }
