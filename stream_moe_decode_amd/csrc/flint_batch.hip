@@ -699,6 +699,84 @@ __global__ void __launch_bounds__(BNT) bk_oproj(const BArgs a, int l) {
   fold_parts<OKC>(a, a.opart, a.cnt + t, t * 16, 16);
 }
 
+// One item of a 4-tile contraction: four 16-row tiles (rows row0 .. row0 + 63) x one input chunk (int4:
+// 128 inputs, bf16: 32), this lane's inputs of its sequence column (zeroed at use when !use; the address
+// stays valid either way) and the column's weight.  int4: s = the four rows' scales of the chunk's two
+// groups, one 16-byte load (the regrouped scales hold 4 rows x 1 group in 8 bytes, groups in order).
+template <int WT>
+struct TileItem {
+  static constexpr int NB = WT == W_I4 ? 4 : 1;
+  uint4 w[4], s[4], b[NB];
+  float wn;
+  bool use;
+};
+
+// Issue every load of one item (chunk cc of the in-input rows row0 ..) with no conditions, so the loads of
+// several items are in flight together.
+template <int WT>
+__device__ __forceinline__ void item_issue(TileItem<WT>& it, const Mat& m, int in, long long row0, int cc,
+                                           const uint16_t* col, bool use, float wn, int kg, int lane) {
+  const int C = in / kChunkIn<WT>, G = in / 64;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    it.w[q] = ld16(m.wt + ((size_t)((row0 >> 4) + q) * C * 64 + lane) * 16 + (size_t)cc * 1024);
+    if constexpr (WT == W_I4) it.s[q] = ld16(m.s4 + (size_t)((row0 + q * 16 + 4 * kg) >> 2) * G * 4 + 8 * cc);
+  }
+#pragma unroll
+  for (int q = 0; q < TileItem<WT>::NB; ++q) {
+    const int x = WT == W_I4 ? (2 * cc + (q >> 1)) * 64 + kg * 16 + (q & 1) * 8 : cc * 32 + kg * 8;
+    it.b[q] = ld16(col + x);
+  }
+  it.wn = wn;
+  it.use = use;
+}
+
+// acc += the item's four tiles . inputs per sequence column; WEIGHTED: each column's product times wn.
+template <int WT, bool WEIGHTED>
+__device__ __forceinline__ void item_math(f32x4_t (&acc)[4], const TileItem<WT>& it, const I4K& k4, bf16x8_t bias) {
+  uint4 b[TileItem<WT>::NB];
+#pragma unroll
+  for (int q = 0; q < TileItem<WT>::NB; ++q) b[q] = it.use ? it.b[q] : make_uint4(0u, 0u, 0u, 0u);
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    f32x4_t d = WEIGHTED ? f32x4_t{0.f, 0.f, 0.f, 0.f} : acc[q];
+    if constexpr (WT == W_I4) {
+      const uint4 sv = it.s[q];
+      const u32x2_t sa = {sv.x, sv.y}, sb = {sv.z, sv.w};
+      i4_chunk(d, it.w[q], sa, sb, b, k4, bias);
+    } else {
+      d = mfma(as_bf16x8(it.w[q]), as_bf16x8(b[0]), d);
+    }
+    if constexpr (WEIGHTED) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) acc[q][r] = fmaf(it.wn, d[r], acc[q][r]);
+    } else {
+      acc[q] = d;
+    }
+  }
+}
+
+// Items k = 0 .. nk - 1 of this wave through a ring of D (3 or 4): item k + D - 1 is issued before the
+// math of item k (past the last, the last again, so the loads carry no condition).  issue(it, k) loads
+// item k, math(it, k) consumes it.
+template <int WT, int D, class Issue, class Math>
+__device__ __forceinline__ void item_ring(int nk, Issue issue, Math math) {
+  static_assert(D == 3 || D == 4, "ring of 3 or 4 items");
+  if (nk <= 0) return;
+  auto clamp = [&](int k) { return k < nk ? k : nk - 1; };
+  TileItem<WT> x[D];
+#pragma unroll
+  for (int i = 0; i < D - 1; ++i) issue(x[i], clamp(i));
+  for (int k = 0;;) {
+#pragma unroll
+    for (int i = 0; i < D; ++i) {  // slot i holds item k; slot (i + D - 1) % D takes item k + D - 1
+      issue(x[(i + D - 1) % D], clamp(k + D - 1));
+      math(x[i], k);
+      if (++k >= nk) return;
+    }
+  }
+}
+
 // Gate and up rows t*64 .. t*64 + 63 of expert e (dense layers: of the dense MLP) for the sequences that
 // selected it, then SwiGLU into h[sequence][slot * expert_inter + row].  Every wave computes all eight
 // 16-row tiles (gate 0-3, up 4-7) over its eighth of the inputs; the partial tiles meet in LDS.
@@ -754,16 +832,19 @@ __global__ void __launch_bounds__(BNT) bk_gateup(const BArgs a, int l) {
   }
 }
 
-// Down rows t*64 .. t*64 + 63 (four 16-row tiles) for chunk c.  MoE: the experts of chunk c (of DKC) that
-// some sequence picked; the work items are (expert, pair of 64-input groups), wave w taking every 8th, each
-// product weighted per sequence by its routing weight (zero for sequences that did not pick the expert).
-// Dense: the pairs of 64-input groups of input chunk c.  Partial sums, added to the residual by the next norm (every
-// workgroup writes its chunk, zeros included).
+// Down rows t*64 .. t*64 + 63 (four 16-row tiles), partial sums of workgroup c, added to the residual by the
+// last of the row block's workgroups (every workgroup writes its partial rows, zeros included).
+// Dense (grid.y = DKC): the pairs of 64-input groups of input chunk c.  MoE (grid.y = DKM): the row block's
+// items are (picked expert in index order, pair of input chunks); workgroup c takes items c, c + DKM, ...
+// and its wave w every BNW-th of those, loading the next item while the MFMAs run on the current one; each
+// product is weighted per sequence by its routing weight (zero for sequences that did not pick the expert).
+constexpr int DN_RING = 3;  // items in flight per wave in the MoE down projection
 template <int WT>
 __global__ void __launch_bounds__(BNT) bk_down(const BArgs a, int l) {
   __shared__ f32x4_t red[BNW][4][64];
-  __shared__ int sel_s[BT * MAX_K];
-  __shared__ float wsel_s[BT * MAX_K];
+  __shared__ float wtab[MAX_E][BT];        // routing weight of (expert, sequence), 0: not picked
+  __shared__ signed char stab[MAX_E][BT];  // slot of the expert in the sequence's top-k, -1: not picked
+  __shared__ int elist[MAX_E];             // picked experts in index order
   __shared__ unsigned long long emask;
   const int t = blockIdx.x, c = blockIdx.y, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int n = lane & 15, kg = lane >> 4;
@@ -780,47 +861,35 @@ __global__ void __launch_bounds__(BNT) bk_down(const BArgs a, int l) {
     const uint16_t* col = n < a.B ? a.h + (size_t)n * a.hstride : nullptr;
     for (int i = ib + wave; i < ie; i += BNW) mma_tiles<WT, 4>(acc, a.dd, a.DI, tile_of, rowmap, col, i * IC, (i + 1) * IC);
   } else {
-    const int eb = part(a.E, DKC, c), ee = part(a.E, DKC, c + 1);
     if (tid == 0) emask = 0ull;
-    for (int i = tid; i < a.B * a.K; i += BNT) {
-      sel_s[i] = gp(a.sel)[i];
-      wsel_s[i] = gp(a.wsel)[i];
+    for (int i = tid; i < MAX_E * BT; i += BNT) {
+      (&wtab[0][0])[i] = 0.f;
+      (&stab[0][0])[i] = -1;
     }
     __syncthreads();
-    for (int i = tid; i < a.B * a.K; i += BNT) atomicOr(&emask, 1ull << sel_s[i]);
-    __syncthreads();
-    // the chunk's experts that some sequence picked, in index order
-    const unsigned long long mk = emask & ((ee >= 64 ? ~0ull : (1ull << ee) - 1ull) & ~((1ull << eb) - 1ull));
-    // items of 256 inputs (int4: two chunks, bf16: eight) of each picked expert
-    constexpr int IC = 256 / kChunkIn<WT>;
-    const int ne = __builtin_popcountll(mk), NI = a.EI / 256, lm = l - a.n_dense;
-    int e = -1, ei = -1, sl = -1;
-    float wn = 0.f;
-    for (int it = wave; it < ne * NI; it += BNW) {
-      const int want = it / NI, ic = it - want * NI;
-      if (want != ei) {  // next expert of this wave: its index, this lane's sequence slot and weight
-        unsigned long long mm = mk;
-        for (int k = 0; k < want; ++k) mm &= mm - 1;
-        e = __builtin_ctzll(mm);
-        ei = want;
-        sl = -1;
-        if (n < a.B)
-          for (int k = 0; k < a.K; ++k)
-            if (sel_s[n * a.K + k] == e) sl = k;
-        wn = sl >= 0 ? wsel_s[n * a.K + sl] : 0.f;
-      }
-      const uint16_t* col = sl >= 0 ? a.h + (size_t)n * a.hstride + (size_t)sl * a.EI : nullptr;
-      auto rowmap = [&](int q, int m) -> long long { return ((long long)lm * a.E + e) * a.H + t * 64 + q * 16 + m; };
-      auto tile_of = [&](int q) -> long long { return (((long long)lm * a.E + e) * a.H >> 4) + t * 4 + q; };
-      f32x4_t d[4];
-#pragma unroll
-      for (int q = 0; q < 4; ++q) d[q] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-      mma_tiles<WT, 4>(d, a.ed, a.EI, tile_of, rowmap, col, ic * IC, (ic + 1) * IC);
-#pragma unroll
-      for (int q = 0; q < 4; ++q)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) acc[q][r] = fmaf(wn, d[q][r], acc[q][r]);
+    if (tid < a.B * a.K) {
+      const int e = gp(a.sel)[tid], q = tid / a.K;
+      stab[e][q] = (signed char)(tid - q * a.K);
+      wtab[e][q] = gp(a.wsel)[tid];
+      atomicOr(&emask, 1ull << e);
     }
+    __syncthreads();
+    const unsigned long long mk = emask;
+    if (tid < MAX_E && ((mk >> tid) & 1ull)) elist[__builtin_popcountll(mk & ((1ull << tid) - 1ull))] = tid;
+    __syncthreads();
+    const int NI = a.EI / kChunkIn<WT>, total = __builtin_popcountll(mk) * NI, lm = l - a.n_dense;
+    // this wave's items are c + DKM (w + BNW k)
+    const int wu = __builtin_amdgcn_readfirstlane(wave), j0 = c + DKM * wu, jstep = DKM * BNW;
+    const I4K k4 = i4k();
+    const bf16x8_t bias = bias136();
+    item_ring<WT, DN_RING>(
+        j0 < total ? (total - j0 + jstep - 1) / jstep : 0,
+        [&](TileItem<WT>& it, int k) {
+          const int jj = j0 + k * jstep, r = jj / NI, e = elist[r], sl = stab[e][n];
+          item_issue<WT>(it, a.ed, a.EI, ((long long)lm * a.E + e) * a.H + t * 64, jj - r * NI,
+                         a.h + (size_t)n * a.hstride + (size_t)(sl > 0 ? sl : 0) * a.EI, sl >= 0, wtab[e][n], kg, lane);
+        },
+        [&](const TileItem<WT>& it, int) { item_math<WT, true>(acc, it, k4, bias); });
   }
 #pragma unroll
   for (int q = 0; q < 4; ++q) red[wave][q][lane] = acc[q];
@@ -835,7 +904,8 @@ __global__ void __launch_bounds__(BNT) bk_down(const BArgs a, int l) {
     for (int w = 0; w < BNW; ++w) v += red[w][tile][ln][r];
     pstore(a.dpart + ((size_t)c * BT + q) * a.H + t * 64 + rr, v);
   }
-  fold_parts<DKC>(a, a.dpart, a.cnt + a.H / 16 + t, t * 64, 64);
+  if (dense) fold_parts<DKC>(a, a.dpart, a.cnt + a.H / 16 + t, t * 64, 64);
+  else fold_parts<DKM>(a, a.dpart, a.cnt + a.H / 16 + t, t * 64, 64);
 }
 
 // lm_head (bf16) rows of this workgroup in 16-row tiles; wave w computes four tiles over half of the
@@ -1408,7 +1478,7 @@ template <int WT> hipError_t run_pass(const BArgs& a, hipStream_t st) {
     hipLaunchKernelGGL(bk_norm<WT>, dim3(a.B), dim3(BNT), 0, st, a, l, (int)NORM_POST);
     const bool dense = l < a.n_dense;
     hipLaunchKernelGGL(bk_gateup<WT>, dense ? dim3(a.DI / 64, 1) : dim3(a.EI / 64, a.E), dim3(BNT), 0, st, a, l);
-    hipLaunchKernelGGL(bk_down<WT>, dim3(a.H / 64, DKC), dim3(BNT), 0, st, a, l);
+    hipLaunchKernelGGL(bk_down<WT>, dim3(a.H / 64, dense ? DKC : DKM), dim3(BNT), 0, st, a, l);
   }
   hipLaunchKernelGGL(bk_norm<WT>, dim3(a.B), dim3(BNT), 0, st, a, a.L, (int)NORM_FINAL);
   hipLaunchKernelGGL(bk_head, dim3(std::min(256, a.V / 16)), dim3(BNT), 0, st, a);

@@ -92,7 +92,8 @@ constexpr int ATT_P = 256;              // cached positions per attention split 
 constexpr int ATT_C = 16;               // positions per chunk of a split (one MFMA score tile)
 constexpr int MAX_SPLITS = 1024;        // attention splits per sequence (max_tokens <= ATT_P * MAX_SPLITS)
 constexpr int OKC = 2;                  // o_proj input chunks (partial sums added by the next norm)
-constexpr int DKC = 16;                 // MoE down expert chunks / dense down input chunks
+constexpr int DKC = 16;                 // dense down input chunks (partial-sum buffers)
+constexpr int DKM = 8;                  // MoE down workgroups per 64-row block (<= DKC)
 
 struct BArgs {
   // model
