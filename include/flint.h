@@ -247,8 +247,9 @@ int flint_prefill_chunk(flint_ctx* ctx, flint_kv* kv, int32_t seq, const int32_t
  *    memory once per launch, `reps` launches (the practical HBM ceiling);
  *  - flint_micro_exchange: microseconds per round of an all-to-all exchange
  *    among `workgroups` (2 .. compute units) co-resident workgroups through
- *    tagged system-scope slots, as the decode kernel hands data between
- *    workgroups; FLINT_ETIMEOUT if a bounded wait ran out;
+ *    tagged system-scope slots written in 8 replicas (one per XCD) and read
+ *    all at once, as the decode kernel hands data between workgroups;
+ *    FLINT_ETIMEOUT if a bounded wait ran out;
  *  - flint_micro_launch: microseconds per back-to-back empty kernel launch.
  * Errors: FLINT_EINVAL, FLINT_ENOMEM, FLINT_EHIP (and FLINT_ETIMEOUT above).
  */

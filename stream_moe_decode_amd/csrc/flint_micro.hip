@@ -28,24 +28,32 @@ __global__ void __launch_bounds__(256) micro_read(const uint8_t* p, size_t per, 
   if (ring[0][threadIdx.x].x == 0x9E3779B9u) gp(sink)[0] = 1u;
 }
 
-// `rounds` all-to-all exchanges: workgroup w publishes (round << 32 | w) in slot w with a system-scope
-// store, then its lanes wait until every slot carries at least that round (system-scope loads).  Each
-// wait is bounded: past the bound the kernel latches *err and the waiting lane leaves, so every
-// workgroup finishes.
-__global__ void __launch_bounds__(64) micro_exchange(unsigned long long* slots, int rounds, uint32_t* err) {
-  const int W = blockIdx.x, G = gridDim.x, lane = threadIdx.x;
+// `rounds` all-to-all exchanges in the decode kernel's form: workgroup w publishes (round << 32 | w) in
+// slot w of each of the NCOPY replicas (one per XCD; lane c stores replica c) with system-scope stores,
+// then thread t reads slot t of replica w % NCOPY (every slot at once) and re-polls it until it carries
+// at least that round.  Each wait is bounded: past the bound the kernel latches *err and the workgroup
+// leaves, so every workgroup finishes.
+__global__ void __launch_bounds__(256) micro_exchange(unsigned long long* slots, int rounds, uint32_t* err) {
+  __shared__ int bad;
+  const int W = blockIdx.x, G = gridDim.x, tid = threadIdx.x;
+  const unsigned long long* mine = slots + (size_t)(W % NCOPY) * G;
+  if (tid == 0) bad = 0;
+  __syncthreads();
   for (int r = 1; r <= rounds; ++r) {
-    if (lane == 0)
-      __hip_atomic_store(gp(slots) + W, ((unsigned long long)r << 32) | (unsigned)W, __ATOMIC_RELAXED,
-                         __HIP_MEMORY_SCOPE_SYSTEM);
-    for (int s = lane; s < G; s += 64) {
+    if (tid < NCOPY)
+      __hip_atomic_store(gp(slots) + (size_t)tid * G + W, ((unsigned long long)r << 32) | (unsigned)W,
+                         __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+    for (int s = tid; s < G; s += 256) {
       int polls = 0;
-      while ((int)(__hip_atomic_load(gp(slots) + s, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM) >> 32) < r)
+      while ((int)(__hip_atomic_load(gp(mine) + s, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM) >> 32) < r)
         if (++polls > (1 << 20)) {
-          __hip_atomic_fetch_or(gp(err), 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-          return;
+          __hip_atomic_fetch_or(gp(err), 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+          bad = 1;
+          break;
         }
     }
+    __syncthreads();
+    if (bad) return;
   }
 }
 
@@ -59,7 +67,7 @@ hipError_t launch_micro_read(const void* p, size_t bytes, uint32_t* sink, int bl
   return hipGetLastError();
 }
 hipError_t launch_micro_exchange(unsigned long long* slots, int workgroups, int rounds, uint32_t* err, hipStream_t st) {
-  hipLaunchKernelGGL(micro_exchange, dim3(workgroups), dim3(64), 0, st, slots, rounds, err);
+  hipLaunchKernelGGL(micro_exchange, dim3(workgroups), dim3(256), 0, st, slots, rounds, err);
   return hipGetLastError();
 }
 hipError_t launch_micro_empty(hipStream_t st) {

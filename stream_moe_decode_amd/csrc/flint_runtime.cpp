@@ -882,15 +882,16 @@ int flint_micro_exchange(flint_ctx* c, int32_t workgroups, int32_t rounds, float
   if (workgroups < 2 || workgroups > prop.multiProcessorCount || rounds < 1)
     return fail(FLINT_EINVAL, "workgroups %d not in [2, %d] or rounds %d < 1", workgroups, prop.multiProcessorCount, rounds);
   void* mem = nullptr;
-  if (hipMalloc(&mem, 8 * (size_t)workgroups + 64) != hipSuccess) return fail(FLINT_ENOMEM, "exchange slots");
+  const size_t bytes = 8 * (size_t)NCOPY * workgroups + 64;  // NCOPY replicas of the slots, then the error word
+  if (hipMalloc(&mem, bytes) != hipSuccess) return fail(FLINT_ENOMEM, "exchange slots");
   unsigned long long* slots = (unsigned long long*)mem;
-  uint32_t* err = (uint32_t*)(slots + workgroups);
+  uint32_t* err = (uint32_t*)(slots + (size_t)NCOPY * workgroups);
   hipEvent_t e0 = nullptr, e1 = nullptr;
   float ms = 0.f;
   uint32_t herr = 0;
   hipError_t e = hipEventCreate(&e0);
   if (e == hipSuccess) e = hipEventCreate(&e1);
-  if (e == hipSuccess) e = hipMemsetAsync(mem, 0, 8 * (size_t)workgroups + 64, c->stream);
+  if (e == hipSuccess) e = hipMemsetAsync(mem, 0, bytes, c->stream);
   if (e == hipSuccess) e = hipEventRecord(e0, c->stream);
   if (e == hipSuccess) e = launch_micro_exchange(slots, workgroups, rounds, err, c->stream);
   if (e == hipSuccess) e = hipEventRecord(e1, c->stream);
