@@ -5,8 +5,10 @@ Workload (default ``int4_49``): 49 layers (0-1 dense SwiGLU, 2-48 MoE with 64
 experts, top-6), hidden 2048, GQA 16/4 x 128, vocab 65536, int4 group-64
 weights with bf16 scales (embedding and lm_head bf16), random-init weights
 ~N(0, 0.02), a synthetic resident KV cache of 8,022 positions ~N(0, 1), then
-K greedy decode steps with the token fed back on the device.  One step is one
-kernel launch (the whole decode step).
+K greedy decode steps with the token fed back on the device, timed in
+--rounds rounds from the same cache state (the median round is reported, every
+round listed under "rounds").  One step is one kernel launch (the whole decode
+step).
 
 Prints one JSON line: tokens/s, ms/step, the HBM roofline of the decode
 kernel (algorithmic bytes per launch / mean launch time from HIP events on
@@ -15,6 +17,7 @@ the CPU oracle timed on a bounded sample of the same workload.
 """
 import argparse
 import json
+import statistics
 import os
 import sys
 import time
@@ -128,16 +131,20 @@ def bench_batch(args, cfg):
     for _ in range(args.warmup):
         decode_step(model.ctx, tok.data_ptr(), kv.handle, tok.data_ptr())
     sync(model.ctx)
-    reset()
     K = args.steps
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record()
-    for _ in range(K):
-        decode_step(model.ctx, tok.data_ptr(), kv.handle, tok.data_ptr())
-    e1.record()
-    torch.cuda.synchronize()
-    sync(model.ctx)
-    total_ms = e0.elapsed_time(e1)
+
+    def one_round():
+        reset()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(K):
+            decode_step(model.ctx, tok.data_ptr(), kv.handle, tok.data_ptr())
+        e1.record()
+        torch.cuda.synchronize()
+        sync(model.ctx)
+        return e0.elapsed_time(e1)
+
+    total_ms, rounds = timed_rounds(args.rounds, K, one_round)
     # the same steps again with the routes recorded: the union of picked experts per layer and step
     reset()
     dbgs = [make_debug(cfg, B, dev, logits=(i == 0)) for i in range(K)]
@@ -191,9 +198,19 @@ def bench_batch(args, cfg):
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
                      "bytes_per_step": int(bytes_total / K), "experts_per_moe_layer": round(float(np.mean(unions)), 2),
                      "scope": "whole step (every kernel of the pass)"},
+        "rounds": rounds,
         "cpu_baseline": cpu_baseline,
     }
     print(json.dumps(out), flush=True)
+
+
+def timed_rounds(n, K, one_round):
+    """Run the K timed steps n times (each round restarts from the same cache state) and return the
+    median round's milliseconds with a summary of every round (the reported value is the median)."""
+    ms = [one_round() for _ in range(max(1, n))]
+    per = [round(m / K, 4) for m in ms]
+    return statistics.median(ms), {"n": len(ms), "ms_per_step": per, "min": min(per), "max": max(per),
+                                   "value_from": "median round"}
 
 
 def bench_concurrency(args, cfg, model, kv, lens, first):
@@ -260,19 +277,24 @@ def bench_prefill(args, cfg):
 
     run()  # warm-up (also makes the batched path's tiled weights)
     sync(model.ctx)
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    e0.record()
-    run()
-    e1.record()
-    torch.cuda.synchronize()
-    sync(model.ctx)
-    ms = e0.elapsed_time(e1)
+
+    def one_round():
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record()
+        run()
+        e1.record()
+        torch.cuda.synchronize()
+        sync(model.ctx)
+        return e0.elapsed_time(e1)
+
+    ms, rounds = timed_rounds(args.rounds, 1, one_round)
     model.free()
-    log(f"prefill of {n} tokens: {ms:.1f} ms")
+    log(f"prefill of {n} tokens: {ms:.1f} ms (median of {rounds['n']})")
     print(json.dumps({
         "metric": "prefill tok/s (one sequence)", "value": round(n / (ms / 1e3), 1), "unit": "tok/s",
-        "n_gpus": 1, "higher_is_better": True, "ms_total": round(ms, 2), "dtype": "bf16", "data": "synthetic",
+        "n_gpus": 1, "higher_is_better": True, "ms_total": round(ms, 2), "rounds": rounds, "dtype": "bf16",
+        "data": "synthetic",
         "config": {"workload": f"{cfg.name}: {n}-token prompt " + (f"appended to {R} cached positions" if R else
                                                                     "from an empty cache"),
                    "prompt": n, "resident": R},
@@ -303,6 +325,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=256)
     ap.add_argument("--warmup", type=int, default=8)
+    ap.add_argument("--rounds", type=int, default=3,
+                    help="timed rounds of --steps steps, each from the same cache state; the median is reported")
     ap.add_argument("--config", default="int4_49")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-steps", type=int, default=4, help="decode steps the oracle is timed on")
@@ -381,15 +405,21 @@ def main():
     torch.cuda.synchronize()
 
     K = args.steps
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    e0.record()
-    for i in range(K):
-        decode_step(model.ctx, tok.data_ptr(), kv.handle, tok.data_ptr())
-    e1.record()
-    torch.cuda.synchronize()
-    sync(model.ctx)
-    total_ms = e0.elapsed_time(e1)
+
+    def one_round():
+        kv.set_lengths([resident])
+        tok.fill_(first)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record()
+        for i in range(K):
+            decode_step(model.ctx, tok.data_ptr(), kv.handle, tok.data_ptr())
+        e1.record()
+        torch.cuda.synchronize()
+        sync(model.ctx)
+        return e0.elapsed_time(e1)
+
+    total_ms, rounds = timed_rounds(args.rounds, K, one_round)
     bytes_total = sum(step_bytes(cfg, resident + i) for i in range(K))
 
     # the same K steps again (cache rolled back), each launch between its own pair of events: the
@@ -491,6 +521,7 @@ def main():
                      "bytes_per_launch": int(bytes_total / K), "weight_bytes_per_step": wb,
                      "kernel_mean_us": round(1e6 * mean_kern_s, 2),
                      "roofline_tok_s": round(HBM_PEAK_GBS * 1e9 / (bytes_total / K), 1)},
+        "rounds": rounds,
         "phases": phases,
         "micro": dict(micro_out, decode_frac_of_stream_read=round(achieved / micro_out["stream_read_gbs"], 4)),
         "cpu_baseline": cpu_baseline,
