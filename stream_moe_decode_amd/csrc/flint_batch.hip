@@ -643,8 +643,7 @@ __global__ void __launch_bounds__(ATT_NT) bk_attn(const BArgs a, int l) {
 // l_s, written in bf16 to out[act_pos(d)] (the o_proj input).  Thread d owns dim d; the splits are taken MB
 // at a time with every load of a block (m, l and o of each split) issued before any is used, and the
 // blocks are folded by the running-max rule.
-constexpr int MB = 32;
-template <int WT>
+template <int WT, int MB = 32>
 __device__ __forceinline__ void merge_head(const float* p, int ns, int hd, uint16_t* out) {
   const int d = threadIdx.x;
   float M = -INFINITY, L = 0.f, O = 0.f;
@@ -1279,29 +1278,30 @@ __global__ void __launch_bounds__(256) pf_combine(const BArgs a) {
   }
 }
 
-// Prefill attention, flash style: workgroup (query block b of 16 tokens, key split s of ATT_P positions,
-// kv head j); wave w is query head j Gq + w over the block's tokens.  Scores are computed transposed,
-// S^T = K Q^T on v_mfma_f32_16x16x32_bf16 (K as the A operand, the query's bf16 high and low parts as B), so
-// that a lane holds 4 keys of one query row: the online softmax of a row stays in its lane group, and the
-// probabilities are already the B operand of O^T += V^T P^T on v_mfma_f32_16x16x16_bf16 (high and low
-// parts again).  V^T comes from row-major V in LDS through the transposing LDS read (ds_read_b64_tr_b16);
-// V's 16-byte units are XOR-swizzled by row so that those reads spread over the banks.  K and V go to LDS
-// 64 keys at a time, double-buffered.  Writes the split's (m, l, o) per token and head; a token's splits
-// past its own causal range are written but never merged.
-constexpr int FA_Q = 16, FA_KS = 64;
+// Prefill attention, flash style: workgroup (query block b of FA_Q tokens, key split s of P positions (a
+// multiple of FA_KS, at least ATT_P), kv head j); wave w is query head j Gq + w over the block's tokens, in FA_SB sub-blocks of 16 whose
+// dependency chains interleave and which share every K and V operand read.  Scores are computed
+// transposed, S^T = K Q^T on v_mfma_f32_16x16x32_bf16 (K as the A operand, the query's bf16 high and low
+// parts as B), so that a lane holds 4 keys of one query row: the online softmax of a row stays in its lane
+// group, and the probabilities are already the B operand of O^T += V^T P^T on v_mfma_f32_16x16x16_bf16
+// (high and low parts again).  V^T comes from row-major V in LDS through the transposing LDS read
+// (ds_read_b64_tr_b16); V's 16-byte units are XOR-swizzled by row so that those reads spread over the
+// banks.  K and V go to LDS 64 keys at a time, double-buffered.  Writes the split's (m, l, o) per token and
+// head; a token's splits past its own causal range are written but never merged.
+constexpr int FA_SB = 2, FA_Q = 16 * FA_SB, FA_KS = 64;
 typedef short s16x4_t __attribute__((ext_vector_type(4)));
 __device__ __forceinline__ f32x4_t mfma16(s16x4_t a, s16x4_t b, f32x4_t c) {
   return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
 }
-__global__ void __launch_bounds__(256) pf_fattn(const BArgs a, int l, int c0, int c1) {
+__global__ void __launch_bounds__(256, 2) pf_fattn(const BArgs a, int l, int c0, int c1, int P) {
   __shared__ uint4 kl[2][FA_KS * 16];  // [chunk of 16 keys][dims / 32][lane]: the A operand of S^T
   __shared__ uint4 vl[2][FA_KS * 16];  // [key][16-byte unit ^ (key & 15)]
   const int b = blockIdx.x, s = blockIdx.y, j = blockIdx.z;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, i = lane & 15, g = lane >> 4;
   const int t0 = c0 + b * FA_Q, tq1 = min(t0 + FA_Q, c1);
-  const int k0 = s * ATT_P, kend = a.p0 + tq1;  // keys [0, kend) are visible to some token of the block
+  const int k0 = s * P, kend = a.p0 + tq1;  // keys [0, kend) are visible to some token of the block
   if (t0 >= c1 || k0 >= kend) return;
-  const int k1 = min(k0 + ATT_P, kend), hd = 128, Gq = a.nq / a.nkv;
+  const int k1 = min(k0 + P, kend), hd = 128, Gq = a.nq / a.nkv;
   const size_t cb = (((size_t)l * a.Bc + a.seq0) * a.nkv + j) * (size_t)a.cap * hd * 2;
   const uint8_t* const kb = a.kc + cb;
   const uint8_t* const vb = a.vc + cb;
@@ -1318,27 +1318,39 @@ __global__ void __launch_bounds__(256) pf_fattn(const BArgs a, int l, int c0, in
     }
   };
   issue(k0, 0);
-  // this wave's query rows as B operands of S^T: token t0 + i, dims 32 sk + 8 g .. + 8, high and low parts
+  // this wave's query rows as B operands of S^T: sub-block sb is token t0 + 16 sb + i, dims 32 sk + 8 g .. + 8,
+  // high and low parts
   const bool act = wave < Gq;
-  const int head = j * Gq + min(wave, Gq - 1), tq = min(t0 + i, tq1 - 1), qpos = a.p0 + t0 + i;
-  const float* qp = a.q + ((size_t)tq * a.nq + head) * hd + g * 8;
+  const int head = j * Gq + min(wave, Gq - 1);
   const float qm = 1.0f / sqrtf((float)hd);
-  bf16x8_t qh[4], ql[4];
+  bf16x8_t qh[FA_SB][4], ql[FA_SB][4];
+  int qpos[FA_SB];
 #pragma unroll
-  for (int sk = 0; sk < 4; ++sk) {
-    const f32x4_t x0 = *(GLOBAL const f32x4_t*)(qp + sk * 32), x1 = *(GLOBAL const f32x4_t*)(qp + sk * 32 + 4);
+  for (int sb = 0; sb < FA_SB; ++sb) {
+    const int tq = min(t0 + 16 * sb + i, tq1 - 1);
+    qpos[sb] = a.p0 + t0 + 16 * sb + i;
+    const float* qp = a.q + ((size_t)tq * a.nq + head) * hd + g * 8;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const float qv = (e < 4 ? x0[e] : x1[e - 4]) * qm;
-      const uint32_t hb = f2bf(qv);
-      qh[sk][e] = __builtin_bit_cast(__bf16, (uint16_t)hb);
-      ql[sk][e] = __builtin_bit_cast(__bf16, (uint16_t)f2bf(qv - bf2f(hb)));
+    for (int sk = 0; sk < 4; ++sk) {
+      const f32x4_t x0 = *(GLOBAL const f32x4_t*)(qp + sk * 32), x1 = *(GLOBAL const f32x4_t*)(qp + sk * 32 + 4);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float qv = (e < 4 ? x0[e] : x1[e - 4]) * qm;
+        const uint32_t hb = f2bf(qv);
+        qh[sb][sk][e] = __builtin_bit_cast(__bf16, (uint16_t)hb);
+        ql[sb][sk][e] = __builtin_bit_cast(__bf16, (uint16_t)f2bf(qv - bf2f(hb)));
+      }
     }
   }
-  float m = -INFINITY, lsum = 0.f;  // of query row i
-  f32x4_t o[8];                     // O^T: dims 16 db + 4 g + r of query row i
+  float m[FA_SB], lsum[FA_SB];  // of query row i of each sub-block
+  f32x4_t o[FA_SB][8];          // O^T: dims 16 db + 4 g + r of query row i
 #pragma unroll
-  for (int db = 0; db < 8; ++db) o[db] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  for (int sb = 0; sb < FA_SB; ++sb) {
+    m[sb] = -INFINITY;
+    lsum[sb] = 0.f;
+#pragma unroll
+    for (int db = 0; db < 8; ++db) o[sb][db] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  }
   const int nst = (k1 - k0 + FA_KS - 1) / FA_KS;
   for (int st = 0; st < nst; ++st) {
     const int ks = k0 + st * FA_KS, buf = st & 1;
@@ -1354,70 +1366,104 @@ __global__ void __launch_bounds__(256) pf_fattn(const BArgs a, int l, int c0, in
       for (int c = 0; c < FA_KS / 16; ++c) {
         const int kc0 = ks + 16 * c;
         if (kc0 >= k1) break;
-        f32x4_t sc = {0.f, 0.f, 0.f, 0.f};  // S^T: keys kc0 + 4 g + r, query row i
+        f32x4_t sc[FA_SB];  // S^T: keys kc0 + 4 g + r, query row i
+#pragma unroll
+        for (int sb = 0; sb < FA_SB; ++sb) sc[sb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int sk = 0; sk < 4; ++sk) {
           const bf16x8_t kop = as_bf16x8(kl[buf][(c * 4 + sk) * 64 + lane]);
-          sc = mfma(kop, qh[sk], sc);
-          sc = mfma(kop, ql[sk], sc);
-        }
-        float sv[4], mx = -INFINITY;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int kp = kc0 + 4 * g + r;
-          sv[r] = kp < k1 && kp <= qpos ? sc[r] : -INFINITY;
-          mx = fmaxf(mx, sv[r]);
+          for (int sb = 0; sb < FA_SB; ++sb) {
+            sc[sb] = mfma(kop, qh[sb][sk], sc[sb]);
+            sc[sb] = mfma(kop, ql[sb][sk], sc[sb]);
+          }
         }
-        mx = fmaxf(mx, swap16(mx));
-        mx = fmaxf(mx, swap32(mx));
-        const float mn = fmaxf(m, mx), mref = mn == -INFINITY ? 0.f : mn;
-        const float alpha = __expf(m - mref);
-        float p[4], ps = 0.f;
+        float alpha[FA_SB];
+        s16x4_t ph[FA_SB], pl[FA_SB];
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          p[r] = __expf(sv[r] - mref);
-          ps += p[r];
-        }
-        ps += swap16(ps);
-        ps += swap32(ps);
-        lsum = lsum * alpha + ps;
-        m = mn;
-        s16x4_t ph, pl;
+        for (int sb = 0; sb < FA_SB; ++sb) {
+          float sv[4], mx = -INFINITY;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const uint32_t hb = f2bf(p[r]);
-          ph[r] = (short)hb;
-          pl[r] = (short)f2bf(p[r] - bf2f(hb));
+          for (int r = 0; r < 4; ++r) {
+            const int kp = kc0 + 4 * g + r;
+            sv[r] = kp < k1 && kp <= qpos[sb] ? sc[sb][r] : -INFINITY;
+            mx = fmaxf(mx, sv[r]);
+          }
+          mx = fmaxf(mx, swap16(mx));
+          mx = fmaxf(mx, swap32(mx));
+          const float mn = fmaxf(m[sb], mx), mref = mn == -INFINITY ? 0.f : mn;
+          alpha[sb] = __expf(m[sb] - mref);
+          float p[4], ps = 0.f;
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            p[r] = __expf(sv[r] - mref);
+            ps += p[r];
+          }
+          ps += swap16(ps);
+          ps += swap32(ps);
+          lsum[sb] = lsum[sb] * alpha[sb] + ps;
+          m[sb] = mn;
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const uint32_t hb = f2bf(p[r]);
+            ph[sb][r] = (short)hb;
+            pl[sb][r] = (short)f2bf(p[r] - bf2f(hb));
+          }
         }
         // V^T operand of dims 16 db .. + 16: this lane passes key row 16 c + 4 g + i / 4, dims 16 db + 4 (i & 3)
         const int row = 16 * c + 4 * g + (i >> 2);
+#pragma unroll
+        for (int sb = 0; sb < FA_SB; ++sb) {
+          if (__builtin_amdgcn_ballot_w64(alpha[sb] != 1.0f)) {  // some row's running max moved (else x 1)
+#pragma unroll
+            for (int db = 0; db < 8; ++db) o[sb][db] *= alpha[sb];
+          }
+        }
 #pragma unroll
         for (int db = 0; db < 8; ++db) {
           const int u = 2 * db + ((i & 3) >> 1);
           const s16x4_t vt = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
               (__attribute__((address_space(3))) s16x4_t*)(vlb + row * 256 + ((u ^ (row & 15)) * 16) + (i & 1) * 8));
-          o[db] *= alpha;
-          o[db] = mfma16(vt, ph, o[db]);
-          o[db] = mfma16(vt, pl, o[db]);
+#pragma unroll
+          for (int sb = 0; sb < FA_SB; ++sb) {
+            o[sb][db] = mfma16(vt, ph[sb], o[sb][db]);
+            o[sb][db] = mfma16(vt, pl[sb], o[sb][db]);
+          }
         }
       }
     }
     __syncthreads();  // every wave is done with this buffer before it is refilled
   }
-  if (!act || t0 + i >= tq1) return;
-  float* dst = a.part + (((size_t)(t0 + i - c0) * a.nq + head) * a.nsmax + s) * (hd + 2);
+  if (!act) return;
 #pragma unroll
-  for (int db = 0; db < 8; ++db) *(GLOBAL f32x4_t*)(dst + 2 + 16 * db + 4 * g) = o[db];
-  if (g == 0) {
-    gp(dst)[0] = m;
-    gp(dst)[1] = lsum;
+  for (int sb = 0; sb < FA_SB; ++sb) {
+    const int t = t0 + 16 * sb + i;
+    if (t >= tq1) continue;
+    float* dst = a.part + (((size_t)(t - c0) * a.nq + head) * a.nsmax + s) * (hd + 2);
+#pragma unroll
+    for (int db = 0; db < 8; ++db) *(GLOBAL f32x4_t*)(dst + 2 + 16 * db + 4 * g) = o[sb][db];
+    if (g == 0) {
+      gp(dst)[0] = m[sb];
+      gp(dst)[1] = lsum[sb];
+    }
   }
 }
-template <int WT>
-__global__ void __launch_bounds__(128) pf_merge(const BArgs a, int c0) {
+template <int WT, int MB>
+__global__ void __launch_bounds__(128) pf_merge(const BArgs a, int c0, int P) {
   const int h = blockIdx.x, n = c0 + blockIdx.y, hd = a.hd;
-  merge_head<WT>(a.part + ((size_t)blockIdx.y * a.nq + h) * a.nsmax * (hd + 2), (a.p0 + n + ATT_P) / ATT_P, hd,
+  merge_head<WT, MB>(a.part + ((size_t)blockIdx.y * a.nq + h) * a.nsmax * (hd + 2), (a.p0 + n + P) / P, hd,
                  a.act + (size_t)n * a.astride + h * hd);
+}
+
+// Key split of a prefill attention call over keys [0, kmax) with `groups` (query block, kv head) pairs:
+// about FA_SPLITS splits per pair (enough workgroups to fill the chip), never shorter than ATT_P keys (the
+// split count the partial buffer is sized for) and in whole FA_KS stages.  Longer splits write and merge
+// fewer partials.
+constexpr int FA_WG = 512;
+inline int fa_split(int kmax, int groups) {
+  const int want = std::max(1, (FA_WG + groups - 1) / groups);
+  const int p = (kmax + want - 1) / want;
+  return std::max(ATT_P, (p + FA_KS - 1) / FA_KS * FA_KS);
 }
 
 template <int WT> hipError_t run_prefill(const BArgs& a0, int n, hipStream_t st) {
@@ -1434,9 +1480,12 @@ template <int WT> hipError_t run_prefill(const BArgs& a0, int n, hipStream_t st)
     hipLaunchKernelGGL((pf_gemm<WT, PF_QKV>), dim3(QR / (16 * PF_W), TB), dim3(PF_NT), 0, st, a, jq);
     for (int c0 = 0; c0 < n; c0 += PF_PB) {
       const int c1 = std::min(n, c0 + PF_PB);
-      hipLaunchKernelGGL(pf_fattn, dim3((c1 - c0 + FA_Q - 1) / FA_Q, (a.p0 + c1 + ATT_P - 1) / ATT_P, a.nkv),
-                         dim3(256), 0, st, a, l, c0, c1);
-      hipLaunchKernelGGL(pf_merge<WT>, dim3(a.nq, c1 - c0), dim3(a.hd), 0, st, a, c0);
+      const int nb = (c1 - c0 + FA_Q - 1) / FA_Q, P = fa_split(a.p0 + c1, nb * a.nkv);
+      hipLaunchKernelGGL(pf_fattn, dim3(nb, (a.p0 + c1 + P - 1) / P, a.nkv), dim3(256), 0, st, a, l, c0, c1, P);
+      if ((a.p0 + c1 + P - 1) / P <= 8)  // splits merged 8 at a time (every load of a block is issued at once)
+        hipLaunchKernelGGL((pf_merge<WT, 8>), dim3(a.nq, c1 - c0), dim3(a.hd), 0, st, a, c0, P);
+      else
+        hipLaunchKernelGGL((pf_merge<WT, 32>), dim3(a.nq, c1 - c0), dim3(a.hd), 0, st, a, c0, P);
     }
     const PfJob jo{a.o, none, (long long)l * (a.H / 16), 0, QD, a.act, a.astride, n, 0, l, nullptr, 0};
     hipLaunchKernelGGL((pf_gemm<WT, PF_ADD>), dim3(a.H / (16 * PF_W), TB), dim3(PF_NT), 0, st, a, jo);
