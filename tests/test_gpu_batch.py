@@ -140,6 +140,44 @@ def test_prefill_passes_match_oracle():
     model.free()
 
 
+@pytest.mark.parametrize("nkv", [4, 2])
+def test_long_prefill_after_resident_cache(nkv):
+    # 512 prompt tokens after 2,100 resident positions: one attention column batch over 2,612 keys.  With 4 kv
+    # heads the call's key splits are 384 positions (7 splits, merged 8 at a time); with 2 kv heads they stay
+    # at 256 (11 splits, merged 32 at a time).  The greedy id, then 2 decode steps over the whole cache
+    from gpu_common import Stepper
+    from stream_moe_decode_amd import prefill_chunk
+    cfg = SMALL.replace(name=f"int4_small_kv{nkv}", n_kv_heads=nkv)
+    model = build(cfg)
+    res, n = 2100, 512
+    cap = res + n + 8
+    kv = model.kv(1, cap)
+    orc = make_oracle(cfg, cap)
+    for l in range(cfg.n_layers):
+        k, v = synth.resident_kv(cfg, l, 0, res)
+        kv.load_resident(l, 0, k, v)
+        orc.set_resident(0, l, k, v)
+    kv.set_lengths([res])
+    orc.len[0] = res
+    prompt = synth.tokens(cfg, n, stream=23)
+    dev = model.device
+    toks = torch.from_numpy(prompt).to(dev)
+    out = torch.zeros(1, dtype=torch.int32, device=dev)
+    print(f"{cfg.name}: prefill of {n} tokens after {res}", flush=True)
+    prefill_chunk(model.ctx, kv.handle, 0, toks.data_ptr(), n, out.data_ptr())
+    sync(model.ctx)
+    r = orc.forward(0, prompt)
+    gpu_id, o_id, gap = int(out.item()), int(r["ids"][-1]), float(r["gap"][-1])
+    print(f"  gpu id {gpu_id} oracle id {o_id} oracle gap {gap:.3g}", flush=True)
+    assert gpu_id == o_id or gap < TIE_EPS
+    assert kv_get_lengths(kv.handle, 1) == [res + n]
+    st = Stepper(cfg, model, kv, orc)
+    tok = gpu_id
+    for _ in range(2):
+        tok = st.step(tok)
+    model.free()
+
+
 def _prefill_then_steps(cfg, chunks, steps=2):
     # prompt chunks through flint_prefill_chunk from an empty cache (each chunk after the previous ones), the
     # greedy id after each chunk against the oracle's, then greedy steps checked like decode steps
