@@ -1021,7 +1021,8 @@ __global__ void regroup_scales_kernel(const uint16_t* s, uint16_t* s4, size_t ro
 constexpr int PF_T = 64;     // tokens per contraction workgroup
 constexpr int PF_W = 8;      // its waves, each one 16-row weight tile against the 64 tokens
 constexpr int PF_NT = PF_W * 64;
-constexpr int PF_DI = 16 / PF_W;  // input loads (4 token rows of 256 bytes each) per wave and stage
+constexpr int PF_DI = 16 / PF_W;  // input loads (4 token rows of 256 bytes each) per wave and 128 inputs
+constexpr int PF_SC = 2;     // 128-input halves per stage
 constexpr int PF_PB = 512;   // columns per attention batch (bounds the partial-result buffer)
 enum { PF_QKV = 0, PF_ADD = 1, PF_SWIGLU = 2, PF_DOWNG = 3 };
 
@@ -1041,14 +1042,14 @@ struct PfJob {
 
 // Output tile (16 PF_W rows x 64 tokens) of one job.  Wave w owns weight tile w (SwiGLU: gate tiles in the
 // first half of the waves, the matching up tiles in the second) and all four 16-token tiles; the tokens'
-// inputs go to LDS 128 inputs at a time (direct-to-LDS loads of 256 contiguous bytes per token row, spread
-// over the waves), double-buffered against the MFMAs of the previous 128, and each wave's weight chunk and
-// scales are loaded into registers one stage ahead.  int4: the codes are unpacked once per stage for the
+// inputs go to LDS 256 inputs per stage (two halves of 128; direct-to-LDS loads of 256 contiguous bytes per
+// token row, spread over the waves), double-buffered against the MFMAs of the previous stage, and each
+// wave's weight chunks and scales are loaded into registers one stage ahead.  int4: the codes are unpacked once per stage for the
 // four token tiles; arithmetic as in the batched path (codes 128 + u, the constant -136 operand, the group
 // scale on each group's fp32 result).
 template <int WT, int EPI>
 __global__ void __launch_bounds__(PF_NT) pf_gemm(const BArgs a, const PfJob j) {
-  __shared__ uint4 abuf[2][PF_T * 16];  // [token][16-byte unit ^ (token & 15)] of 128 inputs
+  __shared__ uint4 abuf[2][PF_SC][PF_T * 16];  // [buffer][half][token][16-byte unit ^ (token & 15)] of 128 inputs
   __shared__ f32x4_t upx[PF_W / 2][4][64];  // SwiGLU: the up tiles' results
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, n = lane & 15, kg = lane >> 4;
   const int rb = blockIdx.x;
@@ -1081,9 +1082,15 @@ __global__ void __launch_bounds__(PF_NT) pf_gemm(const BArgs a, const PfJob j) {
   const long long srow = EPI == PF_QKV ? tile_row(T, 4 * kg, a.hd) : T * 16 + 4 * kg;  // rows 4 kg .. + 3
   const uint16_t* sp = WT == W_I4 ? M.s4 + (size_t)(srow >> 2) * G * 4 : nullptr;
   constexpr int NW4 = WT == W_I4 ? 1 : 4;  // weight chunks per stage
-  auto issue = [&](int s, uint4* buf) {
+  // stage s: halves PF_SC s + h of 128 inputs; a half past the last (K / 128 odd) re-reads the last one, so
+  // that the loads carry no condition, and is not used
+  const int NS = (S + PF_SC - 1) / PF_SC;
+  auto half_of = [&](int s, int h) { return min(PF_SC * s + h, S - 1); };
+  auto issue = [&](int s, uint4 (*buf)[PF_T * 16]) {
 #pragma unroll
-    for (int k = 0; k < PF_DI; ++k) dma16(ap[k] + (size_t)s * 128, &buf[4 * (wave * PF_DI + k) * 16]);
+    for (int h = 0; h < PF_SC; ++h)
+#pragma unroll
+      for (int k = 0; k < PF_DI; ++k) dma16(ap[k] + (size_t)half_of(s, h) * 128, &buf[h][4 * (wave * PF_DI + k) * 16]);
   };
   // the MFMA input operand of token tile t, 32-input slice q: token 16 t + n, 16-byte unit
   // int4: (q / 2) * 8 + 2 kg + (q & 1) (groups of 64 in the code order); bf16: 4 q + kg
@@ -1091,11 +1098,16 @@ __global__ void __launch_bounds__(PF_NT) pf_gemm(const BArgs a, const PfJob j) {
     const int u = WT == W_I4 ? (q >> 1) * 8 + 2 * kg + (q & 1) : 4 * q + kg;
     return as_bf16x8(buf[(16 * t + n) * 16 + (u ^ n)]);
   };
-  uint4 wc[NW4], wn[NW4], sc = make_uint4(0u, 0u, 0u, 0u), sn = sc;
-  auto wload = [&](int s, uint4 (&w)[NW4], uint4& sv) {
+  uint4 wc[PF_SC][NW4], wn[PF_SC][NW4], sc[PF_SC], sn[PF_SC];
+  auto wload = [&](int s, uint4 (&w)[PF_SC][NW4], uint4 (&sv)[PF_SC]) {
 #pragma unroll
-    for (int q = 0; q < NW4; ++q) w[q] = ld16(wp + (size_t)(NW4 * s + q) * 1024);
-    if constexpr (WT == W_I4) sv = ld16(sp + (size_t)(2 * s) * 4);
+    for (int h = 0; h < PF_SC; ++h) {
+      const int hs = half_of(s, h);
+#pragma unroll
+      for (int q = 0; q < NW4; ++q) w[h][q] = ld16(wp + (size_t)(NW4 * hs + q) * 1024);
+      if constexpr (WT == W_I4) sv[h] = ld16(sp + (size_t)(2 * hs) * 4);
+      else sv[h] = make_uint4(0u, 0u, 0u, 0u);
+    }
   };
   f32x4_t acc[4];
 #pragma unroll
@@ -1104,21 +1116,25 @@ __global__ void __launch_bounds__(PF_NT) pf_gemm(const BArgs a, const PfJob j) {
   const bf16x8_t bias = bias136();
   wload(0, wc, sc);
   issue(0, abuf[0]);
-  for (int s = 0; s < S; ++s) {
+  for (int s = 0; s < NS; ++s) {
     int later = 0;
-    if (s + 1 < S) {
+    if (s + 1 < NS) {
       wload(s + 1, wn, sn);
       issue(s + 1, abuf[(s + 1) & 1]);
-      later = NW4 + (WT == W_I4 ? 1 : 0) + PF_DI;
+      later = PF_SC * (NW4 + (WT == W_I4 ? 1 : 0) + PF_DI);
     }
     wait_vmem_dyn(later);  // stage s has landed (every wave's part of it, after the barrier)
     __syncthreads();
-    const uint4* buf = abuf[s & 1];
+#pragma unroll
+    for (int h = 0; h < PF_SC; ++h) {
+    if (PF_SC * s + h >= S) break;  // the re-read half past the last
+    const uint4* buf = abuf[s & 1][h];
     if constexpr (WT == W_I4) {
-      const bf16x8_t c0 = unpack8(wc[0].x, k4), c1 = unpack8(wc[0].y, k4), c2 = unpack8(wc[0].z, k4),
-                     c3 = unpack8(wc[0].w, k4);
-      const float sa[4] = {bf2f(sc.x & 0xFFFFu), bf2f(sc.x >> 16), bf2f(sc.y & 0xFFFFu), bf2f(sc.y >> 16)};
-      const float sb[4] = {bf2f(sc.z & 0xFFFFu), bf2f(sc.z >> 16), bf2f(sc.w & 0xFFFFu), bf2f(sc.w >> 16)};
+      const bf16x8_t c0 = unpack8(wc[h][0].x, k4), c1 = unpack8(wc[h][0].y, k4), c2 = unpack8(wc[h][0].z, k4),
+                     c3 = unpack8(wc[h][0].w, k4);
+      const uint4 sv = sc[h];
+      const float sa[4] = {bf2f(sv.x & 0xFFFFu), bf2f(sv.x >> 16), bf2f(sv.y & 0xFFFFu), bf2f(sv.y >> 16)};
+      const float sb[4] = {bf2f(sv.z & 0xFFFFu), bf2f(sv.z >> 16), bf2f(sv.w & 0xFFFFu), bf2f(sv.w >> 16)};
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
         const bf16x8_t b0 = bop(buf, t, 0), b1 = bop(buf, t, 1), b2 = bop(buf, t, 2), b3 = bop(buf, t, 3);
@@ -1138,12 +1154,16 @@ __global__ void __launch_bounds__(PF_NT) pf_gemm(const BArgs a, const PfJob j) {
 #pragma unroll
       for (int t = 0; t < 4; ++t)
 #pragma unroll
-        for (int q = 0; q < 4; ++q) acc[t] = mfma(as_bf16x8(wc[q]), bop(buf, t, q), acc[t]);
+        for (int q = 0; q < 4; ++q) acc[t] = mfma(as_bf16x8(wc[h][q]), bop(buf, t, q), acc[t]);
+    }
     }
     __syncthreads();  // every wave is done with this buffer before stage s + 2 is loaded into it
 #pragma unroll
-    for (int q = 0; q < NW4; ++q) wc[q] = wn[q];
-    sc = sn;
+    for (int h = 0; h < PF_SC; ++h) {
+#pragma unroll
+      for (int q = 0; q < NW4; ++q) wc[h][q] = wn[h][q];
+      sc[h] = sn[h];
+    }
   }
   // epilogue: lane holds rows 4 kg .. 4 kg + 3 of its tile for token n of each token tile
   if constexpr (EPI == PF_SWIGLU) {

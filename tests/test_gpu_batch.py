@@ -216,6 +216,12 @@ def test_long_prefill_chunks_match_oracle():
     _prefill_then_steps(SMALL, [600, 100])
 
 
+def test_long_prefill_odd_input_halves():
+    # hidden 640: the contractions over the hidden size take 5 halves of 128 inputs, so their last stage holds
+    # one half (the re-read second half is not used); 300 tokens, then 40 more
+    _prefill_then_steps(SMALL.replace(name="int4_small_h640", hidden=640), [300, 40])
+
+
 def test_long_prefill_bf16():
     # the same kernels with bf16 weights: 200 tokens, then 70 more
     _prefill_then_steps(SMALL.replace(name="bf16_b16_small", weight_type=synth.BF16), [200, 70])
