@@ -159,31 +159,44 @@ def bench_batch(args, cfg):
         bytes_total += batch_step_bytes(cfg, [p + i for p in lens], r)
     g_logits = dbgs[0][1]["logits"].cpu().numpy()
     g_routes0 = dbgs[0][1]["routes"].cpu().numpy()
+    g_z0 = dbgs[0][1]["router_logits"].cpu().numpy()
     model.free()
     achieved = bytes_total / (total_ms / 1e3) / 1e9
     log(f"{K} batched steps of {B}: {total_ms:.2f} ms total, {total_ms / K * 1e3:.1f} us/step, "
         f"experts per MoE layer (union) {np.mean(unions):.2f}, {achieved:.1f} GB/s")
 
     cpu_baseline = None
-    if not args.no_cpu_baseline:  # the oracle on the shortest sequence's first step, checked against the GPU
+    if not args.no_cpu_baseline:
+        # the oracle on the first timed step of every sequence (one batch step; it decodes one sequence at a
+        # time, so each sequence's cache is set up in turn, untimed), each checked against the GPU's logits
         import oracle
-        b = int(np.argmin(lens))
-        orc = oracle.Oracle(cfg, lambda l: cache[l], head, cap=lens[b] + 4)
-        for l in range(cfg.n_layers):
-            k, v = synth.resident_kv(cfg, l, b, lens[b])
-            orc.set_resident(0, l, k, v)
-        orc.len[0] = lens[b]
-        t0 = time.perf_counter()
-        r = orc.forward(0, first[b:b + 1].cpu().numpy(), ref_routes=g_routes0[b][None])
-        dt = time.perf_counter() - t0
-        err = float(np.max(np.abs(g_logits[b] - r["logits"][0])) / np.max(np.abs(r["logits"][0])))
         cores = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
-        cpu_baseline = {"value": round(1.0 / dt, 4), "unit": "tok/s", "cores": cores, "kind": "oracle",
-                        "sample": f"one decode step of sequence {b} ({lens[b]} resident positions; the oracle "
-                                  f"decodes one sequence at a time), {dt:.1f} s",
-                        "parity_first_step": {"sequence": b, "logits_max_rel_err": err,
-                                              "routes_flagged": int((r["route_flags"] == 2).sum())}}
-        log(f"oracle: {dt:.1f} s for one step of sequence {b}; logits rel err {err:.3g}")
+        dt, errs, ids_differ, flagged = 0.0, [], 0, 0
+        for b in range(B):
+            orc = oracle.Oracle(cfg, lambda l: cache[l], head, cap=lens[b] + 4)
+            for l in range(cfg.n_layers):
+                k, v = synth.resident_kv(cfg, l, b, lens[b])
+                orc.set_resident(0, l, k, v)
+            orc.len[0] = lens[b]
+            t0 = time.perf_counter()
+            # the parity protocol of the tests: GPU routes followed within a near tie, the tie margin of a layer
+            # widened to twice the measured deviation of its router logits
+            r = orc.forward(0, first[b:b + 1].cpu().numpy(), ref_routes=g_routes0[b][None], tie_eps=1e-3,
+                            ref_z=g_z0[b][None])
+            dt += time.perf_counter() - t0
+            errs.append(float(np.max(np.abs(g_logits[b] - r["logits"][0])) / np.max(np.abs(r["logits"][0]))))
+            # a differing id counts unless the oracle's top-2 gap (relative to max |logit|) is a near tie
+            near = float(r["gap"][0]) < max(1e-3, 2.0 * errs[-1])
+            ids_differ += int(int(np.argmax(g_logits[b])) != int(r["ids"][0]) and not near)
+            flagged += int((r["route_flags"] == 2).sum())
+            del orc
+        cpu_baseline = {"value": round(B / dt, 4), "unit": "tok/s", "cores": cores, "kind": "oracle",
+                        "sample": f"one decode step of each of the {B} sequences at their resident lengths (the "
+                                  f"oracle decodes one sequence at a time; only its steps are timed), {dt:.1f} s",
+                        "parity_first_step": {"sequences": B, "logits_max_rel_err": max(errs),
+                                              "ids_differing_beyond_near_ties": ids_differ,
+                                              "routes_flagged": flagged}}
+        log(f"oracle: {dt:.1f} s for one step of each of {B} sequences; logits rel err max {max(errs):.3g}")
 
     out = {
         "metric": "batch-16 ragged decode tok/s (aggregate) + achieved HBM GB/s (% of peak), 49-layer int4",
@@ -329,7 +342,7 @@ def main():
                     help="timed rounds of --steps steps, each from the same cache state; the median is reported")
     ap.add_argument("--config", default="int4_49")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-steps", type=int, default=4, help="decode steps the oracle is timed on")
+    ap.add_argument("--cpu-steps", type=int, default=12, help="decode steps the oracle is timed on")
     ap.add_argument("--prefill", type=int, default=0, help="time a prompt of this many tokens instead")
     ap.add_argument("--resident", type=int, default=0, help="with --prefill: cached positions the prompt follows")
     ap.add_argument("--concurrency", default="",
