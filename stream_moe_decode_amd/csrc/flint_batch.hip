@@ -1236,26 +1236,36 @@ __global__ void __launch_bounds__(PF_NT) pf_gemm(const BArgs a, const PfJob j) {
   }
 }
 
-// Entries per expert among the chunk's n K (token, slot) picks.
-__global__ void __launch_bounds__(256) pf_count(const BArgs a, int n) {
-  __shared__ float wred[4];
-  const int e = blockIdx.x;
-  int c = 0;
-  for (int i = threadIdx.x; i < n * a.K; i += 256) c += gp(a.sel)[i] == e;
-  float v = wave_sum((float)c);
-  if ((threadIdx.x & 63) == 0) wred[threadIdx.x >> 6] = v;
-  __syncthreads();
-  if (threadIdx.x == 0) gp(a.ecnt)[e] = (int)(wred[0] + wred[1] + wred[2] + wred[3]);
-}
-
 // Expert e's entries (token << 3 | slot) in token order at the sum of the earlier experts' counts, and its
-// blocks of up to 64 entries in the block table after the earlier experts' blocks.
+// blocks of up to 64 entries in the block table after the earlier experts' blocks.  Every workgroup copies
+// the chunk's picks into LDS (one byte each) and counts all experts itself (LDS atomics: the counts do not
+// depend on their order), so no other kernel precedes it; then each wave writes the entries of its quarter
+// of the picks, after the earlier quarters' (two passes over LDS, no barrier inside them).
+constexpr int PF_MAXNK = 4096 * MAX_K;  // picks of the largest chunk
 __global__ void __launch_bounds__(256) pf_fill(const BArgs a, int n) {
+  __shared__ uint8_t ssel[PF_MAXNK];
+  __shared__ int cnt[MAX_E];
   __shared__ int wc[4];
   __shared__ int base[2];
   const int e = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, nk = n * a.K;
+  if (tid < MAX_E) cnt[tid] = 0;
+  __syncthreads();
+  for (int i0 = 0; i0 < nk; i0 += 256 * 8) {  // eight loads in flight per thread (clamped, unconditional)
+    int v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) v[u] = gp(a.sel)[min(i0 + u * 256 + tid, nk - 1)];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int i = i0 + u * 256 + tid;
+      if (i < nk) {
+        ssel[i] = (uint8_t)v[u];
+        atomicAdd(&cnt[v[u]], 1);
+      }
+    }
+  }
+  __syncthreads();
   if (wave == 0) {
-    const int c = lane < a.E ? gp(a.ecnt)[lane] : 0, nb = (c + PF_T - 1) / PF_T;
+    const int c = lane < a.E ? cnt[lane] : 0, nb = (c + PF_T - 1) / PF_T;
     const int off = (int)wave_sum(lane < e ? (float)c : 0.f), boff = (int)wave_sum(lane < e ? (float)nb : 0.f);
     const int tot = (int)wave_sum((float)nb);
     if (lane == 0) {
@@ -1270,19 +1280,23 @@ __global__ void __launch_bounds__(256) pf_fill(const BArgs a, int n) {
         gp(a.blk)[3 * (boff + b) + 2] = off + c;
       }
   }
+  // wave w: picks [q0, q1); first its count, then its entries after the earlier waves'
+  const int q = (nk + 3) / 4, q0 = min(wave * q, nk), q1 = min(q0 + q, nk);
+  int mine = 0;
+  for (int i0 = q0; i0 < q1; i0 += 64) {
+    const int i = i0 + lane;
+    mine += __popcll(__ballot(i < q1 && ssel[min(i, nk - 1)] == e));
+  }
+  if (lane == 0) wc[wave] = mine;
   __syncthreads();
-  int run = base[0];
-  for (int i0 = 0; i0 < nk; i0 += 256) {
-    const int i = i0 + tid;
-    const bool m = i < nk && gp(a.sel)[i] == e;
+  int pos = base[0];
+  for (int w = 0; w < wave; ++w) pos += wc[w];
+  for (int i0 = q0; i0 < q1; i0 += 64) {
+    const int i = i0 + lane;
+    const bool m = i < q1 && ssel[min(i, nk - 1)] == e;
     const unsigned long long bal = __ballot(m);
-    if (lane == 0) wc[wave] = __popcll(bal);
-    __syncthreads();
-    int pre = run;
-    for (int w = 0; w < wave; ++w) pre += wc[w];
-    if (m) gp(a.lst)[pre + __popcll(bal & ((1ull << lane) - 1ull))] = ((i / a.K) << 3) | (i % a.K);
-    run += wc[0] + wc[1] + wc[2] + wc[3];
-    __syncthreads();
+    if (m) gp(a.lst)[pos + __popcll(bal & ((1ull << lane) - 1ull))] = ((i / a.K) << 3) | (i % a.K);
+    pos += __popcll(bal);
   }
 }
 
@@ -1517,7 +1531,6 @@ template <int WT> hipError_t run_prefill(const BArgs& a0, int n, hipStream_t st)
       hipLaunchKernelGGL((pf_gemm<WT, PF_ADD>), dim3(a.H / (16 * PF_W), TB), dim3(PF_NT), 0, st, a, jd);
     } else {
       const long long lm = l - a.n_dense;
-      hipLaunchKernelGGL(pf_count, dim3(a.E), dim3(256), 0, st, a, n);
       hipLaunchKernelGGL(pf_fill, dim3(a.E), dim3(256), 0, st, a, n);
       const PfJob jg{a.eg, a.eu, lm * a.E * (a.EI / 16), a.EI / 16, a.H, a.act, a.astride, 0, 1, l, a.h, a.EI};
       hipLaunchKernelGGL((pf_gemm<WT, PF_SWIGLU>), dim3(a.EI / (8 * PF_W), NBM), dim3(PF_NT), 0, st, a, jg);
