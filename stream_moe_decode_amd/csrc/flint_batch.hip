@@ -674,9 +674,11 @@ __device__ __forceinline__ void merge_head(const float* p, int ns, int hd, uint1
 }
 template <int WT>
 __global__ void __launch_bounds__(128) bk_merge(const BArgs a) {
-  const int h = blockIdx.x, n = blockIdx.y, hd = a.hd;
-  merge_head<WT>(a.part + ((size_t)n * a.nq + h) * a.nsmax * (hd + 2), a.asp[n + 1] - a.asp[n], hd,
-                 a.act + (size_t)n * a.astride + h * hd);
+  const int h = blockIdx.x, n = blockIdx.y, hd = a.hd, ns = a.asp[n + 1] - a.asp[n];
+  const float* p = a.part + ((size_t)n * a.nq + h) * a.nsmax * (hd + 2);
+  uint16_t* out = a.act + (size_t)n * a.astride + h * hd;
+  if (ns <= 16) merge_head<WT, 16>(p, ns, hd, out);  // shorter sequences: blocks of 16 splits (fewer padded loads)
+  else merge_head<WT, 32>(p, ns, hd, out);
 }
 
 // o_proj rows t*16 .. t*16 + 15 over input chunk kc: partial sums, added to the residual by the next norm.
