@@ -47,6 +47,10 @@ class OCfg(ctypes.Structure):
                 ("pad", ctypes.c_int32), ("rope_theta", ctypes.c_double), ("rms_eps", ctypes.c_double)]
 
 
+class ONoise(ctypes.Structure):
+    _fields_ = [("rel", ctypes.c_double), ("state", ctypes.c_uint64)]
+
+
 class OLayer(ctypes.Structure):
     _fields_ = [("attn_norm", ctypes.c_void_p), ("post_norm", ctypes.c_void_p), ("qkv", OMat), ("o", OMat),
                 ("dense", ctypes.c_int32), ("pad", ctypes.c_int32), ("gate", OMat), ("up", OMat), ("down", OMat),
@@ -73,10 +77,10 @@ def lib():
         L.oracle_argmax.argtypes = [vp, i64]
         L.oracle_argmax.restype = i32
         L.oracle_attention_head.argtypes = [vp, vp, vp, i32, i32, i64, vp]
-        L.oracle_layer.argtypes = [vp, vp, vp, vp, i32, i32, i32, vp, vp, dbl, vp, vp, vp, vp, vp]
+        L.oracle_layer.argtypes = [vp, vp, vp, vp, i32, i32, i32, vp, vp, dbl, vp, vp, vp, vp, vp, vp]
         L.oracle_layer.restype = i32
         L.oracle_embed.argtypes = [vp, vp, i32, vp]
-        L.oracle_head.argtypes = [vp, vp, vp, vp, i32, vp, vp, vp]
+        L.oracle_head.argtypes = [vp, vp, vp, vp, i32, vp, vp, vp, vp]
         for f in (L.oracle_linear, L.oracle_rmsnorm, L.oracle_rope, L.oracle_softmax, L.oracle_topk,
                   L.oracle_attention_head, L.oracle_embed, L.oracle_head):
             f.restype = None
@@ -201,6 +205,7 @@ class Oracle:
         shape = (cfg.n_kv_heads, cap, cfg.head_dim)
         self.K = [[np.zeros(shape, np.float32) for _ in range(batch)] for _ in range(cfg.n_layers)]
         self.V = [[np.zeros(shape, np.float32) for _ in range(batch)] for _ in range(cfg.n_layers)]
+        self.noise = None
         self.ocfg = OCfg(cfg.hidden, cfg.n_q_heads, cfg.n_kv_heads, cfg.head_dim, cfg.n_experts, cfg.top_k,
                          cfg.expert_inter, cfg.router_renorm, self.bf, 0, cfg.rope_theta, cfg.rms_eps)
 
@@ -260,27 +265,34 @@ class Oracle:
         lib().oracle_embed(ctypes.byref(E), _p(toks), toks.size, _p(x))
         return x
 
-    def layer(self, l: int, seq: int, x: np.ndarray, p0: int, ref_routes=None, tie_eps: float = 1e-3, ref_z=None):
+    def _noise(self):
+        return None if self.noise is None else ctypes.byref(self.noise)
+
+    def set_noise(self, rel: float, seed: int):
+        """Rounding noise of relative size `rel` before every bf16 rounding (0: none); see ``oracle.cpp``."""
+        self.noise = None if rel == 0 else ONoise(rel, (seed * 0x9E3779B97F4A7C15 + 1) & 0xFFFFFFFFFFFFFFFF or 1)
+
+    def layer(self, l: int, seq: int, x: np.ndarray, p0: int, ref_routes=None, route_margin: float = 0.0):
         """Run layer l over the block x ([n][hidden], modified) at positions p0.. of sequence seq.
 
-        ref_routes [n][top_k] / ref_z [n][n_experts]: another implementation's routes and router logits
-        (see ``oracle_layer``: a different set is adopted when it is a valid top-k within the tolerance)."""
+        ref_routes [n][top_k]: another implementation's routes; a different set is adopted when it is a
+        valid top-k within the fixed relative margin ``route_margin`` (see ``oracle_layer``)."""
         n = x.shape[0]
         keep = []
         L = self._olayer(l, keep)
-        K = self.cfg.top_k
+        K, E = self.cfg.top_k, max(self.cfg.n_experts, 1)
         routes = np.full((n, K), -1, np.int32)
         rw = np.zeros((n, K), np.float32)
         flags = np.zeros(n, np.int32)
         gap = np.full(n, np.inf, np.float32)
+        z = np.zeros((n, E), np.float64)
         ref = None if ref_routes is None else np.ascontiguousarray(ref_routes, np.int32).reshape(n, K)
-        rz = None if ref_z is None else np.ascontiguousarray(ref_z, np.float32).reshape(n, self.cfg.n_experts)
         rc = lib().oracle_layer(ctypes.byref(self.ocfg), ctypes.byref(L), _p(self.K[l][seq]), _p(self.V[l][seq]),
-                                self.cap, p0, n, _p(x), _p(ref), tie_eps, _p(rz), _p(routes), _p(rw), _p(flags),
-                                _p(gap))
+                                self.cap, p0, n, _p(x), _p(ref), route_margin, self._noise(), _p(routes), _p(rw),
+                                _p(flags), _p(gap), _p(z))
         if rc != 0:
             raise ValueError("oracle_layer: capacity exceeded")
-        return routes, rw, flags, gap
+        return routes, rw, flags, gap, z
 
     def head(self, x: np.ndarray, want_logits: bool = True):
         keep = []
@@ -290,37 +302,41 @@ class Oracle:
         logits = np.empty((n, self.cfg.vocab), np.float32) if want_logits else None
         ids = np.empty(n, np.int32)
         gap = np.empty(n, np.float64)
-        lib().oracle_head(ctypes.byref(self.ocfg), ctypes.byref(lm), _p(gf), _p(x), n, _p(logits), _p(ids), _p(gap))
+        lib().oracle_head(ctypes.byref(self.ocfg), ctypes.byref(lm), _p(gf), _p(x), n, _p(logits), _p(ids), _p(gap),
+                          self._noise())
         return logits, ids, gap
 
-    def forward(self, seq: int, toks, ref_routes=None, tie_eps: float = 1e-3, want_logits: bool = True,
-                resid_layer: int | None = None, ref_z=None):
+    def forward(self, seq: int, toks, ref_routes=None, route_margin: float = 0.0, want_logits: bool = True,
+                resid_all: bool = False):
         """Block pass over known tokens at positions len..len+n-1; advances len.
 
-        ref_routes: [n][n_layers][top_k] candidate routes (see ``oracle_layer``).
-        Returns a dict with logits [n][vocab], ids [n], gap [n], routes, route_w,
-        route_flags, route_gap ([n][n_layers][...], -1 / 0 on dense layers) and,
-        if resid_layer is given, the residual after that layer.
+        ref_routes: [n][n_layers][top_k] candidate routes, adopted where they are a valid top-k within
+        ``route_margin`` (see ``oracle_layer``).
+        Returns a dict with logits [n][vocab], ids [n], gap [n], routes, route_w, route_flags, route_gap
+        ([n][n_layers][...], -1 / 0 on dense layers), router_z [n][n_layers][n_experts] (0 on dense layers)
+        and, with resid_all, the residual after every layer, resid [n][n_layers][hidden].
         """
         cfg = self.cfg
         toks = np.ascontiguousarray(toks, np.int32)
         n = toks.size
         p0 = self.len[seq]
         x = self.embed(toks)
-        Ln, K = cfg.n_layers, cfg.top_k
+        Ln, K, E = cfg.n_layers, cfg.top_k, max(cfg.n_experts, 1)
         routes = np.full((n, Ln, K), -1, np.int32)
         rw = np.zeros((n, Ln, K), np.float32)
         flags = np.zeros((n, Ln), np.int32)
         rgap = np.full((n, Ln), np.inf, np.float32)
-        resid = None
+        rz = np.zeros((n, Ln, E), np.float64)
+        resid = np.zeros((n, Ln, cfg.hidden), np.float64) if resid_all else None
         for l in range(Ln):
             ref = None if ref_routes is None else np.ascontiguousarray(np.asarray(ref_routes)[:, l, :])
-            rz = None if ref_z is None else np.ascontiguousarray(np.asarray(ref_z)[:, l, :])
-            r, w, f, g = self.layer(l, seq, x, p0, ref, tie_eps, rz)
+            r, w, f, g, z = self.layer(l, seq, x, p0, ref, route_margin)
             routes[:, l], rw[:, l], flags[:, l], rgap[:, l] = r, w, f, g
-            if resid_layer is not None and l == resid_layer:
-                resid = x.copy()
+            if l >= cfg.n_dense_layers:
+                rz[:, l] = z
+            if resid_all:
+                resid[:, l] = x
         logits, ids, gap = self.head(x, want_logits)
         self.len[seq] = p0 + n
         return {"logits": logits, "ids": ids, "gap": gap, "routes": routes, "route_w": rw,
-                "route_flags": flags, "route_gap": rgap, "resid": resid, "x": x}
+                "route_flags": flags, "route_gap": rgap, "router_z": rz, "resid": resid, "x": x}
