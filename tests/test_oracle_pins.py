@@ -415,10 +415,188 @@ def test_route_tie_adoption_rules():
     assert own["route_gap"][0, 0] == 0.0
     ref = own["routes"].copy()
     ref[0, 0] = [3, 0]
-    r = oracle.Oracle(cfg, lambda l: layers[l], hw, cap=4).forward(0, t, ref_routes=ref)
+    r = oracle.Oracle(cfg, lambda l: layers[l], hw, cap=4).forward(0, t, ref_routes=ref, route_margin=1e-3)
     assert r["route_flags"][0, 0] == 1 and set(r["routes"][0, 0]) == {0, 3}
     bad = own["routes"].copy()
     bad[0, 0] = [6, 7]
-    r = oracle.Oracle(cfg, lambda l: layers[l], hw, cap=4).forward(0, t, ref_routes=bad)
+    r = oracle.Oracle(cfg, lambda l: layers[l], hw, cap=4).forward(0, t, ref_routes=bad, route_margin=1e-3)
     assert r["route_flags"][0, 0] == 2
     np.testing.assert_array_equal(r["routes"][0, 0], [0, 2])
+    # with no margin at all an exactly tied set is still a valid top-2 (min in = max out)
+    r = oracle.Oracle(cfg, lambda l: layers[l], hw, cap=4).forward(0, t, ref_routes=ref, route_margin=0.0)
+    assert r["route_flags"][0, 0] == 1
+
+
+def test_route_adoption_needs_a_gap_below_the_margin():
+    # expert 3's logit 2 % (of max|z|) below expert 2's: swapping them is accepted at a 3 % margin, not at 1 %
+    cfg = _tiny(n_layers=1, n_dense_layers=0)
+    layers, hw = _model(cfg)
+    hw = dict(hw)
+    hw["embed"] = hw["embed"].copy()
+    hw["embed"][11] = 1.0
+    c = np.zeros(cfg.n_experts)
+    c[0], c[2], c[3] = 1.0, 0.5, 0.48
+    layers[0]["router"] = {"w": np.repeat(c[:, None], cfg.hidden, 1).astype(np.float32)}
+    t = np.array([11], np.int32)
+    own = oracle.Oracle(cfg, lambda l: layers[l], hw, cap=4).forward(0, t)
+    np.testing.assert_array_equal(own["routes"][0, 0], [0, 2])
+    assert abs(own["route_gap"][0, 0] - 0.02) < 1e-6
+    ref = own["routes"].copy()
+    ref[0, 0] = [0, 3]
+    for margin, flag in ((0.03, 1), (0.01, 2)):
+        r = oracle.Oracle(cfg, lambda l: layers[l], hw, cap=4).forward(0, t, ref_routes=ref, route_margin=margin)
+        assert r["route_flags"][0, 0] == flag
+
+
+# ------------------------------------------------------------------ closed forms of whole layers
+# (fp32 models: no bf16 rounding, so each case below is exact up to double rounding)
+
+def _silu(t):
+    # the SiLU of the SwiGLU MLP: t * logistic(t), the logistic from scipy
+    from scipy.special import expit
+    return t * expit(t)
+
+
+def _one_hot_swiglu(L, I, H, alpha, beta, out_row, prefix="dense_"):
+    """gate row 0 = alpha e_0, up row 0 = beta e_1, every other gate/up row 0; down column 0 = e_out_row."""
+    g = np.zeros((I, H), np.float32)
+    u = np.zeros((I, H), np.float32)
+    d = np.zeros((H, I), np.float32)
+    g[0, 0], u[0, 1], d[out_row, 0] = alpha, beta, 1.0
+    L[prefix + "gate"], L[prefix + "up"], L[prefix + "down"] = {"w": g}, {"w": u}, {"w": d}
+
+
+def test_swiglu_is_silu_of_gate_times_up():
+    # one dense layer, o_proj zero, a constant embedding row c: the post-attention norm output is
+    # b = k g (k = c / sqrt(c^2 + eps), g the norm weights).  With gate = alpha e_0 and up = beta e_1 the
+    # MLP adds silu(alpha b_0) * beta b_1 to coordinate 5 and nothing elsewhere.  Distinct alpha and beta,
+    # both signs of the gate input: swapping gate and up or flipping SiLU's exponent fails this.
+    cfg = _tiny(n_layers=1, n_dense_layers=1, norm_sigma=0.1)
+    layers, hw = _model(cfg)
+    L = layers[0]
+    L["o"] = _zero(L["o"])
+    H, I = cfg.hidden, cfg.dense_inter
+    hw = dict(hw)
+    hw["embed"] = hw["embed"].copy()
+    c = 0.5
+    hw["embed"][9] = c
+    g = L["post_norm"].astype(np.float64)
+    k = c / math.sqrt(c * c + cfg.rms_eps)
+    for alpha, beta in ((3.0, -0.75), (-2.0, 1.25)):
+        _one_hot_swiglu(L, I, H, alpha, beta, 5)
+        x = oracle.Oracle(cfg, lambda l: layers[l], hw, cap=4).forward(0, np.array([9], np.int32))["x"][0]
+        expect = np.full(H, c)
+        expect[5] += _silu(alpha * k * g[0]) * beta * k * g[1]
+        np.testing.assert_allclose(x, expect, rtol=1e-12, atol=1e-14)
+
+
+def test_moe_output_is_router_weighted_sum_of_distinct_experts():
+    # one MoE layer (8 experts, top-2), o_proj zero, constant embedding row c, norm weights g: b = k g.
+    # Router row e = r_e e_0, so z_e = r_e b_0.  Expert e: gate = alpha e_0, up = beta_e e_0, down writes
+    # coordinate 10 + e, so its output is y_e = silu(alpha b_0) beta_e b_0 on coordinate 10 + e alone.
+    # The layer must add w_e y_e for the two largest z (w = scipy softmax over all 8 logits): a plain
+    # average of the experts, or weights renormalised over the pair, fails this.
+    cfg = _tiny(n_layers=1, n_dense_layers=0, norm_sigma=0.1)
+    layers, hw = _model(cfg)
+    L = layers[0]
+    L["o"] = _zero(L["o"])
+    H, E, I = cfg.hidden, cfg.n_experts, cfg.expert_inter
+    r = np.array([0.3, 1.9, -0.4, 0.8, 2.6, 0.1, -1.2, 1.1])
+    beta = np.array([0.9, -1.4, 0.6, 1.7, 0.5, -0.8, 1.2, 2.0])
+    alpha = 1.5
+    L["router"] = {"w": np.zeros((E, H), np.float32)}
+    L["router"]["w"][:, 0] = r
+    gt, ut, dt = np.zeros((E, I, H), np.float32), np.zeros((E, I, H), np.float32), np.zeros((E, H, I), np.float32)
+    for e in range(E):
+        gt[e, 0, 0], ut[e, 0, 0], dt[e, 10 + e, 0] = alpha, beta[e], 1.0
+    L["exp_gate"], L["exp_up"], L["exp_down"] = {"w": gt}, {"w": ut}, {"w": dt}
+    hw = dict(hw)
+    hw["embed"] = hw["embed"].copy()
+    c = -0.75
+    hw["embed"][4] = c
+    k = c / math.sqrt(c * c + cfg.rms_eps)
+    b0 = k * float(L["post_norm"][0])
+    from scipy.special import softmax
+    z = r.astype(np.float32).astype(np.float64) * b0
+    w = softmax(z)
+    top = np.argsort(-z)[:2]
+    res = oracle.Oracle(cfg, lambda l: layers[l], hw, cap=4).forward(0, np.array([4], np.int32))
+    assert set(res["routes"][0, 0]) == set(top)
+    expect = np.full(H, c)
+    for e in top:
+        expect[10 + e] += w[e] * _silu(alpha * b0) * float(np.float32(beta[e])) * b0
+    np.testing.assert_allclose(res["x"][0], expect, rtol=1e-12, atol=1e-14)
+    np.testing.assert_allclose(res["route_w"][0, 0], w[res["routes"][0, 0]], rtol=1e-6)
+
+
+def test_attention_after_cached_positions_includes_the_new_token():
+    # position 5 after five cached positions whose keys are zero (score 0) and whose values are random.
+    # The new token's query and key are parallel with q.k / sqrt(d) = 60 (RoPE turns both by the same
+    # angles at the same position, so the product is kept): its own value gets all but e^-60 of the weight,
+    # so with W_o = I the residual gains exactly v.  Attention over positions 0..4 only would give the
+    # mean of the cached values instead.
+    cfg = _tiny(n_layers=1, n_dense_layers=1)
+    layers, hw = _model(cfg)
+    L = layers[0]
+    H, d, nq, nkv = cfg.hidden, cfg.head_dim, cfg.n_q_heads, cfg.n_kv_heads
+    assert nq * d == H
+    c = 1.0
+    k = c / math.sqrt(c * c + cfg.rms_eps)       # the normed input is k * ones (norm weights 1)
+    rng = np.random.default_rng(17)
+    t = rng.normal(size=d)
+    t *= math.sqrt(60.0 * math.sqrt(d)) / np.linalg.norm(t) / k   # (k t).(k t) / sqrt(d) = 60
+    wv = rng.normal(size=(nkv * d,)) * 0.3
+    qkv = np.zeros(((nq + 2 * nkv) * d, H), np.float32)
+    for h in range(nq):
+        qkv[h * d:(h + 1) * d] = np.repeat((t / H)[:, None], H, 1)
+    for j in range(nkv):
+        qkv[(nq + j) * d:(nq + j + 1) * d] = np.repeat((t / H)[:, None], H, 1)
+    qkv[(nq + nkv) * d:] = np.repeat((wv / H)[:, None], H, 1)
+    L["qkv"] = {"w": qkv}
+    L["o"] = {"w": np.eye(H, dtype=np.float32)}
+    L["dense_down"] = _zero(L["dense_down"])
+    hw = dict(hw)
+    hw["embed"] = hw["embed"].copy()
+    hw["embed"][2] = c
+    o = oracle.Oracle(cfg, lambda l: layers[l], hw, cap=8)
+    cached_v = rng.normal(size=(nkv, 5, d)).astype(np.float32)
+    o.set_resident(0, 0, np.zeros((nkv, 5, d), np.float32), cached_v)
+    o.len[0] = 5
+    x = o.forward(0, np.array([2], np.int32))["x"][0]
+    v = (k * qkv[(nq + nkv) * d:].astype(np.float64).sum(1)).reshape(nkv, d).astype(np.float32).astype(np.float64)
+    group = nq // nkv
+    expect = c + np.concatenate([v[h // group] for h in range(nq)])
+    np.testing.assert_allclose(x, expect, rtol=1e-9, atol=1e-9)
+
+
+def test_norm_weights_layer_by_layer():
+    # two dense layers with distinct norm weights (1 + N(0, 0.1) each), a constant embedding row c.
+    # Layer 0 adds nothing (o_proj and down zero), so both layers see x = c ones and the input norm output
+    # is k g_in,l: the key each layer caches at position 0 (RoPE is the identity there) is W_k,l (k g_in,l),
+    # a numpy matvec.  Layer 1's MLP is the one-hot SwiGLU on b = k g_post,1.  The logits are
+    # lm_head . (x / rms(x) * g_final).  Taking another layer's or another norm's weights fails this.
+    cfg = _tiny(n_layers=2, n_dense_layers=2, norm_sigma=0.1)
+    layers, hw = _model(cfg)
+    H, I, d, nq, nkv = cfg.hidden, cfg.dense_inter, cfg.head_dim, cfg.n_q_heads, cfg.n_kv_heads
+    assert not np.array_equal(layers[0]["attn_norm"], layers[1]["attn_norm"])
+    for L in layers:
+        L["o"] = _zero(L["o"])
+    layers[0]["dense_down"] = _zero(layers[0]["dense_down"])
+    _one_hot_swiglu(layers[1], I, H, 2.5, -1.125, 3)
+    hw = dict(hw)
+    hw["embed"] = hw["embed"].copy()
+    c = 0.75
+    hw["embed"][1] = c
+    o = oracle.Oracle(cfg, lambda l: layers[l], hw, cap=4)
+    r = o.forward(0, np.array([1], np.int32))
+    k = c / math.sqrt(c * c + cfg.rms_eps)
+    for l in range(2):
+        wk = layers[l]["qkv"]["w"][nq * d:(nq + nkv) * d].astype(np.float64)
+        key = (wk @ (k * layers[l]["attn_norm"].astype(np.float64))).astype(np.float32).reshape(nkv, d)
+        np.testing.assert_allclose(o.K[l][0][:, 0], key, rtol=1e-6, atol=1e-7)
+    g1 = layers[1]["post_norm"].astype(np.float64)
+    x = np.full(H, c)
+    x[3] += _silu(2.5 * k * g1[0]) * -1.125 * k * g1[1]
+    np.testing.assert_allclose(r["x"][0], x, rtol=1e-12, atol=1e-14)
+    f = x / np.sqrt(np.mean(x * x) + cfg.rms_eps) * hw["final_norm"].astype(np.float64)
+    np.testing.assert_allclose(r["logits"][0], hw["lm_head"].astype(np.float64) @ f, rtol=1e-5, atol=1e-7)
