@@ -5,6 +5,9 @@ numbers (``synth.c``) and names the shapes of the workloads.  Every tensor is a
 pure function of ``(seed, tensor id, element index)``, so a layer can be
 regenerated on its own, which keeps the 49-layer models out of host memory.
 
+RMSNorm weights are 1 in the tiny model (as that configuration states) and
+1 + N(0, 0.1), distinct per layer and per norm, everywhere else.
+
 Workloads (shapes from the page "Flint Inference on Apple Silicon: rec
 Megakernel and Tempo9 Compared", section 2: 49 layers, 2048-wide residual,
 top-6 routing, layers 0 and 1 dense; the remaining sizes are the stated
@@ -16,6 +19,7 @@ synthetic configurations of this library):
 * ``int4_49``   int4 group-64 weights (bf16 embeddings and lm_head),
                 8,022 resident positions, 256 greedy tokens.
 * ``int4_b16``  ``int4_49`` at batch 16 with ragged lengths in [512, 8192].
+* ``int4_b16_small``  a 3-layer, 512-wide narrowing of ``int4_b16`` for fast checks.
 """
 from __future__ import annotations
 
@@ -36,6 +40,7 @@ KV_SIGMA = 1.0
 
 # tensor kinds of the stream ids
 EMBED, LMHEAD, QKV, OPROJ, DGATE, DUP, DDOWN, ROUTER, EGATE, EUP, EDOWN, KCACHE, VCACHE, TOKENS, LENGTHS = range(1, 16)
+ANORM, PNORM, FNORM = range(16, 19)
 
 
 def build(force: bool = False) -> str:
@@ -94,6 +99,7 @@ class Config:
     decode: int = 1            # greedy tokens generated
     ragged: tuple = ()         # (lo, hi) of uniform per-sequence lengths, batch > 1
     seed: int = 0
+    norm_sigma: float = 0.1    # RMSNorm weights 1 + N(0, norm_sigma), distinct per layer and per norm (0: all 1)
 
     @property
     def qkv_rows(self):
@@ -118,7 +124,7 @@ class Config:
 CONFIGS = {
     "tiny": Config("tiny", n_layers=2, n_dense_layers=1, hidden=256, n_q_heads=4, n_kv_heads=2, head_dim=64,
                    vocab=1024, dense_inter=512, n_experts=8, top_k=2, expert_inter=128, weight_type=F32,
-                   prompt=8, decode=16),
+                   prompt=8, decode=16, norm_sigma=0.0),
     "moe_layer": Config("moe_layer", n_layers=1, n_dense_layers=0, hidden=2048, n_q_heads=16, n_kv_heads=4,
                         head_dim=128, vocab=65536, dense_inter=6144, n_experts=64, top_k=6, expert_inter=768,
                         weight_type=BF16, resident=1024, decode=1),
@@ -131,6 +137,11 @@ CONFIGS = {
     "int4_b16": Config("int4_b16", n_layers=49, n_dense_layers=2, hidden=2048, n_q_heads=16, n_kv_heads=4,
                        head_dim=128, vocab=65536, dense_inter=6144, n_experts=64, top_k=6, expert_inter=768,
                        weight_type=INT4G64, batch=16, ragged=(512, 8192), decode=1),
+    # int4_b16 narrowed so that the oracle runs in seconds (the batched-path parity tests): 3 layers (1 dense),
+    # hidden 512, 8 query / 2 kv heads of 128, 16 experts top-4 of 256, lengths uniform in [1, 300]
+    "int4_b16_small": Config("int4_b16_small", n_layers=3, n_dense_layers=1, hidden=512, n_q_heads=8,
+                             n_kv_heads=2, head_dim=128, vocab=4096, dense_inter=1024, n_experts=16, top_k=4,
+                             expert_inter=256, weight_type=INT4G64, batch=16, ragged=(1, 300), decode=1),
 }
 
 
@@ -194,12 +205,19 @@ def embed_like(cfg: Config, kind: int):
     return matrix(cfg, kind, 0, 0, cfg.vocab, cfg.hidden, wtype=wt)["w"]
 
 
+def norm_weights(cfg: Config, kind: int, layer: int = 0) -> np.ndarray:
+    """RMSNorm weights [hidden]: 1 + N(0, norm_sigma) (all 1 when norm_sigma is 0)."""
+    if cfg.norm_sigma == 0:
+        return np.ones(cfg.hidden, np.float32)
+    return (1.0 + normal_f32(tensor_id(kind, layer), cfg.hidden, cfg.norm_sigma, cfg.seed)).astype(np.float32)
+
+
 def layer(cfg: Config, l: int) -> dict:
     """All weights of layer ``l`` in the canonical layout."""
     H = cfg.hidden
     d = {
-        "attn_norm": np.ones(H, np.float32),
-        "post_norm": np.ones(H, np.float32),
+        "attn_norm": norm_weights(cfg, ANORM, l),
+        "post_norm": norm_weights(cfg, PNORM, l),
         "qkv": matrix(cfg, QKV, l, 0, cfg.qkv_rows, H),
         "o": matrix(cfg, OPROJ, l, 0, H, cfg.q_dim),
     }
@@ -218,7 +236,7 @@ def layer(cfg: Config, l: int) -> dict:
 
 def head(cfg: Config) -> dict:
     return {"embed": embed_like(cfg, EMBED), "lm_head": embed_like(cfg, LMHEAD),
-            "final_norm": np.ones(cfg.hidden, np.float32)}
+            "final_norm": norm_weights(cfg, FNORM)}
 
 
 def resident_kv(cfg: Config, l: int, seq: int, n_pos: int):
