@@ -38,7 +38,7 @@ extern "C" {
 #define FLINT_ENOMEM 2       /* device or host allocation failed */
 #define FLINT_EHIP 3         /* a HIP runtime call failed */
 #define FLINT_ECAPACITY 4    /* KV cache has no room for the new positions */
-#define FLINT_ETIMEOUT 5     /* a cross-workgroup wait inside the kernel timed out */
+#define FLINT_ETIMEOUT 5     /* a cross-workgroup wait inside the kernel timed out (see flint_set_wait_limit) */
 #define FLINT_ENORESIDENT 6  /* the device cannot hold the persistent grid */
 #define FLINT_EDEVICE 7      /* the kernel flagged bad device data (token id out of range) */
 
@@ -60,7 +60,9 @@ typedef struct flint_config {
   int32_t n_experts;       /* experts per MoE layer (<= 64) */
   int32_t top_k;           /* experts chosen per token (<= 8, top_k * expert_inter <= 6144) */
   int32_t expert_inter;    /* intermediate width of one expert (multiple of 64) */
-  int32_t weight_type;     /* FLINT_W_* */
+  int32_t weight_type;     /* FLINT_W_*; it also fixes the activation type (there is no separate
+                              act_type): fp32 weights run fp32 activations and an fp32 cache, bf16 and
+                              int4 weights bf16 GEMV inputs and a bf16 cache with fp32 accumulation */
   int32_t router_renorm;   /* 0: weight = softmax probability over all experts; 1: renormalised
                               over the top_k selected */
   int32_t grid;            /* persistent workgroups; 0 = one per compute unit */
@@ -110,9 +112,7 @@ typedef struct flint_debug {
   int32_t* routes;      /* [batch][n_layers][top_k] selected experts, descending router logit;
                            -1 on dense layers */
   float* route_w;       /* [batch][n_layers][top_k] expert weights */
-  float* resid;         /* [batch][hidden] fp32 residual after layer resid_layer */
-  int32_t resid_layer;
-  int32_t pad;
+  float* resid;         /* [batch][n_layers][hidden] fp32 residual after every layer */
   uint64_t* phase_ts;   /* [n_layers + 1][16] wall-clock stamps (100 MHz) of workgroup 0 at
                            phase boundaries, for sequence 0.  Row 0: start, end, argmax published,
                            then the shader clock counter (s_memtime) at start and at end.
@@ -128,7 +128,10 @@ typedef struct flint_debug {
 /* ------------------------------------------------------------- entry points */
 
 /*
- * Create a context: validate cfg, query the device, copy the weights into
+ * Create a context for the decode step of section 2 of "Flint Inference on
+ * Apple Silicon: rec Megakernel and Tempo9 Compared" (the model whose layers
+ * that section lists, here any size within the limits of flint_config):
+ * validate cfg, query the device, copy the weights into
  * library-owned device memory and allocate the kernel's scratch.  hip_stream
  * is a hipStream_t (NULL = the default stream) on which all later work of
  * this ctx is enqueued.  Synchronises hip_stream before returning.
@@ -141,7 +144,11 @@ int flint_decode_init(const flint_config* cfg, const flint_weights* w, void* hip
 int flint_decode_free(flint_ctx* ctx);
 
 /*
- * Allocate a KV cache for `batch` sequences of up to max_tokens positions:
+ * Allocate the resident KV cache that decode attends over (section 2 of "Flint
+ * Inference on Apple Silicon: rec Megakernel and Tempo9 Compared": the step
+ * appends the new token's K/V and attends over every cached position; section 1
+ * keeps that cache across turns of one session) for `batch` sequences of up
+ * to max_tokens positions:
  * per layer K and V of [batch][n_kv_heads][max_tokens][head_dim] in the
  * activation type (fp32 for FLINT_W_F32, else bf16), zero-filled, plus the
  * per-sequence lengths (all 0) on the device with a host mirror.  The
@@ -183,7 +190,11 @@ int flint_kv_prefix_match(flint_kv* kv, int32_t seq, const int32_t* tokens, int3
 int flint_kv_layer_ptrs(flint_kv* kv, int32_t layer, void** k, void** v);
 
 /*
- * One greedy decode step for every sequence b of kv: consume the device token
+ * One greedy decode step, the operator list of section 2 of "Flint Inference
+ * on Apple Silicon: rec Megakernel and Tempo9 Compared" (input RMSNorm, QKV,
+ * RoPE, KV append, attention, o_proj, post-attention RMSNorm, router and
+ * top-k, experts or the dense MLP, final norm, lm_head, argmax), for every
+ * sequence b of kv: consume the device token
  * tokens[b] at position len[b], append its K/V, write the argmax token id to
  * out_ids[b] (device) and increment len[b].  tokens and out_ids may alias,
  * so out_ids can be fed back as the next step's tokens without a host round
@@ -221,6 +232,9 @@ int flint_decode_step_debug(flint_ctx* ctx, const int32_t* tokens, flint_kv* kv,
                             const flint_debug* dbg);
 
 /*
+ * Chunked prefill (section 1 of "Flint Inference on Apple Silicon: rec
+ * Megakernel and Tempo9 Compared" prefills prompts in chunks of 4,096 tokens):
+ * the decode step's operators applied to a block of known tokens.
  * Process n (1 <= n <= 4096) known device tokens of sequence seq at positions
  * len[seq] .. len[seq] + n - 1 (causal attention over the cache and the
  * chunk), append their K/V, write the greedy id after the last position to
@@ -259,6 +273,22 @@ int flint_micro_launch(flint_ctx* ctx, int32_t launches, float* us_per_launch);
 
 /* Wait for the ctx stream; report and clear a latched device error. */
 int flint_sync(flint_ctx* ctx);
+
+/*
+ * Bound every cross-workgroup wait of the persistent kernel by `microseconds`
+ * (0 restores the default of one second).  The kernel's workgroups hand data to
+ * each other through spin-waits that assume the whole grid is resident at once
+ * (the condition section 2 of "Flint Inference on Apple Silicon: rec Megakernel
+ * and Tempo9 Compared" notes for device-scope spin barriers); a wait that runs
+ * past the bound gives up and every workgroup of the step winds down and exits.
+ * Such a step, and every step queued behind it before the error is reported,
+ * writes -1 in place of its id, leaves its sequence's length unchanged and may
+ * have written part of the K/V at that position (the next step at that
+ * position overwrites it).  The next call on the ctx (or flint_sync) reports
+ * FLINT_ETIMEOUT once and re-reads the lengths of the ctx's caches.
+ * Synchronizes the ctx's stream.  Errors: FLINT_EINVAL, FLINT_EHIP.
+ */
+int flint_set_wait_limit(flint_ctx* ctx, uint32_t microseconds);
 
 /* Launch shape of the persistent kernel. */
 int flint_device_info(flint_ctx* ctx, int32_t* grid, int32_t* block, int32_t* lds_bytes);

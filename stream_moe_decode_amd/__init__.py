@@ -27,7 +27,7 @@ EXPORTS = ("flint_decode_init", "flint_decode_free", "flint_kv_alloc", "flint_kv
            "flint_kv_get_lengths", "flint_kv_tokens", "flint_kv_prefix_match", "flint_kv_layer_ptrs",
            "flint_decode_step", "flint_decode_step_seqs",
            "flint_decode_step_debug", "flint_prefill_chunk", "flint_micro_stream_read", "flint_micro_exchange",
-           "flint_micro_launch", "flint_sync", "flint_device_info", "flint_last_error")
+           "flint_micro_launch", "flint_sync", "flint_set_wait_limit", "flint_device_info", "flint_last_error")
 
 
 class FlintError(RuntimeError):
@@ -56,8 +56,7 @@ class Weights(ctypes.Structure):
 
 class Debug(ctypes.Structure):
     _fields_ = [("logits", ctypes.c_void_p), ("routes", ctypes.c_void_p), ("route_w", ctypes.c_void_p),
-                ("resid", ctypes.c_void_p), ("resid_layer", ctypes.c_int32), ("pad", ctypes.c_int32),
-                ("phase_ts", ctypes.c_void_p), ("router_logits", ctypes.c_void_p)]
+                ("resid", ctypes.c_void_p), ("phase_ts", ctypes.c_void_p), ("router_logits", ctypes.c_void_p)]
 
 
 _lib = None
@@ -93,6 +92,7 @@ def lib():
             "flint_micro_exchange": [vp, i32, i32, P(ctypes.c_float)],
             "flint_micro_launch": [vp, i32, P(ctypes.c_float)],
             "flint_sync": [vp],
+            "flint_set_wait_limit": [vp, ctypes.c_uint32],
             "flint_device_info": [vp, P(i32), P(i32), P(i32)],
         }
         for name, args in sig.items():
@@ -193,6 +193,11 @@ def decode_step_seqs(ctx: int, kv: int, seqs, tokens_ptr: int, out_ptr: int):
 
 def decode_step_debug(ctx: int, tokens_ptr: int, kv: int, out_ptr: int, dbg: Debug | None):
     _check(lib().flint_decode_step_debug(ctx, tokens_ptr, kv, out_ptr, ctypes.byref(dbg) if dbg is not None else None))
+
+
+def set_wait_limit(ctx: int, microseconds: int):
+    """Bound of every cross-workgroup wait of the persistent kernel (0: the default, 1 s)."""
+    _check(lib().flint_set_wait_limit(ctx, microseconds))
 
 
 def prefill_chunk(ctx: int, kv: int, seq: int, tokens_ptr: int, n: int, out_ptr: int):

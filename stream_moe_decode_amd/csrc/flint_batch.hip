@@ -313,11 +313,13 @@ __global__ void __launch_bounds__(BNT) bk_norm(const BArgs a, int l, int mode) {
       gv[k] = e < H ? gp(g)[e] : 0.f;
     }
   }
-  // the residual after layer dbg_resid_layer is complete at the next layer's input norm (or the final norm)
-  if (a.dbg_resid && ((mode == NORM_INPUT && l - 1 == a.dbg_resid_layer) || (mode == NORM_FINAL && a.L - 1 == a.dbg_resid_layer)))
+  // the residual after layer l - 1 is complete at layer l's input norm (after the last layer: the final norm)
+  if (a.dbg_resid && (mode == NORM_INPUT || mode == NORM_FINAL) && (mode == NORM_FINAL || l > 0)) {
+    const int lr = mode == NORM_FINAL ? a.L - 1 : l - 1;
 #pragma unroll
     for (int k = 0; k < EPT; ++k)
-      if (tid + k * BNT < H) gp(a.dbg_resid)[(size_t)seq * H + tid + k * BNT] = xv[k];
+      if (tid + k * BNT < H) gp(a.dbg_resid)[((size_t)seq * a.L + lr) * H + tid + k * BNT] = xv[k];
+  }
   float ss = 0.f;
 #pragma unroll
   for (int k = 0; k < EPT; ++k) ss += xv[k] * xv[k];

@@ -23,7 +23,7 @@ constexpr int NCOPY = 8;                // replicas of broadcast exchanges (one 
 // LDS weight staging, in items (one 16-byte chunk per lane of a wave) per wave
 constexpr int QKV_CAP = 2, O_CAP = 1, GU_CAP = 6, DN_CAP = 3, LM_CAP = 8;
 constexpr int TAGS_PER_LAUNCH = 1024;   // exchange tags one launch may use
-constexpr uint64_t SPIN_TIMEOUT = 100000000ull;  // 1 s of the 100 MHz wall clock
+constexpr uint64_t SPIN_TIMEOUT = 100000000ull;  // default wait bound: 1 s of the 100 MHz wall clock
 
 enum { W_F32 = 0, W_BF16 = 1, W_I4 = 2 };
 enum { ERR_TIMEOUT = 1u, ERR_TOKEN = 2u, ERR_POS = 4u };
@@ -43,6 +43,7 @@ struct KStatic {
   int qkv_rows, o_slots, h_slots;
   int poll_sleep;        // s_sleep(8) repetitions between polls of a stale slot
   int sentinels;         // slots polled by wave 0 before the bulk read (0: none, up to 64)
+  uint64_t spin_limit;   // a wait gives up after this many ticks of the 100 MHz wall clock
   const uint8_t* embed;
   const uint8_t* lmhead;
   const float* fnorm;
@@ -78,8 +79,7 @@ struct KDyn {
   float* dbg_logits;
   int32_t* dbg_routes;
   float* dbg_rw;
-  float* dbg_resid;
-  int dbg_resid_layer;
+  float* dbg_resid;      // [n_layers][H] residual after each layer of this sequence
   uint64_t* dbg_ts;
   float* dbg_z;          // [n_layers][n_experts] router logits of this sequence
 };
@@ -153,8 +153,7 @@ struct BArgs {
   float* dbg_logits;
   int32_t* dbg_routes;
   float* dbg_rw;
-  float* dbg_resid;
-  int dbg_resid_layer;
+  float* dbg_resid;      // [Bc][L][H] residual after each layer
   float* dbg_z;
 };
 

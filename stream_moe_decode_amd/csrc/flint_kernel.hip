@@ -579,6 +579,7 @@ struct Waiter {
   uint32_t* herr;
   int sleep;
   int sentinels;
+  uint64_t limit;
   bool abort;
 };
 __device__ __forceinline__ void backoff(const Waiter& wt) {
@@ -599,7 +600,7 @@ __device__ __forceinline__ bool poll_timed_out(const Waiter& wt, uint64_t t0, ui
   if ((it & 15) == 0 &&
       (__hip_atomic_load(gp(wt.err), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM) & ERR_TIMEOUT))
     return true;
-  if (now() - t0 > SPIN_TIMEOUT) {
+  if (now() - t0 > wt.limit) {
     raise_error(wt, ERR_TIMEOUT);
     return true;
   }
@@ -753,7 +754,7 @@ __global__ void __launch_bounds__(NT, 1) decode_kernel(const KStatic* __restrict
   const int QR = (nq + 2 * nkv) * hd;                            // q, k, v rows
   const int OSL = kAct32<WT> ? QD : QD / 2;                      // slots of the merged attention output
   const int HSLOTS = ks.h_slots;                                 // slots of the SwiGLU output exchange
-  Waiter wt{ks.err, ks.herr, ks.poll_sleep, ks.sentinels, false};
+  Waiter wt{ks.err, ks.herr, ks.poll_sleep, ks.sentinels, ks.spin_limit, false};
   // context values used inside DMA issue loops and publishes, held in registers
   const Mat m_qkv = ks.qkv, m_o = ks.o, m_r = ks.router, m_dg = ks.dg, m_du = ks.du, m_dd = ks.dd;
   const Mat m_eg = ks.eg, m_eu = ks.eu, m_ed = ks.ed;
@@ -1501,8 +1502,8 @@ __global__ void __launch_bounds__(NT, 1) decode_kernel(const KStatic* __restrict
     if (!ok) break;
     kv_later = l + 1 < L ? issue_kv_front(l + 1) : 0;
     if (stamp) stamp[15] = now();
-    if (d.dbg_resid && W == 0 && l == d.dbg_resid_layer)
-      for (int e = tid; e < H; e += NT) gp(d.dbg_resid)[e] = sm.xres[e];
+    if (d.dbg_resid && W == 0)
+      for (int e = tid; e < H; e += NT) gp(d.dbg_resid)[(size_t)l * H + e] = sm.xres[e];
   }
 
   // ---------------- final norm (its weights are in sm.gn), lm_head, argmax
@@ -1553,13 +1554,16 @@ __global__ void __launch_bounds__(NT, 1) decode_kernel(const KStatic* __restrict
       unsigned long long k = 0;
       for (int w = 0; w < NW; ++w) k = sm.best[w] > k ? sm.best[w] : k;
       __hip_atomic_fetch_max(gp(ks.amax), k, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      const uint32_t prev = __hip_atomic_fetch_add(gp(ks.done), 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+      const uint32_t prev = __hip_atomic_fetch_add(gp(ks.done), 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_SYSTEM);
       if (prev == (uint32_t)G - 1) {  // last workgroup: publish the token, reset for the next launch
         const unsigned long long fin =
             __hip_atomic_exchange(gp(ks.amax), 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         __hip_atomic_store(gp(ks.done), 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        gp(d.out_ids)[d.out_idx] = (int32_t)(0xFFFFFFFFu - (uint32_t)(fin & 0xFFFFFFFFull));
-        gp(d.len)[seq] = pos + 1;
+        // a wait of this step gave up (some layers were not computed): the step leaves the length as it
+        // was and writes -1 in place of an id; the host reports the error once and re-reads the lengths
+        const bool failed = (__hip_atomic_load(gp(ks.err), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM) & ERR_TIMEOUT) != 0;
+        gp(d.out_ids)[d.out_idx] = failed ? -1 : (int32_t)(0xFFFFFFFFu - (uint32_t)(fin & 0xFFFFFFFFull));
+        if (!failed) gp(d.len)[seq] = pos + 1;
         if (d.dbg_ts) gp(d.dbg_ts)[2] = now();
       }
     }

@@ -67,6 +67,7 @@ struct flint_ctx {
   size_t xbuf_words;
   uint64_t launches;
   int live_kv;
+  uint32_t resync_gen;        // bumped when a reported error may have left device lengths behind the host's
 };
 
 struct flint_kv {
@@ -82,6 +83,7 @@ struct flint_kv {
   BArgs bargs;                // its buffers and the pass-invariant arguments
   void* pscratch;             // scratch of the long-chunk prefill (made by its first use), null otherwise
   BArgs pargs;                // bargs with the buffers pointed at pscratch
+  uint32_t resync_gen;        // ctx->resync_gen when hlen was last known to match the device lengths
 };
 
 namespace {
@@ -194,13 +196,37 @@ int copy_mat(flint_ctx* c, const flint_mat& m, size_t count, size_t rows, size_t
 int latched_error(flint_ctx* c) {
   uint32_t e = __atomic_load_n(c->herr_host, __ATOMIC_ACQUIRE);
   if (!e) return FLINT_OK;
-  // clear the device and host words so the error is reported once; the kernel
-  // always completes its argmax hand-off, so no other state needs repair
+  // clear the device and host words so the error is reported once.  A step whose wait gave up (and every
+  // step queued behind it before this report) left its sequence's length unchanged while the host mirror
+  // advanced: every cache of this ctx re-reads its lengths at its next use.
+  (void)hipStreamSynchronize(c->stream);
+  e |= __atomic_load_n(c->herr_host, __ATOMIC_ACQUIRE);
   __atomic_store_n(c->herr_host, 0u, __ATOMIC_RELEASE);
   (void)hipMemsetAsync(c->base.err, 0, sizeof(uint32_t), c->stream);
-  if (e & ERR_TIMEOUT) return fail(FLINT_ETIMEOUT, "a cross-workgroup wait timed out in an earlier step");
+  (void)hipStreamSynchronize(c->stream);
+  if (e & ERR_TIMEOUT) {
+    c->resync_gen++;
+    return fail(FLINT_ETIMEOUT, "a cross-workgroup wait timed out in an earlier step (its length was not advanced)");
+  }
   if (e & ERR_TOKEN) return fail(FLINT_EDEVICE, "an earlier step read a token id outside [0, vocab)");
   return fail(FLINT_EDEVICE, "an earlier step found a device length outside [0, max_tokens)");
+}
+
+// Host mirror of the lengths brought back in line with the device after a reported timeout.
+int resync(flint_kv* kv) {
+  flint_ctx* c = kv->ctx;
+  if (kv->resync_gen == c->resync_gen) return FLINT_OK;
+  HIPCHECK(hipStreamSynchronize(c->stream));
+  HIPCHECK(hipMemcpy(kv->hlen.data(), kv->len, sizeof(int32_t) * kv->batch, hipMemcpyDeviceToHost));
+  kv->resync_gen = c->resync_gen;
+  return FLINT_OK;
+}
+
+// Entry of every call that uses a cache: report a latched error once, then make the host lengths current.
+int enter(flint_ctx* c, flint_kv* kv) {
+  const int rc = latched_error(c);
+  const int rs = resync(kv);
+  return rc ? rc : rs;
 }
 
 int launch(flint_ctx* c, flint_kv* kv, const int32_t* tokens, int tok_idx, int seq, int32_t* out, int out_idx,
@@ -229,8 +255,7 @@ int launch(flint_ctx* c, flint_kv* kv, const int32_t* tokens, int tok_idx, int s
     a.dbg_logits = dbg->logits ? dbg->logits + (size_t)seq * V : nullptr;
     a.dbg_routes = dbg->routes ? dbg->routes + (size_t)seq * L * K : nullptr;
     a.dbg_rw = dbg->route_w ? dbg->route_w + (size_t)seq * L * K : nullptr;
-    a.dbg_resid = dbg->resid ? dbg->resid + (size_t)seq * H : nullptr;
-    a.dbg_resid_layer = dbg->resid_layer;
+    a.dbg_resid = dbg->resid ? dbg->resid + (size_t)seq * L * H : nullptr;
     a.dbg_ts = seq == 0 ? dbg->phase_ts : nullptr;
     a.dbg_z = dbg->router_logits ? dbg->router_logits + (size_t)seq * L * c->cfg.n_experts : nullptr;
   }
@@ -475,6 +500,7 @@ int flint_decode_init(const flint_config* cfg, const flint_weights* w, void* hip
   // exchange polling: tuning knobs for experiments (defaults are the measured best)
   a.poll_sleep = getenv("FLINT_POLL_SLEEP") ? atoi(getenv("FLINT_POLL_SLEEP")) : 0;
   a.sentinels = getenv("FLINT_SENTINELS") ? atoi(getenv("FLINT_SENTINELS")) : 0;
+  a.spin_limit = SPIN_TIMEOUT;
   if (a.sentinels < 0) a.sentinels = 0;
   if (a.sentinels > 64) a.sentinels = 64;
   if (a.poll_sleep < 0) a.poll_sleep = 0;
@@ -565,6 +591,7 @@ int flint_decode_init(const flint_config* cfg, const flint_weights* w, void* hip
   if (hipStreamSynchronize(c->stream) != hipSuccess) return bail(fail(FLINT_EHIP, "hipStreamSynchronize failed"));
   c->launches = 0;
   c->live_kv = 0;
+  c->resync_gen = 0;
   *out = c;
   return FLINT_OK;
 }
@@ -630,6 +657,7 @@ int flint_kv_alloc(flint_ctx* c, int32_t batch, int32_t max_tokens, flint_kv** o
       hipStreamSynchronize(c->stream) != hipSuccess)
     return bail(fail(FLINT_EHIP, "KV cache initialisation failed"));
   kv->hlen.assign(batch, 0);
+  kv->resync_gen = c->resync_gen;
   kv->bscratch = nullptr;
   if (batch > 1 && c->batch_ok && max_tokens <= ATT_P * MAX_SPLITS) {
     int rc2 = batch_scratch(c, kv);
@@ -663,6 +691,7 @@ int flint_kv_set_lengths(flint_kv* kv, const int32_t* lengths) {
   HIPCHECK(hipMemcpyAsync(kv->len, lengths, sizeof(int32_t) * kv->batch, hipMemcpyHostToDevice, kv->ctx->stream));
   HIPCHECK(hipStreamSynchronize(kv->ctx->stream));
   kv->hlen.assign(lengths, lengths + kv->batch);
+  kv->resync_gen = kv->ctx->resync_gen;
   return FLINT_OK;
 }
 
@@ -676,6 +705,8 @@ int flint_kv_get_lengths(flint_kv* kv, int32_t* lengths) {
 int flint_kv_tokens(flint_kv* kv, int32_t seq, int32_t* tokens, int32_t n) {
   if (!kv || !tokens) return fail(FLINT_EINVAL, "NULL argument");
   if (seq < 0 || seq >= kv->batch) return fail(FLINT_EINVAL, "seq %d not in [0, %d)", seq, kv->batch);
+  int rc = resync(kv);
+  if (rc) return rc;
   if (n < 0 || n > kv->hlen[seq]) return fail(FLINT_EINVAL, "n %d not in [0, %d]", n, kv->hlen[seq]);
   if (n == 0) return FLINT_OK;
   HIPCHECK(hipStreamSynchronize(kv->ctx->stream));
@@ -687,6 +718,8 @@ int flint_kv_prefix_match(flint_kv* kv, int32_t seq, const int32_t* tokens, int3
   if (!kv || !matched || (n > 0 && !tokens)) return fail(FLINT_EINVAL, "NULL argument");
   if (seq < 0 || seq >= kv->batch) return fail(FLINT_EINVAL, "seq %d not in [0, %d)", seq, kv->batch);
   if (n < 0) return fail(FLINT_EINVAL, "n %d < 0", n);
+  int rc0 = resync(kv);
+  if (rc0) return rc0;
   const int m = std::min<int>(n, kv->hlen[seq]);
   std::vector<int32_t> rec(m);
   int rc = flint_kv_tokens(kv, seq, rec.data(), m);
@@ -712,7 +745,7 @@ int flint_decode_step_debug(flint_ctx* c, const int32_t* tokens, flint_kv* kv, i
                             const flint_debug* dbg) {
   if (!c || !kv || !tokens || !out_ids) return fail(FLINT_EINVAL, "NULL argument");
   if (kv->ctx != c) return fail(FLINT_EINVAL, "kv belongs to another ctx");
-  int rc = latched_error(c);
+  int rc = enter(c, kv);
   if (rc) return rc;
   for (int b = 0; b < kv->batch; ++b)
     if (kv->hlen[b] + 1 > kv->max_tokens)
@@ -725,7 +758,6 @@ int flint_decode_step_debug(flint_ctx* c, const int32_t* tokens, flint_kv* kv, i
     a.dbg_routes = dbg ? dbg->routes : nullptr;
     a.dbg_rw = dbg ? dbg->route_w : nullptr;
     a.dbg_resid = dbg ? dbg->resid : nullptr;
-    a.dbg_resid_layer = dbg ? dbg->resid_layer : -1;
     a.dbg_z = dbg ? dbg->router_logits : nullptr;
     for (int s0 = 0; s0 < kv->batch; s0 += BT) {
       a.B = std::min(BT, kv->batch - s0);
@@ -755,6 +787,8 @@ int flint_decode_step_seqs(flint_ctx* c, flint_kv* kv, const int32_t* seqs, int3
   if (!c || !kv || !seqs || !tokens || !out_ids) return fail(FLINT_EINVAL, "NULL argument");
   if (kv->ctx != c) return fail(FLINT_EINVAL, "kv belongs to another ctx");
   if (n < 1 || n > kv->batch) return fail(FLINT_EINVAL, "n %d not in [1, %d]", n, kv->batch);
+  int rc = enter(c, kv);
+  if (rc) return rc;
   std::vector<char> seen(kv->batch, 0);
   for (int i = 0; i < n; ++i) {
     const int b = seqs[i];
@@ -764,8 +798,6 @@ int flint_decode_step_seqs(flint_ctx* c, flint_kv* kv, const int32_t* seqs, int3
     if (kv->hlen[b] + 1 > kv->max_tokens)
       return fail(FLINT_ECAPACITY, "sequence %d: length %d + 1 exceeds max_tokens %d", b, kv->hlen[b], kv->max_tokens);
   }
-  int rc = latched_error(c);
-  if (rc) return rc;
   if (kv->bscratch && n >= c->batch_min) {  // batched passes over the listed sequences
     BArgs a = kv->bargs;
     for (int i0 = 0; i0 < n; i0 += BT) {
@@ -792,7 +824,7 @@ int flint_prefill_chunk(flint_ctx* c, flint_kv* kv, int32_t seq, const int32_t* 
   if (kv->ctx != c) return fail(FLINT_EINVAL, "kv belongs to another ctx");
   if (seq < 0 || seq >= kv->batch) return fail(FLINT_EINVAL, "seq %d not in [0, %d)", seq, kv->batch);
   if (n < 1 || n > 4096) return fail(FLINT_EINVAL, "n %d not in [1, 4096]", n);
-  int rc = latched_error(c);
+  int rc = enter(c, kv);
   if (rc) return rc;
   if (kv->hlen[seq] + n > kv->max_tokens)
     return fail(FLINT_ECAPACITY, "sequence %d: length %d + %d exceeds max_tokens %d", seq, kv->hlen[seq], n,
@@ -931,6 +963,15 @@ int flint_sync(flint_ctx* c) {
   if (!c) return fail(FLINT_EINVAL, "ctx is NULL");
   HIPCHECK(hipStreamSynchronize(c->stream));
   return latched_error(c);
+}
+
+int flint_set_wait_limit(flint_ctx* c, uint32_t microseconds) {
+  if (!c) return fail(FLINT_EINVAL, "ctx is NULL");
+  const uint64_t ticks = microseconds ? (uint64_t)microseconds * 100u : SPIN_TIMEOUT;  // 100 MHz clock
+  HIPCHECK(hipStreamSynchronize(c->stream));
+  c->base.spin_limit = ticks;
+  HIPCHECK(hipMemcpy(&c->kdev->spin_limit, &ticks, sizeof ticks, hipMemcpyHostToDevice));
+  return FLINT_OK;
 }
 
 int flint_device_info(flint_ctx* c, int32_t* grid, int32_t* block, int32_t* lds_bytes) {

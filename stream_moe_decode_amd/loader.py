@@ -153,14 +153,19 @@ class DeviceKV:
 
     def read_layer(self, layer: int, seq: int, n: int):
         """K, V of (layer, seq) at positions 0..n-1 as numpy [n_kv][n][head_dim] (fp32 or bf16 bits)."""
+        return self.read_positions(layer, seq, 0, n)
+
+    def read_positions(self, layer: int, seq: int, p0: int, n: int):
+        """K, V of (layer, seq) at positions p0..p0+n-1 as numpy [n_kv][n][head_dim] (fp32 or bf16 bits)."""
         cfg = self.model.cfg
+        assert 0 <= p0 and p0 + n <= self.max_tokens
         dt = np.float32 if cfg.weight_type == W_F32 else np.uint16
         kp, vp = kv_layer_ptrs(self.handle, layer)
         eb = np.dtype(dt).itemsize
         k = np.empty((cfg.n_kv_heads, n, cfg.head_dim), dt)
         v = np.empty_like(k)
         for j in range(cfg.n_kv_heads):
-            off = ((seq * cfg.n_kv_heads + j) * self.max_tokens) * cfg.head_dim * eb
+            off = ((seq * cfg.n_kv_heads + j) * self.max_tokens + p0) * cfg.head_dim * eb
             hip_memcpy(k[j].ctypes.data, kp + off, n * cfg.head_dim * eb, 2)
             hip_memcpy(v[j].ctypes.data, vp + off, n * cfg.head_dim * eb, 2)
         return k, v
@@ -174,7 +179,7 @@ class DeviceKV:
             self.handle = None
 
 
-def make_debug(cfg, batch: int, device, logits=True, routes=True, resid_layer=None, phase_ts=False,
+def make_debug(cfg, batch: int, device, logits=True, routes=True, resid=False, phase_ts=False,
                router_logits=None) -> tuple:
     """Allocate the optional outputs of decode_step_debug; returns (Debug, dict of tensors)."""
     t = {}
@@ -186,10 +191,9 @@ def make_debug(cfg, batch: int, device, logits=True, routes=True, resid_layer=No
         t["routes"] = torch.empty((batch, cfg.n_layers, cfg.top_k), dtype=torch.int32, device=device)
         t["route_w"] = torch.empty((batch, cfg.n_layers, cfg.top_k), dtype=torch.float32, device=device)
         dbg.routes, dbg.route_w = t["routes"].data_ptr(), t["route_w"].data_ptr()
-    if resid_layer is not None:
-        t["resid"] = torch.empty((batch, cfg.hidden), dtype=torch.float32, device=device)
+    if resid:  # residual after every layer
+        t["resid"] = torch.empty((batch, cfg.n_layers, cfg.hidden), dtype=torch.float32, device=device)
         dbg.resid = t["resid"].data_ptr()
-        dbg.resid_layer = resid_layer
     if phase_ts:
         t["phase_ts"] = torch.zeros((cfg.n_layers + 1, 16), dtype=torch.int64, device=device)
         dbg.phase_ts = t["phase_ts"].data_ptr()

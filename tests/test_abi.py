@@ -46,7 +46,7 @@ int main(void) {
          sizeof(flint_mat), sizeof(flint_weights), sizeof(flint_debug));
   F(flint_config, grid) F(flint_config, rope_theta) F(flint_config, rms_eps)
   F(flint_weights, attn_norm) F(flint_weights, qkv) F(flint_weights, exp_down)
-  F(flint_debug, resid_layer) F(flint_debug, phase_ts)
+  F(flint_debug, resid) F(flint_debug, phase_ts)
   return 0;
 }
 """
