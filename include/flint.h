@@ -227,6 +227,22 @@ int flint_decode_step(flint_ctx* ctx, const int32_t* tokens, flint_kv* kv, int32
 int flint_decode_step_seqs(flint_ctx* ctx, flint_kv* kv, const int32_t* seqs, int32_t n, const int32_t* tokens,
                            int32_t* out_ids);
 
+/*
+ * flint_decode_step for callers that cannot allocate device memory at call
+ * time (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc): every sequence of kv runs the persistent kernel, whose
+ * exchange slots and argmax counters live in a fixed 4 MiB array of the
+ * library's device image instead of the context's buffer.  The call allocates
+ * nothing (the array's device address is found once per device by
+ * flint_decode_init).  Every call on a GPU shares that GPU's array: calls
+ * that overlap on one GPU (other streams, other contexts, other threads)
+ * race and give undefined results.  Same arguments, outputs and errors as
+ * flint_decode_step, plus FLINT_EINVAL if the model needs more than the
+ * array's 4 MiB of exchange scratch (the 49-layer 2048-wide shape needs
+ * about 3.5 MB) and FLINT_EHIP if the array was not found at init.
+ */
+int flint_decode_step_noalloc(flint_ctx* ctx, const int32_t* tokens, flint_kv* kv, int32_t* out_ids);
+
 /* flint_decode_step with the optional outputs of `dbg` (may be NULL). */
 int flint_decode_step_debug(flint_ctx* ctx, const int32_t* tokens, flint_kv* kv, int32_t* out_ids,
                             const flint_debug* dbg);

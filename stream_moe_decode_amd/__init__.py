@@ -25,7 +25,7 @@ STATUS_NAMES = {0: "FLINT_OK", 1: "FLINT_EINVAL", 2: "FLINT_ENOMEM", 3: "FLINT_E
 # every symbol include/flint.h declares
 EXPORTS = ("flint_decode_init", "flint_decode_free", "flint_kv_alloc", "flint_kv_free", "flint_kv_set_lengths",
            "flint_kv_get_lengths", "flint_kv_tokens", "flint_kv_prefix_match", "flint_kv_layer_ptrs",
-           "flint_decode_step", "flint_decode_step_seqs",
+           "flint_decode_step", "flint_decode_step_seqs", "flint_decode_step_noalloc",
            "flint_decode_step_debug", "flint_prefill_chunk", "flint_micro_stream_read", "flint_micro_exchange",
            "flint_micro_launch", "flint_sync", "flint_set_wait_limit", "flint_device_info", "flint_last_error")
 
@@ -86,6 +86,7 @@ def lib():
             "flint_kv_layer_ptrs": [vp, i32, P(vp), P(vp)],
             "flint_decode_step": [vp, vp, vp, vp],
             "flint_decode_step_seqs": [vp, vp, P(i32), i32, vp, vp],
+            "flint_decode_step_noalloc": [vp, vp, vp, vp],
             "flint_decode_step_debug": [vp, vp, vp, vp, P(Debug)],
             "flint_prefill_chunk": [vp, vp, i32, vp, i32, vp],
             "flint_micro_stream_read": [vp, ctypes.c_size_t, i32, P(ctypes.c_float)],
@@ -154,6 +155,11 @@ def kv_layer_ptrs(kv: int, layer: int):
 
 def decode_step(ctx: int, tokens_ptr: int, kv: int, out_ptr: int):
     _check(lib().flint_decode_step(ctx, tokens_ptr, kv, out_ptr))
+
+
+def decode_step_noalloc(ctx: int, tokens_ptr: int, kv: int, out_ptr: int):
+    """flint_decode_step with the exchange scratch in the library's fixed device array (allocates nothing)."""
+    _check(lib().flint_decode_step_noalloc(ctx, tokens_ptr, kv, out_ptr))
 
 
 def kv_tokens(kv: int, seq: int, n: int):

@@ -82,6 +82,9 @@ struct KDyn {
   float* dbg_resid;      // [n_layers][H] residual after each layer of this sequence
   uint64_t* dbg_ts;
   float* dbg_z;          // [n_layers][n_experts] router logits of this sequence
+  uint64_t* xbase;       // null: the context's exchange buffer; else the fixed scratch array of the
+                         // non-allocating entry point: argmax counters in words 0 and 8, the context's slot
+                         // layout from word 16
 };
 
 // Batched decode: up to BT sequences per pass go through a sequence of
@@ -180,6 +183,12 @@ hipError_t launch_tile_weights(int wt, const uint8_t* w, uint8_t* dst, size_t ro
 bool shape_is_static(const KStatic& k, int grid);
 // Launch the persistent kernel for weight type wt on `stream` (stat: the compile-time shape).
 hipError_t launch_decode(int wt, bool stat, const KStatic* ks, const KDyn& d, int grid, hipStream_t stream);
+// The fixed exchange scratch of the non-allocating decode entry point: NOALLOC_SCRATCH_WORDS 64-bit words
+// per device (4 MiB).  noalloc_scratch finds this device's copy (device `dev`, current) once per device,
+// clears it once on `stream` and returns its address; noalloc_next_launch counts the launches that use it.
+constexpr size_t NOALLOC_SCRATCH_WORDS = 512 * 1024;
+hipError_t noalloc_scratch(int dev, hipStream_t stream, uint64_t** ptr);
+uint64_t noalloc_next_launch(int dev);
 // Zero `n` 64-bit words with a fill kernel.
 hipError_t launch_fill(uint64_t* p, size_t n, hipStream_t stream);
 // Static LDS bytes of the persistent kernel.

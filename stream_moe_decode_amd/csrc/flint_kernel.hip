@@ -35,6 +35,9 @@
 // output -> residual after the MLP.  Every wait is bounded (1 s); a timeout latches an error
 // word that every other wait also checks, so a failed step always ends.
 
+#include <atomic>
+#include <mutex>
+
 #include "flint_device.h"
 
 namespace flint {
@@ -759,8 +762,15 @@ __global__ void __launch_bounds__(NT, 1) decode_kernel(const KStatic* __restrict
   const Mat m_qkv = ks.qkv, m_o = ks.o, m_r = ks.router, m_dg = ks.dg, m_du = ks.du, m_dd = ks.dd;
   const Mat m_eg = ks.eg, m_eu = ks.eu, m_ed = ks.ed;
   const float *const p_anorm = ks.anorm, *const p_pnorm = ks.pnorm, *const p_fnorm = ks.fnorm;
-  uint64_t *const x_qkv = ks.x_qkv, *const x_part = ks.x_part, *const x_o = ks.x_o;
-  uint64_t *const x_res1 = ks.x_res1, *const x_h = ks.x_h, *const x_res2 = ks.x_res2, *const x_z = ks.x_z;
+  // exchange buffers: the context's, or (d.xbase, the fixed scratch array shared by every model on the
+  // device) the argmax counters at a fixed place in its first 128 bytes and the slots in the context's
+  // layout after them
+  auto rebase = [&](uint64_t* p) { return d.xbase ? d.xbase + 16 + (p - ks.x_qkv) : p; };
+  uint64_t *const x_qkv = rebase(ks.x_qkv), *const x_part = rebase(ks.x_part), *const x_o = rebase(ks.x_o);
+  uint64_t *const x_res1 = rebase(ks.x_res1), *const x_h = rebase(ks.x_h), *const x_res2 = rebase(ks.x_res2);
+  uint64_t *const x_z = rebase(ks.x_z);
+  unsigned long long* const p_amax = d.xbase ? (unsigned long long*)d.xbase : ks.amax;
+  uint32_t* const p_done = d.xbase ? (uint32_t*)(d.xbase + 8) : ks.done;
   uint8_t* const kc = d.kc;
   uint8_t* const vc = d.vc;
   const int seq = d.seq, B = d.B, cap = d.cap;
@@ -1553,12 +1563,12 @@ __global__ void __launch_bounds__(NT, 1) decode_kernel(const KStatic* __restrict
     if (tid == 0) {
       unsigned long long k = 0;
       for (int w = 0; w < NW; ++w) k = sm.best[w] > k ? sm.best[w] : k;
-      __hip_atomic_fetch_max(gp(ks.amax), k, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      const uint32_t prev = __hip_atomic_fetch_add(gp(ks.done), 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_SYSTEM);
+      __hip_atomic_fetch_max(gp(p_amax), k, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      const uint32_t prev = __hip_atomic_fetch_add(gp(p_done), 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_SYSTEM);
       if (prev == (uint32_t)G - 1) {  // last workgroup: publish the token, reset for the next launch
         const unsigned long long fin =
-            __hip_atomic_exchange(gp(ks.amax), 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        __hip_atomic_store(gp(ks.done), 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            __hip_atomic_exchange(gp(p_amax), 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(gp(p_done), 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         // a wait of this step gave up (some layers were not computed): the step leaves the length as it
         // was and writes -1 in place of an id; the host reports the error once and re-reads the lengths
         const bool failed = (__hip_atomic_load(gp(ks.err), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM) & ERR_TIMEOUT) != 0;
@@ -1574,6 +1584,41 @@ __global__ void __launch_bounds__(NT, 1) decode_kernel(const KStatic* __restrict
   }
   wait_vmem();
 }
+
+// ---------------------------------------------------------------- the non-allocating entry point's scratch
+
+// Exchange slots and argmax counters of flint_decode_step_noalloc, for callers that cannot allocate device
+// memory: a fixed array in the library's device image (each GPU holds its own copy for the life of the
+// process).  Host code never passes the array's name to a kernel (on the host it only stands for the
+// symbol): its device address is looked up once per device and that address is passed.
+static __device__ __align__(256) uint64_t scratch[NOALLOC_SCRATCH_WORDS];
+
+namespace {
+constexpr int MAX_DEVICES = 64;
+std::mutex g_na_mutex;
+uint64_t* g_na_ptr[MAX_DEVICES];
+std::atomic<uint64_t> g_na_launches[MAX_DEVICES];
+}  // namespace
+
+hipError_t noalloc_scratch(int dev, hipStream_t stream, uint64_t** ptr) {
+  if (dev < 0 || dev >= MAX_DEVICES) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_na_mutex);
+  if (!g_na_ptr[dev]) {
+    void* p = nullptr;
+    hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (!p) return hipErrorInvalidSymbol;
+    // every slot starts untagged and the argmax counters at zero
+    e = launch_fill((uint64_t*)p, NOALLOC_SCRATCH_WORDS, stream);
+    if (e == hipSuccess) e = hipStreamSynchronize(stream);
+    if (e != hipSuccess) return e;
+    g_na_ptr[dev] = (uint64_t*)p;
+  }
+  *ptr = g_na_ptr[dev];
+  return hipSuccess;
+}
+
+uint64_t noalloc_next_launch(int dev) { return g_na_launches[dev].fetch_add(1); }
 
 __global__ void fill_kernel(uint64_t* p, size_t n) {
   for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x) p[i] = 0;

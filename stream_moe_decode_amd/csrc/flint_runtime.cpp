@@ -64,7 +64,9 @@ struct flint_ctx {
   const uint8_t* lmt;         // lm_head in the tiled layout (with `tiled`)
   uint32_t* herr_host;        // host-mapped error word
   uint64_t* xbuf;
-  size_t xbuf_words;
+  size_t xbuf_words;          // exchange slots; the argmax hand-off counters follow (16 words)
+  uint64_t* na_ptr;           // this device's fixed scratch array (flint_decode_step_noalloc), or null
+  hipError_t na_status;       // result of finding it
   uint64_t launches;
   int live_kv;
   uint32_t resync_gen;        // bumped when a reported error may have left device lengths behind the host's
@@ -230,13 +232,22 @@ int enter(flint_ctx* c, flint_kv* kv) {
 }
 
 int launch(flint_ctx* c, flint_kv* kv, const int32_t* tokens, int tok_idx, int seq, int32_t* out, int out_idx,
-           const flint_debug* dbg) {
-  if (c->launches > 0 && c->launches % (1ull << 22) == 0) {
-    // tags restart: clear every exchange slot so no stale tag can match
-    HIPCHECK(launch_fill(c->xbuf, c->xbuf_words, c->stream));
-  }
+           const flint_debug* dbg, bool noalloc = false) {
   KDyn a;
   memset(&a, 0, sizeof a);
+  uint64_t n;
+  if (noalloc) {
+    // the fixed scratch is shared by every context on this device: tags come from the device's own count
+    n = noalloc_next_launch(c->device);
+    if (n > 0 && n % (1ull << 22) == 0) HIPCHECK(launch_fill(c->na_ptr, NOALLOC_SCRATCH_WORDS, c->stream));
+    a.xbase = c->na_ptr;
+  } else {
+    n = c->launches;
+    if (n > 0 && n % (1ull << 22) == 0) {
+      // tags restart: clear every exchange slot so no stale tag can match
+      HIPCHECK(launch_fill(c->xbuf, c->xbuf_words, c->stream));
+    }
+  }
   a.kc = (uint8_t*)kv->k;
   a.vc = (uint8_t*)kv->v;
   a.B = kv->batch;
@@ -249,7 +260,7 @@ int launch(flint_ctx* c, flint_kv* kv, const int32_t* tokens, int tok_idx, int s
   a.seq = seq;
   a.out_ids = out;
   a.out_idx = out_idx;
-  a.epoch = 1u + (uint32_t)(c->launches % (1ull << 22)) * (uint32_t)TAGS_PER_LAUNCH;
+  a.epoch = 1u + (uint32_t)(n % (1ull << 22)) * (uint32_t)TAGS_PER_LAUNCH;
   if (dbg) {
     const int H = c->cfg.hidden, V = c->cfg.vocab, L = c->cfg.n_layers, K = c->cfg.top_k;
     a.dbg_logits = dbg->logits ? dbg->logits + (size_t)seq * V : nullptr;
@@ -260,7 +271,7 @@ int launch(flint_ctx* c, flint_kv* kv, const int32_t* tokens, int tok_idx, int s
     a.dbg_z = dbg->router_logits ? dbg->router_logits + (size_t)seq * L * c->cfg.n_experts : nullptr;
   }
   HIPCHECK(launch_decode(c->cfg.weight_type, c->stat, c->kdev, a, c->grid, c->stream));
-  c->launches++;
+  if (!noalloc) c->launches++;
   return FLINT_OK;
 }
 
@@ -535,8 +546,9 @@ int flint_decode_init(const flint_config* cfg, const flint_weights* w, void* hip
   const size_t n_o = NCOPY * 2 * (size_t)a.o_slots, n_res = NCOPY * 2 * H, n_h = NCOPY * 2 * (size_t)a.h_slots;
   const size_t n_z = NCOPY * 2 * (size_t)std::max(1, cfg->n_experts);
   c->xbuf_words = n_qkv + n_part + n_o + 2 * n_res + n_h + n_z;
+  // the argmax hand-off counters follow the slots in the same buffer (16 words, two 64-byte lines)
   void* xb;
-  if ((rc = dalloc(c, &xb, c->xbuf_words * 8 + 256))) return bail(rc);
+  if ((rc = dalloc(c, &xb, (c->xbuf_words + 16) * 8 + 256))) return bail(rc);
   c->xbuf = (uint64_t*)xb;
   a.x_qkv = c->xbuf;
   a.x_part = a.x_qkv + n_qkv;
@@ -548,8 +560,8 @@ int flint_decode_init(const flint_config* cfg, const flint_weights* w, void* hip
   void* misc;
   if ((rc = dalloc(c, &misc, 256))) return bail(rc);
   a.err = (uint32_t*)misc;
-  a.done = (uint32_t*)((char*)misc + 64);
-  a.amax = (unsigned long long*)((char*)misc + 128);
+  a.amax = (unsigned long long*)(c->xbuf + c->xbuf_words);
+  a.done = (uint32_t*)(c->xbuf + c->xbuf_words + 8);
   if (hipHostMalloc((void**)&c->herr_host, 64, hipHostMallocMapped) != hipSuccess)
     return bail(fail(FLINT_ENOMEM, "hipHostMalloc of the error word failed"));
   *c->herr_host = 0;
@@ -586,7 +598,10 @@ int flint_decode_init(const flint_config* cfg, const flint_weights* w, void* hip
   c->kdev = (KStatic*)kd;
   if (hipMemcpyAsync(kd, &a, sizeof(KStatic), hipMemcpyHostToDevice, c->stream) != hipSuccess)
     return bail(fail(FLINT_EHIP, "copy of the kernel constants failed"));
-  if (launch_fill(c->xbuf, c->xbuf_words, c->stream) != hipSuccess) return bail(fail(FLINT_EHIP, "fill kernel failed"));
+  if (launch_fill(c->xbuf, c->xbuf_words + 16, c->stream) != hipSuccess) return bail(fail(FLINT_EHIP, "fill kernel failed"));
+  // the fixed exchange scratch of flint_decode_step_noalloc on this device (found once per device)
+  c->na_ptr = nullptr;
+  c->na_status = noalloc_scratch(c->device, c->stream, &c->na_ptr);
   if (hipMemsetAsync(misc, 0, 256, c->stream) != hipSuccess) return bail(fail(FLINT_EHIP, "hipMemsetAsync failed"));
   if (hipStreamSynchronize(c->stream) != hipSuccess) return bail(fail(FLINT_EHIP, "hipStreamSynchronize failed"));
   c->launches = 0;
@@ -780,6 +795,28 @@ int flint_decode_step_debug(flint_ctx* c, const int32_t* tokens, flint_kv* kv, i
 
 int flint_decode_step(flint_ctx* c, const int32_t* tokens, flint_kv* kv, int32_t* out_ids) {
   return flint_decode_step_debug(c, tokens, kv, out_ids, nullptr);
+}
+
+int flint_decode_step_noalloc(flint_ctx* c, const int32_t* tokens, flint_kv* kv, int32_t* out_ids) {
+  if (!c || !kv || !tokens || !out_ids) return fail(FLINT_EINVAL, "NULL argument");
+  if (kv->ctx != c) return fail(FLINT_EINVAL, "kv belongs to another ctx");
+  const size_t need = c->xbuf_words + 16;
+  if (need > NOALLOC_SCRATCH_WORDS)
+    return fail(FLINT_EINVAL, "this model needs %zu bytes of exchange scratch; the fixed array holds %zu", need * 8,
+                NOALLOC_SCRATCH_WORDS * 8);
+  if (c->na_status != hipSuccess || !c->na_ptr)
+    return fail(FLINT_EHIP, "the fixed scratch array was not found at init: %s", hipGetErrorString(c->na_status));
+  int rc = enter(c, kv);
+  if (rc) return rc;
+  for (int b = 0; b < kv->batch; ++b)
+    if (kv->hlen[b] + 1 > kv->max_tokens)
+      return fail(FLINT_ECAPACITY, "sequence %d: length %d + 1 exceeds max_tokens %d", b, kv->hlen[b], kv->max_tokens);
+  for (int b = 0; b < kv->batch; ++b) {  // every sequence on the persistent kernel
+    rc = launch(c, kv, tokens, b, b, out_ids, b, nullptr, true);
+    if (rc) return rc;
+    kv->hlen[b]++;
+  }
+  return FLINT_OK;
 }
 
 int flint_decode_step_seqs(flint_ctx* c, flint_kv* kv, const int32_t* seqs, int32_t n, const int32_t* tokens,
