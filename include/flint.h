@@ -116,7 +116,7 @@ typedef struct flint_debug {
   uint64_t* phase_ts;   /* [n_layers + 1][16] wall-clock stamps (100 MHz) of workgroup 0 at
                            phase boundaries, for sequence 0.  Row 0: start, end, argmax published,
                            then the shader clock counter (s_memtime) at start and at end.
-                           Row l + 1 (layer l), in order: 0 input norm, 1 QKV, 2 q/k/v published,
+                           Row l + 1 (layer l, the first 56 layers), in order: 0 input norm, 1 QKV, 2 q/k/v published,
                            3 q gathered, 4 attention partial published, 5 splits merged, 6 merged
                            output gathered, 7 o_proj published, 8 residual gathered, 9 post norm,
                            10 router, 11 top-k (10 and 11 are 0 on dense layers), 12 SwiGLU

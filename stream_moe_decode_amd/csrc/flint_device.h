@@ -243,17 +243,19 @@ __device__ __forceinline__ void kv_issue(uint4* buf, const uint8_t* base, int c0
 }
 
 // K rows [c0, c0 + np) (np <= 128) of one bf16 cache slice with head_dim 128,
-// laid out as the A operand of v_mfma_f32_16x16x32_bf16: 16-byte slot
-// (b * 4 + s) * 64 + L holds dims s * 32 + (L / 16) * 8 .. + 8 of position
-// b * 16 + L % 16 (positions past the end repeat the last one).  The DMA
-// addresses are chosen per lane, so the layout costs nothing.
+// row-major in LDS (256 B per position) with the 16-byte units of position p
+// XOR-swizzled by p % 16: unit u of row p sits at slot p * 16 + (u ^ (p % 16)).
+// Each wave instruction reads 1 KB of contiguous cache (4 whole rows); the
+// swizzle makes the MFMA operand reads (16 rows, one unit each) conflict-free.
+// Rows past the end repeat the last one.
+__device__ __forceinline__ int k_slot(int p, int u) { return p * 16 + (u ^ (p & 15)); }
 __device__ __forceinline__ void k_issue_mfma(uint4* buf, const uint8_t* base, int c0, int np) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int nq = (np + 15) / 16 * 4;
-  for (int q = wave; q < nq; q += NW) {
-    const int b = q >> 2, sk = q & 3;
-    const int pr = min(b * 16 + (lane & 15), np - 1);
-    dma16(base + (size_t)(c0 + pr) * 256 + sk * 64 + (lane >> 4) * 16, &buf[q * 64]);
+  const int ni = (np * 16 + 63) / 64;
+  for (int gi = wave; gi < ni; gi += NW) {
+    const int sl = gi * 64 + lane, p = sl >> 4, pr = min(p, np - 1);
+    const int u = (sl & 15) ^ (p & 15);
+    dma16(base + (size_t)(c0 + pr) * 256 + u * 16, &buf[gi * 64]);
   }
 }
 

@@ -23,6 +23,7 @@ constexpr int NCOPY = 8;                // replicas of broadcast exchanges (one 
 // LDS weight staging, in items (one 16-byte chunk per lane of a wave) per wave
 constexpr int QKV_CAP = 2, O_CAP = 1, GU_CAP = 6, DN_CAP = 3, LM_CAP = 8;
 constexpr int TAGS_PER_LAUNCH = 1024;   // exchange tags one launch may use
+constexpr int STAMP_LAYERS = 56;        // layers whose phase stamps the debug output records
 constexpr uint64_t SPIN_TIMEOUT = 100000000ull;  // default wait bound: 1 s of the 100 MHz wall clock
 
 enum { W_F32 = 0, W_BF16 = 1, W_I4 = 2 };

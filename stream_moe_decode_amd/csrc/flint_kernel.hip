@@ -108,6 +108,8 @@ struct Smem {
   float wsel[MAX_K];
   float wred[NW * 2];
   unsigned long long best[NW];
+  uint32_t st_base[STAMP_LAYERS];        // phase stamps (debug, thread 0 of workgroup 0): each layer's start after
+  uint16_t st[STAMP_LAYERS][16];         // the step's, its 16 stamps after that (10 ns ticks); stored at the end
   int flag;                              // sticky: a wait of this workgroup failed
 };
 
@@ -147,28 +149,52 @@ template <int WT> __device__ __forceinline__ void act_sums(const uint32_t* act, 
   }
 }
 // RMSNorm of the residual with the weights sm.gn (brought in by this
-// workgroup's DMA), as the next GEMV input actA in the layout of OW.
+// workgroup's DMA), as the next GEMV input actA in the layout of OW (and, with
+// sums, the int4 chunk sums).  Thread t takes elements 4t .. 4t + 3 (H <= 4 NT),
+// which is also the 16-byte unit of sm.gn its own wave brought in, so the
+// weights need only this wave's wait; two barriers in all.  half: which half of
+// sm.wred holds the wave sums (consecutive norms alternate, so no barrier is
+// needed before writing them).
 // later: vector memory operations this wave issued after the norm weights' DMA (they may stay in flight).
 template <int WT, int OW = WT>
-__device__ __forceinline__ void rmsnorm_act(Smem& sm, int H, float eps, bool sums, int later = 0) {
-  const int tid = threadIdx.x;
-  wait_vmem_dyn(later);  // this wave's part of sm.gn has landed; block_sum's barrier publishes it
-  float ss = 0.f;
-  for (int e = tid; e < H; e += NT) ss += sm.xres[e] * sm.xres[e];
-  ss = block_sum(sm, ss);
-  const float inv = 1.0f / sqrtf(ss / (float)H + eps);
-  for (int e = tid; e < H; e += NT) act_put<OW>(sm.actA, e, act_round<WT>(sm.xres[e] * inv * sm.gn[e]));
+__device__ __forceinline__ void rmsnorm_act(Smem& sm, int H, float eps, bool sums, int later = 0, int half = 0) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  wait_vmem_dyn(later);
+  const int e0 = 4 * tid;
+  const bool mine = e0 < H;
+  const float4 x = mine ? *reinterpret_cast<const float4*>(&sm.xres[e0]) : make_float4(0.f, 0.f, 0.f, 0.f);
+  float ss = x.x * x.x + x.y * x.y + x.z * x.z + x.w * x.w;
+  ss = wave_sum(ss);
+  if (lane == 0) sm.wred[half * NW + wave] = ss;
   __syncthreads();
-  if (sums) {
-    act_sums<OW>(sm.actA, sm.asumA, H);
-    __syncthreads();
+  float t = 0.f;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) t += sm.wred[half * NW + w];
+  const float inv = 1.0f / sqrtf(t / (float)H + eps);
+  if (mine) {
+    const float4 g = *reinterpret_cast<const float4*>(&sm.gn[e0]);
+    const float y0 = act_round<WT>(x.x * inv * g.x), y1 = act_round<WT>(x.y * inv * g.y);
+    const float y2 = act_round<WT>(x.z * inv * g.z), y3 = act_round<WT>(x.w * inv * g.w);
+    act_put<OW>(sm.actA, e0, y0);
+    act_put<OW>(sm.actA, e0 + 1, y1);
+    act_put<OW>(sm.actA, e0 + 2, y2);
+    act_put<OW>(sm.actA, e0 + 3, y3);
+    if constexpr (OW == W_I4) {
+      if (sums) {  // the 32 elements of chunk t / 8 belong to 8 consecutive threads
+        const float cs = group_sum((y0 + y1) + (y2 + y3), 8);
+        if ((tid & 7) == 0) sm.asumA[e0 >> 5] = cs;
+      }
+    }
   }
+  __syncthreads();
 }
 // Bring n floats (n a multiple of 64) into sm.gn by DMA; wave w moves 1 KB units w, w + NW, ...
-__device__ __forceinline__ void gn_issue(Smem& sm, const float* src, int n) {
+// Waves w0 .. NW - 1 share the work.
+__device__ __forceinline__ void gn_issue(Smem& sm, const float* src, int n, int w0 = 0) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int units = n / 4;  // 16-byte units
-  for (int gi = wave; gi * 64 < units; gi += NW) {
+  if (wave < w0) return;
+  for (int gi = wave - w0; gi * 64 < units; gi += NW - w0) {
     const int unit = min(gi * 64 + lane, units - 1);
     dma16(src + 4 * unit, &sm.gn[gi * 256]);
   }
@@ -624,9 +650,13 @@ __device__ __forceinline__ bool sync_ok(Smem& sm, Waiter& wt) {
 // k < nsent); then every thread reads its items once (8 loads in flight) and
 // re-polls only those still stale.  Called by the whole workgroup; returns
 // false (uniformly) if a wait failed.
-template <class IndexFn, class SentFn, class PutFn>
+// GT: threads that read slots (the first GT of the workgroup; the others only take part in the barriers,
+// e.g. while their DMAs are in flight: a wave's loads complete in order, so a poll issued behind a DMA burst
+// would return only after the burst).
+template <int GT = NT, class IndexFn, class SentFn, class PutFn>
 __device__ __forceinline__ bool gather(Smem& sm, const uint64_t* src, int n, uint32_t tag, IndexFn index, SentFn sent,
                                        int nsent, PutFn put, Waiter& wt) {
+  static_assert(GT % 64 == 0 && GT >= 64 && GT <= NT, "whole waves poll");
   const int tid = threadIdx.x;
   if (nsent > wt.sentinels) nsent = wt.sentinels;
   if (tid < 64 && tid < nsent && !wt.abort) {  // sentinels == 0: every thread polls its own slots at once
@@ -644,8 +674,7 @@ __device__ __forceinline__ bool gather(Smem& sm, const uint64_t* src, int n, uin
     }
   }
   if (!sync_ok(sm, wt)) return false;
-  constexpr int GT = NT;
-  for (int b0 = 0; b0 < n; b0 += 8 * GT) {
+  for (int b0 = 0; b0 < n && tid < GT; b0 += 8 * GT) {
     uint64_t v[8];
 #pragma unroll
     for (int k = 0; k < 8; ++k) {
@@ -683,11 +712,11 @@ __device__ __forceinline__ bool gather(Smem& sm, const uint64_t* src, int n, uin
 }
 
 // Gather n contiguous slots, sentinels spread evenly.
-template <class PutFn>
+template <int GT = NT, class PutFn>
 __device__ __forceinline__ bool gather_flat(Smem& sm, const uint64_t* src, int n, uint32_t tag, PutFn put,
                                             Waiter& wt) {
   const int ns = n < 64 ? n : 64;
-  return gather(
+  return gather<GT>(
       sm, src, n, tag, [](int i) { return i; }, [=](int k, int m) { return (int)(((long long)(k + 1) * n) / m) - 1; },
       ns, put, wt);
 }
@@ -759,9 +788,14 @@ __global__ void __launch_bounds__(NT, 1) decode_kernel(const KStatic* __restrict
   const int HSLOTS = ks.h_slots;                                 // slots of the SwiGLU output exchange
   Waiter wt{ks.err, ks.herr, ks.poll_sleep, ks.sentinels, ks.spin_limit, false};
   // context values used inside DMA issue loops and publishes, held in registers
-  const Mat m_qkv = ks.qkv, m_o = ks.o, m_r = ks.router, m_dg = ks.dg, m_du = ks.du, m_dd = ks.dd;
-  const Mat m_eg = ks.eg, m_eu = ks.eu, m_ed = ks.ed;
-  const float *const p_anorm = ks.anorm, *const p_pnorm = ks.pnorm, *const p_fnorm = ks.fnorm;
+  // context values stay in LDS and are read where they are used (an LDS read never waits for the vector
+  // memory counter; held in registers across the layer loop they were spilled to scratch memory, and
+  // each reload of a spill waited behind every store and DMA issued before it)
+  const Mat &m_qkv = ks.qkv, &m_o = ks.o, &m_r = ks.router, &m_dg = ks.dg, &m_du = ks.du, &m_dd = ks.dd;
+  const Mat &m_eg = ks.eg, &m_eu = ks.eu, &m_ed = ks.ed;
+  const float* const& p_anorm = ks.anorm;
+  const float* const& p_pnorm = ks.pnorm;
+  const float* const& p_fnorm = ks.fnorm;
   // exchange buffers: the context's, or (d.xbase, the fixed scratch array shared by every model on the
   // device) the argmax counters at a fixed place in its first 128 bytes and the slots in the context's
   // layout after them
@@ -809,10 +843,9 @@ __global__ void __launch_bounds__(NT, 1) decode_kernel(const KStatic* __restrict
     tok = 0;
   }
   if (W == 0 && tid == 0) gp(d.hist)[(size_t)seq * cap + pos] = tok;  // the cache's token record
-  if (stamps) {
-    stamps[0] = now();
-    stamps[3] = __builtin_amdgcn_s_memtime();  // shader clock, to relate the stamps to cycles
-  }
+  // stamps stay in LDS until the step ends: a store among the layers' counted DMA waits (or a wait that also
+  // covers a store) would change what the stamps measure
+  const uint64_t t_start = stamps ? now() : 0, c_start = stamps ? __builtin_amdgcn_s_memtime() : 0;
   if (tid == 0) sm.flag = 0;
 
   const int T = pos + 1;
@@ -855,13 +888,16 @@ __global__ void __launch_bounds__(NT, 1) decode_kernel(const KStatic* __restrict
     else kv_issue(sm.u.att.kbuf, kc + cb, t0, np0, rowb);
     kv_issue(sm.u.att.vbuf, vc + cb, t0, np0, rowb);
     auto per_wave = [&](int n) { return n > wave ? (n - wave + NW - 1) / NW : 0; };
-    const int nk = MFMA_QK ? (np0 + 15) / 16 * 4 : (np0 * rowb / 16 + 63) / 64;
+    const int nk = MFMA_QK ? (np0 * 16 + 63) / 64 : (np0 * rowb / 16 + 63) / 64;
     return per_wave(nk) + per_wave((np0 * rowb / 16 + 63) / 64);
   };
-  int kv_later = 0;  // this layer's front chunk DMAs, issued after the previous layer's last exchange
+  // A layer's first attention chunk (its K/V rows, the largest read of the layer) is requested right after
+  // the layer's q/k/v are published: issuing it earlier stalls the issuing waves (the requests of all
+  // workgroups take the chip ~2.7 us to serve at 8,022 positions) ahead of the norm and the QKV rows, which
+  // do not need it; the q/k/v exchange's polls then complete behind it, when the attention needs both.
+  const int kv_later = 0;
 
   issue_qkv(0);
-  issue_kv_front(0);
   gn_issue(sm, p_anorm, H);
   for (int e = tid; e < H; e += NT) {  // embedding row -> residual
     if constexpr (kAct32<WT>)
@@ -877,7 +913,12 @@ __global__ void __launch_bounds__(NT, 1) decode_kernel(const KStatic* __restrict
   for (int l = 0; l < L; ++l) {
     const uint32_t tag = d.epoch + (uint32_t)l * 8u;
     const int par = l & 1;
-    GLOBAL uint64_t* stamp = stamps ? stamps + (size_t)(l + 1) * 16 : nullptr;
+    uint16_t* const stamp = stamps && l < STAMP_LAYERS ? sm.st[l] : nullptr;
+    const uint64_t lbase = stamp ? now() : 0;
+    if (stamp) sm.st_base[l] = (uint32_t)(lbase - t_start);
+    auto stampit = [&](int k) {
+      if (stamp) stamp[k] = (uint16_t)(now() - lbase);
+    };
     const size_t cbase = (((size_t)l * B + seq) * nkv + (attn ? aj : 0)) * kvstride;
     const uint8_t* const kbase = kc + cbase * ebytes;
     const uint8_t* const vbase = vc + cbase * ebytes;
@@ -886,7 +927,7 @@ __global__ void __launch_bounds__(NT, 1) decode_kernel(const KStatic* __restrict
 
     // ---------------- input RMSNorm (recomputed by every workgroup)
     rmsnorm_act<WT>(sm, H, ks.eps, ASUM_A, kv_later);
-    if (stamp) stamp[0] = now();
+    stampit(0);
 
     // ---------------- QKV rows (staged during the previous layer), RoPE, publish, KV append
     {
@@ -895,7 +936,7 @@ __global__ void __launch_bounds__(NT, 1) decode_kernel(const KStatic* __restrict
                                              [&](int q, float v) { sm.ytmp[q] = v; }, kv_later);
     }
     __syncthreads();
-    if (stamp) stamp[1] = now();
+    stampit(1);
     for (int q2 = tid; q2 < qpe - qpb; q2 += NT) {  // RoPE on q and k heads: pairs (i, i + hd/2)
       const int head = (qpb + q2) / half;
       if (head < nq + nkv) {
@@ -923,7 +964,8 @@ __global__ void __launch_bounds__(NT, 1) decode_kernel(const KStatic* __restrict
       }
     }
     gn_issue(sm, p_pnorm + (size_t)l * H, H);  // post-attention norm weights, read after the o_proj exchange
-    if (stamp) stamp[2] = now();
+    issue_kv_front(l);
+    stampit(2);
 
     // ---------------- attention partial over positions [t0, t1) of kv head aj
     if (attn) {
@@ -966,7 +1008,7 @@ __global__ void __launch_bounds__(NT, 1) decode_kernel(const KStatic* __restrict
         ok = sync_ok(sm, wt);
       }
       if (!ok) break;
-      if (stamp) stamp[3] = now();
+      stampit(3);
       // running output: every wave accumulates all heads over its positions (lane: DPV dims)
       constexpr int DPVM = MAX_HD / 64;
       const int DPV = hd / 64, PST = Gq <= 4 ? 4 : 8;
@@ -998,10 +1040,8 @@ __global__ void __launch_bounds__(NT, 1) decode_kernel(const KStatic* __restrict
               reinterpret_cast<float*>(kr)[e] = at.kn[e];
               reinterpret_cast<float*>(vr)[e] = at.vn[e];
             } else {
-              if constexpr (MFMA_QK) {  // the row's dims sit in 16 slots of the operand layout
-                const int pr = pos - c0, b = pr >> 4, i = pr & 15, sk = e >> 5, gq = (e >> 3) & 3;
-                reinterpret_cast<uint16_t*>(at.kbuf)[((b * 4 + sk) * 64 + gq * 16 + i) * 8 + (e & 7)] =
-                    (uint16_t)f2bf(at.kn[e]);
+              if constexpr (MFMA_QK) {  // the row's units are swizzled by the position
+                reinterpret_cast<uint16_t*>(at.kbuf)[k_slot(pos - c0, e >> 3) * 8 + (e & 7)] = (uint16_t)f2bf(at.kn[e]);
               } else {
                 reinterpret_cast<uint16_t*>(kr)[e] = (uint16_t)f2bf(at.kn[e]);
               }
@@ -1027,7 +1067,8 @@ __global__ void __launch_bounds__(NT, 1) decode_kernel(const KStatic* __restrict
             f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int sk = 0; sk < 4; ++sk) {
-              const bf16x8_t a = __builtin_bit_cast(bf16x8_t, at.kbuf[(b * 4 + sk) * 64 + lane]);
+              const bf16x8_t a =
+                  __builtin_bit_cast(bf16x8_t, at.kbuf[k_slot(b * 16 + (lane & 15), sk * 4 + (lane >> 4))]);
               acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qh[sk], acc, 0, 0, 0);
               acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, ql[sk], acc, 0, 0, 0);
             }
@@ -1181,7 +1222,7 @@ __global__ void __launch_bounds__(NT, 1) decode_kernel(const KStatic* __restrict
         xstore(dst + (size_t)h * (hd + 2) + (tid & 1), slot(tag + 1, __float_as_uint(v)));
       }
     }
-    if (stamp) stamp[4] = now();
+    stampit(4);
 
     // o_proj rows of this workgroup: stage their weights before the merge waits
     __syncthreads();  // the attention layout of the shared region is dead
@@ -1249,7 +1290,7 @@ __global__ void __launch_bounds__(NT, 1) decode_kernel(const KStatic* __restrict
       }
     }
     if (!ok) break;
-    if (stamp) stamp[5] = now();
+    stampit(5);
 
     // ---------------- o_proj rows + residual
     ok = gather_flat(sm, copy_of(x_o, OSL, par), OSL, tag + 2,
@@ -1263,7 +1304,7 @@ __global__ void __launch_bounds__(NT, 1) decode_kernel(const KStatic* __restrict
                      },
                      wt);
     if (!ok) break;
-    if (stamp) stamp[6] = now();
+    stampit(6);
     if constexpr (ASUM_A) {
       act_sums<WT>(sm.actA, sm.asumA, QD);
       __syncthreads();
@@ -1277,7 +1318,7 @@ __global__ void __launch_bounds__(NT, 1) decode_kernel(const KStatic* __restrict
       idx = orb + q;
       return __float_as_uint(sm.xres[orb + q] + sm.ytmp[q]);
     });
-    if (stamp) stamp[7] = now();
+    stampit(7);
     // router rows of this workgroup (one wave per row): the first row of each wave is staged before
     // the wait for the residual (chunk lane + 64 j of the row in item j)
     const int rbb = dense ? 0 : part(E_, G, W), rbe = dense ? 0 : part(E_, G, W + 1);
@@ -1296,11 +1337,11 @@ __global__ void __launch_bounds__(NT, 1) decode_kernel(const KStatic* __restrict
     ok = gather_flat(sm, copy_of(x_res1, H, par), H, tag + 3,
                      [&](int i, uint32_t p) { sm.xres[i] = __uint_as_float(p); }, wt);
     if (!ok) break;
-    if (stamp) stamp[8] = now();
+    stampit(8);
 
     // ---------------- post-attention RMSNorm (recomputed by every workgroup)
-    rmsnorm_act<WT>(sm, H, ks.eps, ASUM_A);
-    if (stamp) stamp[9] = now();
+    rmsnorm_act<WT>(sm, H, ks.eps, ASUM_A, 0, 1);
+    stampit(9);
 
     int nunit, inner;  // SwiGLU elements this layer produces, and the down projection's input width
     if (dense) {
@@ -1335,7 +1376,7 @@ __global__ void __launch_bounds__(NT, 1) decode_kernel(const KStatic* __restrict
       if (!ok) break;
       if (d.dbg_z && W == 0)
         for (int e = tid; e < E_; e += NT) gp(d.dbg_z)[(size_t)l * E_ + e] = sm.z[e];
-      if (stamp) stamp[10] = now();
+      stampit(10);
       // top-k by rank, in every wave (identical results; a wave reads only its own writes):
       // lane e counts the experts that beat it (larger logit, or equal logit and lower index)
       {
@@ -1355,15 +1396,16 @@ __global__ void __launch_bounds__(NT, 1) decode_kernel(const KStatic* __restrict
           part += j < E_ && kj > key;
         }
         rk[wave * 64 + lane] = part;
-        __syncthreads();
-        int rank = 0;
-#pragma unroll
-        for (int w = 0; w < NW; ++w) rank += rk[w * 64 + lane];
+        // the softmax needs no ranks: it runs while the other waves finish their counts
         const float zmax = wave_max(zl);
         const float pe = lane < E_ ? __expf(zl - zmax) : 0.f;
         const float den = wave_sum(pe);
         const float w = pe / den;
-        const float wsum = wave_sum(lane < E_ && rank < K_ ? w : 0.f);
+        __syncthreads();
+        int rank = 0;
+#pragma unroll
+        for (int w = 0; w < NW; ++w) rank += rk[w * 64 + lane];
+        const float wsum = ks.renorm ? wave_sum(lane < E_ && rank < K_ ? w : 0.f) : 1.f;
         if (lane < E_ && rank < K_) {
           sm.sel[rank] = lane;
           sm.wsel[rank] = ks.renorm ? w / wsum : w;
@@ -1377,7 +1419,7 @@ __global__ void __launch_bounds__(NT, 1) decode_kernel(const KStatic* __restrict
       }
       nunit = K_ * EI_;
       inner = EI_;
-      if (stamp) stamp[11] = now();
+      stampit(11);
     }
 
     // ---------------- gate/up rows of this workgroup's SwiGLU elements
@@ -1388,7 +1430,8 @@ __global__ void __launch_bounds__(NT, 1) decode_kernel(const KStatic* __restrict
     const int wstride = inner / kChunkElems<WT> * kChunkWords<WT>;  // words of one rank's h
     // this workgroup's units are contiguous: unless they span more than two experts, the selected
     // experts of the first and the next rank are all a row needs
-    const Mat mg = dense ? m_dg : m_eg, mu = dense ? m_du : m_eu;
+    const Mat& mg = dense ? m_dg : m_eg;
+    const Mat& mu = dense ? m_du : m_eu;
     const int gk0 = dense ? 0 : div_small(ue0, EI_, inv_ei);
     const bool two = !dense && une <= EI_;
     const int gsel0 = dense ? 0 : sm.sel[gk0], gsel1 = (!dense && gk0 + 1 < K_) ? sm.sel[gk0 + 1] : gsel0;
@@ -1456,7 +1499,7 @@ __global__ void __launch_bounds__(NT, 1) decode_kernel(const KStatic* __restrict
     else if constexpr (NI_DNM > 0 && NI_DNM <= DN_CAP) lstage_issue_static<WT, NI_DNM>(lstage(sm.u.mlp.dn), gdn, 0, dn_rowfn_x, gdn.wave);
     else lstage_issue<WT>(lstage(sm.u.mlp.dn), gdn, 0, dn_rowfn);
     gn_issue(sm, l + 1 < L ? p_anorm + (size_t)(l + 1) * H : p_fnorm, H);
-    if (stamp) stamp[12] = now();
+    stampit(12);
     // ---------------- gather the SwiGLU output, down projection + residual
     ok = gather_flat(sm, copy_of(x_h, HSLOTS, par), kAct32<WT> ? nunit : nunit / 2, tag + 4,
                      [&](int i, uint32_t p) {
@@ -1472,7 +1515,7 @@ __global__ void __launch_bounds__(NT, 1) decode_kernel(const KStatic* __restrict
     if (!ok) break;
     act_sums<WT>(sm.u.mlp.hbuf, sm.u.mlp.asumH, nunit);
     __syncthreads();
-    if (stamp) stamp[13] = now();
+    stampit(13);
     if (dense) {
       const auto ar = act_regs<WT, CP_DN>(gdn, sm.u.mlp.hbuf, sm.u.mlp.asumH);
       gemv_auto<WT, CP_DN, NI_DND, DN_CAP>(lstage(sm.u.mlp.dn), gdn, true, ar, dn_rowfn,
@@ -1506,12 +1549,11 @@ __global__ void __launch_bounds__(NT, 1) decode_kernel(const KStatic* __restrict
     // the shared region is free: the next layer's QKV weights load during the exchange; its first
     // attention chunk after it (the exchange's loads would otherwise return only after the chunk)
     if (l + 1 < L) issue_qkv(l + 1);
-    if (stamp) stamp[14] = now();
+    stampit(14);
     ok = gather_flat(sm, copy_of(x_res2, H, par), H, tag + 5,
                      [&](int i, uint32_t p) { sm.xres[i] = __uint_as_float(p); }, wt);
     if (!ok) break;
-    kv_later = l + 1 < L ? issue_kv_front(l + 1) : 0;
-    if (stamp) stamp[15] = now();
+    stampit(15);
     if (d.dbg_resid && W == 0)
       for (int e = tid; e < H; e += NT) gp(d.dbg_resid)[(size_t)l * H + e] = sm.xres[e];
   }
@@ -1580,7 +1622,11 @@ __global__ void __launch_bounds__(NT, 1) decode_kernel(const KStatic* __restrict
   }
   if (stamps) {
     stamps[1] = now();
+    stamps[0] = t_start;
+    stamps[3] = c_start;
     stamps[4] = __builtin_amdgcn_s_memtime();
+    for (int l = 0; l < L && l < STAMP_LAYERS; ++l)
+      for (int j = 0; j < 16; ++j) stamps[(size_t)(l + 1) * 16 + j] = t_start + sm.st_base[l] + sm.st[l][j];
   }
   wait_vmem();
 }
