@@ -898,6 +898,7 @@ __global__ void __launch_bounds__(NT, 1) decode_kernel(const KStatic* __restrict
   const int kv_later = 0;
 
   issue_qkv(0);
+  issue_kv_front(0);
   gn_issue(sm, p_anorm, H);
   for (int e = tid; e < H; e += NT) {  // embedding row -> residual
     if constexpr (kAct32<WT>)
@@ -964,7 +965,6 @@ __global__ void __launch_bounds__(NT, 1) decode_kernel(const KStatic* __restrict
       }
     }
     gn_issue(sm, p_pnorm + (size_t)l * H, H);  // post-attention norm weights, read after the o_proj exchange
-    issue_kv_front(l);
     stampit(2);
 
     // ---------------- attention partial over positions [t0, t1) of kv head aj
@@ -1548,7 +1548,10 @@ __global__ void __launch_bounds__(NT, 1) decode_kernel(const KStatic* __restrict
     });
     // the shared region is free: the next layer's QKV weights load during the exchange; its first
     // attention chunk after it (the exchange's loads would otherwise return only after the chunk)
-    if (l + 1 < L) issue_qkv(l + 1);
+    if (l + 1 < L) {
+      issue_qkv(l + 1);
+      issue_kv_front(l + 1);
+    }
     stampit(14);
     ok = gather_flat(sm, copy_of(x_res2, H, par), H, tag + 5,
                      [&](int i, uint32_t p) { sm.xres[i] = __uint_as_float(p); }, wt);
