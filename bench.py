@@ -321,6 +321,14 @@ def parity_margins():
         return json.load(f)["groups"]["deep"]
 
 
+# The 16 stamps a layer records, in kernel order; each phase ends at its stamp.
+PHASE_NAMES = ("input_norm", "qkv_gemv", "rope_publish_kv_append", "qkv_exchange", "attention_publish",
+               "merge_exchange_publish", "attn_out_exchange", "o_proj_publish", "residual_exchange",
+               "post_norm", "router_logit_exchange", "top_k", "gate_up_swiglu_publish", "swiglu_exchange",
+               "down_publish", "residual_exchange_2")
+PHASE_STEPS = 3
+
+
 def kernel_digest():
     """sha256 (16 hex digits) over every source compiled into the persistent decode kernel."""
     import hashlib
@@ -469,30 +477,36 @@ def main():
     log(f"{K} steps: {total_ms:.2f} ms total; per-launch events: kernel mean {1e6 * mean_kern_s:.1f} us, "
         f"min {1e3 * min(kern_ms):.1f} us, max {1e3 * max(kern_ms):.1f} us")
 
-    # per-phase time per layer (workgroup 0's wall-clock stamps), one extra step at `resident`
-    kv.set_lengths([resident])
-    tok.fill_(first)
-    dbg, t = make_debug(cfg, 1, dev, logits=True, routes=False, phase_ts=True)
-    decode_step_debug(model.ctx, tok.data_ptr(), kv.handle, tok.data_ptr(), dbg)
-    sync(model.ctx)
-    ts = t["phase_ts"].cpu().numpy().astype(np.int64)
-    gpu_logits0 = t["logits"][0].cpu().numpy()
-    gpu_id0 = int(tok.item())
+    # per-phase time per layer (workgroup 0's wall-clock stamps): PHASE_STEPS extra steps, each at `resident`
     tick_us = 0.01  # 100 MHz
-    att, moe = [], []
-    prev = ts[0, 0]
-    for l in range(cfg.n_layers):
-        # stamps of layer l (kernel order): [8] residual after o_proj gathered, [15] residual after the MLP
-        row = ts[l + 1]
-        if l >= cfg.n_dense_layers:
-            att.append((row[8] - prev) * tick_us)
-            moe.append((row[15] - row[8]) * tick_us)
-        prev = row[15]
-    head_us = (ts[0, 1] - prev) * tick_us
+    att, moe, head, table = [], [], [], []
+    for rep in range(PHASE_STEPS):
+        kv.set_lengths([resident])
+        tok.fill_(first)
+        dbg, t = make_debug(cfg, 1, dev, logits=True, routes=False, phase_ts=True)
+        decode_step_debug(model.ctx, tok.data_ptr(), kv.handle, tok.data_ptr(), dbg)
+        sync(model.ctx)
+        ts = t["phase_ts"].cpu().numpy().astype(np.int64)
+        if rep == 0:
+            gpu_logits0 = t["logits"][0].cpu().numpy()
+            gpu_id0 = int(tok.item())
+        prev = ts[0, 0]
+        for l in range(min(cfg.n_layers, len(ts) - 1)):
+            # stamps of layer l (kernel order): [8] residual after o_proj gathered, [15] residual after the MLP
+            row = ts[l + 1]
+            if l >= cfg.n_dense_layers:
+                att.append((row[8] - prev) * tick_us)
+                moe.append((row[15] - row[8]) * tick_us)
+                table.append(np.diff(np.concatenate([[prev], row[:16]])) * tick_us)
+            prev = row[15]
+        head.append((ts[0, 1] - prev) * tick_us)
     phases = {"attention_us_per_layer": round(float(np.mean(att)), 2) if att else None,
               "moe_us_per_layer": round(float(np.mean(moe)), 2) if moe else None,
-              "head_us": round(float(head_us), 2), "source": "workgroup-0 s_memrealtime stamps, one step at "
-                                                             f"position {resident}"}
+              "head_us": round(float(np.mean(head)), 2),
+              "moe_layer_phases_us": ({n: round(float(v), 2) for n, v in zip(PHASE_NAMES, np.mean(table, 0))}
+                                      if table else None),
+              "source": f"workgroup-0 s_memrealtime stamps, {PHASE_STEPS} steps at position {resident}, "
+                        "mean over the MoE layers"}
     from stream_moe_decode_amd import micro
     micro_out = micro(model.ctx)  # the measurement helpers, beside the decode numbers
     model.free()
