@@ -292,7 +292,7 @@ int flint_sync(flint_ctx* ctx);
 
 /*
  * Bound every cross-workgroup wait of the persistent kernel by `microseconds`
- * (0 restores the default of one second).  The kernel's workgroups hand data to
+ * (0 restores the default of one second; bounds above 42.9 s are clamped to it).  The kernel's workgroups hand data to
  * each other through spin-waits that assume the whole grid is resident at once
  * (the condition section 2 of "Flint Inference on Apple Silicon: rec Megakernel
  * and Tempo9 Compared" notes for device-scope spin barriers); a wait that runs

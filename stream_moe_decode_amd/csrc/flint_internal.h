@@ -24,7 +24,7 @@ constexpr int NCOPY = 8;                // replicas of broadcast exchanges (one 
 constexpr int QKV_CAP = 2, O_CAP = 1, GU_CAP = 6, DN_CAP = 3, LM_CAP = 8;
 constexpr int TAGS_PER_LAUNCH = 1024;   // exchange tags one launch may use
 constexpr int STAMP_LAYERS = 56;        // layers whose phase stamps the debug output records
-constexpr uint64_t SPIN_TIMEOUT = 100000000ull;  // default wait bound: 1 s of the 100 MHz wall clock
+constexpr uint32_t SPIN_TIMEOUT = 100000000u;  // default wait bound: 1 s of the 100 MHz wall clock
 
 enum { W_F32 = 0, W_BF16 = 1, W_I4 = 2 };
 enum { ERR_TIMEOUT = 1u, ERR_TOKEN = 2u, ERR_POS = 4u };
@@ -44,7 +44,8 @@ struct KStatic {
   int qkv_rows, o_slots, h_slots;
   int poll_sleep;        // s_sleep(8) repetitions between polls of a stale slot
   int sentinels;         // slots polled by wave 0 before the bulk read (0: none, up to 64)
-  uint64_t spin_limit;   // a wait gives up after this many ticks of the 100 MHz wall clock
+  uint32_t spin_limit;   // a wait gives up after this many ticks of the 100 MHz wall clock (fills the
+                         // padding before the pointers: the fields after it keep their offsets)
   const uint8_t* embed;
   const uint8_t* lmhead;
   const float* fnorm;

@@ -90,11 +90,13 @@ struct HeadLds {                         // lm_head: two staging buffers (bf16 /
 struct Smem {
   KStatic ks;                            // the context, copied once per launch: its fields are read with
                                          // LDS loads, never with vector loads that would wait for the DMAs
-  float xres[MAX_H];                     // residual (every workgroup keeps all of it)
-  uint32_t actA[MAX_QD];                 // GEMV input: fp32 words or bf16 pairs (also the lm_head input)
-  float asumA[MAX_QD / 32];              // int4: sum of each 32-element chunk of actA
-  float gn[MAX_H];                       // weights of the next RMSNorm (DMA target)
-  float ytmp[MAX_YROWS];                 // this workgroup's GEMV results of a phase
+  // arrays read or written 16 bytes at a time start on 16-byte boundaries whatever the context's size
+  // (a misaligned 16-byte LDS access is split: one such layout doubled the o_proj phase)
+  alignas(16) float xres[MAX_H];         // residual (every workgroup keeps all of it)
+  alignas(16) uint32_t actA[MAX_QD];     // GEMV input: fp32 words or bf16 pairs (also the lm_head input)
+  alignas(16) float asumA[MAX_QD / 32];  // int4: sum of each 32-element chunk of actA
+  alignas(16) float gn[MAX_H];           // weights of the next RMSNorm (DMA target)
+  alignas(16) float ytmp[MAX_YROWS];     // this workgroup's GEMV results of a phase
   f32x2_t rcs[MAX_QPAIRS];               // RoPE (cos, sin) of this workgroup's QKV pairs at this position
   union {
     AttnLds att;
@@ -608,7 +610,7 @@ struct Waiter {
   uint32_t* herr;
   int sleep;
   int sentinels;
-  uint64_t limit;
+  uint32_t limit;
   bool abort;
 };
 __device__ __forceinline__ void backoff(const Waiter& wt) {

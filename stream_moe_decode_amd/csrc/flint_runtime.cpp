@@ -1004,7 +1004,9 @@ int flint_sync(flint_ctx* c) {
 
 int flint_set_wait_limit(flint_ctx* c, uint32_t microseconds) {
   if (!c) return fail(FLINT_EINVAL, "ctx is NULL");
-  const uint64_t ticks = microseconds ? (uint64_t)microseconds * 100u : SPIN_TIMEOUT;  // 100 MHz clock
+  // 100 MHz clock; bounds beyond 2^32 ticks (42.9 s) are clamped
+  const uint64_t t64 = microseconds ? (uint64_t)microseconds * 100u : SPIN_TIMEOUT;
+  const uint32_t ticks = t64 > 0xFFFFFFFFull ? 0xFFFFFFFFu : (uint32_t)t64;
   HIPCHECK(hipStreamSynchronize(c->stream));
   c->base.spin_limit = ticks;
   HIPCHECK(hipMemcpy(&c->kdev->spin_limit, &ticks, sizeof ticks, hipMemcpyHostToDevice));
