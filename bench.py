@@ -479,7 +479,7 @@ def main():
 
     # per-phase time per layer (workgroup 0's wall-clock stamps): PHASE_STEPS extra steps, each at `resident`
     tick_us = 0.01  # 100 MHz
-    att, moe, head, table = [], [], [], []
+    att, moe, head_us, table = [], [], [], []
     for rep in range(PHASE_STEPS):
         kv.set_lengths([resident])
         tok.fill_(first)
@@ -499,10 +499,10 @@ def main():
                 moe.append((row[15] - row[8]) * tick_us)
                 table.append(np.diff(np.concatenate([[prev], row[:16]])) * tick_us)
             prev = row[15]
-        head.append((ts[0, 1] - prev) * tick_us)
+        head_us.append((ts[0, 1] - prev) * tick_us)
     phases = {"attention_us_per_layer": round(float(np.mean(att)), 2) if att else None,
               "moe_us_per_layer": round(float(np.mean(moe)), 2) if moe else None,
-              "head_us": round(float(np.mean(head)), 2),
+              "head_us": round(float(np.mean(head_us)), 2),
               "moe_layer_phases_us": ({n: round(float(v), 2) for n, v in zip(PHASE_NAMES, np.mean(table, 0))}
                                       if table else None),
               "source": f"workgroup-0 s_memrealtime stamps, {PHASE_STEPS} steps at position {resident}, "
