@@ -52,6 +52,8 @@ template <int WT> __device__ __forceinline__ float act_round(float v) { return k
 
 // ---------------------------------------------------------------- shared memory
 
+typedef short s16x4_t __attribute__((ext_vector_type(4)));  // 4 bf16 bit patterns: a 16x16x16 MFMA operand
+
 // Weight staging in LDS: item i of wave w is 64 lanes x 16 B at w16[(i * NW + w) * 64 + lane]
 // and, for int4, the dword holding the item's scale at s32[(i * NW + w) * 64 + lane].
 template <int CAP> struct StageLds {
@@ -886,12 +888,16 @@ __global__ void __launch_bounds__(NT, 1) decode_kernel(const KStatic* __restrict
     if (!attn || t1 <= t0) return 0;
     const size_t cb = (((size_t)l * B + seq) * nkv + aj) * kvstride * ebytes;
     const int np0 = min(CHP, t1 - t0);
-    if constexpr (MFMA_QK) k_issue_mfma(sm.u.att.kbuf, kc + cb, t0, np0);
-    else kv_issue(sm.u.att.kbuf, kc + cb, t0, np0, rowb);
-    kv_issue(sm.u.att.vbuf, vc + cb, t0, np0, rowb);
+    if constexpr (MFMA_QK) {  // V rows swizzled like K: the transposing operand reads are conflict-free
+      k_issue_mfma(sm.u.att.kbuf, kc + cb, t0, np0);
+      k_issue_mfma(sm.u.att.vbuf, vc + cb, t0, np0);
+    } else {
+      kv_issue(sm.u.att.kbuf, kc + cb, t0, np0, rowb);
+      kv_issue(sm.u.att.vbuf, vc + cb, t0, np0, rowb);
+    }
     auto per_wave = [&](int n) { return n > wave ? (n - wave + NW - 1) / NW : 0; };
     const int nk = MFMA_QK ? (np0 * 16 + 63) / 64 : (np0 * rowb / 16 + 63) / 64;
-    return per_wave(nk) + per_wave((np0 * rowb / 16 + 63) / 64);
+    return 2 * per_wave(nk);
   };
   // A layer's first attention chunk (its K/V rows, the largest read of the layer) is requested right after
   // the layer's q/k/v are published: issuing it earlier stalls the issuing waves (the requests of all
@@ -1019,6 +1025,14 @@ __global__ void __launch_bounds__(NT, 1) decode_kernel(const KStatic* __restrict
       for (int h = 0; h < MAX_GQ; ++h)
 #pragma unroll
         for (int e = 0; e < DPVM; ++e) o[h][e] = 0.f;
+      // MFMA path: wave w holds O^T for dims 16 w .. 16 w + 15: lane 16 g + i has dims 16 w + 4 g + j
+      // (j = 0..3) of head i
+      f32x4_t o4 = {0.f, 0.f, 0.f, 0.f};
+      // MFMA path: the probabilities as the B operand of O^T += V^T P^T, bf16 high parts then low parts:
+      // K-step kk, lane 16 g + h, element j holds P[h][16 kk + 4 g + j] (zero past the chunk and for the
+      // heads Gq .. 15)
+      uint16_t* const pb = reinterpret_cast<uint16_t*>(at.pt);
+      constexpr int PB_HALF = MAX_CHUNK_POS / 2 / 16 * 64 * 4;  // 128 positions per chunk at head_dim 128
       if (tid < Gq) {
         at.mst[tid] = -INFINITY;
         at.lst[tid] = 0.f;
@@ -1027,9 +1041,13 @@ __global__ void __launch_bounds__(NT, 1) decode_kernel(const KStatic* __restrict
         const int np = min(CHP, t1 - c0);
         if (c0 != t0) {  // later chunks (long contexts): load now
           __syncthreads();  // every wave is done with the previous chunk
-          if constexpr (MFMA_QK) k_issue_mfma(at.kbuf, kbase, c0, np);
-          else kv_issue(at.kbuf, kbase, c0, np, rowb);
-          kv_issue(at.vbuf, vbase, c0, np, rowb);
+          if constexpr (MFMA_QK) {
+            k_issue_mfma(at.kbuf, kbase, c0, np);
+            k_issue_mfma(at.vbuf, vbase, c0, np);
+          } else {
+            kv_issue(at.kbuf, kbase, c0, np, rowb);
+            kv_issue(at.vbuf, vbase, c0, np, rowb);
+          }
         }
         wait_vmem();
         __syncthreads();
@@ -1042,12 +1060,13 @@ __global__ void __launch_bounds__(NT, 1) decode_kernel(const KStatic* __restrict
               reinterpret_cast<float*>(kr)[e] = at.kn[e];
               reinterpret_cast<float*>(vr)[e] = at.vn[e];
             } else {
-              if constexpr (MFMA_QK) {  // the row's units are swizzled by the position
+              if constexpr (MFMA_QK) {  // the rows' units are swizzled by the position
                 reinterpret_cast<uint16_t*>(at.kbuf)[k_slot(pos - c0, e >> 3) * 8 + (e & 7)] = (uint16_t)f2bf(at.kn[e]);
+                reinterpret_cast<uint16_t*>(at.vbuf)[k_slot(pos - c0, e >> 3) * 8 + (e & 7)] = (uint16_t)f2bf(at.vn[e]);
               } else {
                 reinterpret_cast<uint16_t*>(kr)[e] = (uint16_t)f2bf(at.kn[e]);
+                reinterpret_cast<uint16_t*>(vr)[e] = (uint16_t)f2bf(at.vn[e]);
               }
-              reinterpret_cast<uint16_t*>(vr)[e] = (uint16_t)f2bf(at.vn[e]);
             }
           }
           __syncthreads();
@@ -1080,6 +1099,8 @@ __global__ void __launch_bounds__(NT, 1) decode_kernel(const KStatic* __restrict
               if (n < Gq && pr < np) at.sc[n * CHP + pr] = acc[r];
             }
           }
+          // the probability operands start at zero (the softmax fills the chunk's positions of its heads)
+          for (int idx = tid; idx < 2 * PB_HALF / 8; idx += NT) reinterpret_cast<uint4*>(pb)[idx] = uint4{0u, 0u, 0u, 0u};
         } else {
         // scores: LPK lanes read one K row (16 B each), RPI rows per wave instruction
           constexpr int DPL = kAct32<WT> ? 4 : 8;  // dims per lane
@@ -1133,7 +1154,14 @@ __global__ void __launch_bounds__(NT, 1) decode_kernel(const KStatic* __restrict
           float ls = 0.f;
           for (int i = lane; i < np; i += 64) {
             const float pr = __expf(sh[i] - mn);
-            at.pt[i * PST + h] = pr;
+            if constexpr (MFMA_QK) {
+              const uint32_t hb = f2bf(pr);
+              const int idx = ((i >> 4) * 64 + ((i >> 2) & 3) * 16 + h) * 4 + (i & 3);
+              pb[idx] = (uint16_t)hb;
+              pb[PB_HALF + idx] = (uint16_t)f2bf(pr - bf2f(hb));
+            } else {
+              at.pt[i * PST + h] = pr;
+            }
             ls += pr;
           }
           ls = wave_sum(ls);
@@ -1143,9 +1171,36 @@ __global__ void __launch_bounds__(NT, 1) decode_kernel(const KStatic* __restrict
             at.lst[h] = at.lst[h] * alpha + ls;
           }
         }
-        if (Gq < PST)  // padding heads of pt stay zero
+        if (!MFMA_QK && Gq < PST)  // padding heads of pt stay zero
           for (int i = tid; i < np * (PST - Gq); i += NT) at.pt[(i / (PST - Gq)) * PST + Gq + i % (PST - Gq)] = 0.f;
         __syncthreads();
+        if constexpr (MFMA_QK) {
+          // O^T += V^T P^T on v_mfma_f32_16x16x16_bf16 (P as bf16 high and low parts): the A operand (16 dims
+          // x 16 positions) comes from the swizzled V rows through the transposing LDS read, this lane
+          // passing position 16 kk + 4 g + i / 4, dims 16 w + 4 (i % 4) .. + 3
+          const int g = lane >> 4, i = lane & 15;
+          const float f = i < Gq ? at.fac[i] : 0.f;
+#pragma unroll
+          for (int j = 0; j < 4; ++j) o4[j] *= f;
+          const uint8_t* vlb = reinterpret_cast<const uint8_t*>(at.vbuf);
+          const int u = 2 * wave + ((i & 3) >> 1);
+          const int nk = (np + 15) / 16;
+          for (int kk = 0; kk < nk; ++kk) {
+            const int row = 16 * kk + 4 * g + (i >> 2);
+            s16x4_t vt = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (__attribute__((address_space(3))) s16x4_t*)(vlb + row * 256 + ((u ^ (row & 15)) * 16) + (i & 1) * 8));
+            if (16 * kk + 16 > np) {  // rows past the chunk may hold anything: their zero probabilities
+#pragma unroll                      // must not meet a NaN
+              for (int j = 0; j < 4; ++j)
+                if (16 * kk + 4 * g + j >= np) vt[j] = 0;
+            }
+            const s16x4_t ph = *reinterpret_cast<const s16x4_t*>(pb + (kk * 64 + lane) * 4);
+            const s16x4_t pl = *reinterpret_cast<const s16x4_t*>(pb + PB_HALF + (kk * 64 + lane) * 4);
+            o4 = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vt, ph, o4, 0, 0, 0);
+            o4 = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vt, pl, o4, 0, 0, 0);
+          }
+          continue;
+        }
         // P.V: wave w takes positions w, w + NW, ...; all heads at once
 #pragma unroll
         for (int h = 0; h < MAX_GQ; ++h) {
@@ -1201,12 +1256,19 @@ __global__ void __launch_bounds__(NT, 1) decode_kernel(const KStatic* __restrict
       // sum the waves' outputs (the K rows are dead: their buffer holds the partial sums)
       float* red = reinterpret_cast<float*>(at.kbuf);
       __syncthreads();
+      if constexpr (MFMA_QK) {  // each wave holds whole dims: no sum over waves
+        const int g = lane >> 4, i = lane & 15;
+        if (i < Gq)
 #pragma unroll
-      for (int h = 0; h < MAX_GQ; ++h)
-        if (h < Gq)
+          for (int j = 0; j < 4; ++j) red[i * hd + 16 * wave + 4 * g + j] = o4[j];
+      } else {
 #pragma unroll
-          for (int e = 0; e < DPVM; ++e)
-            if (e < DPV) red[(wave * MAX_GQ + h) * hd + lane * DPV + e] = o[h][e];
+        for (int h = 0; h < MAX_GQ; ++h)
+          if (h < Gq)
+#pragma unroll
+            for (int e = 0; e < DPVM; ++e)
+              if (e < DPV) red[(wave * MAX_GQ + h) * hd + lane * DPV + e] = o[h][e];
+      }
       __syncthreads();
       // publish (m, l, o) of each head of this split, contiguous: slot ((split * Gq + h) * (hd + 2) + field)
       // of the kv head's block; every slot is tagged
@@ -1214,8 +1276,12 @@ __global__ void __launch_bounds__(NT, 1) decode_kernel(const KStatic* __restrict
       for (int idx = tid; idx < Gq * hd; idx += NT) {
         const int h = idx / hd, e = idx % hd;
         float t = 0.f;
+        if constexpr (MFMA_QK) {
+          t = red[h * hd + e];
+        } else {
 #pragma unroll
-        for (int w = 0; w < NW; ++w) t += red[(w * MAX_GQ + h) * hd + e];
+          for (int w = 0; w < NW; ++w) t += red[(w * MAX_GQ + h) * hd + e];
+        }
         xstore(dst + (size_t)h * (hd + 2) + 2 + e, slot(tag + 1, __float_as_uint(t)));
       }
       if (tid < 2 * Gq) {
