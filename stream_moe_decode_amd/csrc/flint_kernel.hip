@@ -1033,6 +1033,10 @@ __global__ void __launch_bounds__(NT, 1) decode_kernel(const KStatic* __restrict
       // heads Gq .. 15)
       uint16_t* const pb = reinterpret_cast<uint16_t*>(at.pt);
       constexpr int PB_HALF = MAX_CHUNK_POS / 2 / 16 * 64 * 4;  // 128 positions per chunk at head_dim 128
+      float* const bmax = at.sc;                 // MFMA path: [wave][head] block maxima, then block sums
+      float* const bsum = at.sc + NW * MAX_GQ;
+      float sv[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};  // MFMA path: this lane's scores of the chunk
+      float alpha_r = 0.f;                       // MFMA path: rescale of the running output for head lane % 16
       if (tid < Gq) {
         at.mst[tid] = -INFINITY;
         at.lst[tid] = 0.f;
@@ -1083,8 +1087,13 @@ __global__ void __launch_bounds__(NT, 1) decode_kernel(const KStatic* __restrict
             qh[sk] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(&at.qop[0][(sk * 64 + lane) * 8]));
             ql[sk] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(&at.qop[1][(sk * 64 + lane) * 8]));
           }
-          const int nb = (np + 15) / 16;
-          for (int b = wave; b < nb; b += NW) {
+          // a chunk holds at most 128 positions here: wave w scores block w of 16 positions and keeps them in
+          // registers (-inf for positions past the chunk and heads past Gq); each block's maximum per head
+          // meets the others' in LDS
+          const int b = wave;
+#pragma unroll
+          for (int r = 0; r < 4; ++r) sv[r] = -INFINITY;
+          if (b * 16 < np) {
             f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int sk = 0; sk < 4; ++sk) {
@@ -1094,13 +1103,12 @@ __global__ void __launch_bounds__(NT, 1) decode_kernel(const KStatic* __restrict
               acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, ql[sk], acc, 0, 0, 0);
             }
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-              const int pr = b * 16 + (lane >> 4) * 4 + r;
-              if (n < Gq && pr < np) at.sc[n * CHP + pr] = acc[r];
-            }
+            for (int r = 0; r < 4; ++r) sv[r] = (n < Gq && b * 16 + (lane >> 4) * 4 + r < np) ? acc[r] : -INFINITY;
           }
-          // the probability operands start at zero (the softmax fills the chunk's positions of its heads)
-          for (int idx = tid; idx < 2 * PB_HALF / 8; idx += NT) reinterpret_cast<uint4*>(pb)[idx] = uint4{0u, 0u, 0u, 0u};
+          float bm = fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3]));
+          bm = fmaxf(bm, swap16(bm));
+          bm = fmaxf(bm, swap32(bm));
+          if (lane < Gq) bmax[wave * MAX_GQ + lane] = bm;
         } else {
         // scores: LPK lanes read one K row (16 B each), RPI rows per wave instruction
           constexpr int DPL = kAct32<WT> ? 4 : 8;  // dims per lane
@@ -1142,8 +1150,45 @@ __global__ void __launch_bounds__(NT, 1) decode_kernel(const KStatic* __restrict
           }
         }
         __syncthreads();
+        if constexpr (MFMA_QK) {
+          // softmax from the registers: every wave finds each head's maximum over the blocks, writes its
+          // block's probabilities as the B operand of the P.V below (lane 16 g + i, K-step = block, element r:
+          // P[i][16 b + 4 g + r], bf16 high and low parts) and its block's sum per head
+          const int i = lane & 15;
+          float mc = -INFINITY;
+#pragma unroll
+          for (int w = 0; w < NW; ++w) mc = fmaxf(mc, bmax[w * MAX_GQ + (i < Gq ? i : 0)]);
+          const float mo = i < Gq ? at.mst[i] : -INFINITY;
+          const float mn = fmaxf(mo, mc);
+          alpha_r = mo == -INFINITY ? 0.f : __expf(mo - mn);
+          float ls = 0.f;
+          if (wave * 16 < np) {
+            s16x4_t ph, pl;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+              const float pr = i < Gq ? __expf(sv[r] - mn) : 0.f;
+              const uint32_t hb = f2bf(pr);
+              ph[r] = (short)hb;
+              pl[r] = (short)f2bf(pr - bf2f(hb));
+              ls += pr;
+            }
+            *reinterpret_cast<s16x4_t*>(pb + (wave * 64 + lane) * 4) = ph;
+            *reinterpret_cast<s16x4_t*>(pb + PB_HALF + (wave * 64 + lane) * 4) = pl;
+          }
+          ls += swap16(ls);
+          ls += swap32(ls);
+          if (lane < Gq) bsum[wave * MAX_GQ + lane] = ls;
+          __syncthreads();
+          if (tid < Gq) {  // the running maximum and sum of head tid (lane tid of wave 0 holds its values)
+            float t = 0.f;
+#pragma unroll
+            for (int w = 0; w < NW; ++w) t += bsum[w * MAX_GQ + tid];
+            at.mst[tid] = mn;
+            at.lst[tid] = at.lst[tid] * alpha_r + t;
+          }
+        }
         // softmax, one wave per head: probabilities to pt, the running max / sum and rescale factor to LDS
-        for (int h = wave; h < Gq; h += NW) {
+        for (int h = wave; !MFMA_QK && h < Gq; h += NW) {
           const float* sh = at.sc + h * CHP;
           float mc = -INFINITY;
           for (int i = lane; i < np; i += 64) mc = fmaxf(mc, sh[i]);
@@ -1173,15 +1218,14 @@ __global__ void __launch_bounds__(NT, 1) decode_kernel(const KStatic* __restrict
         }
         if (!MFMA_QK && Gq < PST)  // padding heads of pt stay zero
           for (int i = tid; i < np * (PST - Gq); i += NT) at.pt[(i / (PST - Gq)) * PST + Gq + i % (PST - Gq)] = 0.f;
-        __syncthreads();
+        if (!MFMA_QK) __syncthreads();
         if constexpr (MFMA_QK) {
           // O^T += V^T P^T on v_mfma_f32_16x16x16_bf16 (P as bf16 high and low parts): the A operand (16 dims
           // x 16 positions) comes from the swizzled V rows through the transposing LDS read, this lane
           // passing position 16 kk + 4 g + i / 4, dims 16 w + 4 (i % 4) .. + 3
           const int g = lane >> 4, i = lane & 15;
-          const float f = i < Gq ? at.fac[i] : 0.f;
 #pragma unroll
-          for (int j = 0; j < 4; ++j) o4[j] *= f;
+          for (int j = 0; j < 4; ++j) o4[j] *= alpha_r;
           const uint8_t* vlb = reinterpret_cast<const uint8_t*>(at.vbuf);
           const int u = 2 * wave + ((i & 3) >> 1);
           const int nk = (np + 15) / 16;
