@@ -1229,19 +1229,31 @@ __global__ void __launch_bounds__(NT, 1) decode_kernel(const KStatic* __restrict
           const uint8_t* vlb = reinterpret_cast<const uint8_t*>(at.vbuf);
           const int u = 2 * wave + ((i & 3) >> 1);
           const int nk = (np + 15) / 16;
-          for (int kk = 0; kk < nk; ++kk) {
-            const int row = 16 * kk + 4 * g + (i >> 2);
-            s16x4_t vt = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                (__attribute__((address_space(3))) s16x4_t*)(vlb + row * 256 + ((u ^ (row & 15)) * 16) + (i & 1) * 8));
-            if (16 * kk + 16 > np) {  // rows past the chunk may hold anything: their zero probabilities
-#pragma unroll                      // must not meet a NaN
-              for (int j = 0; j < 4; ++j)
-                if (16 * kk + 4 * g + j >= np) vt[j] = 0;
+          // four K-steps at a time: their operand reads are issued together, then their products
+          for (int k0 = 0; k0 < nk; k0 += 4) {
+            s16x4_t vt[4], ph[4], pl[4];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+              const int kk = min(k0 + q, nk - 1);  // past the last K-step: a repeated read, not used
+              const int row = 16 * kk + 4 * g + (i >> 2);
+              vt[q] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                  (__attribute__((address_space(3))) s16x4_t*)(vlb + row * 256 + ((u ^ (row & 15)) * 16) + (i & 1) * 8));
+              ph[q] = *reinterpret_cast<const s16x4_t*>(pb + (kk * 64 + lane) * 4);
+              pl[q] = *reinterpret_cast<const s16x4_t*>(pb + PB_HALF + (kk * 64 + lane) * 4);
             }
-            const s16x4_t ph = *reinterpret_cast<const s16x4_t*>(pb + (kk * 64 + lane) * 4);
-            const s16x4_t pl = *reinterpret_cast<const s16x4_t*>(pb + PB_HALF + (kk * 64 + lane) * 4);
-            o4 = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vt, ph, o4, 0, 0, 0);
-            o4 = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vt, pl, o4, 0, 0, 0);
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+              const int kk = k0 + q;
+              if (kk < nk) {
+                if (16 * kk + 16 > np) {  // rows past the chunk may hold anything: their zero probabilities
+#pragma unroll                            // must not meet a NaN
+                  for (int j = 0; j < 4; ++j)
+                    if (16 * kk + 4 * g + j >= np) vt[q][j] = 0;
+                }
+                o4 = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vt[q], ph[q], o4, 0, 0, 0);
+                o4 = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vt[q], pl[q], o4, 0, 0, 0);
+              }
+            }
           }
           continue;
         }
