@@ -61,10 +61,13 @@ def test_tiny_bf16_and_int4_variants():
         _greedy(cfg)
 
 
-def test_moe_layer_bf16_one_step():
-    # one MoE layer at full width over 1,024 resident positions: the layer's output residual against the
-    # oracle's at 2e-2 (end to end) and at the per-layer bound, routes, logits
-    cfg = synth.CONFIGS["moe_layer"]
+@pytest.mark.parametrize("resident", [1024, 9000, 16383])
+def test_moe_layer_bf16_one_step(resident):
+    # one MoE layer at full width over the resident positions: the layer's output residual against the
+    # oracle's at 2e-2 (end to end) and at the per-layer bound, routes, logits.  The attention splits of
+    # 64 per kv head take 1,025 positions as one chunk each, 9,001 as two chunks of which the second is
+    # ragged, and 16,384 as two whole chunks of 128 (the online softmax carried across chunks)
+    cfg = synth.CONFIGS["moe_layer"].replace(resident=resident)
     model = build(cfg)
     cap = cfg.resident + 8
     kv = model.kv(1, cap)
