@@ -143,6 +143,19 @@ template <int WT> __device__ __forceinline__ void act_put(uint32_t* act, int e, 
     reinterpret_cast<uint16_t*>(act)[p] = (uint16_t)f2bf(v);
   }
 }
+// Elements e, e + 1 (e even) given as a pair of bf16 bit patterns (low half first), stored as they are:
+// in the int4 layout element e + 1 sits two halfwords after element e.
+template <int WT> __device__ __forceinline__ void act_put2_bits(uint32_t* act, int e, uint32_t bits) {
+  static_assert(!kAct32<WT>, "bf16 inputs only");
+  if constexpr (WT == W_I4) {
+    const int p = (e >> 5) * (2 * kChunkWords<WT>) + ((e & 24) | ((e & 3) << 1) | ((e >> 2) & 1));
+    uint16_t* const a16 = reinterpret_cast<uint16_t*>(act);
+    a16[p] = (uint16_t)(bits & 0xFFFFu);
+    a16[p + 2] = (uint16_t)(bits >> 16);
+  } else {
+    act[e >> 1] = bits;
+  }
+}
 // After act_put of n elements (and a barrier): chunk sums for the int4 bias.
 template <int WT> __device__ __forceinline__ void act_sums(const uint32_t* act, float* asum, int n) {
   if constexpr (WT == W_I4) {
@@ -1356,6 +1369,9 @@ __global__ void __launch_bounds__(NT, 1) decode_kernel(const KStatic* __restrict
 
     // ---------------- merge the splits: this workgroup's pairs of output dims
     {
+      constexpr int MNF = SS ? 2 + 2 * (SH::NQ * SH::HD / 2 / SH::G) : 1;  // fields gathered per split
+      static_assert(!SS || ((SH::NQ * SH::HD / 2) % SH::G == 0 && (SH::HD / 2) % ((MNF - 2) / 2) == 0),
+                    "the static shape merges whole runs of dims inside one head");
       const int pb = mpb, pe = mpe;
       const uint64_t* srcp = x_part + (size_t)par * nq * (hd + 2) * S;
       int e0 = 2 * pb;
@@ -1368,7 +1384,9 @@ __global__ void __launch_bounds__(NT, 1) decode_kernel(const KStatic* __restrict
         ok = gather(
             sm, srcp, n, tag + 1,
             [&](int i) {
-              const int sp = div_small(i, nf, inv_nf), f = i - sp * nf;
+              // the static shape: every workgroup merges one whole run of MNF - 2 dims of one head, so the
+              // field count is a constant and the division a multiply
+              const int sp = SS ? i / MNF : div_small(i, nf, inv_nf), f = i - sp * nf;
               return hblk + (size_t)sp * Gq * (hd + 2) + (f < 2 ? f : 2 + eh0 + (f - 2));
             },
             [=](int k, int m) { return (((k + 1) * S) / m - 1) * nf; }, S < 64 ? S : 64,  // m fields
@@ -1422,8 +1440,7 @@ __global__ void __launch_bounds__(NT, 1) decode_kernel(const KStatic* __restrict
                        if constexpr (kAct32<WT>) {
                          act_put<WT>(sm.actA, i, __uint_as_float(p));
                        } else {
-                         act_put<WT>(sm.actA, 2 * i, bf2f(p & 0xFFFF));
-                         act_put<WT>(sm.actA, 2 * i + 1, bf2f(p >> 16));
+                         act_put2_bits<WT>(sm.actA, 2 * i, p);
                        }
                      },
                      wt);
@@ -1631,8 +1648,7 @@ __global__ void __launch_bounds__(NT, 1) decode_kernel(const KStatic* __restrict
                        if constexpr (kAct32<WT>) {
                          act_put<WT>(sm.u.mlp.hbuf, i, __uint_as_float(p));
                        } else {
-                         act_put<WT>(sm.u.mlp.hbuf, 2 * i, bf2f(p & 0xFFFF));
-                         act_put<WT>(sm.u.mlp.hbuf, 2 * i + 1, bf2f(p >> 16));
+                         act_put2_bits<WT>(sm.u.mlp.hbuf, 2 * i, p);
                        }
                      },
                      wt);
