@@ -280,11 +280,16 @@ int flint_prefill_chunk(flint_ctx* ctx, flint_kv* kv, int32_t seq, const int32_t
  *    tagged system-scope slots written in 8 replicas (one per XCD) and read
  *    all at once, as the decode kernel hands data between workgroups;
  *    FLINT_ETIMEOUT if a bounded wait ran out;
+ *  - flint_micro_exchange_xcd: the same round confined to each XCD: workgroup
+ *    w exchanges with the workgroups of its XCD only (w mod 8, where the
+ *    dispatcher places it), through device-scope slots that stay in that
+ *    XCD's L2; `workgroups` a multiple of 8, at least 16;
  *  - flint_micro_launch: microseconds per back-to-back empty kernel launch.
  * Errors: FLINT_EINVAL, FLINT_ENOMEM, FLINT_EHIP (and FLINT_ETIMEOUT above).
  */
 int flint_micro_stream_read(flint_ctx* ctx, size_t bytes, int32_t reps, float* gbps);
 int flint_micro_exchange(flint_ctx* ctx, int32_t workgroups, int32_t rounds, float* us_per_round);
+int flint_micro_exchange_xcd(flint_ctx* ctx, int32_t workgroups, int32_t rounds, float* us_per_round);
 int flint_micro_launch(flint_ctx* ctx, int32_t launches, float* us_per_launch);
 
 /* Wait for the ctx stream; report and clear a latched device error. */

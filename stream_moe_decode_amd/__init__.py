@@ -26,7 +26,7 @@ STATUS_NAMES = {0: "FLINT_OK", 1: "FLINT_EINVAL", 2: "FLINT_ENOMEM", 3: "FLINT_E
 EXPORTS = ("flint_decode_init", "flint_decode_free", "flint_kv_alloc", "flint_kv_free", "flint_kv_set_lengths",
            "flint_kv_get_lengths", "flint_kv_tokens", "flint_kv_prefix_match", "flint_kv_layer_ptrs",
            "flint_decode_step", "flint_decode_step_seqs", "flint_decode_step_noalloc",
-           "flint_decode_step_debug", "flint_prefill_chunk", "flint_micro_stream_read", "flint_micro_exchange",
+           "flint_decode_step_debug", "flint_prefill_chunk", "flint_micro_stream_read", "flint_micro_exchange", "flint_micro_exchange_xcd",
            "flint_micro_launch", "flint_sync", "flint_set_wait_limit", "flint_device_info", "flint_last_error")
 
 
@@ -91,6 +91,7 @@ def lib():
             "flint_prefill_chunk": [vp, vp, i32, vp, i32, vp],
             "flint_micro_stream_read": [vp, ctypes.c_size_t, i32, P(ctypes.c_float)],
             "flint_micro_exchange": [vp, i32, i32, P(ctypes.c_float)],
+            "flint_micro_exchange_xcd": [vp, i32, i32, P(ctypes.c_float)],
             "flint_micro_launch": [vp, i32, P(ctypes.c_float)],
             "flint_sync": [vp],
             "flint_set_wait_limit": [vp, ctypes.c_uint32],
@@ -179,13 +180,16 @@ def kv_prefix_match(kv: int, seq: int, tokens) -> int:
 
 def micro(ctx: int) -> dict:
     """The measurement helpers: stream-read GB/s (1 GiB, 10 reads), exchange us per round at 64 / 128 / 256
-    workgroups (1,000 rounds), empty-launch us (1,000 launches)."""
+    workgroups (1,000 rounds), the same round confined to each XCD at 256 workgroups, empty-launch us (1,000
+    launches)."""
     L, f = lib(), ctypes.c_float()
     _check(L.flint_micro_stream_read(ctx, 1 << 30, 10, ctypes.byref(f)))
     out = {"stream_read_gbs": round(f.value, 1), "exchange_us_per_round": {}}
     for g in (64, 128, 256):
         _check(L.flint_micro_exchange(ctx, g, 1000, ctypes.byref(f)))
         out["exchange_us_per_round"][str(g)] = round(f.value, 3)
+    _check(L.flint_micro_exchange_xcd(ctx, 256, 1000, ctypes.byref(f)))
+    out["exchange_xcd_us_per_round"] = {"256": round(f.value, 3)}
     _check(L.flint_micro_launch(ctx, 1000, ctypes.byref(f)))
     out["empty_launch_us"] = round(f.value, 3)
     return out

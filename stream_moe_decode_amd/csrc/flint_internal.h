@@ -171,7 +171,8 @@ size_t prefill_part_floats(int nq, int nsmax, int hd);
 
 // Measurement helpers (flint_micro.hip).
 hipError_t launch_micro_read(const void* p, size_t bytes, uint32_t* sink, int blocks, hipStream_t st);
-hipError_t launch_micro_exchange(unsigned long long* slots, int workgroups, int rounds, uint32_t* err, hipStream_t st);
+hipError_t launch_micro_exchange(unsigned long long* slots, int workgroups, int rounds, uint32_t* err, hipStream_t st,
+                                 bool xcd);
 hipError_t launch_micro_empty(hipStream_t st);
 // s4[((r / 4) * G + g) * 4 + r % 4] = s[r * G + g] for r < rows (a multiple of 4), g < G.
 hipError_t launch_regroup_scales(const uint16_t* s, uint16_t* s4, size_t rows, int G, hipStream_t stream);

@@ -57,6 +57,33 @@ __global__ void __launch_bounds__(256) micro_exchange(unsigned long long* slots,
   }
 }
 
+// The same round confined to each XCD: workgroup W belongs to group W % 8 (the XCD the dispatcher places
+// it on), writes one slot of its group with a device-scope store (it stays in the XCD's L2) and polls the
+// G / 8 slots of its group with device-scope loads.
+__global__ void __launch_bounds__(256) micro_exchange_xcd(unsigned long long* slots, int rounds, uint32_t* err) {
+  __shared__ int bad;
+  const int W = blockIdx.x, G = gridDim.x, tid = threadIdx.x;
+  unsigned long long* const grp = slots + (size_t)(W % NCOPY) * G;
+  if (tid == 0) bad = 0;
+  __syncthreads();
+  for (int r = 1; r <= rounds; ++r) {
+    if (tid == 0)
+      __hip_atomic_store(gp(grp) + W, ((unsigned long long)r << 32) | (unsigned)W, __ATOMIC_RELAXED,
+                         __HIP_MEMORY_SCOPE_AGENT);
+    for (int s = W % NCOPY + NCOPY * tid; s < G; s += NCOPY * 256) {
+      int polls = 0;
+      while ((int)(__hip_atomic_load(gp(grp) + s, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >> 32) < r)
+        if (++polls > (1 << 20)) {
+          __hip_atomic_fetch_or(gp(err), 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+          bad = 1;
+          break;
+        }
+    }
+    __syncthreads();
+    if (bad) return;
+  }
+}
+
 __global__ void micro_empty() {}
 
 }  // namespace
@@ -66,8 +93,12 @@ hipError_t launch_micro_read(const void* p, size_t bytes, uint32_t* sink, int bl
   hipLaunchKernelGGL(micro_read, dim3(blocks), dim3(256), 0, st, (const uint8_t*)p, per, sink);
   return hipGetLastError();
 }
-hipError_t launch_micro_exchange(unsigned long long* slots, int workgroups, int rounds, uint32_t* err, hipStream_t st) {
-  hipLaunchKernelGGL(micro_exchange, dim3(workgroups), dim3(256), 0, st, slots, rounds, err);
+hipError_t launch_micro_exchange(unsigned long long* slots, int workgroups, int rounds, uint32_t* err, hipStream_t st,
+                                 bool xcd) {
+  if (xcd)
+    hipLaunchKernelGGL(micro_exchange_xcd, dim3(workgroups), dim3(256), 0, st, slots, rounds, err);
+  else
+    hipLaunchKernelGGL(micro_exchange, dim3(workgroups), dim3(256), 0, st, slots, rounds, err);
   return hipGetLastError();
 }
 hipError_t launch_micro_empty(hipStream_t st) {

@@ -944,12 +944,15 @@ int flint_micro_stream_read(flint_ctx* c, size_t bytes, int32_t reps, float* gbp
   return FLINT_OK;
 }
 
-int flint_micro_exchange(flint_ctx* c, int32_t workgroups, int32_t rounds, float* us_per_round) {
+namespace {
+int micro_exchange(flint_ctx* c, int32_t workgroups, int32_t rounds, float* us_per_round, bool xcd) {
   if (!c || !us_per_round) return fail(FLINT_EINVAL, "NULL argument");
   hipDeviceProp_t prop;
   HIPCHECK(hipGetDeviceProperties(&prop, c->device));
   if (workgroups < 2 || workgroups > prop.multiProcessorCount || rounds < 1)
     return fail(FLINT_EINVAL, "workgroups %d not in [2, %d] or rounds %d < 1", workgroups, prop.multiProcessorCount, rounds);
+  if (xcd && (workgroups % NCOPY != 0 || workgroups < 2 * NCOPY))
+    return fail(FLINT_EINVAL, "workgroups %d: a multiple of %d, at least %d", workgroups, NCOPY, 2 * NCOPY);
   void* mem = nullptr;
   const size_t bytes = 8 * (size_t)NCOPY * workgroups + 64;  // NCOPY replicas of the slots, then the error word
   if (hipMalloc(&mem, bytes) != hipSuccess) return fail(FLINT_ENOMEM, "exchange slots");
@@ -962,7 +965,7 @@ int flint_micro_exchange(flint_ctx* c, int32_t workgroups, int32_t rounds, float
   if (e == hipSuccess) e = hipEventCreate(&e1);
   if (e == hipSuccess) e = hipMemsetAsync(mem, 0, bytes, c->stream);
   if (e == hipSuccess) e = hipEventRecord(e0, c->stream);
-  if (e == hipSuccess) e = launch_micro_exchange(slots, workgroups, rounds, err, c->stream);
+  if (e == hipSuccess) e = launch_micro_exchange(slots, workgroups, rounds, err, c->stream, xcd);
   if (e == hipSuccess) e = hipEventRecord(e1, c->stream);
   if (e == hipSuccess) e = hipEventSynchronize(e1);
   if (e == hipSuccess) e = hipEventElapsedTime(&ms, e0, e1);
@@ -974,6 +977,15 @@ int flint_micro_exchange(flint_ctx* c, int32_t workgroups, int32_t rounds, float
   if (herr) return fail(FLINT_ETIMEOUT, "exchange: a wait exceeded its bound");
   *us_per_round = ms * 1e3f / rounds;
   return FLINT_OK;
+}
+}  // namespace
+
+int flint_micro_exchange(flint_ctx* c, int32_t workgroups, int32_t rounds, float* us_per_round) {
+  return micro_exchange(c, workgroups, rounds, us_per_round, false);
+}
+
+int flint_micro_exchange_xcd(flint_ctx* c, int32_t workgroups, int32_t rounds, float* us_per_round) {
+  return micro_exchange(c, workgroups, rounds, us_per_round, true);
 }
 
 int flint_micro_launch(flint_ctx* c, int32_t launches, float* us_per_launch) {

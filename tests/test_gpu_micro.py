@@ -14,7 +14,7 @@ def test_micro_helpers():
     m = micro(model.ctx)
     print("micro", m)
     assert 500.0 < m["stream_read_gbs"] < 8000.0  # below the 8 TB/s peak
-    for g, us in m["exchange_us_per_round"].items():
+    for g, us in list(m["exchange_us_per_round"].items()) + list(m["exchange_xcd_us_per_round"].items()):
         assert 0.0 < us < 100.0, (g, us)
     assert 0.0 < m["empty_launch_us"] < 100.0
     model.free()
