@@ -87,6 +87,14 @@ __device__ __forceinline__ void dma16(const void* g, void* l) {
   __builtin_amdgcn_global_load_lds(g, (lds_void*)l, 16, 0, 0);
 }
 __device__ __forceinline__ void dma4(const void* g, void* l) { __builtin_amdgcn_global_load_lds(g, (lds_void*)l, 4, 0, 0); }
+// The same 16-byte request written as inline assembly, so that the compiler does not see it: the compiler
+// cannot tell which LDS a request writes, and after one it makes every later LDS access wait for all
+// outstanding requests.  The caller waits for this one itself (vmcnt) before anything reads its bytes.
+// M0 (the LDS address) is an input the compiler sets; one wait state separates that write from the request.
+__device__ __forceinline__ void dma16_untracked(const void* g, void* l) {
+  const uint32_t m = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_void*)l);
+  asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off" : : "v"(g), "{m0}"(m) : "memory");
+}
 
 template <int WT> constexpr bool kAct32 = (WT == W_F32);
 template <int WT> constexpr int kChunkElems = WT == W_F32 ? 4 : (WT == W_BF16 ? 8 : 32);
@@ -249,13 +257,15 @@ __device__ __forceinline__ void kv_issue(uint4* buf, const uint8_t* base, int c0
 // swizzle makes the MFMA operand reads (16 rows, one unit each) conflict-free.
 // Rows past the end repeat the last one.
 __device__ __forceinline__ int k_slot(int p, int u) { return p * 16 + (u ^ (p & 15)); }
+template <bool UNTRACKED = false>
 __device__ __forceinline__ void k_issue_mfma(uint4* buf, const uint8_t* base, int c0, int np) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int ni = (np * 16 + 63) / 64;
   for (int gi = wave; gi < ni; gi += NW) {
     const int sl = gi * 64 + lane, p = sl >> 4, pr = min(p, np - 1);
     const int u = (sl & 15) ^ (p & 15);
-    dma16(base + (size_t)(c0 + pr) * 256 + u * 16, &buf[gi * 64]);
+    if constexpr (UNTRACKED) dma16_untracked(base + (size_t)(c0 + pr) * 256 + u * 16, &buf[gi * 64]);
+    else dma16(base + (size_t)(c0 + pr) * 256 + u * 16, &buf[gi * 64]);
   }
 }
 

@@ -893,33 +893,34 @@ __global__ void __launch_bounds__(NT, 1) decode_kernel(const KStatic* __restrict
   const int dpb = part(DI_ / 2, G, W), dpe = part(DI_ / 2, G, W + 1);  // dense SwiGLU pairs
   const int xpb = part(K_ * EI_ / 2, G, W), xpe = part(K_ * EI_ / 2, G, W + 1);  // expert pairs
   const float inv_ei = 1.0f / (float)EI_, inv_k = 1.0f / (float)K_;
-  // QKV weights of layer l and the first attention chunk of layer l (into the shared region); the chunk's
-  // issue returns the number of DMA instructions this wave issued (waits that need only earlier loads
-  // leave them in flight)
+  // QKV weights of layer l and the K and / or V rows of its first attention chunk (into the shared region)
   auto issue_qkv = [&](int l) { issue_auto<WT, NI_QKV, QKV_CAP>(lstage(sm.u.att.sq), gq, qkv_rowfn(l)); };
-  auto issue_kv_front = [&](int l) -> int {
-    if (!attn || t1 <= t0) return 0;
+  auto issue_kv_front = [&](int l, bool k, bool v) {
+    if (!attn || t1 <= t0) return;
     const size_t cb = (((size_t)l * B + seq) * nkv + aj) * kvstride * ebytes;
     const int np0 = min(CHP, t1 - t0);
     if constexpr (MFMA_QK) {  // V rows swizzled like K: the transposing operand reads are conflict-free
-      k_issue_mfma(sm.u.att.kbuf, kc + cb, t0, np0);
-      k_issue_mfma(sm.u.att.vbuf, vc + cb, t0, np0);
+      if (k) k_issue_mfma(sm.u.att.kbuf, kc + cb, t0, np0);
+      if (v) k_issue_mfma(sm.u.att.vbuf, vc + cb, t0, np0);
     } else {
-      kv_issue(sm.u.att.kbuf, kc + cb, t0, np0, rowb);
-      kv_issue(sm.u.att.vbuf, vc + cb, t0, np0, rowb);
+      if (k) kv_issue(sm.u.att.kbuf, kc + cb, t0, np0, rowb);
+      if (v) kv_issue(sm.u.att.vbuf, vc + cb, t0, np0, rowb);
     }
-    auto per_wave = [&](int n) { return n > wave ? (n - wave + NW - 1) / NW : 0; };
-    const int nk = MFMA_QK ? (np0 * 16 + 63) / 64 : (np0 * rowb / 16 + 63) / 64;
-    return 2 * per_wave(nk);
   };
-  // A layer's first attention chunk (its K/V rows, the largest read of the layer) is requested right after
-  // the layer's q/k/v are published: issuing it earlier stalls the issuing waves (the requests of all
-  // workgroups take the chip ~2.7 us to serve at 8,022 positions) ahead of the norm and the QKV rows, which
-  // do not need it; the q/k/v exchange's polls then complete behind it, when the attention needs both.
+  // The MoE layers' down products request the K rows of the next layer's first chunk (their LDS overlaps
+  // only the gate/up staging, dead by then) without the compiler seeing the requests, so that the
+  // products' LDS reads do not wait for them: the chip serves them while the products run, and only the
+  // V rows (over the down staging) and the QKV rows wait for the products to end.  The attention waits
+  // for every request (vmcnt(0)) before it reads a chunk.
+  static_assert(offsetof(AttnLds, kbuf) + sizeof(AttnLds::kbuf) <= sizeof(StageLds<GU_CAP>) &&
+                    offsetof(MlpLds, gu) == 0,
+                "the K rows overlap only the gate/up staging");
+  // Elsewhere a layer's first attention chunk is requested at the end of the layer before, ahead of the
+  // residual exchange's polls; every wait that follows is a full one (no later loads left in flight).
   const int kv_later = 0;
 
   issue_qkv(0);
-  issue_kv_front(0);
+  issue_kv_front(0, true, true);
   gn_issue(sm, p_anorm, H);
   for (int e = tid; e < H; e += NT) {  // embedding row -> residual
     if constexpr (kAct32<WT>)
@@ -946,6 +947,7 @@ __global__ void __launch_bounds__(NT, 1) decode_kernel(const KStatic* __restrict
     const uint8_t* const vbase = vc + cbase * ebytes;
     const bool dense = l < ks.n_dense;
     const int lmoe = l - ks.n_dense;
+    bool front_early = false;  // the next layer's K rows were requested during the down products
 
     // ---------------- input RMSNorm (recomputed by every workgroup)
     rmsnorm_act<WT>(sm, H, ks.eps, ASUM_A, kv_later);
@@ -1664,6 +1666,13 @@ __global__ void __launch_bounds__(NT, 1) decode_kernel(const KStatic* __restrict
       auto out = [&](int q, float v) { sm.ytmp[q] = v; };
       if constexpr (NI_DNM > 0 && NI_DNM <= DN_CAP) {
         wait_vmem();
+        if constexpr (MFMA_QK) {
+          if (l + 1 < L && attn && t0 < t1) {
+            const size_t cb = (((size_t)(l + 1) * B + seq) * nkv + aj) * kvstride * ebytes;
+            k_issue_mfma<true>(sm.u.att.kbuf, kc + cb, t0, min(CHP, t1 - t0));
+            front_early = true;
+          }
+        }
         compute_static_rows<WT, NI_DNM, NI_DNM % 3 == 0 ? 3 : 1>(lstage(sm.u.mlp.dn), gdn, dn_rowfn_x,
                                                                  [&](int rp, float v) {
                                                                    const int k = rp / R8;
@@ -1690,7 +1699,7 @@ __global__ void __launch_bounds__(NT, 1) decode_kernel(const KStatic* __restrict
     // attention chunk after it (the exchange's loads would otherwise return only after the chunk)
     if (l + 1 < L) {
       issue_qkv(l + 1);
-      issue_kv_front(l + 1);
+      issue_kv_front(l + 1, !front_early, true);
     }
     stampit(14);
     ok = gather_flat(sm, copy_of(x_res2, H, par), H, tag + 5,
