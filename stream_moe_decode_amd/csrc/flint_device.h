@@ -95,6 +95,10 @@ __device__ __forceinline__ void dma16_untracked(const void* g, void* l) {
   const uint32_t m = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_void*)l);
   asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off" : : "v"(g), "{m0}"(m) : "memory");
 }
+__device__ __forceinline__ void dma4_untracked(const void* g, void* l) {
+  const uint32_t m = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_void*)l);
+  asm volatile("s_nop 0\n\tglobal_load_lds_dword %0, off" : : "v"(g), "{m0}"(m) : "memory");
+}
 
 template <int WT> constexpr bool kAct32 = (WT == W_F32);
 template <int WT> constexpr int kChunkElems = WT == W_F32 ? 4 : (WT == W_BF16 ? 8 : 32);

@@ -309,7 +309,7 @@ __device__ __forceinline__ void lstage_issue(const LStage& st, const Geo& g, int
 // Issue NIS items (known at compile time) starting at item k0: every chunk
 // address first (any LDS reads the row function needs are batched), then the
 // DMA instructions back to back.
-template <int WT, int NIS, class RowFn>
+template <int WT, int NIS, bool UNTRACKED = false, class RowFn>
 __device__ __forceinline__ void lstage_issue_static(const LStage& st, const Geo& g, int k0, RowFn rowfn, int cw) {
   const uint8_t* wp[NIS];
   const uint16_t* sp[NIS];
@@ -326,8 +326,13 @@ __device__ __forceinline__ void lstage_issue_static(const LStage& st, const Geo&
 #pragma unroll
   for (int i = 0; i < NIS; ++i)
     if (ok[i]) {
-      dma16(wp[i], &st.w16[(i * NW + cw) * 64]);
-      if constexpr (WT == W_I4) dma4(sp[i], &st.s32[(i * NW + cw) * 64]);
+      if constexpr (UNTRACKED) {
+        dma16_untracked(wp[i], &st.w16[(i * NW + cw) * 64]);
+        if constexpr (WT == W_I4) dma4_untracked(sp[i], &st.s32[(i * NW + cw) * 64]);
+      } else {
+        dma16(wp[i], &st.w16[(i * NW + cw) * 64]);
+        if constexpr (WT == W_I4) dma4(sp[i], &st.s32[(i * NW + cw) * 64]);
+      }
     }
 }
 
@@ -838,6 +843,11 @@ __global__ void __launch_bounds__(NT, 1) decode_kernel(const KStatic* __restrict
   // items per wave of each GEMV of the static shape (0: general rounds)
   constexpr int NI_QKV = nis_of(2 * even_share((SH::NQ + 2 * SH::NKV) * SH::HD / 2, SH::G), CP_QKV);
   constexpr int NI_O = nis_of(even_share(SH::H, SH::G), CP_O);
+  // the o_proj staging lies inside the QKV staging (the start of both layouts), clear of the attention's buffers
+  constexpr bool kEarlyO = SS && NI_O > 0 && NI_O <= O_CAP && CP_O > 0 && NI_O / CP_O <= 16;
+  static_assert(!kEarlyO || (offsetof(MergeLds, so) == 0 && offsetof(AttnLds, sq) == 0 &&
+                             sizeof(StageLds<O_CAP>) <= sizeof(StageLds<QKV_CAP>)),
+                "the early o_proj rows overlap only the QKV staging");
   constexpr int NI_GUM = nis_of(4 * even_share(SH::K * SH::EI / 2, SH::G), CP_GU);
   constexpr int NI_GUD = nis_of(4 * even_share(SH::DI / 2, SH::G), CP_GU);
   constexpr int NI_DND = nis_of(even_share(SH::H, SH::G), CP_DN);
@@ -949,6 +959,9 @@ __global__ void __launch_bounds__(NT, 1) decode_kernel(const KStatic* __restrict
     const int lmoe = l - ks.n_dense;
     bool front_early = false;  // the next layer's K rows were requested during the down products
 
+    const Geo go = geo<WT>(ore - orb, QD);  // o_proj rows of this workgroup
+    auto o_rowfn = [&](int q) { return mrow<WT>(m_o, (long long)l * H + orb + q, QD, sm.actA, sm.asumA); };
+
     // ---------------- input RMSNorm (recomputed by every workgroup)
     rmsnorm_act<WT>(sm, H, ks.eps, ASUM_A, kv_later);
     stampit(0);
@@ -960,6 +973,11 @@ __global__ void __launch_bounds__(NT, 1) decode_kernel(const KStatic* __restrict
                                              [&](int q, float v) { sm.ytmp[q] = v; }, kv_later);
     }
     __syncthreads();
+    // the static shape requests its o_proj rows now, over the QKV staging every wave has finished reading,
+    // out of the compiler's sight: the chip serves them long before the merge, whose exchange then waits
+    // for no weights, and nothing before the o_proj products reads them (the attention's wait for its
+    // chunk covers them as well)
+    if constexpr (kEarlyO) lstage_issue_static<WT, NI_O, true>(lstage(sm.u.mg.so), go, 0, o_rowfn, go.wave);
     stampit(1);
     for (int q2 = tid; q2 < qpe - qpb; q2 += NT) {  // RoPE on q and k heads: pairs (i, i + hd/2)
       const int head = (qpb + q2) / half;
@@ -1363,11 +1381,9 @@ __global__ void __launch_bounds__(NT, 1) decode_kernel(const KStatic* __restrict
     }
     stampit(4);
 
-    // o_proj rows of this workgroup: stage their weights before the merge waits
+    // elsewhere the o_proj rows of this workgroup are staged before the merge waits
     __syncthreads();  // the attention layout of the shared region is dead
-    const Geo go = geo<WT>(ore - orb, QD);
-    auto o_rowfn = [&](int q) { return mrow<WT>(m_o, (long long)l * H + orb + q, QD, sm.actA, sm.asumA); };
-    issue_auto<WT, NI_O, O_CAP>(lstage(sm.u.mg.so), go, o_rowfn);
+    if constexpr (!kEarlyO) issue_auto<WT, NI_O, O_CAP>(lstage(sm.u.mg.so), go, o_rowfn);
 
     // ---------------- merge the splits: this workgroup's pairs of output dims
     {
