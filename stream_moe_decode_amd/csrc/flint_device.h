@@ -55,9 +55,11 @@ __device__ __forceinline__ int div_small(int n, int d, float inv) {
   return q;
 }
 // s_waitcnt vmcnt(N): all but this wave's N most recent vector memory operations have completed
+// (also a compiler barrier: LDS reads of bytes that requests out of the compiler's sight wrote stay after it)
 template <int N> __device__ __forceinline__ void wait_vmem_n() {
   static_assert(N >= 0 && N < 64, "vmcnt has 6 bits");
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
+  asm volatile("" ::: "memory");
 }
 __device__ __forceinline__ void wait_vmem() { wait_vmem_n<0>(); }
 // vmcnt(n) for a run-time n (waits for everything when n is outside 0..15)
@@ -91,13 +93,13 @@ __device__ __forceinline__ void dma4(const void* g, void* l) { __builtin_amdgcn_
 // cannot tell which LDS a request writes, and after one it makes every later LDS access wait for all
 // outstanding requests.  The caller waits for this one itself (vmcnt) before anything reads its bytes.
 // M0 (the LDS address) is an input the compiler sets; one wait state separates that write from the request.
-__device__ __forceinline__ void dma16_untracked(const void* g, void* l) {
-  const uint32_t m = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_void*)l);
-  asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off" : : "v"(g), "{m0}"(m) : "memory");
+// LDS byte address of a generic pointer into LDS: its low 32 bits (the shared aperture sits above them)
+__device__ __forceinline__ uint32_t lds_offset(const void* l) { return (uint32_t)(uintptr_t)l; }
+__device__ __forceinline__ void dma16_untracked(const void* g, uint32_t lds) {
+  asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off" : : "v"(g), "{m0}"(__builtin_amdgcn_readfirstlane(lds)) : "memory");
 }
-__device__ __forceinline__ void dma4_untracked(const void* g, void* l) {
-  const uint32_t m = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_void*)l);
-  asm volatile("s_nop 0\n\tglobal_load_lds_dword %0, off" : : "v"(g), "{m0}"(m) : "memory");
+__device__ __forceinline__ void dma4_untracked(const void* g, uint32_t lds) {
+  asm volatile("s_nop 0\n\tglobal_load_lds_dword %0, off" : : "v"(g), "{m0}"(__builtin_amdgcn_readfirstlane(lds)) : "memory");
 }
 
 template <int WT> constexpr bool kAct32 = (WT == W_F32);
@@ -265,10 +267,11 @@ template <bool UNTRACKED = false>
 __device__ __forceinline__ void k_issue_mfma(uint4* buf, const uint8_t* base, int c0, int np) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int ni = (np * 16 + 63) / 64;
+  const uint32_t lb = lds_offset(buf);
   for (int gi = wave; gi < ni; gi += NW) {
     const int sl = gi * 64 + lane, p = sl >> 4, pr = min(p, np - 1);
     const int u = (sl & 15) ^ (p & 15);
-    if constexpr (UNTRACKED) dma16_untracked(base + (size_t)(c0 + pr) * 256 + u * 16, &buf[gi * 64]);
+    if constexpr (UNTRACKED) dma16_untracked(base + (size_t)(c0 + pr) * 256 + u * 16, lb + (uint32_t)gi * 1024u);
     else dma16(base + (size_t)(c0 + pr) * 256 + u * 16, &buf[gi * 64]);
   }
 }

@@ -207,13 +207,15 @@ __device__ __forceinline__ void rmsnorm_act(Smem& sm, int H, float eps, bool sum
 }
 // Bring n floats (n a multiple of 64) into sm.gn by DMA; wave w moves 1 KB units w, w + NW, ...
 // Waves w0 .. NW - 1 share the work.
+template <bool UNTRACKED = false>
 __device__ __forceinline__ void gn_issue(Smem& sm, const float* src, int n, int w0 = 0) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int units = n / 4;  // 16-byte units
   if (wave < w0) return;
   for (int gi = wave - w0; gi * 64 < units; gi += NW - w0) {
     const int unit = min(gi * 64 + lane, units - 1);
-    dma16(src + 4 * unit, &sm.gn[gi * 256]);
+    if constexpr (UNTRACKED) dma16_untracked(src + 4 * unit, lds_offset(&sm.gn[gi * 256]));
+    else dma16(src + 4 * unit, &sm.gn[gi * 256]);
   }
 }
 
@@ -327,8 +329,8 @@ __device__ __forceinline__ void lstage_issue_static(const LStage& st, const Geo&
   for (int i = 0; i < NIS; ++i)
     if (ok[i]) {
       if constexpr (UNTRACKED) {
-        dma16_untracked(wp[i], &st.w16[(i * NW + cw) * 64]);
-        if constexpr (WT == W_I4) dma4_untracked(sp[i], &st.s32[(i * NW + cw) * 64]);
+        dma16_untracked(wp[i], lds_offset(&st.w16[(i * NW + cw) * 64]));
+        if constexpr (WT == W_I4) dma4_untracked(sp[i], lds_offset(&st.s32[(i * NW + cw) * 64]));
       } else {
         dma16(wp[i], &st.w16[(i * NW + cw) * 64]);
         if constexpr (WT == W_I4) dma4(sp[i], &st.s32[(i * NW + cw) * 64]);
@@ -337,9 +339,9 @@ __device__ __forceinline__ void lstage_issue_static(const LStage& st, const Geo&
 }
 
 // Round 0 of a GEMV: the static issue when its NIS items fit the capacity, else the general loop.
-template <int WT, int NIS, int CAP, class RowFn>
+template <int WT, int NIS, int CAP, bool UNTRACKED = false, class RowFn>
 __device__ __forceinline__ void issue_auto(const LStage& st, const Geo& g, RowFn rowfn) {
-  if constexpr (NIS > 0 && NIS <= CAP) lstage_issue_static<WT, NIS>(st, g, 0, rowfn, g.wave);
+  if constexpr (NIS > 0 && NIS <= CAP) lstage_issue_static<WT, NIS, UNTRACKED>(st, g, 0, rowfn, g.wave);
   else lstage_issue<WT>(st, g, 0, rowfn);
 }
 
@@ -838,6 +840,11 @@ __global__ void __launch_bounds__(NT, 1) decode_kernel(const KStatic* __restrict
   constexpr int CP_DN = cpl_fit<WT, SH>(SH::DI, DN_CAP), CP_LM = cpl_fit<HW, SH>(SH::H, LM_CAP);
   // attention scores on MFMA: bf16 cache rows of 128 dims, at most 4 query heads per kv head
   constexpr bool MFMA_QK = SS && !kAct32<WT> && SH::HD == 128 && SH::NQ / SH::NKV <= 4;
+  // The static shape's weight, norm and K/V requests are made out of the compiler's sight (inline
+  // assembly): the compiler cannot tell which LDS a request writes, so it would make every later LDS
+  // access, and every barrier, wait for all outstanding requests; here each reader waits for its own
+  // bytes explicitly (vmcnt) and the exchanges' polls go out while the requests are in flight.
+  constexpr bool UT = SS;
   constexpr bool ASUM_A = WT == W_I4;  // int4 GEMVs take the chunk sums of actA from LDS
   constexpr int RCH = (MAX_H / kChunkElems<WT> + 63) / 64;  // router row chunks per lane
   // items per wave of each GEMV of the static shape (0: general rounds)
@@ -904,14 +911,14 @@ __global__ void __launch_bounds__(NT, 1) decode_kernel(const KStatic* __restrict
   const int xpb = part(K_ * EI_ / 2, G, W), xpe = part(K_ * EI_ / 2, G, W + 1);  // expert pairs
   const float inv_ei = 1.0f / (float)EI_, inv_k = 1.0f / (float)K_;
   // QKV weights of layer l and the K and / or V rows of its first attention chunk (into the shared region)
-  auto issue_qkv = [&](int l) { issue_auto<WT, NI_QKV, QKV_CAP>(lstage(sm.u.att.sq), gq, qkv_rowfn(l)); };
+  auto issue_qkv = [&](int l) { issue_auto<WT, NI_QKV, QKV_CAP, UT>(lstage(sm.u.att.sq), gq, qkv_rowfn(l)); };
   auto issue_kv_front = [&](int l, bool k, bool v) {
     if (!attn || t1 <= t0) return;
     const size_t cb = (((size_t)l * B + seq) * nkv + aj) * kvstride * ebytes;
     const int np0 = min(CHP, t1 - t0);
     if constexpr (MFMA_QK) {  // V rows swizzled like K: the transposing operand reads are conflict-free
-      if (k) k_issue_mfma(sm.u.att.kbuf, kc + cb, t0, np0);
-      if (v) k_issue_mfma(sm.u.att.vbuf, vc + cb, t0, np0);
+      if (k) k_issue_mfma<UT>(sm.u.att.kbuf, kc + cb, t0, np0);
+      if (v) k_issue_mfma<UT>(sm.u.att.vbuf, vc + cb, t0, np0);
     } else {
       if (k) kv_issue(sm.u.att.kbuf, kc + cb, t0, np0, rowb);
       if (v) kv_issue(sm.u.att.vbuf, vc + cb, t0, np0, rowb);
@@ -931,7 +938,7 @@ __global__ void __launch_bounds__(NT, 1) decode_kernel(const KStatic* __restrict
 
   issue_qkv(0);
   issue_kv_front(0, true, true);
-  gn_issue(sm, p_anorm, H);
+  gn_issue<UT>(sm, p_anorm, H);
   for (int e = tid; e < H; e += NT) {  // embedding row -> residual
     if constexpr (kAct32<WT>)
       sm.xres[e] = gp(reinterpret_cast<const float*>(ks.embed))[(long long)tok * H + e];
@@ -1005,7 +1012,7 @@ __global__ void __launch_bounds__(NT, 1) decode_kernel(const KStatic* __restrict
         else gp(reinterpret_cast<uint16_t*>(base))[off] = (uint16_t)f2bf(sm.ytmp[q]);
       }
     }
-    gn_issue(sm, p_pnorm + (size_t)l * H, H);  // post-attention norm weights, read after the o_proj exchange
+    gn_issue<UT>(sm, p_pnorm + (size_t)l * H, H);  // post-attention norm weights, read after the o_proj exchange
     stampit(2);
 
     // ---------------- attention partial over positions [t0, t1) of kv head aj
@@ -1079,8 +1086,8 @@ __global__ void __launch_bounds__(NT, 1) decode_kernel(const KStatic* __restrict
         if (c0 != t0) {  // later chunks (long contexts): load now
           __syncthreads();  // every wave is done with the previous chunk
           if constexpr (MFMA_QK) {
-            k_issue_mfma(at.kbuf, kbase, c0, np);
-            k_issue_mfma(at.vbuf, vbase, c0, np);
+            k_issue_mfma<UT>(at.kbuf, kbase, c0, np);
+            k_issue_mfma<UT>(at.vbuf, vbase, c0, np);
           } else {
             kv_issue(at.kbuf, kbase, c0, np, rowb);
             kv_issue(at.vbuf, vbase, c0, np, rowb);
@@ -1383,7 +1390,7 @@ __global__ void __launch_bounds__(NT, 1) decode_kernel(const KStatic* __restrict
 
     // elsewhere the o_proj rows of this workgroup are staged before the merge waits
     __syncthreads();  // the attention layout of the shared region is dead
-    if constexpr (!kEarlyO) issue_auto<WT, NI_O, O_CAP>(lstage(sm.u.mg.so), go, o_rowfn);
+    if constexpr (!kEarlyO) issue_auto<WT, NI_O, O_CAP, UT>(lstage(sm.u.mg.so), go, o_rowfn);
 
     // ---------------- merge the splits: this workgroup's pairs of output dims
     {
@@ -1488,8 +1495,13 @@ __global__ void __launch_bounds__(NT, 1) decode_kernel(const KStatic* __restrict
 #pragma unroll
       for (int j = 0; j < RCH; ++j) {
         const int c = lane + 64 * j < RC ? lane + 64 * j : 0;
-        dma16(src.w + 16ll * c, &rst.w16[(j * NW + wave) * 64]);
-        if constexpr (WT == W_I4) dma4(src.s + ((c >> 1) & ~1), &rst.s32[(j * NW + wave) * 64]);
+        if constexpr (UT) {
+          dma16_untracked(src.w + 16ll * c, lds_offset(&rst.w16[(j * NW + wave) * 64]));
+          if constexpr (WT == W_I4) dma4_untracked(src.s + ((c >> 1) & ~1), lds_offset(&rst.s32[(j * NW + wave) * 64]));
+        } else {
+          dma16(src.w + 16ll * c, &rst.w16[(j * NW + wave) * 64]);
+          if constexpr (WT == W_I4) dma4(src.s + ((c >> 1) & ~1), &rst.s32[(j * NW + wave) * 64]);
+        }
       }
     };
     if (rbb + wave < rbe) router_issue(rbb + wave);
@@ -1626,8 +1638,8 @@ __global__ void __launch_bounds__(NT, 1) decode_kernel(const KStatic* __restrict
     };
     const Geo ggu = geo<WT>(2 * une, H);
     const Geo gdn = geo<WT>(dense ? dre - drb : (dre - drb) * K, inner);
-    if (dense) issue_auto<WT, NI_GUD, GU_CAP>(lstage(sm.u.mlp.gu), ggu, gu_rowfn);
-    else issue_auto<WT, NI_GUM, GU_CAP>(lstage(sm.u.mlp.gu), ggu, gu_rowfn);
+    if (dense) issue_auto<WT, NI_GUD, GU_CAP, UT>(lstage(sm.u.mlp.gu), ggu, gu_rowfn);
+    else issue_auto<WT, NI_GUM, GU_CAP, UT>(lstage(sm.u.mlp.gu), ggu, gu_rowfn);
     {
       const auto ar = act_regs<WT, CP_GU>(ggu, sm.actA, sm.asumA);
       auto out = [&](int q, float v) { sm.ytmp[q] = v; };
@@ -1654,10 +1666,10 @@ __global__ void __launch_bounds__(NT, 1) decode_kernel(const KStatic* __restrict
         return hv[0] | (hv[1] << 16);
       });
     // the down weights and the next norm's weights load during the SwiGLU exchange
-    if (dense) issue_auto<WT, NI_DND, DN_CAP>(lstage(sm.u.mlp.dn), gdn, dn_rowfn);
-    else if constexpr (NI_DNM > 0 && NI_DNM <= DN_CAP) lstage_issue_static<WT, NI_DNM>(lstage(sm.u.mlp.dn), gdn, 0, dn_rowfn_x, gdn.wave);
+    if (dense) issue_auto<WT, NI_DND, DN_CAP, UT>(lstage(sm.u.mlp.dn), gdn, dn_rowfn);
+    else if constexpr (NI_DNM > 0 && NI_DNM <= DN_CAP) lstage_issue_static<WT, NI_DNM, UT>(lstage(sm.u.mlp.dn), gdn, 0, dn_rowfn_x, gdn.wave);
     else lstage_issue<WT>(lstage(sm.u.mlp.dn), gdn, 0, dn_rowfn);
-    gn_issue(sm, l + 1 < L ? p_anorm + (size_t)(l + 1) * H : p_fnorm, H);
+    gn_issue<UT>(sm, l + 1 < L ? p_anorm + (size_t)(l + 1) * H : p_fnorm, H);
     stampit(12);
     // ---------------- gather the SwiGLU output, down projection + residual
     ok = gather_flat(sm, copy_of(x_h, HSLOTS, par), kAct32<WT> ? nunit : nunit / 2, tag + 4,
