@@ -1021,6 +1021,7 @@ __global__ void __launch_bounds__(NT, 1) decode_kernel(const KStatic* __restrict
       AttnLds& at = sm.u.att;
       if (t0 < t1) {
         const uint64_t* src = copy_of(x_qkv, QR, par);
+        wait_vmem();  // EXPERIMENT: polls go out once this wave's requests have landed
         const int nqs = Gq * hd;
         const bool last = t1 == T;  // this split holds the new token: its k, v come from the exchange
         const int n = nqs + (last ? 2 * hd : 0);
@@ -1399,6 +1400,7 @@ __global__ void __launch_bounds__(NT, 1) decode_kernel(const KStatic* __restrict
                     "the static shape merges whole runs of dims inside one head");
       const int pb = mpb, pe = mpe;
       const uint64_t* srcp = x_part + (size_t)par * nq * (hd + 2) * S;
+      wait_vmem();  // EXPERIMENT
       int e0 = 2 * pb;
       while (e0 < 2 * pe) {  // one head at a time (uniform loop)
         const int h = e0 / hd, eh0 = e0 % hd;
