@@ -1021,7 +1021,11 @@ __global__ void __launch_bounds__(NT, 1) decode_kernel(const KStatic* __restrict
       AttnLds& at = sm.u.att;
       if (t0 < t1) {
         const uint64_t* src = copy_of(x_qkv, QR, par);
-        wait_vmem();  // EXPERIMENT: polls go out once this wave's requests have landed
+        // polls go out once this wave's stores (q/k/v, the K/V append) and requests have completed: in
+        // alternating runs that beats polling behind them here and in the merge, the merged-output and the
+        // residual exchanges, while the exchanges behind a weight burst (router logits, SwiGLU, residual
+        // after the MoE) do better polling behind the burst
+        wait_vmem();
         const int nqs = Gq * hd;
         const bool last = t1 == T;  // this split holds the new token: its k, v come from the exchange
         const int n = nqs + (last ? 2 * hd : 0);
@@ -1400,7 +1404,7 @@ __global__ void __launch_bounds__(NT, 1) decode_kernel(const KStatic* __restrict
                     "the static shape merges whole runs of dims inside one head");
       const int pb = mpb, pe = mpe;
       const uint64_t* srcp = x_part + (size_t)par * nq * (hd + 2) * S;
-      wait_vmem();  // EXPERIMENT
+      wait_vmem();  // polls once this wave's stores (the attention partials) have completed
       int e0 = 2 * pb;
       while (e0 < 2 * pe) {  // one head at a time (uniform loop)
         const int h = e0 / hd, eh0 = e0 % hd;
@@ -1462,6 +1466,7 @@ __global__ void __launch_bounds__(NT, 1) decode_kernel(const KStatic* __restrict
     stampit(5);
 
     // ---------------- o_proj rows + residual
+    wait_vmem();  // polls once this wave's stores (the merged dims) have completed
     ok = gather_flat(sm, copy_of(x_o, OSL, par), OSL, tag + 2,
                      [&](int i, uint32_t p) {
                        if constexpr (kAct32<WT>) {
@@ -1506,6 +1511,7 @@ __global__ void __launch_bounds__(NT, 1) decode_kernel(const KStatic* __restrict
         }
       }
     };
+    wait_vmem();  // likewise (the o_proj rows); the router rows are requested after it, ahead of the polls
     if (rbb + wave < rbe) router_issue(rbb + wave);
     ok = gather_flat(sm, copy_of(x_res1, H, par), H, tag + 3,
                      [&](int i, uint32_t p) { sm.xres[i] = __uint_as_float(p); }, wt);
