@@ -924,14 +924,15 @@ __global__ void __launch_bounds__(NT, 1) decode_kernel(const KStatic* __restrict
       if (v) kv_issue(sm.u.att.vbuf, vc + cb, t0, np0, rowb);
     }
   };
-  // The MoE layers' down products request the K rows of the next layer's first chunk (their LDS overlaps
-  // only the gate/up staging, dead by then) without the compiler seeing the requests, so that the
-  // products' LDS reads do not wait for them: the chip serves them while the products run, and only the
-  // V rows (over the down staging) and the QKV rows wait for the products to end.  The attention waits
-  // for every request (vmcnt(0)) before it reads a chunk.
+  // The MoE layers' down products request the next layer's QKV rows and the K rows of its first chunk
+  // (their LDS overlaps only the gate/up staging, dead by then) without the compiler seeing the requests,
+  // so that the products' LDS reads do not wait for them: the chip serves them while the products run,
+  // and only the V rows (over the down staging) wait for the products to end.  The QKV products and the
+  // attention wait for every request (vmcnt(0)) before they read their rows.
   static_assert(offsetof(AttnLds, kbuf) + sizeof(AttnLds::kbuf) <= sizeof(StageLds<GU_CAP>) &&
+                    offsetof(AttnLds, sq) + sizeof(AttnLds::sq) <= sizeof(StageLds<GU_CAP>) &&
                     offsetof(MlpLds, gu) == 0,
-                "the K rows overlap only the gate/up staging");
+                "the QKV staging and the K rows overlap only the gate/up staging");
   // Elsewhere a layer's first attention chunk is requested at the end of the layer before, ahead of the
   // residual exchange's polls; every wait that follows is a full one (no later loads left in flight).
   const int kv_later = 0;
@@ -964,7 +965,7 @@ __global__ void __launch_bounds__(NT, 1) decode_kernel(const KStatic* __restrict
     const uint8_t* const vbase = vc + cbase * ebytes;
     const bool dense = l < ks.n_dense;
     const int lmoe = l - ks.n_dense;
-    bool front_early = false;  // the next layer's K rows were requested during the down products
+    bool front_early = false;  // the next layer's QKV and K rows were requested during the down products
 
     const Geo go = geo<WT>(ore - orb, QD);  // o_proj rows of this workgroup
     auto o_rowfn = [&](int q) { return mrow<WT>(m_o, (long long)l * H + orb + q, QD, sm.actA, sm.asumA); };
@@ -1704,6 +1705,7 @@ __global__ void __launch_bounds__(NT, 1) decode_kernel(const KStatic* __restrict
         wait_vmem();
         if constexpr (MFMA_QK) {
           if (l + 1 < L && attn && t0 < t1) {
+            issue_qkv(l + 1);
             const size_t cb = (((size_t)(l + 1) * B + seq) * nkv + aj) * kvstride * ebytes;
             k_issue_mfma<true>(sm.u.att.kbuf, kc + cb, t0, min(CHP, t1 - t0));
             front_early = true;
@@ -1734,7 +1736,7 @@ __global__ void __launch_bounds__(NT, 1) decode_kernel(const KStatic* __restrict
     // the shared region is free: the next layer's QKV weights load during the exchange; its first
     // attention chunk after it (the exchange's loads would otherwise return only after the chunk)
     if (l + 1 < L) {
-      issue_qkv(l + 1);
+      if (!front_early) issue_qkv(l + 1);
       issue_kv_front(l + 1, !front_early, true);
     }
     stampit(14);
