@@ -173,17 +173,21 @@ template <int WT> __device__ __forceinline__ void act_sums(const uint32_t* act, 
 // sm.wred holds the wave sums (consecutive norms alternate, so no barrier is
 // needed before writing them).
 // later: vector memory operations this wave issued after the norm weights' DMA (they may stay in flight).
-template <int WT, int OW = WT>
+// PRE: the wave sums of squares are already in sm.wred (written by the gather that brought the residual,
+// before its closing barrier), so the norm starts from them.
+template <int WT, int OW = WT, bool PRE = false>
 __device__ __forceinline__ void rmsnorm_act(Smem& sm, int H, float eps, bool sums, int later = 0, int half = 0) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   wait_vmem_dyn(later);
   const int e0 = 4 * tid;
   const bool mine = e0 < H;
   const float4 x = mine ? *reinterpret_cast<const float4*>(&sm.xres[e0]) : make_float4(0.f, 0.f, 0.f, 0.f);
-  float ss = x.x * x.x + x.y * x.y + x.z * x.z + x.w * x.w;
-  ss = wave_sum(ss);
-  if (lane == 0) sm.wred[half * NW + wave] = ss;
-  __syncthreads();
+  if constexpr (!PRE) {
+    float ss = x.x * x.x + x.y * x.y + x.z * x.z + x.w * x.w;
+    ss = wave_sum(ss);
+    if (lane == 0) sm.wred[half * NW + wave] = ss;
+    __syncthreads();
+  }
   float t = 0.f;
 #pragma unroll
   for (int w = 0; w < NW; ++w) t += sm.wred[half * NW + w];
@@ -677,9 +681,13 @@ __device__ __forceinline__ bool sync_ok(Smem& sm, Waiter& wt) {
 // GT: threads that read slots (the first GT of the workgroup; the others only take part in the barriers,
 // e.g. while their DMAs are in flight: a wave's loads complete in order, so a poll issued behind a DMA burst
 // would return only after the burst).
-template <int GT = NT, class IndexFn, class SentFn, class PutFn>
+struct NoHook {
+  __device__ void operator()() const {}
+};
+// pre() runs in every thread just before the closing barrier (after the last put).
+template <int GT = NT, class IndexFn, class SentFn, class PutFn, class PreFn = NoHook>
 __device__ __forceinline__ bool gather(Smem& sm, const uint64_t* src, int n, uint32_t tag, IndexFn index, SentFn sent,
-                                       int nsent, PutFn put, Waiter& wt) {
+                                       int nsent, PutFn put, Waiter& wt, PreFn pre = PreFn{}) {
   static_assert(GT % 64 == 0 && GT >= 64 && GT <= NT, "whole waves poll");
   const int tid = threadIdx.x;
   if (nsent > wt.sentinels) nsent = wt.sentinels;
@@ -732,17 +740,18 @@ __device__ __forceinline__ bool gather(Smem& sm, const uint64_t* src, int n, uin
       if (i < n) put(i, (uint32_t)v[k]);
     }
   }
+  pre();
   return sync_ok(sm, wt);
 }
 
 // Gather n contiguous slots, sentinels spread evenly.
-template <int GT = NT, class PutFn>
+template <int GT = NT, class PutFn, class PreFn = NoHook>
 __device__ __forceinline__ bool gather_flat(Smem& sm, const uint64_t* src, int n, uint32_t tag, PutFn put,
-                                            Waiter& wt) {
+                                            Waiter& wt, PreFn pre = PreFn{}) {
   const int ns = n < 64 ? n : 64;
   return gather<GT>(
       sm, src, n, tag, [](int i) { return i; }, [=](int k, int m) { return (int)(((long long)(k + 1) * n) / m) - 1; },
-      ns, put, wt);
+      ns, put, wt, pre);
 }
 
 // Publish `count` values into a replicated exchange buffer [NCOPY][2 parities][n]:
@@ -940,12 +949,18 @@ __global__ void __launch_bounds__(NT, 1) decode_kernel(const KStatic* __restrict
   issue_qkv(0);
   issue_kv_front(0, true, true);
   gn_issue<UT>(sm, p_anorm, H);
+  float ss0 = 0.f;  // the first input norm's sum of squares, as the residual gathers keep it for later ones
   for (int e = tid; e < H; e += NT) {  // embedding row -> residual
+    float v;
     if constexpr (kAct32<WT>)
-      sm.xres[e] = gp(reinterpret_cast<const float*>(ks.embed))[(long long)tok * H + e];
+      v = gp(reinterpret_cast<const float*>(ks.embed))[(long long)tok * H + e];
     else
-      sm.xres[e] = bf2f(gp(reinterpret_cast<const uint16_t*>(ks.embed))[(long long)tok * H + e]);
+      v = bf2f(gp(reinterpret_cast<const uint16_t*>(ks.embed))[(long long)tok * H + e]);
+    sm.xres[e] = v;
+    ss0 = fmaf(v, v, ss0);
   }
+  ss0 = wave_sum(ss0);
+  if (lane == 0) sm.wred[wave] = ss0;
   for (int q2 = tid; q2 < qpe - qpb; q2 += NT)  // RoPE of this workgroup's pairs at this position
     sm.rcs[q2] = *(GLOBAL const f32x2_t*)(d.rope + (size_t)pos * half + (qpb + q2) % half);
   wait_vmem();
@@ -971,7 +986,7 @@ __global__ void __launch_bounds__(NT, 1) decode_kernel(const KStatic* __restrict
     auto o_rowfn = [&](int q) { return mrow<WT>(m_o, (long long)l * H + orb + q, QD, sm.actA, sm.asumA); };
 
     // ---------------- input RMSNorm (recomputed by every workgroup)
-    rmsnorm_act<WT>(sm, H, ks.eps, ASUM_A, kv_later);
+    rmsnorm_act<WT, WT, true>(sm, H, ks.eps, ASUM_A, kv_later);
     stampit(0);
 
     // ---------------- QKV rows (staged during the previous layer), RoPE, publish, KV append
@@ -1514,13 +1529,25 @@ __global__ void __launch_bounds__(NT, 1) decode_kernel(const KStatic* __restrict
     };
     wait_vmem();  // likewise (the o_proj rows); the router rows are requested after it, ahead of the polls
     if (rbb + wave < rbe) router_issue(rbb + wave);
-    ok = gather_flat(sm, copy_of(x_res1, H, par), H, tag + 3,
-                     [&](int i, uint32_t p) { sm.xres[i] = __uint_as_float(p); }, wt);
+    // the gathered residual's squares are summed on the way in: the post-attention norm starts from them
+    float ss1 = 0.f;
+    ok = gather_flat(
+        sm, copy_of(x_res1, H, par), H, tag + 3,
+        [&](int i, uint32_t p) {
+          const float v = __uint_as_float(p);
+          sm.xres[i] = v;
+          ss1 = fmaf(v, v, ss1);
+        },
+        wt,
+        [&]() {
+          ss1 = wave_sum(ss1);
+          if (lane == 0) sm.wred[NW + wave] = ss1;
+        });
     if (!ok) break;
     stampit(8);
 
     // ---------------- post-attention RMSNorm (recomputed by every workgroup)
-    rmsnorm_act<WT>(sm, H, ks.eps, ASUM_A, 0, 1);
+    rmsnorm_act<WT, WT, true>(sm, H, ks.eps, ASUM_A, 0, 1);
     stampit(9);
 
     int nunit, inner;  // SwiGLU elements this layer produces, and the down projection's input width
@@ -1740,8 +1767,19 @@ __global__ void __launch_bounds__(NT, 1) decode_kernel(const KStatic* __restrict
       issue_kv_front(l + 1, !front_early, true);
     }
     stampit(14);
-    ok = gather_flat(sm, copy_of(x_res2, H, par), H, tag + 5,
-                     [&](int i, uint32_t p) { sm.xres[i] = __uint_as_float(p); }, wt);
+    float ss2 = 0.f;  // likewise for the next input norm (or the final norm)
+    ok = gather_flat(
+        sm, copy_of(x_res2, H, par), H, tag + 5,
+        [&](int i, uint32_t p) {
+          const float v = __uint_as_float(p);
+          sm.xres[i] = v;
+          ss2 = fmaf(v, v, ss2);
+        },
+        wt,
+        [&]() {
+          ss2 = wave_sum(ss2);
+          if (lane == 0) sm.wred[wave] = ss2;
+        });
     if (!ok) break;
     stampit(15);
     if (d.dbg_resid && W == 0)
@@ -1751,7 +1789,7 @@ __global__ void __launch_bounds__(NT, 1) decode_kernel(const KStatic* __restrict
   // ---------------- final norm (its weights are in sm.gn), lm_head, argmax
   {
     __syncthreads();
-    rmsnorm_act<WT, HW>(sm, H, ks.eps, false);
+    rmsnorm_act<WT, HW, true>(sm, H, ks.eps, false);
     const int vb = ok ? part(V_, G, W) : 0, ve = ok ? part(V_, G, W + 1) : 0;
     float bv = -INFINITY;
     int bi = 0x7FFFFFFF;
