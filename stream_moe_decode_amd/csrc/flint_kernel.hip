@@ -1370,41 +1370,50 @@ __global__ void __launch_bounds__(NT, 1) decode_kernel(const KStatic* __restrict
                 if (e < DPV) o[h][e] = fmaf(pr[h], v[e], o[h][e]);
         }
       }
+      uint64_t* dst = x_part + (size_t)par * nq * (hd + 2) * S + ((size_t)aj * S + as) * Gq * (hd + 2);
+      if constexpr (MFMA_QK) {
+        // each wave holds whole dims (16 w .. 16 w + 15 of every head): it publishes them from registers,
+        // lane 16 h + d taking dim 16 w + d of head h (from lane 16 (d / 4) + h, element d % 4) so that
+        // each head's 16 dims go out as one contiguous run
+        const int h = lane >> 4, d = lane & 15, src = 16 * (d >> 2) + h;
+        float v = 0.f;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const float t = __int_as_float(__builtin_amdgcn_ds_bpermute(src * 4, __float_as_int(o4[j])));
+          if ((d & 3) == j) v = t;
+        }
+        if (h < Gq) xstore(dst + (size_t)h * (hd + 2) + 2 + 16 * wave + d, slot(tag + 1, __float_as_uint(v)));
+        if (tid < 2 * Gq) {
+          const int hh = tid >> 1;
+          const float mlv = (tid & 1) ? at.lst[hh] : at.mst[hh];
+          xstore(dst + (size_t)hh * (hd + 2) + (tid & 1), slot(tag + 1, __float_as_uint(mlv)));
+        }
+      }
       // sum the waves' outputs (the K rows are dead: their buffer holds the partial sums)
       float* red = reinterpret_cast<float*>(at.kbuf);
-      __syncthreads();
-      if constexpr (MFMA_QK) {  // each wave holds whole dims: no sum over waves
-        const int g = lane >> 4, i = lane & 15;
-        if (i < Gq)
-#pragma unroll
-          for (int j = 0; j < 4; ++j) red[i * hd + 16 * wave + 4 * g + j] = o4[j];
-      } else {
+      if constexpr (!MFMA_QK) {
+        __syncthreads();
 #pragma unroll
         for (int h = 0; h < MAX_GQ; ++h)
           if (h < Gq)
 #pragma unroll
             for (int e = 0; e < DPVM; ++e)
               if (e < DPV) red[(wave * MAX_GQ + h) * hd + lane * DPV + e] = o[h][e];
-      }
-      __syncthreads();
-      // publish (m, l, o) of each head of this split, contiguous: slot ((split * Gq + h) * (hd + 2) + field)
-      // of the kv head's block; every slot is tagged
-      uint64_t* dst = x_part + (size_t)par * nq * (hd + 2) * S + ((size_t)aj * S + as) * Gq * (hd + 2);
-      for (int idx = tid; idx < Gq * hd; idx += NT) {
-        const int h = idx / hd, e = idx % hd;
-        float t = 0.f;
-        if constexpr (MFMA_QK) {
-          t = red[h * hd + e];
-        } else {
+        __syncthreads();
+        // publish (m, l, o) of each head of this split, contiguous: slot ((split * Gq + h) * (hd + 2) + field)
+        // of the kv head's block; every slot is tagged
+        for (int idx = tid; idx < Gq * hd; idx += NT) {
+          const int h = idx / hd, e = idx % hd;
+          float t = 0.f;
 #pragma unroll
           for (int w = 0; w < NW; ++w) t += red[(w * MAX_GQ + h) * hd + e];
+          xstore(dst + (size_t)h * (hd + 2) + 2 + e, slot(tag + 1, __float_as_uint(t)));
         }
-        xstore(dst + (size_t)h * (hd + 2) + 2 + e, slot(tag + 1, __float_as_uint(t)));
-      }
-      if (tid < 2 * Gq) {
-        const int h = tid >> 1;
-        const float v = (tid & 1) ? at.lst[h] : at.mst[h];
-        xstore(dst + (size_t)h * (hd + 2) + (tid & 1), slot(tag + 1, __float_as_uint(v)));
+        if (tid < 2 * Gq) {
+          const int h = tid >> 1;
+          const float v = (tid & 1) ? at.lst[h] : at.mst[h];
+          xstore(dst + (size_t)h * (hd + 2) + (tid & 1), slot(tag + 1, __float_as_uint(v)));
+        }
       }
     }
     stampit(4);
