@@ -900,6 +900,17 @@ __global__ void __launch_bounds__(NT, 1) decode_kernel(const KStatic* __restrict
   const int ebytes = kAct32<WT> ? 4 : 2;
   const int rowb = hd * ebytes;                 // bytes of one cached K or V row
   const int CHP = KV_LDS / rowb;                // positions per attention chunk
+  // A split one chunk plus at most TAIL_POS positions long (contexts just past 64 x 128 positions) has its
+  // tail's K/V rows requested right after the QKV products, into the part of the QKV staging that the
+  // early o_proj rows leave free, and takes the tail as a ninth block of 16 positions in the same pass
+  // as the chunk (scored by wave 0, its probabilities after the block maxima and sums in the score
+  // buffer, one more K-step of the P.V): no second chunk.
+  constexpr int TAIL_POS = 16, TAIL_OFF = (int)sizeof(StageLds<O_CAP>);
+  static_assert(offsetof(AttnLds, sq) == 0 && TAIL_OFF + 2 * TAIL_POS * 256 <= (int)sizeof(StageLds<QKV_CAP>),
+                "the tail's K and V rows fit between the early o_proj rows and the K buffer");
+  const bool tail_pre = MFMA_QK && kEarlyO && attn && t1 - t0 > CHP && t1 - t0 - CHP <= TAIL_POS;
+  uint4* const ktail = reinterpret_cast<uint4*>(reinterpret_cast<uint8_t*>(&sm.u.att) + TAIL_OFF);
+  uint4* const vtail = ktail + TAIL_POS * 16;
   const size_t kvstride = (size_t)cap * hd;     // elements per (layer, seq, kv head)
   bool ok = true;  // false once a wait failed: skip to the argmax hand-off so the launch still ends cleanly
 
@@ -1001,6 +1012,12 @@ __global__ void __launch_bounds__(NT, 1) decode_kernel(const KStatic* __restrict
     // for no weights, and nothing before the o_proj products reads them (the attention's wait for its
     // chunk covers them as well)
     if constexpr (kEarlyO) lstage_issue_static<WT, NI_O, true>(lstage(sm.u.mg.so), go, 0, o_rowfn, go.wave);
+    if constexpr (MFMA_QK) {
+      if (tail_pre) {  // the new token's rows among them are replaced from the exchange before use
+        k_issue_mfma<true>(ktail, kbase, t0 + CHP, t1 - t0 - CHP);
+        k_issue_mfma<true>(vtail, vbase, t0 + CHP, t1 - t0 - CHP);
+      }
+    }
     stampit(1);
     for (int q2 = tid; q2 < qpe - qpb; q2 += NT) {  // RoPE on q and k heads: pairs (i, i + hd/2)
       const int head = (qpb + q2) / half;
@@ -1097,13 +1114,18 @@ __global__ void __launch_bounds__(NT, 1) decode_kernel(const KStatic* __restrict
       float* const bmax = at.sc;                 // MFMA path: [wave][head] block maxima, then block sums
       float* const bsum = at.sc + NW * MAX_GQ;
       float sv[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};  // MFMA path: this lane's scores of the chunk
+      float st8[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};  // and of the tail block (wave 0)
       float alpha_r = 0.f;                       // MFMA path: rescale of the running output for head lane % 16
       if (tid < Gq) {
         at.mst[tid] = -INFINITY;
         at.lst[tid] = 0.f;
       }
-      for (int c0 = t0; c0 < t1; c0 += CHP) {
+      const int nt = tail_pre ? t1 - t0 - CHP : 0;  // positions of the tail block (MFMA path)
+      uint16_t* const pb8 = reinterpret_cast<uint16_t*>(at.sc + 2 * NW * MAX_GQ);  // its probabilities
+      for (int c0 = t0; c0 < t1 - nt; c0 += CHP) {
         const int np = min(CHP, t1 - c0);
+        uint4* const kb = at.kbuf;
+        uint4* const vbm = at.vbuf;
         if (c0 != t0) {  // later chunks (long contexts): load now
           __syncthreads();  // every wave is done with the previous chunk
           if constexpr (MFMA_QK) {
@@ -1117,6 +1139,13 @@ __global__ void __launch_bounds__(NT, 1) decode_kernel(const KStatic* __restrict
         wait_vmem();
         __syncthreads();
         // the new token's row: k, v from the exchange replace what the DMA read
+        if (nt > 0 && pos >= c0 + np && pos < c0 + np + nt) {  // in the tail block (MFMA path)
+          for (int e = tid; e < hd; e += NT) {
+            reinterpret_cast<uint16_t*>(ktail)[k_slot(pos - c0 - np, e >> 3) * 8 + (e & 7)] = (uint16_t)f2bf(at.kn[e]);
+            reinterpret_cast<uint16_t*>(vtail)[k_slot(pos - c0 - np, e >> 3) * 8 + (e & 7)] = (uint16_t)f2bf(at.vn[e]);
+          }
+          __syncthreads();
+        }
         if (pos >= c0 && pos < c0 + np) {
           uint8_t* kr = reinterpret_cast<uint8_t*>(at.kbuf) + (size_t)(pos - c0) * rowb;
           uint8_t* vr = reinterpret_cast<uint8_t*>(at.vbuf) + (size_t)(pos - c0) * rowb;
@@ -1126,8 +1155,8 @@ __global__ void __launch_bounds__(NT, 1) decode_kernel(const KStatic* __restrict
               reinterpret_cast<float*>(vr)[e] = at.vn[e];
             } else {
               if constexpr (MFMA_QK) {  // the rows' units are swizzled by the position
-                reinterpret_cast<uint16_t*>(at.kbuf)[k_slot(pos - c0, e >> 3) * 8 + (e & 7)] = (uint16_t)f2bf(at.kn[e]);
-                reinterpret_cast<uint16_t*>(at.vbuf)[k_slot(pos - c0, e >> 3) * 8 + (e & 7)] = (uint16_t)f2bf(at.vn[e]);
+                reinterpret_cast<uint16_t*>(kb)[k_slot(pos - c0, e >> 3) * 8 + (e & 7)] = (uint16_t)f2bf(at.kn[e]);
+                reinterpret_cast<uint16_t*>(vbm)[k_slot(pos - c0, e >> 3) * 8 + (e & 7)] = (uint16_t)f2bf(at.vn[e]);
               } else {
                 reinterpret_cast<uint16_t*>(kr)[e] = (uint16_t)f2bf(at.kn[e]);
                 reinterpret_cast<uint16_t*>(vr)[e] = (uint16_t)f2bf(at.vn[e]);
@@ -1159,7 +1188,7 @@ __global__ void __launch_bounds__(NT, 1) decode_kernel(const KStatic* __restrict
 #pragma unroll
             for (int sk = 0; sk < 4; ++sk) {
               const bf16x8_t a =
-                  __builtin_bit_cast(bf16x8_t, at.kbuf[k_slot(b * 16 + (lane & 15), sk * 4 + (lane >> 4))]);
+                  __builtin_bit_cast(bf16x8_t, kb[k_slot(b * 16 + (lane & 15), sk * 4 + (lane >> 4))]);
               acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qh[sk], acc, 0, 0, 0);
               acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, ql[sk], acc, 0, 0, 0);
             }
@@ -1167,6 +1196,18 @@ __global__ void __launch_bounds__(NT, 1) decode_kernel(const KStatic* __restrict
             for (int r = 0; r < 4; ++r) sv[r] = (n < Gq && b * 16 + (lane >> 4) * 4 + r < np) ? acc[r] : -INFINITY;
           }
           float bm = fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3]));
+          if (nt > 0 && wave == 0) {  // the tail block
+            f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int sk = 0; sk < 4; ++sk) {
+              const bf16x8_t a = __builtin_bit_cast(bf16x8_t, ktail[k_slot(lane & 15, sk * 4 + (lane >> 4))]);
+              acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qh[sk], acc, 0, 0, 0);
+              acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, ql[sk], acc, 0, 0, 0);
+            }
+#pragma unroll
+            for (int r = 0; r < 4; ++r) st8[r] = (n < Gq && (lane >> 4) * 4 + r < nt) ? acc[r] : -INFINITY;
+            bm = fmaxf(bm, fmaxf(fmaxf(st8[0], st8[1]), fmaxf(st8[2], st8[3])));
+          }
           bm = fmaxf(bm, swap16(bm));
           bm = fmaxf(bm, swap32(bm));
           if (lane < Gq) bmax[wave * MAX_GQ + lane] = bm;
@@ -1236,6 +1277,19 @@ __global__ void __launch_bounds__(NT, 1) decode_kernel(const KStatic* __restrict
             *reinterpret_cast<s16x4_t*>(pb + (wave * 64 + lane) * 4) = ph;
             *reinterpret_cast<s16x4_t*>(pb + PB_HALF + (wave * 64 + lane) * 4) = pl;
           }
+          if (nt > 0 && wave == 0) {
+            s16x4_t ph, pl;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+              const float pr = i < Gq ? __expf(st8[r] - mn) : 0.f;
+              const uint32_t hb = f2bf(pr);
+              ph[r] = (short)hb;
+              pl[r] = (short)f2bf(pr - bf2f(hb));
+              ls += pr;
+            }
+            *reinterpret_cast<s16x4_t*>(pb8 + lane * 4) = ph;
+            *reinterpret_cast<s16x4_t*>(pb8 + 256 + lane * 4) = pl;
+          }
           ls += swap16(ls);
           ls += swap32(ls);
           if (lane < Gq) bsum[wave * MAX_GQ + lane] = ls;
@@ -1287,7 +1341,7 @@ __global__ void __launch_bounds__(NT, 1) decode_kernel(const KStatic* __restrict
           const int g = lane >> 4, i = lane & 15;
 #pragma unroll
           for (int j = 0; j < 4; ++j) o4[j] *= alpha_r;
-          const uint8_t* vlb = reinterpret_cast<const uint8_t*>(at.vbuf);
+          const uint8_t* vlb = reinterpret_cast<const uint8_t*>(vbm);
           const int u = 2 * wave + ((i & 3) >> 1);
           const int nk = (np + 15) / 16;
           // four K-steps at a time: their operand reads are issued together, then their products
@@ -1315,6 +1369,19 @@ __global__ void __launch_bounds__(NT, 1) decode_kernel(const KStatic* __restrict
                 o4 = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vt[q], pl[q], o4, 0, 0, 0);
               }
             }
+          }
+          if (nt > 0) {  // the tail block: one more K-step, V rows from the tail buffer
+            const int row = 4 * g + (i >> 2);
+            const uint8_t* vtb = reinterpret_cast<const uint8_t*>(vtail);
+            s16x4_t vt = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (__attribute__((address_space(3))) s16x4_t*)(vtb + row * 256 + ((u ^ (row & 15)) * 16) + (i & 1) * 8));
+            const s16x4_t ph = *reinterpret_cast<const s16x4_t*>(pb8 + lane * 4);
+            const s16x4_t pl = *reinterpret_cast<const s16x4_t*>(pb8 + 256 + lane * 4);
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+              if (4 * g + j >= nt) vt[j] = 0;
+            o4 = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vt, ph, o4, 0, 0, 0);
+            o4 = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vt, pl, o4, 0, 0, 0);
           }
           continue;
         }

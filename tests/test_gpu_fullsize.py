@@ -2,7 +2,9 @@
 These build the 49-layer models, so each test takes tens of seconds.
 
   * int4, 8,022 resident positions: 16 greedy steps, each end to end against
-    the oracle, every 4th (and the last) layer by layer.
+    the oracle, every 4th (and the last) layer by layer; likewise 10 steps from
+    8,188 positions (the contexts cross 64 x 128 positions: two attention chunks
+    per split, the second a short tail).
   * bf16, a 2,048-token prompt through the long-chunk prefill: the prefill is
     run twice and must write bit-identical K/V and id; at sampled prompt
     positions the oracle runs one step from the GPU's cache of the earlier
@@ -33,12 +35,14 @@ def _layers(cfg):
     return {l: synth.layer(cfg, l) for l in range(cfg.n_layers)}
 
 
-def test_int4_49_decode_16_steps_at_8022_positions():
-    cfg = synth.CONFIGS["int4_49"]
+@pytest.mark.parametrize("resident,steps", [(8022, 16), (8188, 10)])
+def test_int4_49_decode_steps(resident, steps):
+    # 8,022 positions: the metric's context, one attention chunk per split.  From 8,188: the contexts
+    # cross 64 x 128 positions, where a split's second chunk is a short tail (its rows requested early)
+    cfg = synth.CONFIGS["int4_49"].replace(resident=resident)
     layers = _layers(cfg)
     print(f"{cfg.name}: building the device model", flush=True)
     model = build(cfg, layers=layers)
-    steps = 16
     cap = cfg.resident + steps + 4
     kv = model.kv(1, cap)
     orc = make_oracle(cfg, cap, layers=layers)
