@@ -487,6 +487,39 @@ __device__ __forceinline__ void compute_static(const LStage& st, const Geo& g, i
   }
 }
 
+// The same for rows of one chunk per lane, item by item as the requests land (loads complete in order:
+// item p has landed once no more than `later` plus the requests of the items after it are outstanding),
+// so that the products of the first items overlap the arrival of the last.
+template <int WT, int NIS, class OutFn>
+__device__ __forceinline__ void compute_static_stream(const LStage& st, const Geo& g, const ActRegs<WT, 1>& ar,
+                                                      OutFn outfn, int later) {
+  static_assert(NIS <= 16, "at most 16 rows per wave");
+  constexpr int R = NIS <= 1 ? 1 : NIS <= 2 ? 2 : NIS <= 4 ? 4 : NIS <= 8 ? 8 : 16;
+  constexpr int PER = WT == W_I4 ? 2 : 1;  // requests per item (weights, scales)
+  const int lane = threadIdx.x & 63;
+  const I4K k4 = i4k();
+  // this wave's items with a row (row wave + p * NW): their requests were issued, the others' not
+  const int nv = g.nrows > g.wave ? min(NIS, (g.nrows - g.wave + NW - 1) / NW) : 0;
+  float acc[R];
+#pragma unroll
+  for (int p = 0; p < R; ++p) acc[p] = 0.f;
+#pragma unroll
+  for (int p = 0; p < NIS; ++p) {
+    if (p < nv) {
+      wait_vmem_dyn(later + PER * (nv - 1 - p));
+      const uint4 w = st.w16[(p * NW + g.wave) * 64 + lane];
+      const float sc = WT == W_I4 ? chunk_scale(st.s32[(p * NW + g.wave) * 64 + lane], lane) : 1.f;
+      acc[p] = chunk_dot<WT>(w, ar.c[0], sc, k4);
+    }
+  }
+  const float v = reduce_rows<R>(acc);
+  const int rho = row_of<R>(lane);
+  if ((lane & (64 / R - 1)) == 0 && rho < NIS) {
+    const int r = g.wave + rho * NW;
+    if (r < g.nrows) outfn(r, v);
+  }
+}
+
 // Compute NIS staged items of this wave whose activation chunk depends on the
 // row (read from LDS through rowfn), any lanes per row, one chunk per lane per
 // row (static shapes): loads of a batch of NB items first, then their dot
@@ -524,21 +557,25 @@ __device__ __forceinline__ void compute_static_rows(const LStage& st, const Geo&
 
 // A staged GEMV of the static shape whose items fit one round of NIS items per wave; later: vector
 // memory operations this wave issued after the stage's DMA (they may stay in flight).
-template <int WT, int CPLR, int NIS, class RowFn, class OutFn>
+template <int WT, int CPLR, int NIS, bool STREAM = false, class RowFn, class OutFn>
 __device__ __forceinline__ void gemv_static(const LStage& st, const Geo& g, bool issued, const ActRegs<WT, CPLR>& ar,
                                             RowFn rowfn, OutFn outfn, int later = 0) {
   if (!issued) lstage_issue_static<WT, NIS>(st, g, 0, rowfn, g.wave);
-  wait_vmem_dyn(issued ? later : 0);
-  compute_static<WT, CPLR, NIS>(st, g, 0, ar, outfn);
+  if constexpr (STREAM && CPLR == 1) {
+    compute_static_stream<WT, NIS>(st, g, ar, outfn, issued ? later : 0);
+  } else {
+    wait_vmem_dyn(issued ? later : 0);
+    compute_static<WT, CPLR, NIS>(st, g, 0, ar, outfn);
+  }
 }
 
 // The single-round static path when the wave's NIS items (known at compile
 // time, 0 = not) fit the capacity CAP, else the general rounds.
-template <int WT, int CPLR, int NIS, int CAP, class RowFn, class OutFn>
+template <int WT, int CPLR, int NIS, int CAP, bool STREAM = false, class RowFn, class OutFn>
 __device__ __forceinline__ void gemv_auto(const LStage& st, const Geo& g, bool issued, const ActRegs<WT, CPLR>& ar,
                                           RowFn rowfn, OutFn outfn, int later = 0) {
   if constexpr (CPLR > 0 && NIS > 0 && NIS <= CAP && NIS / CPLR <= 16)
-    gemv_static<WT, CPLR, NIS>(st, g, issued, ar, rowfn, outfn, later);
+    gemv_static<WT, CPLR, NIS, STREAM>(st, g, issued, ar, rowfn, outfn, later);
   else
     gemv_lds<WT, CPLR>(st, g, issued, ar, rowfn, outfn);  // waits for everything (later ignored)
 }
@@ -1756,7 +1793,7 @@ __global__ void __launch_bounds__(NT, 1) decode_kernel(const KStatic* __restrict
       const auto ar = act_regs<WT, CP_GU>(ggu, sm.actA, sm.asumA);
       auto out = [&](int q, float v) { sm.ytmp[q] = v; };
       if (dense) gemv_auto<WT, CP_GU, NI_GUD, GU_CAP>(lstage(sm.u.mlp.gu), ggu, true, ar, gu_rowfn, out);
-      else gemv_auto<WT, CP_GU, NI_GUM, GU_CAP>(lstage(sm.u.mlp.gu), ggu, true, ar, gu_rowfn, out);
+      else gemv_auto<WT, CP_GU, NI_GUM, GU_CAP, true>(lstage(sm.u.mlp.gu), ggu, true, ar, gu_rowfn, out);
     }
     __syncthreads();
     // SwiGLU of this workgroup's units: fp32 one value per slot, else a bf16 pair of adjacent units
