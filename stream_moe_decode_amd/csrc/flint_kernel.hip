@@ -677,8 +677,7 @@ struct Waiter {
   bool abort;
 };
 __device__ __forceinline__ void backoff(const Waiter& wt) {
-  __builtin_amdgcn_s_sleep(1);
-  for (int z = 0; z < wt.sleep; ++z) __builtin_amdgcn_s_sleep(8);
+  for (int z = 0; z < wt.sleep; ++z) __builtin_amdgcn_s_sleep(8);  // none by default: re-poll at once
 }
 
 // Latch an error: atomically in device memory, by a plain system-scope store
@@ -689,12 +688,14 @@ __device__ __forceinline__ void raise_error(const Waiter& wt, uint32_t bits) {
 }
 
 // True once this wait should give up: another wait has timed out, or this one
-// has run for longer than the timeout (which it then reports).
-__device__ __forceinline__ bool poll_timed_out(const Waiter& wt, uint64_t t0, uint32_t it) {
+// has run for longer than the timeout (which it then reports).  t0: the clock
+// when the wait began, tn: when this round of polls was issued (both read
+// ahead of loads, so the clock's latency hides behind theirs).
+__device__ __forceinline__ bool poll_timed_out(const Waiter& wt, uint64_t t0, uint64_t tn, uint32_t it) {
   if ((it & 15) == 0 &&
       (__hip_atomic_load(gp(wt.err), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM) & ERR_TIMEOUT))
     return true;
-  if (now() - t0 > wt.limit) {
+  if (tn - t0 > wt.limit) {
     raise_error(wt, ERR_TIMEOUT);
     return true;
   }
@@ -730,12 +731,14 @@ __device__ __forceinline__ bool gather(Smem& sm, const uint64_t* src, int n, uin
   if (nsent > wt.sentinels) nsent = wt.sentinels;
   if (tid < 64 && tid < nsent && !wt.abort) {  // sentinels == 0: every thread polls its own slots at once
     const uint64_t* p = src + index(sent(tid, nsent));
+    const uint64_t t0 = now();
     if ((uint32_t)(xload(p) >> 32) != tag) {
-      const uint64_t t0 = now();
       uint32_t it = 0;
-      while ((uint32_t)(xload(p) >> 32) != tag) {
+      while (true) {
         backoff(wt);
-        if (poll_timed_out(wt, t0, ++it)) {
+        const uint64_t tn = now();
+        if ((uint32_t)(xload(p) >> 32) == tag) break;
+        if (poll_timed_out(wt, t0, tn, ++it)) {
           wt.abort = true;
           break;
         }
@@ -744,6 +747,7 @@ __device__ __forceinline__ bool gather(Smem& sm, const uint64_t* src, int n, uin
   }
   if (!sync_ok(sm, wt)) return false;
   for (int b0 = 0; b0 < n && tid < GT; b0 += 8 * GT) {
+    const uint64_t t0 = now();
     uint64_t v[8];
 #pragma unroll
     for (int k = 0; k < 8; ++k) {
@@ -755,17 +759,17 @@ __device__ __forceinline__ bool gather(Smem& sm, const uint64_t* src, int n, uin
     for (int k = 0; k < 8; ++k)
       if ((uint32_t)(v[k] >> 32) != tag) pending |= 1u << k;
     if (pending) {
-      const uint64_t t0 = now();
       uint32_t it = 0;
       while (pending) {
         backoff(wt);
+        const uint64_t tn = now();
 #pragma unroll
         for (int k = 0; k < 8; ++k)
           if (pending & (1u << k)) v[k] = xload(src + index(b0 + tid + k * GT));
 #pragma unroll
         for (int k = 0; k < 8; ++k)
           if ((pending & (1u << k)) && (uint32_t)(v[k] >> 32) == tag) pending &= ~(1u << k);
-        if (pending && poll_timed_out(wt, t0, ++it)) {
+        if (pending && poll_timed_out(wt, t0, tn, ++it)) {
           wt.abort = true;
           break;
         }
