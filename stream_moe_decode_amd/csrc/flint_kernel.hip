@@ -191,7 +191,7 @@ __device__ __forceinline__ void rmsnorm_act(Smem& sm, int H, float eps, bool sum
   float t = 0.f;
 #pragma unroll
   for (int w = 0; w < NW; ++w) t += sm.wred[half * NW + w];
-  const float inv = 1.0f / sqrtf(t / (float)H + eps);
+  const float inv = __builtin_amdgcn_rsqf(t * (1.0f / (float)H) + eps);  // the hardware reciprocal square root
   if (mine) {
     const float4 g = *reinterpret_cast<const float4*>(&sm.gn[e0]);
     const float y0 = act_round<WT>(x.x * inv * g.x), y1 = act_round<WT>(x.y * inv * g.y);
