@@ -175,10 +175,11 @@ template <int WT> __device__ __forceinline__ void act_sums(const uint32_t* act, 
 // later: vector memory operations this wave issued after the norm weights' DMA (they may stay in flight).
 // PRE: the wave sums of squares are already in sm.wred (written by the gather that brought the residual,
 // before its closing barrier), so the norm starts from them.
-template <int WT, int OW = WT, bool PRE = false>
+// WAIT = false: the caller knows the weights have landed and every wave has passed a barrier since.
+template <int WT, int OW = WT, bool PRE = false, bool WAIT = true>
 __device__ __forceinline__ void rmsnorm_act(Smem& sm, int H, float eps, bool sums, int later = 0, int half = 0) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  wait_vmem_dyn(later);
+  if constexpr (WAIT) wait_vmem_dyn(later);
   const int e0 = 4 * tid;
   const bool mine = e0 < H;
   const float4 x = mine ? *reinterpret_cast<const float4*>(&sm.xres[e0]) : make_float4(0.f, 0.f, 0.f, 0.f);
@@ -1038,7 +1039,10 @@ __global__ void __launch_bounds__(NT, 1) decode_kernel(const KStatic* __restrict
     auto o_rowfn = [&](int q) { return mrow<WT>(m_o, (long long)l * H + orb + q, QD, sm.actA, sm.asumA); };
 
     // ---------------- input RMSNorm (recomputed by every workgroup)
-    rmsnorm_act<WT, WT, true>(sm, H, ks.eps, ASUM_A, kv_later);
+    // static shape: this norm's weights were requested before the previous layer's down products, which
+    // waited for every request of each wave (the first layer's, before the loop), so the norm need not wait
+    // for the residual's publish or the requests issued since
+    rmsnorm_act<WT, WT, true, !SS>(sm, H, ks.eps, ASUM_A, kv_later);
     stampit(0);
 
     // ---------------- QKV rows (staged during the previous layer), RoPE, publish, KV append
